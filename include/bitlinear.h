@@ -1,0 +1,204 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) ternary BitLinear library.
+ *
+ * The library computes the BitNet b1.58 BitLinear forward pass over I2_S
+ * packed ternary weights:
+ *
+ *   RMSNorm of each activation row  ->  per-row absmax int8 quantisation
+ *   ->  ternary-code x int8 contraction with int32 accumulation, minus the
+ *       activation sum  ->  rescale to fp32.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [HF-38087] huggingface/transformers PR #38087 "Add optional RMSNorm
+ *              support to BitNet quantization (config + layers)", section
+ *              "What does this PR do?": RMSNorm (eps default 1e-6) is applied
+ *              to the activations before quantisation.
+ *   [CPPB-7]   eejd/cpp-bitnet PR #7 "fix: I2_S ARM kernel layout +
+ *              squared-ReLU FFN": summary bullets "I2_S NEON kernel for the
+ *              canonical layout" and "llama-quantize I2_S emits the canonical
+ *              layout", section "Known gaps", and the commit messages of the
+ *              NEON kernel and of the I2_S quantizer.
+ *
+ * Conventions shared by every entry point
+ *   - W is [N][K] row-major (K contiguous), x is fp32 [M][K] row-major, y is
+ *     fp32 [M][N] row-major, gamma is fp32 [K]; y = RMSNorm/quant(x) W^T.
+ *   - Every array pointer is a DEVICE pointer owned by the caller, except
+ *     where a parameter says "host".  The library allocates no device memory
+ *     and keeps no mutable global state; calls on different streams may run
+ *     concurrently.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failing check returns its status and enqueues nothing.  No C++
+ *     exception crosses this interface and the library never aborts.
+ *   - Preconditions checked everywhere they apply: M, N, K >= 1 and
+ *     K % 128 == 0 (rows are whole I2_S blocks, [CPPB-7] "Known gaps")
+ *     -> BL_ERR_SHAPE; non-NULL pointers -> BL_ERR_INVALID_ARG; x, y, q,
+ *     packed_w and the workspace 16-byte aligned -> BL_ERR_ALIGN.
+ *   - Sizes are limited to M*K, N*K/4 and M*N below 2^40 elements and to
+ *     M, N < 2^31 (BL_ERR_SHAPE beyond).
+ *
+ * I2_S packed weight buffer (the persistent format) [CPPB-7]
+ *   N*K/4 bytes of 2-bit codes followed by a 32-byte trailer.  Each run of
+ *   128 weights of a row (a block) takes 32 bytes: weight j of the block is
+ *   in byte j % 32, field j / 32, field g in bits (7-2g)..(6-2g).  The stored
+ *   code is w/scale + 1 (-1 -> 0, 0 -> 1, +1 -> 2); consumers subtract the
+ *   activation sum.  The trailer is the per-tensor scale (fp32, little
+ *   endian) followed by 28 zero bytes.  Row n occupies bytes
+ *   [n*K/4, (n+1)*K/4).
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BL_OK = 0,
+    BL_ERR_INVALID_ARG = 1, /* NULL pointer, bad enum, non-positive eps ...  */
+    BL_ERR_SHAPE = 2,       /* size < 1, K % 128 != 0, or too large          */
+    BL_ERR_ALIGN = 3,       /* a pointer that must be 16-byte aligned is not */
+    BL_ERR_NOT_TERNARY = 4, /* pack: input is not ternary x one scale        */
+    BL_ERR_WORKSPACE = 5,   /* workspace smaller than bitlinear_workspace_bytes */
+    BL_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed    */
+} bl_status;
+
+/* Matmul route.  Both routes return bit-identical results; the choice only
+ * affects speed.  AUTO takes the decode kernel for M <= 16 and the MFMA
+ * tile kernel above. */
+typedef enum {
+    BL_PATH_AUTO = 0,
+    BL_PATH_GEMV = 1, /* decode kernel, any M (tokens in groups of 16) */
+    BL_PATH_GEMM = 2  /* prefill tile kernel, any M                    */
+} bl_path;
+
+/* Launch options for bitlinear_forward_ex / bitlinear_matmul_i2s_ex.
+ *   path:    a bl_path value.
+ *   fuse:    forward only.  -1 = automatic; 0 = separate quantisation
+ *            kernel; 1 = RMSNorm + quantisation recomputed inside every
+ *            workgroup of the decode kernel (GEMV route only, M <= 4).
+ *   variant: 0 = automatic; otherwise an index into the route's table of
+ *            launch shapes (1..bitlinear_num_variants(path)); every variant
+ *            returns bit-identical results.
+ * Unknown values -> BL_ERR_INVALID_ARG. */
+typedef struct {
+    int32_t path;
+    int32_t fuse;
+    int32_t variant;
+    int32_t reserved; /* must be 0 */
+} bl_launch;
+
+/* Human-readable name of a status value (static string, never NULL). */
+const char *bitlinear_status_string(int status);
+
+/* Library ABI version (this header: 1). */
+int bitlinear_abi_version(void);
+
+/* Number of launch-shape variants of a route (BL_PATH_GEMV or BL_PATH_GEMM);
+ * 0 for anything else. */
+int bitlinear_num_variants(int path);
+
+/* Bytes of an I2_S buffer for an N x K tensor: N*K/4 + 32.  Returns 0 when
+ * N < 1, K < 1 or K % 128 != 0. */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Bytes of workspace bitlinear_forward needs for M rows of length K: int8
+ * q[M][K], fp32 inv[M], int32 qsum[M], each segment 256-byte aligned.
+ * Returns 0 when M < 1 or K < 1. */
+size_t bitlinear_workspace_bytes(int64_t M, int64_t K);
+
+/* I2_S packer [CPPB-7, summary bullet "llama-quantize I2_S emits the
+ * canonical layout", and "Known gaps": scale = first non-zero |w|, input
+ * must be ternary x scale, rows divisible by 128].
+ *   w:           device, fp32 [N][K]; every value must be 0 or +-s for one
+ *                finite s (-0.0 counts as 0).
+ *   packed:      device, bitlinear_packed_bytes(N, K) bytes, 16-byte aligned;
+ *                written with the codes and the trailer.
+ *   w_scale_out: HOST pointer, may be NULL; receives s (0.0f when W == 0).
+ * Synchronous: returns after the work on `stream` has finished.  Returns
+ * BL_ERR_NOT_TERNARY when two non-zero magnitudes differ or a value is not
+ * finite; `packed` is then unspecified (its trailer scale reads 0). */
+bl_status bitlinear_pack_i2s(const float *w, int64_t N, int64_t K,
+                             uint8_t *packed, float *w_scale_out, void *stream);
+
+/* Unpacker (the to_float direction of the format) [CPPB-7, NEON-kernel
+ * commit]: w_out[n][k] = (code(n,k) - 1) * s, s read from the trailer.
+ *   packed: device, as written by bitlinear_pack_i2s.
+ *   w_out:  device, fp32 [N][K], 16-byte aligned.
+ * Asynchronous on `stream`.  A stored code 3 (never written by the packer)
+ * decodes to +2*s. */
+bl_status bitlinear_unpack_i2s(const uint8_t *packed, int64_t N, int64_t K,
+                               float *w_out, void *stream);
+
+/* Reads the per-tensor scale from the trailer into *out_host (HOST pointer).
+ * Synchronous on `stream`. */
+bl_status bitlinear_read_scale(const uint8_t *packed, int64_t N, int64_t K,
+                               float *out_host, void *stream);
+
+/* BitLinear forward [HF-38087 "What does this PR do?" for the RMSNorm before
+ * quantisation; CPPB-7 NEON-kernel commit for the i2 x i8 contraction and
+ * the activation-sum offset]:
+ *   r_m    = 1 / sqrt(sum_k x[m][k]^2 / K + eps)          (fp32)
+ *   xn     = (x[m][k] * r_m) * gamma[k]                  (fp32)
+ *   inv_m  = 127 / max(max_k |xn|, 1e-5)                 (fp32)
+ *   q      = clamp(round_half_even(xn * inv_m), -128, 127)   (int8)
+ *   acc    = sum_k code(n,k) * q[m][k] - sum_k q[m][k]   (int32, exact)
+ *   y[m][n]= (float)acc * (w_scale / inv_m)              (fp32)
+ * The sum of squares is taken in one fixed order (64 partial fp32 FMA
+ * chains, chain j taking the elements k with (k/4) % 64 == j in increasing k,
+ * then a halving tree over the chains), so the int8 codes are reproducible.
+ *   x:        device fp32 [M][K]; gamma: device fp32 [K]; eps > 0 (the
+ *             pages' default is 1e-6) else BL_ERR_INVALID_ARG.
+ *   packed_w: device I2_S buffer of W[N][K]; its trailer is not read:
+ *             w_scale is the scale (from bitlinear_pack_i2s or
+ *             bitlinear_read_scale).
+ *   y:        device fp32 [M][N]; every element is written.
+ *   workspace: device, >= bitlinear_workspace_bytes(M, K) bytes, 16-byte
+ *             aligned, else BL_ERR_WORKSPACE; holds q, inv and qsum after the
+ *             call.
+ * Asynchronous on `stream`; no host synchronisation. */
+bl_status bitlinear_forward(const float *x, const uint8_t *packed_w,
+                            float w_scale, const float *gamma, float eps,
+                            int64_t M, int64_t K, int64_t N, float *y,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* bitlinear_forward with explicit launch options (NULL = automatic).  For
+ * route/launch-shape independence tests and tuning. */
+bl_status bitlinear_forward_ex(const float *x, const uint8_t *packed_w,
+                               float w_scale, const float *gamma, float eps,
+                               int64_t M, int64_t K, int64_t N, float *y,
+                               void *workspace, size_t workspace_bytes,
+                               const bl_launch *launch, void *stream);
+
+/* Stage: RMSNorm + per-row absmax int8 quantisation (the first two steps of
+ * bitlinear_forward, bit-identical to them).
+ *   q: device int8 [M][K] (16-byte aligned); inv: device fp32 [M];
+ *   qsum: device int32 [M].  Asynchronous on `stream`. */
+bl_status bitlinear_act_quant(const float *x, const float *gamma, float eps,
+                              int64_t M, int64_t K, int8_t *q, float *inv,
+                              int32_t *qsum, void *stream);
+
+/* Stage: acc[m][n] = sum_k code(n,k) * q[m][k] - qsum[m] (int32, exact).
+ * qsum is taken as given (it is sum_k q[m][k] when it comes from
+ * bitlinear_act_quant).  acc: device int32 [M][N].  Asynchronous. */
+bl_status bitlinear_matmul_i2s(const int8_t *q, const int32_t *qsum,
+                               const uint8_t *packed_w, int64_t M, int64_t K,
+                               int64_t N, int32_t *acc, void *stream);
+
+/* bitlinear_matmul_i2s with explicit launch options (NULL = automatic;
+ * `fuse` must be -1 or 0). */
+bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum,
+                                  const uint8_t *packed_w, int64_t M,
+                                  int64_t K, int64_t N, int32_t *acc,
+                                  const bl_launch *launch, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,200 @@
+"""CPU oracle of the ternary BitLinear forward path -- numpy wrapper.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by
+the benchmark's CPU-baseline leg, never by the product package.  The oracle
+and the HIP library share no code; this module never imports
+``ternary_bit_linear_amd``.
+
+The arithmetic lives in ``oracle.c`` (plain loops, fp32 where the method's
+integer decisions are taken, fp64 for the final rescale).  This wrapper
+builds it with gcc when no build is present and marshals numpy arrays.
+
+Sources: huggingface/transformers PR #38087 "Add optional RMSNorm support to
+BitNet quantization (config + layers)" (RMSNorm before quantisation, eps
+1e-6); eejd/cpp-bitnet PR #7 "fix: I2_S ARM kernel layout + squared-ReLU FFN"
+(I2_S layout, code offset, per-tensor scale, trailer, K % 128).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK = 0
+ERR_SHAPE = 2
+ERR_NOT_TERNARY = 4
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc, no fp contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+               "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        L.oracle_packed_bytes.restype = i64
+        L.oracle_packed_bytes.argtypes = [i64, i64]
+        L.oracle_pack_i2s.restype = ctypes.c_int
+        L.oracle_pack_i2s.argtypes = [p, i64, i64, p, p]
+        L.oracle_unpack_i2s.restype = ctypes.c_int
+        L.oracle_unpack_i2s.argtypes = [p, i64, i64, p]
+        L.oracle_code_at.restype = ctypes.c_int
+        L.oracle_code_at.argtypes = [p, i64, i64, i64]
+        L.oracle_read_scale.restype = ctypes.c_float
+        L.oracle_read_scale.argtypes = [p, i64, i64]
+        L.oracle_sumsq_o64.restype = ctypes.c_float
+        L.oracle_sumsq_o64.argtypes = [p, i64]
+        L.oracle_rmsnorm.restype = ctypes.c_int
+        L.oracle_rmsnorm.argtypes = [p, p, ctypes.c_float, i64, i64, p]
+        L.oracle_act_quant.restype = ctypes.c_int
+        L.oracle_act_quant.argtypes = [p, p, ctypes.c_float, i64, i64, p, p, p, p]
+        L.oracle_matmul_i2s.restype = ctypes.c_int
+        L.oracle_matmul_i2s.argtypes = [p, p, p, i64, i64, i64, p]
+        L.oracle_rescale.restype = ctypes.c_int
+        L.oracle_rescale.argtypes = [p, p, ctypes.c_float, i64, i64, p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+class OracleError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: oracle status {status}")
+        self.status = status
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib().oracle_packed_bytes(N, K))
+
+
+def pack_i2s(w: np.ndarray) -> tuple[np.ndarray, float]:
+    """fp32 W[N][K] (ternary x scale) -> (uint8[N*K/4 + 32], scale)."""
+    w = _f32(w)
+    N, K = w.shape
+    out = np.zeros(max(packed_bytes(N, K), 1), dtype=np.uint8)
+    sc = np.zeros(1, dtype=np.float32)
+    st = lib().oracle_pack_i2s(_ptr(w), N, K, _ptr(out), _ptr(sc))
+    if st != OK:
+        raise OracleError(st, "pack_i2s")
+    return out, float(sc[0])
+
+
+def unpack_i2s(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    w = np.empty((N, K), dtype=np.float32)
+    st = lib().oracle_unpack_i2s(_ptr(packed), N, K, _ptr(w))
+    if st != OK:
+        raise OracleError(st, "unpack_i2s")
+    return w
+
+
+def code_at(packed: np.ndarray, K: int, n: int, k: int) -> int:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    return int(lib().oracle_code_at(_ptr(packed), K, n, k))
+
+
+def read_scale(packed: np.ndarray, N: int, K: int) -> float:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    return float(lib().oracle_read_scale(_ptr(packed), N, K))
+
+
+def sumsq_o64(v: np.ndarray) -> np.float32:
+    v = _f32(v).ravel()
+    return np.float32(lib().oracle_sumsq_o64(_ptr(v), v.size))
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    x = _f32(np.atleast_2d(x))
+    gamma = _f32(gamma)
+    M, K = x.shape
+    xn = np.empty_like(x)
+    st = lib().oracle_rmsnorm(_ptr(x), _ptr(gamma), ctypes.c_float(eps), M, K, _ptr(xn))
+    if st != OK:
+        raise OracleError(st, "rmsnorm")
+    return xn
+
+
+def act_quant(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-6):
+    """-> (q int8[M][K], inv fp32[M], qsum int32[M])."""
+    x = _f32(np.atleast_2d(x))
+    gamma = _f32(gamma)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.int8)
+    inv = np.empty(M, dtype=np.float32)
+    qsum = np.empty(M, dtype=np.int32)
+    xn = np.empty((M, K), dtype=np.float32)
+    st = lib().oracle_act_quant(_ptr(x), _ptr(gamma), ctypes.c_float(eps), M, K,
+                                _ptr(q), _ptr(inv), _ptr(qsum), _ptr(xn))
+    if st != OK:
+        raise OracleError(st, "act_quant")
+    return q, inv, qsum
+
+
+def matmul_i2s(q: np.ndarray, qsum: np.ndarray, packed: np.ndarray, N: int) -> np.ndarray:
+    """-> acc int32[M][N] = sum_k code(n,k) q[m,k] - qsum[m]."""
+    q = np.ascontiguousarray(np.atleast_2d(q), dtype=np.int8)
+    qsum = np.ascontiguousarray(qsum, dtype=np.int32)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    M, K = q.shape
+    acc = np.empty((M, N), dtype=np.int32)
+    st = lib().oracle_matmul_i2s(_ptr(q), _ptr(qsum), _ptr(packed), M, K, N, _ptr(acc))
+    if st != OK:
+        raise OracleError(st, "matmul_i2s")
+    return acc
+
+
+def rescale(acc: np.ndarray, inv: np.ndarray, w_scale: float) -> np.ndarray:
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    inv = _f32(inv)
+    M, N = acc.shape
+    y = np.empty((M, N), dtype=np.float64)
+    st = lib().oracle_rescale(_ptr(acc), _ptr(inv), ctypes.c_float(w_scale), M, N, _ptr(y))
+    if st != OK:
+        raise OracleError(st, "rescale")
+    return y
+
+
+def forward(x: np.ndarray, packed: np.ndarray, w_scale: float, gamma: np.ndarray,
+            eps: float, N: int) -> np.ndarray:
+    """Whole forward; returns fp64 y[M][N]."""
+    q, inv, qsum = act_quant(x, gamma, eps)
+    acc = matmul_i2s(q, qsum, packed, N)
+    return rescale(acc, inv, w_scale)
+
+
+def packed_rows(packed: np.ndarray, K: int, rows) -> np.ndarray:
+    """Packed bytes of the selected weight rows (rows are contiguous K/4-byte
+    runs when K % 128 == 0), with a zero trailer, for sampled checks."""
+    rows = np.asarray(rows, dtype=np.int64)
+    rb = K // 4
+    idx = (rows[:, None] * rb + np.arange(rb)[None, :]).ravel()
+    out = np.zeros(rows.size * rb + 32, dtype=np.uint8)
+    out[: rows.size * rb] = np.asarray(packed)[idx]
+    return out

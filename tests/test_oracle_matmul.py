@@ -1,0 +1,134 @@
+"""Pins of the oracle's ternary x int8 contraction and rescale.
+
+Page: eejd/cpp-bitnet PR #7 "fix: I2_S ARM kernel layout + squared-ReLU FFN",
+NEON-kernel commit: stored codes are not -1/0/+1 and the caller subtracts the
+activation sum; the prompt-processing GEMM must write every output.
+
+The contraction is exact integer arithmetic, so the brute-force checks below
+take the ternary pattern t the weights were drawn from (never the packed
+bytes) and compare exactly.
+"""
+import numpy as np
+import pytest
+
+from ternary_bit_linear_amd import workloads as wl
+
+
+def brute_acc(q, t):
+    """sum_k t[n][k] * q[m][k] in int64, from the ternary pattern."""
+    return q.astype(np.int64) @ t.astype(np.int64).T
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (3, 128, 8), (2, 256, 5), (5, 384, 7),
+                                   (1, 1024, 33)])
+def test_brute_force_tiny(orc, M, K, N):
+    x = wl.activations(11 + M, M, K)
+    w, t = wl.ternary(12 + N, N, K, 1 / 3, 0.02)
+    g = wl.gamma(13, K, "u0.8-1.2")
+    packed, s = orc.pack_i2s(w)
+    q, inv, qsum = orc.act_quant(x, g, 1e-6)
+    acc = orc.matmul_i2s(q, qsum, packed, N)
+    assert np.array_equal(acc.astype(np.int64), brute_acc(q, t))
+    y = orc.forward(x, packed, s, g, 1e-6, N)
+    # fp64 from the dequantised operands: y = sum_k (q/inv) * (t*s)
+    y64 = (q.astype(np.float64) / inv.astype(np.float64)[:, None]) @ (t.astype(np.float64) * s).T
+    assert np.allclose(y, y64, rtol=1e-12, atol=1e-300)
+
+
+def test_offset_identity_every_pattern(orc):
+    """sum c*q - sum q == sum (c-1)*q for every code pattern of a block,
+    and the 'double correction' (codes read as -1/0/+1 AND the sum
+    subtracted) is wrong."""
+    rng = np.random.default_rng(1)
+    K = 128
+    q = rng.integers(-128, 128, (1, K)).astype(np.int8)
+    qsum = q.astype(np.int32).sum(axis=1)
+    for trial in range(40):
+        t = rng.integers(-1, 2, (4, K)).astype(np.int8)
+        packed, _ = orc.pack_i2s(t.astype(np.float32))
+        acc = orc.matmul_i2s(q, qsum, packed, 4)
+        truth = brute_acc(q, t)
+        assert np.array_equal(acc.astype(np.int64), truth)
+        double = truth - qsum[:, None]
+        if qsum[0] != 0:
+            assert not np.array_equal(acc.astype(np.int64), double)
+
+
+def test_zero_weights(orc):
+    x = wl.activations(21, 3, 256)
+    g = np.ones(256, np.float32)
+    packed, s = orc.pack_i2s(np.zeros((4, 256), np.float32))
+    assert s == 0.0
+    y = orc.forward(x, packed, s, g, 1e-6, 4)
+    assert np.all(y == 0)
+    q, inv, qsum = orc.act_quant(x, g, 1e-6)
+    assert np.all(orc.matmul_i2s(q, qsum, packed, 4) == 0)
+
+
+def test_identity_weights(orc):
+    """W = s I (N = K): acc[m][n] = q[m][n]."""
+    K = 256
+    x = wl.activations(22, 4, K)
+    g = wl.gamma(23, K, "u0.8-1.2")
+    packed, s = orc.pack_i2s(np.eye(K, dtype=np.float32) * np.float32(0.5))
+    q, inv, qsum = orc.act_quant(x, g, 1e-6)
+    acc = orc.matmul_i2s(q, qsum, packed, K)
+    assert np.array_equal(acc, q.astype(np.int32))
+    y = orc.rescale(acc, inv, s)
+    assert np.array_equal(y, q.astype(np.float64) * (0.5 / inv.astype(np.float64))[:, None])
+
+
+def test_all_plus_one(orc):
+    K = 384
+    x = wl.activations(24, 3, K)
+    g = np.ones(K, np.float32)
+    packed, _ = orc.pack_i2s(np.ones((6, K), np.float32))
+    q, inv, qsum = orc.act_quant(x, g, 1e-6)
+    acc = orc.matmul_i2s(q, qsum, packed, 6)
+    assert np.all(acc == qsum[:, None])
+
+
+def test_sign_symmetry(orc):
+    M, K, N = 3, 256, 9
+    x = wl.activations(25, M, K)
+    w, _ = wl.ternary(26, N, K, 0.4, 0.015)
+    g = wl.gamma(27, K, "u0.8-1.2")
+    p, s = orc.pack_i2s(w)
+    pn, sn = orc.pack_i2s(-w)
+    y = orc.forward(x, p, s, g, 1e-6, N)
+    assert np.array_equal(orc.forward(x, pn, sn, g, 1e-6, N), -y)
+    assert np.array_equal(orc.forward(-x, p, s, g, 1e-6, N), -y)
+
+
+def test_rows_independent(orc):
+    M, K, N = 5, 256, 6
+    x = wl.activations(28, M, K)
+    w, _ = wl.ternary(29, N, K, 1 / 3, 0.02)
+    g = wl.gamma(30, K, "u0.8-1.2")
+    p, s = orc.pack_i2s(w)
+    y = orc.forward(x, p, s, g, 1e-6, N)
+    for m in range(M):
+        assert np.array_equal(orc.forward(x[m:m + 1], p, s, g, 1e-6, N), y[m:m + 1])
+
+
+def test_accumulator_bounds():
+    """|acc| <= 127 * K and sum c*q <= 2 * 128 * K stay inside int32 for the
+    largest row length used (K = 28672)."""
+    K = 28672
+    assert 127 * K < 2 ** 31 and 2 * 128 * K + 128 * K < 2 ** 31
+    assert 128 * K < 2 ** 24  # (float)acc is exact
+
+
+def test_packed_rows_sampling(orc):
+    """Sampled checks use the rows of the packed buffer: the contraction of a
+    row subset equals the same rows of the full result."""
+    M, K, N = 2, 256, 12
+    x = wl.activations(31, M, K)
+    w, _ = wl.ternary(32, N, K, 1 / 3, 0.02)
+    g = np.ones(K, np.float32)
+    p, s = orc.pack_i2s(w)
+    q, inv, qsum = orc.act_quant(x, g, 1e-6)
+    full = orc.matmul_i2s(q, qsum, p, N)
+    rows = [0, 5, 11]
+    sub = orc.matmul_i2s(q, qsum, orc.packed_rows(p, K, rows), len(rows))
+    assert np.array_equal(sub, full[:, rows])
