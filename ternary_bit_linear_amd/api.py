@@ -1,0 +1,211 @@
+"""Python binding of ``libbitlinear.so`` (the C ABI in ``include/bitlinear.h``).
+
+Argument marshalling only: every step of the BitLinear path runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory (tensors are
+allocated here and their pointers passed down) and the stream
+(``torch.cuda.current_stream()``).  There is no fallback: if the library is
+missing, loading it raises.
+
+Functions mirror the C entry points: :func:`pack_i2s`, :func:`unpack_i2s`,
+:func:`read_scale`, :func:`forward`, :func:`act_quant`, :func:`matmul_i2s`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_NOT_TERNARY, ERR_WORKSPACE, ERR_HIP = range(7)
+PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+
+# Every symbol the header declares, with (restype, argtypes).
+_i64, _p, _f, _i, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+
+
+class Launch(ctypes.Structure):
+    """bl_launch: path (bl_path), fuse (-1/0/1), variant (0 = auto)."""
+    _fields_ = [("path", ctypes.c_int32), ("fuse", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+SIGNATURES = {
+    "bitlinear_status_string": (ctypes.c_char_p, [_i]),
+    "bitlinear_abi_version": (_i, []),
+    "bitlinear_num_variants": (_i, [_i]),
+    "bitlinear_packed_bytes": (_sz, [_i64, _i64]),
+    "bitlinear_workspace_bytes": (_sz, [_i64, _i64]),
+    "bitlinear_pack_i2s": (_i, [_p, _i64, _i64, _p, _p, _p]),
+    "bitlinear_unpack_i2s": (_i, [_p, _i64, _i64, _p, _p]),
+    "bitlinear_read_scale": (_i, [_p, _i64, _i64, _p, _p]),
+    "bitlinear_forward": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p, _sz, _p]),
+    "bitlinear_forward_ex": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p, _sz,
+                                  ctypes.POINTER(Launch), _p]),
+    "bitlinear_act_quant": (_i, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
+    "bitlinear_matmul_i2s": (_i, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
+    "bitlinear_matmul_i2s_ex": (_i, [_p, _p, _p, _i64, _i64, _i64, _p,
+                                     ctypes.POINTER(Launch), _p]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m ternary_bit_linear_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib().bitlinear_status_string(status).decode()
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise BitLinearError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _launch(path, fuse, variant):
+    if path == PATH_AUTO and fuse == -1 and variant == 0:
+        return None
+    return ctypes.byref(Launch(path, fuse, variant, 0))
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib().bitlinear_packed_bytes(N, K))
+
+
+def workspace_bytes(M: int, K: int) -> int:
+    return int(lib().bitlinear_workspace_bytes(M, K))
+
+
+def num_variants(path: int) -> int:
+    return int(lib().bitlinear_num_variants(path))
+
+
+def pack_i2s(w):
+    """fp32 W[N][K] (ternary x scale, on the GPU) -> (uint8 packed tensor of
+    N*K/4 + 32 bytes, scale).  Synchronous."""
+    torch = _torch()
+    N, K = w.shape
+    nb = packed_bytes(N, K)
+    if nb == 0:
+        raise BitLinearError(ERR_SHAPE, "pack_i2s")
+    packed = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    sc = ctypes.c_float(0.0)
+    _check(lib().bitlinear_pack_i2s(_dev(w, torch.float32, "w"), N, K,
+                                    ctypes.c_void_p(packed.data_ptr()),
+                                    ctypes.byref(sc), _stream()), "pack_i2s")
+    return packed, sc.value
+
+
+def unpack_i2s(packed, N: int, K: int):
+    torch = _torch()
+    w = torch.empty((N, K), dtype=torch.float32, device=packed.device)
+    _check(lib().bitlinear_unpack_i2s(_dev(packed, torch.uint8, "packed"), N, K,
+                                      ctypes.c_void_p(w.data_ptr()), _stream()), "unpack_i2s")
+    return w
+
+
+def read_scale(packed, N: int, K: int) -> float:
+    torch = _torch()
+    v = ctypes.c_float(0.0)
+    _check(lib().bitlinear_read_scale(_dev(packed, torch.uint8, "packed"), N, K,
+                                      ctypes.byref(v), _stream()), "read_scale")
+    return v.value
+
+
+def act_quant(x, gamma, eps: float = 1e-6):
+    """-> (q int8 [M][K], inv fp32 [M], qsum int32 [M])."""
+    torch = _torch()
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    inv = torch.empty(M, dtype=torch.float32, device=x.device)
+    qsum = torch.empty(M, dtype=torch.int32, device=x.device)
+    _check(lib().bitlinear_act_quant(_dev(x, torch.float32, "x"), _dev(gamma, torch.float32, "gamma"),
+                                     eps, M, K, ctypes.c_void_p(q.data_ptr()),
+                                     ctypes.c_void_p(inv.data_ptr()),
+                                     ctypes.c_void_p(qsum.data_ptr()), _stream()), "act_quant")
+    return q, inv, qsum
+
+
+def matmul_i2s(q, qsum, packed, N: int, path: int = PATH_AUTO, variant: int = 0):
+    """-> acc int32 [M][N] = sum_k code(n,k) q[m,k] - qsum[m]."""
+    torch = _torch()
+    M, K = q.shape
+    acc = torch.empty((M, N), dtype=torch.int32, device=q.device)
+    _check(lib().bitlinear_matmul_i2s_ex(_dev(q, torch.int8, "q"), _dev(qsum, torch.int32, "qsum"),
+                                         _dev(packed, torch.uint8, "packed"), M, K, N,
+                                         ctypes.c_void_p(acc.data_ptr()),
+                                         _launch(path, -1, variant), _stream()), "matmul_i2s")
+    return acc
+
+
+def new_workspace(M: int, K: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(workspace_bytes(M, K), dtype=torch.uint8, device=device)
+
+
+def forward(x, packed, w_scale: float, gamma, eps: float = 1e-6, N: int | None = None,
+            out=None, workspace=None, path: int = PATH_AUTO, fuse: int = -1, variant: int = 0):
+    """y = BitLinear(x) with I2_S weights; x fp32 [M][K] -> y fp32 [M][N]."""
+    torch = _torch()
+    M, K = x.shape
+    if N is None:
+        N = (packed.numel() - 32) * 4 // K
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(M, K, x.device)
+    _check(lib().bitlinear_forward_ex(
+        _dev(x, torch.float32, "x"), _dev(packed, torch.uint8, "packed"), w_scale,
+        _dev(gamma, torch.float32, "gamma"), eps, M, K, N, _dev(out, torch.float32, "out"),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _launch(path, fuse, variant), _stream()), "forward")
+    return out
+
+
+def workspace_views(workspace, M: int, K: int):
+    """(q, inv, qsum) views of a forward workspace (for inspection)."""
+    torch = _torch()
+    a = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    q = workspace[: M * K].view(torch.int8).view(M, K)
+    o = a(M * K)
+    inv = workspace[o: o + 4 * M].view(torch.float32)
+    o += a(4 * M)
+    qsum = workspace[o: o + 4 * M].view(torch.int32)
+    return q, inv, qsum

@@ -1,0 +1,250 @@
+// api.hip -- the exported C ABI (declared in include/bitlinear.h): host-side
+// argument validation, workspace carving and route dispatch.  Every check
+// runs before anything is enqueued; no exception leaves this file.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/bitlinear.h"
+#include "common.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int kGemvMaxM = 16;   // AUTO: decode route up to 16 tokens
+constexpr int kFuseMaxM = 4;    // fused norm + quant inside the decode kernel
+constexpr int64_t kFuseMaxLds = 32 * 1024;  // M*K bytes of LDS for the fused decode kernel
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+bl_status check_mk(int64_t M, int64_t K) {
+    if (M < 1 || K < 1 || K % bl::kBlockWeights != 0) return BL_ERR_SHAPE;
+    if (M > kMaxDim || K > kMaxDim || M * K >= kMaxElems) return BL_ERR_SHAPE;
+    return BL_OK;
+}
+
+bl_status check_nk(int64_t N, int64_t K) {
+    if (N < 1 || K < 1 || K % bl::kBlockWeights != 0) return BL_ERR_SHAPE;
+    if (N > kMaxDim || K > kMaxDim || N * K >= kMaxElems) return BL_ERR_SHAPE;
+    // grids of the pack kernels: N*K/64 chunks in 256-thread blocks
+    if ((N * (K / 64) + 255) / 256 > kMaxDim) return BL_ERR_SHAPE;
+    return BL_OK;
+}
+
+bl_status check_mn(int64_t M, int64_t N) {
+    if (M * N >= kMaxElems) return BL_ERR_SHAPE;
+    return BL_OK;
+}
+
+bl_status check_launch(const bl_launch *l, bool forward) {
+    if (!l) return BL_OK;
+    if (l->path < BL_PATH_AUTO || l->path > BL_PATH_GEMM) return BL_ERR_INVALID_ARG;
+    if (l->fuse < -1 || l->fuse > 1 || (!forward && l->fuse == 1)) return BL_ERR_INVALID_ARG;
+    if (l->reserved != 0) return BL_ERR_INVALID_ARG;
+    if (l->variant < 0) return BL_ERR_INVALID_ARG;
+    if (l->variant > 0) {
+        const int path = l->path == BL_PATH_AUTO ? 0 : l->path;
+        if (path == 0) return BL_ERR_INVALID_ARG;  // a variant needs an explicit route
+        const int nv = path == BL_PATH_GEMV ? bl::gemv_num_variants() : bl::gemm_num_variants();
+        if (l->variant > nv) return BL_ERR_INVALID_ARG;
+    }
+    return BL_OK;
+}
+
+inline bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+struct Workspace {
+    int8_t *q;
+    float *inv;
+    int32_t *qsum;
+};
+
+Workspace carve(void *ws, int64_t M, int64_t K) {
+    uint8_t *p = static_cast<uint8_t *>(ws);
+    Workspace w;
+    w.q = reinterpret_cast<int8_t *>(p);
+    p += align256((size_t)(M * K));
+    w.inv = reinterpret_cast<float *>(p);
+    p += align256((size_t)M * 4);
+    w.qsum = reinterpret_cast<int32_t *>(p);
+    return w;
+}
+
+// Shared tail of forward / matmul: route choice and launch of the
+// contraction, with y (rescale epilogue) or acc (int32 epilogue).
+bl_status run_contraction(const float *x, const float *gamma, float eps,
+                          const int8_t *q, const float *inv, const int32_t *qsum,
+                          const uint8_t *packed, float w_scale, int64_t M, int64_t K,
+                          int64_t N, float *y, int32_t *acc, bool fused,
+                          const bl_launch *l, hipStream_t s) {
+    int path = l ? l->path : BL_PATH_AUTO;
+    if (path == BL_PATH_AUTO) path = (M <= kGemvMaxM) ? BL_PATH_GEMV : BL_PATH_GEMM;
+    const int variant = l ? l->variant : 0;
+    if (path == BL_PATH_GEMV) {
+        if (!fused && (M + 15) / 16 > 65535) return BL_ERR_SHAPE;
+        return hip_status(bl::launch_gemv(x, gamma, eps, q, inv, qsum, packed, w_scale, M, K,
+                                          N, y, acc, fused, variant, s));
+    }
+    if ((M + 63) / 64 > 65535) return BL_ERR_SHAPE;
+    return hip_status(bl::launch_gemm(q, inv, qsum, packed, w_scale, M, K, N, y, acc, variant, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bitlinear_status_string(int status) {
+    switch (status) {
+        case BL_OK: return "BL_OK";
+        case BL_ERR_INVALID_ARG: return "BL_ERR_INVALID_ARG: invalid argument";
+        case BL_ERR_SHAPE: return "BL_ERR_SHAPE: size < 1, K % 128 != 0, or too large";
+        case BL_ERR_ALIGN: return "BL_ERR_ALIGN: pointer not 16-byte aligned";
+        case BL_ERR_NOT_TERNARY: return "BL_ERR_NOT_TERNARY: weights are not ternary x one scale";
+        case BL_ERR_WORKSPACE: return "BL_ERR_WORKSPACE: workspace too small";
+        case BL_ERR_HIP: return "BL_ERR_HIP: HIP runtime or launch failure";
+        default: return "unknown bitlinear status";
+    }
+}
+
+int bitlinear_abi_version(void) { return 1; }
+
+int bitlinear_num_variants(int path) {
+    if (path == BL_PATH_GEMV) return bl::gemv_num_variants();
+    if (path == BL_PATH_GEMM) return bl::gemm_num_variants();
+    return 0;
+}
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+    if (check_nk(N, K) != BL_OK) return 0;
+    return (size_t)(N * (K / 4)) + bl::kTrailerBytes;
+}
+
+size_t bitlinear_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim || M * K >= kMaxElems) return 0;
+    return align256((size_t)(M * K)) + align256((size_t)M * 4) + align256((size_t)M * 4);
+}
+
+bl_status bitlinear_pack_i2s(const float *w, int64_t N, int64_t K, uint8_t *packed,
+                             float *w_scale_out, void *stream) {
+    if (bl_status st = check_nk(N, K)) return st;
+    if (!w || !packed) return BL_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(packed)) return BL_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    uint8_t *trailer = packed + N * (K / 4);
+    if (bl::launch_pack_init(trailer, s) != hipSuccess) return BL_ERR_HIP;
+    if (bl::launch_pack_scan(w, N, K, packed, s) != hipSuccess) return BL_ERR_HIP;
+    uint32_t stats[2] = {0u, 0u};
+    if (hipMemcpyAsync(stats, trailer, sizeof stats, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return BL_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return BL_ERR_HIP;
+    const uint32_t mn = stats[0], mx = stats[1];
+    bl_status st = BL_OK;
+    float scale = 0.0f;
+    if (mx == 0u) {
+        scale = 0.0f;  // W == 0: every code 1
+    } else if (mn != mx || mx >= 0x7f800000u) {
+        st = BL_ERR_NOT_TERNARY;  // two magnitudes, or inf / NaN
+    } else {
+        std::memcpy(&scale, &mx, sizeof scale);
+    }
+    if (bl::launch_pack_finalize(trailer, scale, s) != hipSuccess) return BL_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return BL_ERR_HIP;
+    if (st == BL_OK && w_scale_out) *w_scale_out = scale;
+    return st;
+}
+
+bl_status bitlinear_unpack_i2s(const uint8_t *packed, int64_t N, int64_t K, float *w_out,
+                               void *stream) {
+    if (bl_status st = check_nk(N, K)) return st;
+    if (!packed || !w_out) return BL_ERR_INVALID_ARG;
+    if (!aligned16(packed) || !aligned16(w_out)) return BL_ERR_ALIGN;
+    return hip_status(bl::launch_unpack(packed, N, K, w_out, as_stream(stream)));
+}
+
+bl_status bitlinear_read_scale(const uint8_t *packed, int64_t N, int64_t K, float *out_host,
+                               void *stream) {
+    if (bl_status st = check_nk(N, K)) return st;
+    if (!packed || !out_host) return BL_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    float v = 0.0f;
+    if (hipMemcpyAsync(&v, packed + N * (K / 4), sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return BL_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return BL_ERR_HIP;
+    *out_host = v;
+    return BL_OK;
+}
+
+bl_status bitlinear_act_quant(const float *x, const float *gamma, float eps, int64_t M,
+                              int64_t K, int8_t *q, float *inv, int32_t *qsum, void *stream) {
+    if (bl_status st = check_mk(M, K)) return st;
+    if (!x || !gamma || !q || !inv || !qsum) return BL_ERR_INVALID_ARG;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return BL_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(q)) return BL_ERR_ALIGN;
+    return hip_status(bl::launch_act_quant(x, gamma, eps, M, K, q, inv, qsum, as_stream(stream)));
+}
+
+bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum, const uint8_t *packed_w,
+                                  int64_t M, int64_t K, int64_t N, int32_t *acc,
+                                  const bl_launch *launch, void *stream) {
+    if (bl_status st = check_mk(M, K)) return st;
+    if (bl_status st = check_nk(N, K)) return st;
+    if (bl_status st = check_mn(M, N)) return st;
+    if (!q || !qsum || !packed_w || !acc) return BL_ERR_INVALID_ARG;
+    if (bl_status st = check_launch(launch, false)) return st;
+    if (!aligned16(q) || !aligned16(packed_w)) return BL_ERR_ALIGN;
+    return run_contraction(nullptr, nullptr, 0.0f, q, nullptr, qsum, packed_w, 0.0f, M, K, N,
+                           nullptr, acc, false, launch, as_stream(stream));
+}
+
+bl_status bitlinear_matmul_i2s(const int8_t *q, const int32_t *qsum, const uint8_t *packed_w,
+                               int64_t M, int64_t K, int64_t N, int32_t *acc, void *stream) {
+    return bitlinear_matmul_i2s_ex(q, qsum, packed_w, M, K, N, acc, nullptr, stream);
+}
+
+bl_status bitlinear_forward_ex(const float *x, const uint8_t *packed_w, float w_scale,
+                               const float *gamma, float eps, int64_t M, int64_t K, int64_t N,
+                               float *y, void *workspace, size_t workspace_bytes,
+                               const bl_launch *launch, void *stream) {
+    if (bl_status st = check_mk(M, K)) return st;
+    if (bl_status st = check_nk(N, K)) return st;
+    if (bl_status st = check_mn(M, N)) return st;
+    if (!x || !packed_w || !gamma || !y || !workspace) return BL_ERR_INVALID_ARG;
+    if (!(eps > 0.0f) || !std::isfinite(eps) || !std::isfinite(w_scale)) return BL_ERR_INVALID_ARG;
+    if (bl_status st = check_launch(launch, true)) return st;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(packed_w) || !aligned16(y) ||
+        !aligned16(workspace))
+        return BL_ERR_ALIGN;
+    if (workspace_bytes < bitlinear_workspace_bytes(M, K)) return BL_ERR_WORKSPACE;
+
+    const int path = launch ? launch->path : BL_PATH_AUTO;
+    const bool gemv = path == BL_PATH_GEMV || (path == BL_PATH_AUTO && M <= kGemvMaxM);
+    const bool fits = M <= kFuseMaxM && M * K <= kFuseMaxLds;
+    bool fused;
+    if (!launch || launch->fuse == -1)
+        fused = gemv && fits;
+    else
+        fused = launch->fuse == 1;
+    if (fused && !(gemv && fits)) return BL_ERR_INVALID_ARG;
+
+    hipStream_t s = as_stream(stream);
+    const Workspace ws = carve(workspace, M, K);
+    if (!fused) {
+        if (bl::launch_act_quant(x, gamma, eps, M, K, ws.q, ws.inv, ws.qsum, s) != hipSuccess)
+            return BL_ERR_HIP;
+    }
+    return run_contraction(x, gamma, eps, ws.q, ws.inv, ws.qsum, packed_w, w_scale, M, K, N, y,
+                           nullptr, fused, launch, s);
+}
+
+bl_status bitlinear_forward(const float *x, const uint8_t *packed_w, float w_scale,
+                            const float *gamma, float eps, int64_t M, int64_t K, int64_t N,
+                            float *y, void *workspace, size_t workspace_bytes, void *stream) {
+    return bitlinear_forward_ex(x, packed_w, w_scale, gamma, eps, M, K, N, y, workspace,
+                                workspace_bytes, nullptr, stream);
+}
+
+}  // extern "C"

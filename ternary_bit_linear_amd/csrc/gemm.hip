@@ -1,0 +1,176 @@
+// gemm.hip -- prefill route of the ternary x int8 contraction (gfx950).
+//
+// acc[m][n] = sum_k code(n, k) * q[m][k] - qsum[m], then optionally
+// y[m][n] = (float)acc * (w_scale / inv[m]).
+// [eejd/cpp-bitnet PR #7 "fix: I2_S ARM kernel layout + squared-ReLU FFN":
+// the prompt-processing GEMM over I2_S codes and int8 activations, which
+// must write every output; codes offset by the activation sum.]
+//
+// Design.  A workgroup owns a BM x BN output tile (tokens x weight rows) and
+// walks K in steps of 256 (two I2_S blocks).  Per step the int8 activation
+// tile (BM x 256) is staged in LDS with coalesced 16-byte loads (rows padded
+// to 272 bytes so the 16 lanes of an MFMA row-group hit distinct banks);
+// the packed weights go straight from global memory to registers -- one
+// 16-byte load per lane per 16 weight rows, i.e. 64 weights -- and are
+// expanded there by shift+mask into the int8 B operand of
+// v_mfma_i32_16x16x64_i8 (codes 0/1/2; the activation sum is subtracted in
+// the epilogue).  Each wave computes a (BM/WM) x (BN/WN) sub-tile with
+// int32 accumulators in registers.
+#include "common.hpp"
+
+namespace bl {
+namespace {
+
+constexpr int kLdsRow = kStepK + 16;  // padded LDS row of the activation tile
+
+template <int BM, int BN, int WM, int WN, bool OUT_Y>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ inv,
+    const int32_t *__restrict__ qsum, const uint8_t *__restrict__ packed,
+    float w_scale, int M, int K, int N, float *__restrict__ y,
+    int32_t *__restrict__ acc_out) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int MI = TM / 16, NI = TN / 16;
+    constexpr int CHUNKS = BM * (kStepK / 16);  // 16-byte chunks of the A tile
+    static_assert(CHUNKS % NT == 0, "A tile chunks per thread");
+    __shared__ __align__(16) int8_t a_lds[BM * kLdsRow];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+    const int j = lane & 15, kg = lane >> 4;
+    const int m0 = blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN;
+
+    const int nsteps = (K + kStepK - 1) / kStepK;
+    const int nblocks = K / kBlockWeights;
+    const size_t rowbytes = (size_t)K / 4;
+
+    const uint8_t *brow[NI];
+    bool bval[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+        const int n = n0 + wn * TN + 16 * ni + j;
+        bval[ni] = n < N;
+        brow[ni] = packed + (size_t)(bval[ni] ? n : 0) * rowbytes + 16 * kg;
+    }
+
+    v4i acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4i{0, 0, 0, 0};
+
+    for (int s = 0; s < nsteps; ++s) {
+        // Stage the activation tile.
+#pragma unroll
+        for (int c = 0; c < CHUNKS / NT; ++c) {
+            const int idx = tid + c * NT;
+            const int row = idx / (kStepK / 16);
+            const int col = (idx % (kStepK / 16)) * 16;
+            const int m = m0 + row;
+            const int k = s * kStepK + col;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (m < M && k < K) v = *reinterpret_cast<const uint4 *>(q + (size_t)m * K + k);
+            *reinterpret_cast<uint4 *>(a_lds + row * kLdsRow + col) = v;
+        }
+        // Packed weights of this step, straight to registers.
+        const bool kv = 2 * s + (kg >> 1) < nblocks;
+        uint4 b[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+            b[ni] = (kv && bval[ni]) ? *reinterpret_cast<const uint4 *>(brow[ni] + (size_t)s * kStepBytes)
+                                     : make_uint4(0, 0, 0, 0);
+        __syncthreads();
+        const int koff = (kg >> 1) * kBlockWeights + 16 * (kg & 1);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            v4i bf[NI];
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) bf[ni] = unpack_field(b[ni], g);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const v4i a = *reinterpret_cast<const v4i *>(
+                    a_lds + (wm * TM + 16 * mi + j) * kLdsRow + koff + 32 * g);
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16(a, bf[ni], acc[mi][ni]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: D(i, j) of a 16x16 tile is lane j + 16*(i/4), register i%4.
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = m0 + wm * TM + 16 * mi + 4 * kg + c;
+            if (m >= M) continue;
+            const int qs = qsum[m];
+            const float sc = OUT_Y ? (w_scale / inv[m]) : 0.0f;
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int n = n0 + wn * TN + 16 * ni + j;
+                if (n >= N) continue;
+                const int v = acc[mi][ni][c] - qs;
+                if (OUT_Y)
+                    y[(size_t)m * N + n] = (float)v * sc;
+                else
+                    acc_out[(size_t)m * N + n] = v;
+            }
+        }
+    }
+}
+
+struct Tile {
+    int BM, BN, WM, WN;
+};
+// Launch-shape table; every entry computes bit-identical results.
+constexpr Tile kTiles[] = {{128, 128, 2, 2}, {64, 128, 1, 4}, {128, 64, 2, 2},
+                           {64, 64, 2, 2},   {256, 128, 4, 2}};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_tile(const int8_t *q, const float *inv, const int32_t *qsum,
+                       const uint8_t *packed, float w_scale, int64_t M, int64_t K,
+                       int64_t N, float *y, int32_t *acc, hipStream_t s) {
+    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+    const dim3 block(WM * WN * 64);
+    if (y)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true>), grid, block, 0, s, q, inv,
+                           qsum, packed, w_scale, (int)M, (int)K, (int)N, y, acc);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false>), grid, block, 0, s, q, inv,
+                           qsum, packed, w_scale, (int)M, (int)K, (int)N, y, acc);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_num_variants() { return kNumTiles; }
+
+hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
+                       const uint8_t *packed, float w_scale, int64_t M,
+                       int64_t K, int64_t N, float *y, int32_t *acc,
+                       int variant, hipStream_t s) {
+    int v = variant;
+    if (v <= 0) v = 1;
+#define BL_GEMM_CASE(idx)                                                           \
+    case idx:                                                                       \
+        return launch_tile<kTiles[idx - 1].BM, kTiles[idx - 1].BN, kTiles[idx - 1].WM, \
+                           kTiles[idx - 1].WN>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+    switch (v) {
+        BL_GEMM_CASE(1)
+        BL_GEMM_CASE(2)
+        BL_GEMM_CASE(3)
+        BL_GEMM_CASE(4)
+        BL_GEMM_CASE(5)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef BL_GEMM_CASE
+}
+
+}  // namespace bl

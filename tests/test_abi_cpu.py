@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports every symbol the header declares, and
+rejects bad arguments on the host before touching the GPU (no device is
+needed: every call below fails validation, so nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ternary_bit_linear_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+F = ctypes.c_void_p
+A = 0x10000  # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10004  # a misaligned one
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(api.LIB_PATH):
+        pytest.fail("libbitlinear.so is not built (run __graft_entry__.build())")
+    return api.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(api.SIGNATURES), "binding signatures cover the header"
+
+
+def test_version_and_strings(L):
+    assert L.bitlinear_abi_version() == 1
+    for st in range(7):
+        s = L.bitlinear_status_string(st)
+        assert s and s.decode().startswith("BL_")
+    assert L.bitlinear_status_string(99) == b"unknown bitlinear status"
+    assert L.bitlinear_num_variants(api.PATH_GEMV) >= 2
+    assert L.bitlinear_num_variants(api.PATH_GEMM) >= 2
+    assert L.bitlinear_num_variants(0) == 0
+
+
+@pytest.mark.parametrize("N,K,expect", [(1, 128, 64), (640, 2560, 409632), (8192, 28672, 58720288),
+                                        (1, 100, 0), (0, 128, 0), (3, 0, 0), (-1, 128, 0)])
+def test_packed_bytes(L, N, K, expect):
+    assert L.bitlinear_packed_bytes(N, K) == expect
+
+
+def test_workspace_bytes(L):
+    assert L.bitlinear_workspace_bytes(1, 256) == 256 + 256 + 256
+    assert L.bitlinear_workspace_bytes(512, 2560) == 512 * 2560 + 2048 + 2048
+    assert L.bitlinear_workspace_bytes(0, 256) == 0
+
+
+def fwd(L, x=A, p=A, s=0.02, g=A, eps=1e-6, M=1, K=256, N=256, y=A, ws=A, wsb=1 << 20, launch=None):
+    return L.bitlinear_forward_ex(F(x), F(p), s, F(g), eps, M, K, N, F(y), F(ws), wsb, launch, None)
+
+
+@pytest.mark.parametrize("M,K,N", [(0, 256, 4), (1, 100, 4), (1, 256, 0), (1, 64, 4),
+                                   (-3, 256, 4), (1, 1 << 41, 4)])
+def test_forward_shape_errors(L, M, K, N):
+    assert fwd(L, M=M, K=K, N=N) == api.ERR_SHAPE
+
+
+@pytest.mark.parametrize("which", ["x", "p", "g", "y", "ws"])
+def test_forward_null(L, which):
+    assert fwd(L, **{which: 0}) == api.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", ["x", "p", "g", "y", "ws"])
+def test_forward_align(L, which):
+    assert fwd(L, **{which: MIS}) == api.ERR_ALIGN
+
+
+@pytest.mark.parametrize("eps", [0.0, -1e-6, float("inf"), float("nan")])
+def test_forward_eps(L, eps):
+    assert fwd(L, eps=eps) == api.ERR_INVALID_ARG
+
+
+def test_forward_workspace(L):
+    need = L.bitlinear_workspace_bytes(4, 256)
+    assert fwd(L, M=4, wsb=need - 1) == api.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("launch", [(3, -1, 0, 0), (0, 2, 0, 0), (1, -1, 99, 0), (0, -1, 1, 0),
+                                    (1, -1, 0, 7), (2, 1, 0, 0), (1, -1, -1, 0)])
+def test_forward_bad_launch(L, launch):
+    lp = ctypes.byref(api.Launch(*launch))
+    assert fwd(L, launch=lp) == api.ERR_INVALID_ARG
+
+
+def test_fused_needs_small_m(L):
+    lp = ctypes.byref(api.Launch(api.PATH_GEMV, 1, 0, 0))
+    assert fwd(L, M=8, wsb=1 << 20, launch=lp) == api.ERR_INVALID_ARG
+
+
+def test_pack_errors(L):
+    assert L.bitlinear_pack_i2s(F(A), 4, 100, F(A), None, None) == api.ERR_SHAPE
+    assert L.bitlinear_pack_i2s(F(0), 4, 128, F(A), None, None) == api.ERR_INVALID_ARG
+    assert L.bitlinear_pack_i2s(F(A), 4, 128, F(0), None, None) == api.ERR_INVALID_ARG
+    assert L.bitlinear_pack_i2s(F(MIS), 4, 128, F(A), None, None) == api.ERR_ALIGN
+    assert L.bitlinear_unpack_i2s(F(A), 4, 96, F(A), None) == api.ERR_SHAPE
+    assert L.bitlinear_unpack_i2s(F(A), 4, 128, F(MIS), None) == api.ERR_ALIGN
+    out = ctypes.c_float()
+    assert L.bitlinear_read_scale(F(A), 0, 128, ctypes.byref(out), None) == api.ERR_SHAPE
+    assert L.bitlinear_read_scale(F(A), 2, 128, None, None) == api.ERR_INVALID_ARG
+
+
+def test_stage_errors(L):
+    aq = L.bitlinear_act_quant
+    assert aq(F(A), F(A), 1e-6, 2, 200, F(A), F(A), F(A), None) == api.ERR_SHAPE
+    assert aq(F(A), F(0), 1e-6, 2, 256, F(A), F(A), F(A), None) == api.ERR_INVALID_ARG
+    assert aq(F(A), F(A), 0.0, 2, 256, F(A), F(A), F(A), None) == api.ERR_INVALID_ARG
+    assert aq(F(A), F(A), 1e-6, 2, 256, F(MIS), F(A), F(A), None) == api.ERR_ALIGN
+    mm = L.bitlinear_matmul_i2s_ex
+    assert mm(F(A), F(A), F(A), 2, 130, 4, F(A), None, None) == api.ERR_SHAPE
+    assert mm(F(A), F(0), F(A), 2, 256, 4, F(A), None, None) == api.ERR_INVALID_ARG
+    fused = ctypes.byref(api.Launch(api.PATH_GEMV, 1, 0, 0))
+    assert mm(F(A), F(A), F(A), 2, 256, 4, F(A), fused, None) == api.ERR_INVALID_ARG
+    assert L.bitlinear_matmul_i2s(F(MIS), F(A), F(A), 2, 256, 4, F(A), None) == api.ERR_ALIGN
+
+
+def test_product_never_imports_oracle():
+    """The product package must not reach the oracle (test infrastructure)."""
+    pkg = os.path.join(ROOT, "ternary_bit_linear_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text.lower()) or f == "workloads.py", f
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(api, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        api.lib()

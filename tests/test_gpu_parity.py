@@ -1,0 +1,298 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle.
+
+Integer results (packed bytes, int8 q, int32 qsum/acc) and the fp32 inv are
+compared bit for bit; fp32 y within 1e-5 relative of the oracle's fp64 y
+(and exactly 0 where the oracle's is 0).  Shapes span several tiles and
+ragged tails; the full-size workloads are checked on sampled outputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from ternary_bit_linear_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-5
+
+
+def announce(*a):
+    print("[gpu-case]", *a, file=sys.__stderr__, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def bl(torch):
+    from ternary_bit_linear_amd import api
+    api.lib()
+    return api
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def check_y(y, y64):
+    y = np.asarray(y, np.float64)
+    assert y.shape == y64.shape
+    assert np.all(np.isfinite(y)), "unwritten or non-finite outputs"
+    zero = y64 == 0
+    assert np.all(y[zero] == 0)
+    err = np.abs(y - y64)
+    bad = err > RTOL * np.abs(y64)
+    assert not bad.any(), f"{bad.sum()} outputs beyond 1e-5 rel; max rel {np.max(err[~zero] / np.abs(y64[~zero]))}"
+
+
+# ---------------------------------------------------------------- packing
+
+PACK_SHAPES = [(1, 128), (3, 256), (17, 384), (100, 1024), (640, 2560), (2560, 6912)]
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES)
+def test_pack_parity(torch, bl, orc, N, K):
+    announce("pack", N, K)
+    w, _ = wl.ternary(100 + N, N, K, 1 / 3, 0.02)
+    ref, s_ref = orc.pack_i2s(w)
+    packed, s = bl.pack_i2s(dev(torch, w))
+    torch.cuda.synchronize()
+    assert s == s_ref
+    assert np.array_equal(host(packed), ref)
+    assert bl.read_scale(packed, N, K) == s_ref
+    back = bl.unpack_i2s(packed, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(back), w)
+
+
+def test_pack_full_size(torch, bl, orc):
+    """The packing workload: fp32 ternary x 0.02, N = 8192 x K = 28672."""
+    N, K = wl.PACK_SHAPE
+    announce("pack full", N, K)
+    w, _ = wl.ternary(5000, N, K, 1 / 3, 0.02)
+    ref, s_ref = orc.pack_i2s(w)
+    packed, s = bl.pack_i2s(dev(torch, w))
+    torch.cuda.synchronize()
+    assert s == s_ref
+    assert np.array_equal(host(packed), ref)
+
+
+def test_pack_golden(torch, bl):
+    from tests.test_oracle_pack import golden_weights, load_golden
+    for c in load_golden():
+        announce("pack golden", c["name"])
+        packed, s = bl.pack_i2s(dev(torch, golden_weights(c)))
+        torch.cuda.synchronize()
+        nb = c["N"] * c["K"] // 4
+        assert host(packed)[:nb].tolist() == c["bytes"].tolist()
+        assert host(packed)[nb:].tolist() == c["trailer"].tolist()
+
+
+@pytest.mark.parametrize("bad", ["two_magnitudes", "nan", "inf"])
+def test_pack_not_ternary(torch, bl, bad):
+    announce("pack not ternary", bad)
+    w = np.zeros((4, 256), np.float32)
+    w[0, 3], w[3, 255] = 0.5, -0.5
+    w[2, 100] = {"two_magnitudes": 0.25, "nan": np.nan, "inf": np.inf}[bad]
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.pack_i2s(dev(torch, w))
+    assert e.value.status == bl.ERR_NOT_TERNARY
+
+
+def test_pack_all_zero(torch, bl):
+    announce("pack zero")
+    packed, s = bl.pack_i2s(torch.zeros((5, 384), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    p = host(packed)
+    assert s == 0.0 and np.all(p[:5 * 96] == 0x55) and np.all(p[5 * 96:] == 0)
+
+
+# ---------------------------------------------------------------- RMSNorm + int8
+
+AQ_CASES = [(1, 128, 0.0), (1, 256, 0.0), (3, 384, 0.0), (4, 2560, 0.01), (5, 6912, 0.0),
+            (16, 8192, 0.01), (64, 2560, 0.01), (7, 28672, 0.0), (33, 640, 0.0)]
+
+
+@pytest.mark.parametrize("M,K,outl", AQ_CASES)
+def test_act_quant_parity(torch, bl, orc, M, K, outl):
+    announce("act_quant", M, K, outl)
+    x = wl.activations(200 + M + K, M, K, outl)
+    x[0] *= np.float32(1e-3)  # a row whose mean square is near eps
+    g = wl.gamma(201, K, "u0.8-1.2")
+    q_r, inv_r, qs_r = orc.act_quant(x, g, 1e-6)
+    q, inv, qs = bl.act_quant(dev(torch, x), dev(torch, g), 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), q_r)
+    assert np.array_equal(host(inv).view(np.uint32), inv_r.view(np.uint32))
+    assert np.array_equal(host(qs), qs_r)
+
+
+def test_act_quant_ties_and_zero_rows(torch, bl, orc):
+    from tests.test_oracle_norm_quant import tie_case
+    announce("act_quant ties")
+    x, g, eps, expect, n = tie_case()
+    x = np.concatenate([x, np.zeros_like(x), -x])
+    q, inv, qs = bl.act_quant(dev(torch, x), dev(torch, g), eps)
+    torch.cuda.synchronize()
+    q = host(q)
+    assert q[0, 1:1 + n].tolist() == expect.tolist()
+    assert np.all(q[1] == 0) and host(qs)[1] == 0
+    assert np.array_equal(q[2], -q[0])
+    q_r, inv_r, qs_r = orc.act_quant(x, g, eps)
+    assert np.array_equal(q, q_r) and np.array_equal(host(inv), inv_r)
+
+
+# ---------------------------------------------------------------- contraction
+
+def mm_case(M, K, N, seed):
+    x = wl.activations(seed, M, K, 0.01)
+    w, t = wl.ternary(seed + 1, N, K, 0.4, 0.015)
+    g = wl.gamma(seed + 2, K, "u0.8-1.2")
+    return x, w, t, g
+
+
+MM_SHAPES = [(1, 128, 16), (1, 256, 100), (2, 384, 33), (5, 2560, 640), (16, 1024, 48),
+             (17, 384, 70), (31, 256, 64), (32, 640, 129), (33, 1280, 31), (64, 2560, 256),
+             (65, 384, 300), (130, 1152, 200)]
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("M,K,N", MM_SHAPES)
+def test_matmul_parity(torch, bl, orc, path, M, K, N):
+    announce("matmul", path, M, K, N)
+    x, w, t, g = mm_case(M, K, N, 300 + M + N)
+    packed_r, _ = orc.pack_i2s(w)
+    q, inv, qs = orc.act_quant(x, g, 1e-6)
+    acc_r = orc.matmul_i2s(q, qs, packed_r, N)
+    assert np.array_equal(acc_r.astype(np.int64), q.astype(np.int64) @ t.astype(np.int64).T)
+    P = dev(torch, packed_r)
+    Q, QS = dev(torch, q), dev(torch, qs)
+    for v in range(1, bl.num_variants(path) + 1):
+        acc = bl.matmul_i2s(Q, QS, P, N, path=path, variant=v)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(acc), acc_r), f"variant {v}"
+
+
+FWD_SHAPES = [(1, 256, 256), (1, 2560, 640), (2, 384, 100), (3, 1024, 77), (4, 6912, 160),
+              (7, 512, 513), (16, 2560, 256), (17, 256, 64), (64, 1024, 200), (100, 384, 90)]
+
+
+@pytest.mark.parametrize("M,K,N", FWD_SHAPES)
+def test_forward_parity(torch, bl, orc, M, K, N):
+    announce("forward", M, K, N)
+    x, w, t, g = mm_case(M, K, N, 400 + M + K)
+    packed_r, s = orc.pack_i2s(w)
+    y64 = orc.forward(x, packed_r, s, g, 1e-6, N)
+    X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = bl.new_workspace(M, K)
+    y = bl.forward(X, P, s, G, 1e-6, N, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    check_y(host(y), y64)
+    # the workspace holds this call's q / inv / qsum
+    q_r, inv_r, qs_r = orc.act_quant(x, g, 1e-6)
+    q, inv, qs = bl.workspace_views(ws, M, K)
+    assert np.array_equal(host(q), q_r) and np.array_equal(host(inv), inv_r)
+    assert np.array_equal(host(qs), qs_r)
+    # every route / fusion / launch shape gives the same bits
+    ref = host(y).copy()
+    opts = [(1, 0, 0), (2, 0, 0)] + [(2, 0, v) for v in range(1, bl.num_variants(2) + 1)]
+    opts += [(1, 0, v) for v in range(1, bl.num_variants(1) + 1)]
+    if M <= 4 and M * K <= 32768:
+        opts += [(1, 1, v) for v in range(1, bl.num_variants(1) + 1)]
+    for path, fuse, v in opts:
+        out.fill_(float("nan"))
+        y2 = bl.forward(X, P, s, G, 1e-6, N, out=out, workspace=ws, path=path, fuse=fuse, variant=v)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y2), ref), (path, fuse, v)
+
+
+def test_forward_quant_is_applied(torch, bl, orc):
+    """The output is the quantised path's, not a plain fp32 x W^T."""
+    M, K, N = 2, 1024, 64
+    x, w, t, g = mm_case(M, K, N, 77)
+    packed_r, s = orc.pack_i2s(w)
+    y = host(bl.forward(dev(torch, x), dev(torch, packed_r), s, dev(torch, g), 1e-6, N))
+    xn = orc.rmsnorm(x, g, 1e-6).astype(np.float64)
+    plain = xn @ w.astype(np.float64).T
+    assert np.abs(y - plain).max() > 1e-4 * np.abs(plain).max()
+    check_y(y, orc.forward(x, packed_r, s, g, 1e-6, N))
+
+
+def test_forward_zero_weights_and_identity(torch, bl, orc):
+    announce("forward special W")
+    K = 256
+    x = wl.activations(88, 3, K)
+    g = np.ones(K, np.float32)
+    P0, s0 = bl.pack_i2s(torch.zeros((16, K), dtype=torch.float32, device="cuda"))
+    y0 = host(bl.forward(dev(torch, x), P0, s0, dev(torch, g), 1e-6, 16))
+    assert np.all(y0 == 0)
+    PI, sI = bl.pack_i2s(torch.eye(K, dtype=torch.float32, device="cuda") * 0.5)
+    yI = host(bl.forward(dev(torch, x), PI, sI, dev(torch, g), 1e-6, K))
+    q, inv, _ = orc.act_quant(x, g, 1e-6)
+    check_y(yI, q.astype(np.float64) * (0.5 / inv.astype(np.float64))[:, None])
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def run_linear(torch, bl, orc, work, i, sample_rows=None, sample_cols=None):
+    L = work.linears[i]
+    announce("workload", work.name, L.name, L.M, L.K, L.N)
+    x, w, t, g = work.inputs(i)
+    X, G = dev(torch, x), dev(torch, g)
+    P, s = bl.pack_i2s(dev(torch, w))
+    ws = bl.new_workspace(L.M, L.K)
+    y = host(bl.forward(X, P, s, G, work.eps, L.N, workspace=ws))
+    assert np.all(np.isfinite(y))
+    q_r, inv_r, qs_r = orc.act_quant(x, g, work.eps)
+    q, inv, qs = (host(a) for a in bl.workspace_views(ws, L.M, L.K))
+    assert np.array_equal(q, q_r) and np.array_equal(inv, inv_r) and np.array_equal(qs, qs_r)
+    rows = np.arange(L.M) if sample_rows is None else sample_rows
+    cols = np.arange(L.N) if sample_cols is None else sample_cols
+    acc = q_r[rows].astype(np.int64) @ t[cols].astype(np.int64).T
+    y64 = acc * (np.float64(s) / inv_r[rows].astype(np.float64))[:, None]
+    check_y(y[np.ix_(rows, cols)], y64)
+    return y
+
+
+@pytest.mark.parametrize("i", range(7))
+def test_workload_decode_layer(torch, bl, orc, i):
+    run_linear(torch, bl, orc, wl.DECODE_LAYER, i)
+
+
+@pytest.mark.parametrize("i", range(7))
+def test_workload_prefill_layer(torch, bl, orc, i):
+    L = wl.PREFILL_LAYER.linears[i]
+    rng = np.random.default_rng(i)
+    rows = np.unique(np.concatenate([[0, L.M - 1], rng.integers(0, L.M, 14)]))
+    cols = np.unique(np.concatenate([[0, L.N - 1], rng.integers(0, L.N, 500)]))
+    run_linear(torch, bl, orc, wl.PREFILL_LAYER, i, rows, cols)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("i", range(3))
+def test_workload_ffn70b(torch, bl, orc, M, i):
+    work = wl.ffn70b(M)
+    L = work.linears[i]
+    rng = np.random.default_rng(i + M)
+    cols = np.unique(np.concatenate([[0, L.N - 1], rng.integers(0, L.N, 3000)]))
+    run_linear(torch, bl, orc, work, i, None, cols)
+
+
+@pytest.mark.parametrize("M", wl.SWEEP_M)
+def test_workload_sweep(torch, bl, orc, M):
+    work = wl.sweep(M)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 12)]))
+    cols = np.unique(np.concatenate([[0, 8191], rng.integers(0, 8192, 1000)]))
+    run_linear(torch, bl, orc, work, 0, rows, cols)
