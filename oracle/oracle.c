@@ -32,7 +32,7 @@
  *     endian) and 28 zero bytes; row length K must be a multiple of 128.
  *   - RMSNorm: xn = (x * r) * gamma with r = 1 / sqrt(sum(x^2)/K + eps), in
  *     fp32 with correctly rounded division and square root.  The sum of
- *     squares uses one pinned order, "O64", defined at oracle_sumsq_o64.
+ *     squares uses one pinned order, "O256", defined at oracle_sumsq.
  *   - int8 quantisation: per token, inv = 127 / max(amax, 1e-5),
  *     q = clamp(round-half-even(xn * inv), -128, 127), qsum = sum(q).
  *   - y = acc * (w_scale / inv), computed here in fp64 from the exact int32
@@ -164,22 +164,29 @@ int oracle_unpack_i2s(const uint8_t *packed, int64_t N, int64_t K, float *w) {
     return ORC_OK;
 }
 
-/* O64 sum of squares of one row, the pinned fp32 order (the pages fix no
- * order; one is needed because the result decides integer codes):
- *   64 partial sums p[0..63], all +0.0f;
- *   for k = 0, 1, ..., K-1: p[(k/4) % 64] = fmaf(v[k], v[k], p[(k/4) % 64]);
- *   then halve: for s = 32, 16, 8, 4, 2, 1: p[j] = p[j] + p[j+s] for j < s;
- *   result p[0]. */
-float oracle_sumsq_o64(const float *v, int64_t K) {
-    float p[64];
-    for (int j = 0; j < 64; ++j) p[j] = 0.0f;
+/* Sum of squares of one row in the pinned fp32 order "O256" (the pages fix
+ * no order; one is needed because the result decides integer codes):
+ *   256 partial sums p[0..255], all +0.0f;
+ *   for k = 0, 1, ..., K-1: p[(k/4) % 256] = fmaf(v[k], v[k], p[(k/4) % 256]);
+ *   each group of 64 partials p[64w .. 64w+63] (w = 0..3) is halved:
+ *     for s = 32, 16, 8, 4, 2, 1: p[64w+j] = p[64w+j] + p[64w+j+s] for j < s,
+ *   giving g[w] = p[64w];
+ *   result (g[0] + g[1]) + (g[2] + g[3]). */
+float oracle_sumsq(const float *v, int64_t K) {
+    float p[256];
+    for (int j = 0; j < 256; ++j) p[j] = 0.0f;
     for (int64_t k = 0; k < K; ++k) {
-        int j = (int)((k / 4) % 64);
+        int j = (int)((k / 4) % 256);
         p[j] = fmaf(v[k], v[k], p[j]);
     }
-    for (int s = 32; s >= 1; s /= 2)
-        for (int j = 0; j < s; ++j) p[j] = p[j] + p[j + s];
-    return p[0];
+    float g[4];
+    for (int w = 0; w < 4; ++w) {
+        float *q = p + 64 * w;
+        for (int s = 32; s >= 1; s /= 2)
+            for (int j = 0; j < s; ++j) q[j] = q[j] + q[j + s];
+        g[w] = q[0];
+    }
+    return (g[0] + g[1]) + (g[2] + g[3]);
 }
 
 /* RMSNorm of one token row, fp32 [HF-38087, "What does this PR do?": the
@@ -187,7 +194,7 @@ float oracle_sumsq_o64(const float *v, int64_t K) {
  * quantisation]: r = 1 / sqrt(sumsq / K + eps); xn = (x * r) * gamma. */
 static void rmsnorm_row(const float *x, const float *gamma, float eps,
                         int64_t K, float *xn) {
-    float ss = oracle_sumsq_o64(x, K);
+    float ss = oracle_sumsq(x, K);
     float ms = ss / (float)K;
     float r = 1.0f / sqrtf(ms + eps);
     for (int64_t k = 0; k < K; ++k) xn[k] = (x[k] * r) * gamma[k];

@@ -62,8 +62,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_code_at.argtypes = [p, i64, i64, i64]
         L.oracle_read_scale.restype = ctypes.c_float
         L.oracle_read_scale.argtypes = [p, i64, i64]
-        L.oracle_sumsq_o64.restype = ctypes.c_float
-        L.oracle_sumsq_o64.argtypes = [p, i64]
+        L.oracle_sumsq.restype = ctypes.c_float
+        L.oracle_sumsq.argtypes = [p, i64]
         L.oracle_rmsnorm.restype = ctypes.c_int
         L.oracle_rmsnorm.argtypes = [p, p, ctypes.c_float, i64, i64, p]
         L.oracle_act_quant.restype = ctypes.c_int
@@ -125,9 +125,10 @@ def read_scale(packed: np.ndarray, N: int, K: int) -> float:
     return float(lib().oracle_read_scale(_ptr(packed), N, K))
 
 
-def sumsq_o64(v: np.ndarray) -> np.float32:
+def sumsq(v: np.ndarray) -> np.float32:
+    """Sum of squares of one row in the pinned O256 order."""
     v = _f32(v).ravel()
-    return np.float32(lib().oracle_sumsq_o64(_ptr(v), v.size))
+    return np.float32(lib().oracle_sumsq(_ptr(v), v.size))
 
 
 def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-6) -> np.ndarray:
