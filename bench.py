@@ -81,38 +81,60 @@ class Prepared:
                         out=d["y"], workspace=d["ws"])
 
 
+def capture(torch, fn):
+    """Capture fn() (which enqueues on the current stream) into a HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # untimed eager pass (allocator / module warm-up before capture)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def time_steps(torch, api, prep, steps, warmup):
-    for r in range(warmup):
-        prep.step(api, r)
+    """ms per step over exactly `steps` steps, replayed from one HIP graph
+    (the host does not pace the GPU), after `warmup` untimed steps."""
+    gw = capture(torch, lambda: [prep.step(api, r) for r in range(max(1, warmup))])
+    gt = capture(torch, lambda: [prep.step(api, warmup + r) for r in range(steps)])
+    gw.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for r in range(steps):
-        prep.step(api, warmup + r)
+    gt.replay()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps  # ms per step
 
 
-def time_launches(torch, api, prep, steps):
-    """Average duration of each forward launch (the decode route is a single
-    fused kernel per BitLinear), from HIP events recorded on the launch
-    stream around every launch of `steps` further steps."""
-    per = []
-    for r in range(steps):
-        for d in prep.lin:
-            L = d["L"]
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            api.forward(d["x"], d["P"][r % prep.copies], d["s"], d["g"], prep.work.eps, L.N,
-                        out=d["y"], workspace=d["ws"])
-            b.record()
-            per.append((L, a, b))
-    torch.cuda.synchronize()
-    by_name = {}
-    for L, a, b in per:
-        by_name.setdefault(L.name, (L, []))[1].append(a.elapsed_time(b) * 1e-3)  # s
-    return by_name
+def time_launches(torch, api, prep, reps=None):
+    """Mean duration of each BitLinear's forward launch: a HIP graph of
+    `reps` back-to-back launches of that one shape (rotating weight copies),
+    timed with events on the launch stream."""
+    out = {}
+    reps = reps or prep.copies
+    for d in prep.lin:
+        L = d["L"]
+
+        def run(d=d, L=L):
+            for r in range(reps):
+                api.forward(d["x"], d["P"][r % prep.copies], d["s"], d["g"], prep.work.eps, L.N,
+                            out=d["y"], workspace=d["ws"])
+        g = capture(torch, run)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[L.name] = (L, e0.elapsed_time(e1) * 1e-3 / reps)  # s per launch
+        del g
+    return out
 
 
 def linear_bytes(L):
@@ -158,7 +180,7 @@ def cpu_baseline(work, budget_s=12.0):
             orc.forward(x, p, s, g, work.eps, n_keep)
         n += 1
         el = time.perf_counter() - t0
-        if el > budget_s or n >= 1000:
+        if el > budget_s or n >= 100000:
             break
     per_step = el / n / row_frac
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
@@ -175,10 +197,9 @@ def secondary_prefill(torch, api, steps, warmup):
     ms = time_steps(torch, api, prep, steps, warmup)
     ops = wl.PREFILL_LAYER.int_ops()
     tops = ops / (ms * 1e-3) / 1e12
-    by = time_launches(torch, api, prep, max(3, steps // 4))
+    by = time_launches(torch, api, prep)
     per = {}
-    for name, (L, ts) in by.items():
-        t = float(np.mean(ts))
+    for name, (L, t) in by.items():
         per[name] = {"M": L.M, "K": L.K, "N": L.N, "us": round(t * 1e6, 2),
                      "TOPS": round(2 * L.M * L.N * L.K / t / 1e12, 1)}
     return {"workload": wl.PREFILL_LAYER.name, "metric": "int8 TOPS (M=512 GEMM)",
@@ -212,11 +233,10 @@ def main():
     ms = time_steps(torch, api, prep, args.steps, args.warmup)
     step_bytes = sum(linear_bytes(L) for L in work.linears)
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    by = time_launches(torch, api, prep, max(5, args.steps // 4))
+    by = time_launches(torch, api, prep)
 
     # Dominant kernel: the forward launch of the largest BitLinear shape.
-    dom_name, (dom_L, dom_t) = max(by.items(), key=lambda kv: linear_bytes(kv[1][0]))
-    dom_s = float(np.mean(dom_t))
+    dom_name, (dom_L, dom_s) = max(by.items(), key=lambda kv: linear_bytes(kv[1][0]))
     M = work.linears[0].M
     decode = M <= 16
     if decode:
@@ -233,10 +253,10 @@ def main():
         ach = 2 * dom_L.M * dom_L.N * dom_L.K / dom_s / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS,
                 "unit": "TOPS", "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None,
-                "kernel": "act_quant + gemm_kernel", "launch": f"{dom_name} M={dom_L.M} "
+                "kernel": "act_quant_kernel + gemm_kernel", "launch": f"{dom_name} M={dom_L.M} "
                 f"K={dom_L.K} N={dom_L.N}", "avg_launch_us": round(dom_s * 1e6, 3)}
-    per_linear = {n: {"M": L.M, "K": L.K, "N": L.N, "us": round(float(np.mean(t)) * 1e6, 3),
-                      "GBs": round(linear_bytes(L) / float(np.mean(t)) / 1e9, 1)}
+    per_linear = {n: {"M": L.M, "K": L.K, "N": L.N, "us": round(t * 1e6, 3),
+                      "GBs": round(linear_bytes(L) / t / 1e9, 1)}
                   for n, (L, t) in by.items()}
 
     out = {

@@ -35,8 +35,8 @@
  *     K % 128 == 0 (rows are whole I2_S blocks, [CPPB-7] "Known gaps")
  *     -> BL_ERR_SHAPE; non-NULL pointers -> BL_ERR_INVALID_ARG; x, y, q,
  *     packed_w and the workspace 16-byte aligned -> BL_ERR_ALIGN.
- *   - Sizes are limited to M*K, N*K/4 and M*N below 2^40 elements and to
- *     M, N < 2^31 (BL_ERR_SHAPE beyond).
+ *   - Sizes are limited to M*K, N*K/4 and M*N below 2^40 elements, to
+ *     M, N < 2^31 and to K <= 2^22 (BL_ERR_SHAPE beyond).
  *
  * I2_S packed weight buffer (the persistent format) [CPPB-7]
  *   N*K/4 bytes of 2-bit codes followed by a 32-byte trailer.  Each run of

@@ -6,38 +6,34 @@
 // [eejd/cpp-bitnet PR #7, NEON-kernel commit: the activations enter the
 // ternary dot product as int8 together with their sum.]
 //
-// One 256-thread block per 4 token rows; each wave computes one row's sum of
-// squares in the fixed order of wave_sumsq, then the block quantises the rows
-// one by one with coalesced float4 loads of x and gamma.  HBM traffic is
-// 4*M*K bytes of x (re-read from L2 twice), 4*K of gamma, M*K of q out.
+// One wave per token row (wave_act_quant_row): every load of x and gamma is
+// issued at once through range-checked buffer loads, reductions are wave
+// shuffles only (no LDS, no barrier).  Rows up to 3072 elements are read
+// once; longer rows take three passes (the second and third from L2).  HBM
+// traffic per row: 4K (x) + 4K (gamma, L2-resident after the first rows) +
+// K (q) + 8 bytes.
 #include "common.hpp"
 
 namespace bl {
 namespace {
 
-struct GlobalSink {
-    int8_t *q;
+struct GlobalRowSink {
+    int8_t *q;  // row base
     float *inv;
     int32_t *qsum;
-    int64_t K;
-    __device__ void store_q(int m, int k, uint32_t v) {
-        *reinterpret_cast<uint32_t *>(q + (size_t)m * K + k) = v;
-    }
-    __device__ void store_row(int m, float iv, int qs) {
-        inv[m] = iv;
-        qsum[m] = qs;
+    __device__ void store_q(int k, uint32_t v) { *reinterpret_cast<uint32_t *>(q + k) = v; }
+    __device__ void store_row(float iv, int qs) {
+        *inv = iv;
+        *qsum = qs;
     }
 };
 
-__global__ __launch_bounds__(256) void act_quant_kernel(
-    const float *__restrict__ x, const float *__restrict__ gamma, float eps,
-    int M, int K, int8_t *__restrict__ q, float *__restrict__ inv,
-    int32_t *__restrict__ qsum) {
-    __shared__ float red[8];
-    const int m0 = blockIdx.x * 4;
-    const int rows = min(4, M - m0);
-    GlobalSink sink{q + (size_t)m0 * K, inv + m0, qsum + m0, K};
-    block_act_quant<256>(x + (size_t)m0 * K, gamma, eps, rows, K, red, sink);
+__global__ __launch_bounds__(64) void act_quant_kernel(
+    const float *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
+    int8_t *__restrict__ q, float *__restrict__ inv, int32_t *__restrict__ qsum) {
+    const int m = blockIdx.x;
+    GlobalRowSink sink{q + (size_t)m * K, inv + m, qsum + m};
+    wave_act_quant_row<3>(x + (size_t)m * K, gamma, eps, K, sink);
 }
 
 }  // namespace
@@ -45,9 +41,8 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
 hipError_t launch_act_quant(const float *x, const float *gamma, float eps,
                             int64_t M, int64_t K, int8_t *q, float *inv,
                             int32_t *qsum, hipStream_t s) {
-    const unsigned blocks = (unsigned)((M + 3) / 4);
-    hipLaunchKernelGGL(act_quant_kernel, dim3(blocks), dim3(256), 0, s, x,
-                       gamma, eps, (int)M, (int)K, q, inv, qsum);
+    hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)M), dim3(64), 0, s, x, gamma, eps,
+                       (int)K, q, inv, qsum);
     return hipGetLastError();
 }
 

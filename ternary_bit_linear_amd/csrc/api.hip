@@ -11,9 +11,11 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Row length limit: keeps every per-tile buffer view below 2^31 bytes.
+constexpr int64_t kMaxK = int64_t(1) << 22;
 constexpr int kGemvMaxM = 16;   // AUTO: decode route up to 16 tokens
-constexpr int kFuseMaxM = 4;    // fused norm + quant inside the decode kernel
-constexpr int64_t kFuseMaxLds = 32 * 1024;  // M*K bytes of LDS for the fused decode kernel
+using bl::kFuseMaxLds;
+using bl::kFuseMaxM;
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -22,13 +24,13 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 bl_status check_mk(int64_t M, int64_t K) {
-    if (M < 1 || K < 1 || K % bl::kBlockWeights != 0) return BL_ERR_SHAPE;
+    if (M < 1 || K < 1 || K % bl::kBlockWeights != 0 || K > kMaxK) return BL_ERR_SHAPE;
     if (M > kMaxDim || K > kMaxDim || M * K >= kMaxElems) return BL_ERR_SHAPE;
     return BL_OK;
 }
 
 bl_status check_nk(int64_t N, int64_t K) {
-    if (N < 1 || K < 1 || K % bl::kBlockWeights != 0) return BL_ERR_SHAPE;
+    if (N < 1 || K < 1 || K % bl::kBlockWeights != 0 || K > kMaxK) return BL_ERR_SHAPE;
     if (N > kMaxDim || K > kMaxDim || N * K >= kMaxElems) return BL_ERR_SHAPE;
     // grids of the pack kernels: N*K/64 chunks in 256-thread blocks
     if ((N * (K / 64) + 255) / 256 > kMaxDim) return BL_ERR_SHAPE;

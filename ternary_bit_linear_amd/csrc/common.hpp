@@ -30,16 +30,21 @@ constexpr int kBlockBytes = 32;       // bytes per I2_S block
 constexpr int kStepK = 256;           // k per contraction step (two blocks)
 constexpr int kStepBytes = 64;        // packed bytes of one row per step
 constexpr int kTrailerBytes = 32;
+// Dynamic LDS budgets of the decode kernel: q of the fused form (M*K bytes,
+// M <= kFuseMaxM) and of the staged form (16 token rows at most).
+constexpr int kFuseMaxM = 4;
+constexpr int64_t kFuseMaxLds = 32 * 1024;
+constexpr int64_t kGemvStageMaxLds = 48 * 1024;
 
 // Codes of field g of a 16-byte packed chunk, one byte per k, as the int8
 // MFMA operand.
-__device__ __forceinline__ v4i unpack_field(const uint4 &p, int g) {
+__device__ __forceinline__ v4i unpack_field(const v4i &p, int g) {
     const int sh = 6 - 2 * g;
     v4i r;
-    r.x = (int)((p.x >> sh) & 0x03030303u);
-    r.y = (int)((p.y >> sh) & 0x03030303u);
-    r.z = (int)((p.z >> sh) & 0x03030303u);
-    r.w = (int)((p.w >> sh) & 0x03030303u);
+    r.x = (int)(((uint32_t)p.x >> sh) & 0x03030303u);
+    r.y = (int)(((uint32_t)p.y >> sh) & 0x03030303u);
+    r.z = (int)(((uint32_t)p.z >> sh) & 0x03030303u);
+    r.w = (int)(((uint32_t)p.w >> sh) & 0x03030303u);
     return r;
 }
 
@@ -50,36 +55,59 @@ __device__ __forceinline__ v4i mfma16(const v4i &a, const v4i &b, const v4i &c) 
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Sum of squares of one row in the library's fixed order: lane j of a wave
-// owns the elements k with (k / 4) % 64 == j and accumulates them with
-// fused multiply-adds in increasing k; the 64 partial sums are then combined
-// by a halving tree (j + 32 into j, then j + 16 into j, ... then j + 1 into
-// j).  The xor butterfly below evaluates exactly that tree; every lane ends
-// with the same value.
-__device__ __forceinline__ float wave_sumsq(const float *__restrict__ row, int K, int lane) {
-    float p = 0.0f;
-    for (int k = 4 * lane; k < K; k += 4 * kWave) {
-        const float4 v = *reinterpret_cast<const float4 *>(row + k);
-        p = __builtin_fmaf(v.x, v.x, p);
-        p = __builtin_fmaf(v.y, v.y, p);
-        p = __builtin_fmaf(v.z, v.z, p);
-        p = __builtin_fmaf(v.w, v.w, p);
-    }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_xor(p, s, kWave);
-    return p;
+// Range-checked 16-byte loads through a buffer resource: an offset at or
+// beyond `bytes` returns zeros (no branch, no clamped address), which is how
+// every kernel here handles ragged tiles.  `bytes` must be < 2^31.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    // dword3 = 0x00020000: 32-bit data format, the raw-buffer setting on gfx9.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_float4(__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z),
+                       __int_as_float(v.w));
+}
+
+// Halving-tree reduction of the 64 lanes of a wave into lane 0:
+// level s = 32, 16, 8, 4, 2, 1 adds lane j + s into lane j (j < s).  Lane
+// 0's result is exactly the tree the pinned sum-of-squares order defines.
+// Level 32 crosses the wave halves (ds_bpermute), level 16 swaps 16-lane
+// groups (ds_swizzle, bitmask mode xor 16), levels 8..1 stay inside a
+// 16-lane row (DPP row_shl).  Other lanes end with partial values; the
+// result is read with readfirstlane (a wave-uniform scalar).
+template <class Op>
+__device__ __forceinline__ int wave_tree_i(int v, Op op) {
+    v = op(v, __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) << 2), v));
+    v = op(v, __builtin_amdgcn_ds_swizzle(v, 0x401F));
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x108, 0xF, 0xF, false));  // row_shl:8
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false));  // row_shl:4
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x102, 0xF, 0xF, false));  // row_shl:2
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x101, 0xF, 0xF, false));  // row_shl:1
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ float wave_tree_sum_f(float v) {
+    return __int_as_float(wave_tree_i(__float_as_int(v), [](int a, int b) {
+        return __float_as_int(__int_as_float(a) + __int_as_float(b));
+    }));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, kWave));
-    return v;
+    return __int_as_float(wave_tree_i(__float_as_int(v), [](int a, int b) {
+        return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+    }));
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, kWave);
-    return v;
+    return wave_tree_i(v, [](int a, int b) { return a + b; });
 }
 
 __device__ __forceinline__ int quant_one(float xn, float inv) {
@@ -93,74 +121,267 @@ __device__ __forceinline__ uint32_t pack_char4(int a, int b, int c, int d) {
            ((uint32_t)(c & 0xff) << 16) | ((uint32_t)(d & 0xff) << 24);
 }
 
-// RMSNorm + absmax int8 quantisation of `rows` (<= 4) consecutive token rows
-// by a block of NT threads (NT = 256 or 512).  Wave w < rows computes the sum
-// of squares of row w in the fixed order; then the whole block computes, per
-// row, amax of xn = (x * r) * gamma, inv = 127 / max(amax, 1e-5), and
-// q = clamp(rint(xn * inv), -128, 127) with qsum = sum q.  Sink receives
-// store_q(row, k, packed 4 x int8) and store_row(row, inv, qsum).
-// `red` is >= 2 * NT / 64 floats of shared memory; the block must call this
-// uniformly.
-template <int NT, class Sink>
-__device__ __forceinline__ void block_act_quant(const float *__restrict__ x,
-                                                const float *__restrict__ gamma,
-                                                float eps, int rows, int K,
-                                                float *red, Sink &sink) {
-    constexpr int NW = NT / kWave;
-    static_assert(NW >= 4 && NW <= 8, "block_act_quant: 256 or 512 threads");
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wid = tid >> 6;
-    __shared__ float r_sh[4];
-    if (wid < rows) {
-        const float ss = wave_sumsq(x + (size_t)wid * K, K, lane);
-        const float ms = ss / (float)K;
-        const float r = 1.0f / sqrtf(ms + eps);
-        if (lane == 0) r_sh[wid] = r;
-    }
+// Block-wide reductions over exactly 256 threads (4 waves).  `red` is 4
+// words of shared memory; the caller's block must reach these uniformly.
+//
+// Sum of squares of one row in the library's fixed order "O256": thread t
+// owns the elements k with (k / 4) % 256 == t and accumulates their squares
+// with fused multiply-adds in increasing k (its float4 loads at
+// k = 4t + 1024 i, in increasing i); the 64 partials of each wave are
+// combined by a halving tree (lane j + 32 into j, then j + 16, ... j + 1;
+// wave_tree_sum_f); the four wave totals are then added as
+// (g0 + g1) + (g2 + g3).
+__device__ __forceinline__ float block_sumsq_finish(float p, float *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    p = wave_tree_sum_f(p);
+    if (lane == 0) red[wid] = p;
     __syncthreads();
-    for (int m = 0; m < rows; ++m) {
-        const float r = r_sh[m];
-        const float *xr = x + (size_t)m * K;
-        float amax = 0.0f;
-        for (int k = 4 * tid; k < K; k += 4 * NT) {
-            const float4 v = *reinterpret_cast<const float4 *>(xr + k);
-            const float4 g = *reinterpret_cast<const float4 *>(gamma + k);
-            amax = fmaxf(amax, fabsf((v.x * r) * g.x));
-            amax = fmaxf(amax, fabsf((v.y * r) * g.y));
-            amax = fmaxf(amax, fabsf((v.z * r) * g.z));
-            amax = fmaxf(amax, fabsf((v.w * r) * g.w));
-        }
-        amax = wave_max(amax);
-        if (lane == 0) red[wid] = amax;
-        __syncthreads();
-        amax = red[0];
+    const float t = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    v = wave_max(v);
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    const float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ int block_sum_int(int v, float *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    v = wave_sum_int(v);
+    int *ri = reinterpret_cast<int *>(red);
+    if (lane == 0) ri[wid] = v;
+    __syncthreads();
+    const int t = ri[0] + ri[1] + ri[2] + ri[3];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ float4 xn4(const float4 &x, const float4 &g, float r) {
+    return make_float4((x.x * r) * g.x, (x.y * r) * g.y, (x.z * r) * g.z, (x.w * r) * g.w);
+}
+
+__device__ __forceinline__ float amax4(float a, const float4 &v) {
+    return fmaxf(fmaxf(fmaxf(a, fabsf(v.x)), fmaxf(fabsf(v.y), fabsf(v.z))), fabsf(v.w));
+}
+
+// RMSNorm + absmax int8 quantisation of one token row (HF-38087: RMSNorm on
+// the activations before quantisation; the int8 codes and their sum feed the
+// I2_S contraction):
+//   r = 1 / sqrt(sumsq / K + eps)      (O256 order, IEEE division and root)
+//   xn = (x * r) * gamma,  inv = 127 / max(max |xn|, 1e-5)
+//   q = clamp(rint(xn * inv), -128, 127),  qsum = sum q.
+// Sink receives store_q(k, 4 packed int8) and store_row(inv, qsum).
+
+// Block form (256 threads): thread t owns O256 chain t, i.e. the float4
+// groups at k = 4t + 1024 i.  Rows of up to 1024 * CH elements keep x and
+// gamma in registers (one global round trip); `issued()` runs once every
+// wave of the block has issued those loads (a barrier), so loads the caller
+// issues there queue behind them and do not delay the normalisation.  LONG rows (K > 1024 * CH) are
+// streamed in chunks of CH float4 per thread, three times.
+template <int CH, bool LONG, class Sink, class Hook>
+__device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
+                                                    const float *__restrict__ gamma,
+                                                    float eps, int K, float *red,
+                                                    Sink &sink, Hook &&issued) {
+    const int t4 = 4 * threadIdx.x;
+    constexpr int STRIDE = 1024;
+    if constexpr (!LONG) {  // K <= 1024 * CH
+        const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+        const auto rg = make_rsrc(gamma, 4u * (uint32_t)K);
+        float4 xv[CH], gv[CH];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) amax = fmaxf(amax, red[w]);
+        for (int i = 0; i < CH; ++i) {
+            const int k = t4 + STRIDE * i;
+            const uint32_t off = k < K ? 4u * (uint32_t)k : kOOB;
+            xv[i] = buf_load_f4(rx, off);
+            gv[i] = buf_load_f4(rg, off);
+        }
+        // Every wave's x / gamma loads are issued before any load the hook
+        // issues, so they do not queue behind another wave's weight misses.
+        __builtin_amdgcn_s_barrier();
+        issued();
+        float p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            p = __builtin_fmaf(xv[i].x, xv[i].x, p);
+            p = __builtin_fmaf(xv[i].y, xv[i].y, p);
+            p = __builtin_fmaf(xv[i].z, xv[i].z, p);
+            p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+        }
+        const float ss = block_sumsq_finish(p, red);
+        const float r = 1.0f / sqrtf(ss / (float)K + eps);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) amax = amax4(amax, xn4(xv[i], gv[i], r));
+        amax = block_max(amax, red);
         const float inv = 127.0f / fmaxf(amax, 1e-5f);
         int qs = 0;
-        for (int k = 4 * tid; k < K; k += 4 * NT) {
-            const float4 v = *reinterpret_cast<const float4 *>(xr + k);
-            const float4 g = *reinterpret_cast<const float4 *>(gamma + k);
-            const int a = quant_one((v.x * r) * g.x, inv);
-            const int b = quant_one((v.y * r) * g.y, inv);
-            const int c = quant_one((v.z * r) * g.z, inv);
-            const int d = quant_one((v.w * r) * g.w, inv);
-            qs += a + b + c + d;
-            sink.store_q(m, k, pack_char4(a, b, c, d));
-        }
-        qs = wave_sum_int(qs);
-        if (lane == 0) reinterpret_cast<int *>(red)[NW + wid] = qs;
-        __syncthreads();
-        if (tid == 0) {
-            const int *ri = reinterpret_cast<const int *>(red) + NW;
-            int total = 0;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) total += ri[w];
-            sink.store_row(m, inv, total);
+        for (int i = 0; i < CH; ++i) {
+            const int k = t4 + STRIDE * i;
+            if (k < K) {
+                const float4 v = xn4(xv[i], gv[i], r);
+                const int a = quant_one(v.x, inv), b = quant_one(v.y, inv);
+                const int c = quant_one(v.z, inv), d = quant_one(v.w, inv);
+                qs += a + b + c + d;
+                sink.store_q(k, pack_char4(a, b, c, d));
+            }
         }
-        __syncthreads();
+        qs = block_sum_int(qs, red);
+        if (threadIdx.x == 0) sink.store_row(inv, qs);
+        return;
+    } else {
+    issued();
+    // Long rows: three streamed passes.
+    const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+    const auto rg = make_rsrc(gamma, 4u * (uint32_t)K);
+    auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
+    float p = 0.0f;
+    for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
+        float4 xv[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            p = __builtin_fmaf(xv[i].x, xv[i].x, p);
+            p = __builtin_fmaf(xv[i].y, xv[i].y, p);
+            p = __builtin_fmaf(xv[i].z, xv[i].z, p);
+            p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+        }
     }
+    const float ss = block_sumsq_finish(p, red);
+    const float r = 1.0f / sqrtf(ss / (float)K + eps);
+    float amax = 0.0f;
+    for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
+        float4 xv[CH], gv[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
+            gv[i] = buf_load_f4(rg, off_of(c0 + t4 + STRIDE * i));
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) amax = amax4(amax, xn4(xv[i], gv[i], r));
+    }
+    amax = block_max(amax, red);
+    const float inv = 127.0f / fmaxf(amax, 1e-5f);
+    int qs = 0;
+    for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
+        float4 xv[CH], gv[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
+            gv[i] = buf_load_f4(rg, off_of(c0 + t4 + STRIDE * i));
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int k = c0 + t4 + STRIDE * i;
+            if (k < K) {
+                const float4 v = xn4(xv[i], gv[i], r);
+                const int a = quant_one(v.x, inv), b = quant_one(v.y, inv);
+                const int c = quant_one(v.z, inv), d = quant_one(v.w, inv);
+                qs += a + b + c + d;
+                sink.store_q(k, pack_char4(a, b, c, d));
+            }
+        }
+    }
+    qs = block_sum_int(qs, red);
+    if (threadIdx.x == 0) sink.store_row(inv, qs);
+    }
+}
+
+// Wave form (64 threads, no LDS, no barrier): lane j owns the four O256
+// chains j, 64 + j, 128 + j, 192 + j, i.e. the float4 groups at
+// k = 1024 i + 256 w + 4 j (w = 0..3).  Each chain group w is reduced by the
+// same halving tree (wave_tree_sum_f) and the four totals are added as
+// (g0 + g1) + (g2 + g3) -- the same bits as the block form.  Rows of up to
+// 1024 * CI elements stay in registers; longer rows take three passes.
+template <int CI, class Sink>
+__device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
+                                                   const float *__restrict__ gamma,
+                                                   float eps, int K, Sink &sink) {
+    const int lane = threadIdx.x & 63;
+    const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+    const auto rg = make_rsrc(gamma, 4u * (uint32_t)K);
+    auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bool in_regs = K <= 1024 * CI;
+    float4 xv[CI][4], gv[CI][4];
+    for (int c0 = 0; c0 < K; c0 += 1024 * CI) {
+#pragma unroll
+        for (int i = 0; i < CI; ++i)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
+                xv[i][w] = buf_load_f4(rx, off);
+                if (in_regs) gv[i][w] = buf_load_f4(rg, off);
+            }
+#pragma unroll
+        for (int i = 0; i < CI; ++i)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                p[w] = __builtin_fmaf(xv[i][w].x, xv[i][w].x, p[w]);
+                p[w] = __builtin_fmaf(xv[i][w].y, xv[i][w].y, p[w]);
+                p[w] = __builtin_fmaf(xv[i][w].z, xv[i][w].z, p[w]);
+                p[w] = __builtin_fmaf(xv[i][w].w, xv[i][w].w, p[w]);
+            }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) p[w] = wave_tree_sum_f(p[w]);
+    const float ss = (p[0] + p[1]) + (p[2] + p[3]);
+    const float r = 1.0f / sqrtf(ss / (float)K + eps);
+    float amax = 0.0f;
+    for (int c0 = 0; c0 < K; c0 += 1024 * CI) {
+        if (!in_regs) {
+#pragma unroll
+            for (int i = 0; i < CI; ++i)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
+                    xv[i][w] = buf_load_f4(rx, off);
+                    gv[i][w] = buf_load_f4(rg, off);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < CI; ++i)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) amax = amax4(amax, xn4(xv[i][w], gv[i][w], r));
+    }
+    amax = wave_max(amax);
+    const float inv = 127.0f / fmaxf(amax, 1e-5f);
+    int qs = 0;
+    for (int c0 = 0; c0 < K; c0 += 1024 * CI) {
+        if (!in_regs) {
+#pragma unroll
+            for (int i = 0; i < CI; ++i)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
+                    xv[i][w] = buf_load_f4(rx, off);
+                    gv[i][w] = buf_load_f4(rg, off);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < CI; ++i)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int k = c0 + 1024 * i + 256 * w + 4 * lane;
+                if (k < K) {
+                    const float4 v = xn4(xv[i][w], gv[i][w], r);
+                    const int a = quant_one(v.x, inv), b = quant_one(v.y, inv);
+                    const int c = quant_one(v.z, inv), d = quant_one(v.w, inv);
+                    qs += a + b + c + d;
+                    sink.store_q(k, pack_char4(a, b, c, d));
+                }
+            }
+    }
+    qs = wave_sum_int(qs);
+    if (lane == 0) sink.store_row(inv, qs);
 }
 
 }  // namespace bl
@@ -180,6 +401,7 @@ hipError_t launch_act_quant(const float *x, const float *gamma, float eps,
 // acc - qsum to `acc`.  With fused = true, q/inv/qsum are recomputed in
 // every workgroup from x, gamma, eps (M <= 4, M*K bytes of LDS) and
 // workgroup 0 writes them to q/inv/qsum (which are then outputs).
+// `variant` 0 picks a launch shape from M, K, N.
 hipError_t launch_gemv(const float *x, const float *gamma, float eps,
                        const int8_t *q, const float *inv, const int32_t *qsum,
                        const uint8_t *packed, float w_scale, int64_t M,

@@ -15,7 +15,9 @@
 // expanded there by shift+mask into the int8 B operand of
 // v_mfma_i32_16x16x64_i8 (codes 0/1/2; the activation sum is subtracted in
 // the epilogue).  Each wave computes a (BM/WM) x (BN/WN) sub-tile with
-// int32 accumulators in registers.
+// int32 accumulators in registers.  All loads are range-checked buffer
+// loads (ragged M, N and K tails read zeros) issued a full step ahead of
+// their use: LDS is double-buffered, one barrier per step.
 #include "common.hpp"
 
 namespace bl {
@@ -32,9 +34,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 16, NI = TN / 16;
-    constexpr int CHUNKS = BM * (kStepK / 16);  // 16-byte chunks of the A tile
-    static_assert(CHUNKS % NT == 0, "A tile chunks per thread");
-    __shared__ __align__(16) int8_t a_lds[BM * kLdsRow];
+    constexpr int CH = BM * (kStepK / 16) / NT;  // 16-byte A chunks per thread per step
+    static_assert(BM * (kStepK / 16) % NT == 0, "A tile chunks per thread");
+    __shared__ __align__(16) int8_t a_lds[2][BM * kLdsRow];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -46,16 +48,40 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
 
     const int nsteps = (K + kStepK - 1) / kStepK;
     const int nblocks = K / kBlockWeights;
-    const size_t rowbytes = (size_t)K / 4;
+    const uint32_t rowbytes = (uint32_t)K / 4;
+    // Range-checked views of this tile's activation rows and weight rows:
+    // rows past M or N read as zero.
+    const auto rq = make_rsrc(q + (size_t)m0 * K, (uint32_t)min(BM, M - m0) * (uint32_t)K);
+    const auto rw = make_rsrc(packed + (size_t)n0 * rowbytes,
+                              (uint32_t)min(BN, N - n0) * rowbytes);
 
-    const uint8_t *brow[NI];
-    bool bval[NI];
+    auto load_a = [&](v4i(&areg)[CH], int s) {
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-        const int n = n0 + wn * TN + 16 * ni + j;
-        bval[ni] = n < N;
-        brow[ni] = packed + (size_t)(bval[ni] ? n : 0) * rowbytes + 16 * kg;
-    }
+        for (int c = 0; c < CH; ++c) {
+            const int idx = tid + c * NT;
+            const int row = idx / (kStepK / 16);
+            const int k = s * kStepK + (idx % (kStepK / 16)) * 16;
+            areg[c] = buf_load16(rq, k < K ? (uint32_t)row * (uint32_t)K + (uint32_t)k : kOOB);
+        }
+    };
+    auto store_a = [&](int8_t *lds, const v4i(&areg)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int idx = tid + c * NT;
+            const int row = idx / (kStepK / 16);
+            const int col = (idx % (kStepK / 16)) * 16;
+            *reinterpret_cast<v4i *>(lds + row * kLdsRow + col) = areg[c];
+        }
+    };
+    auto load_b = [&](v4i(&breg)[NI], int s) {
+        const bool kv = 2 * s + (kg >> 1) < nblocks;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+            const uint32_t row = (uint32_t)(wn * TN + 16 * ni + j);
+            breg[ni] = buf_load16(rw, kv ? row * rowbytes + (uint32_t)s * kStepBytes + 16u * kg
+                                         : kOOB);
+        }
+    };
 
     v4i acc[MI][NI];
 #pragma unroll
@@ -63,41 +89,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4i{0, 0, 0, 0};
 
-    for (int s = 0; s < nsteps; ++s) {
-        // Stage the activation tile.
-#pragma unroll
-        for (int c = 0; c < CHUNKS / NT; ++c) {
-            const int idx = tid + c * NT;
-            const int row = idx / (kStepK / 16);
-            const int col = (idx % (kStepK / 16)) * 16;
-            const int m = m0 + row;
-            const int k = s * kStepK + col;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (m < M && k < K) v = *reinterpret_cast<const uint4 *>(q + (size_t)m * K + k);
-            *reinterpret_cast<uint4 *>(a_lds + row * kLdsRow + col) = v;
-        }
-        // Packed weights of this step, straight to registers.
-        const bool kv = 2 * s + (kg >> 1) < nblocks;
-        uint4 b[NI];
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-            b[ni] = (kv && bval[ni]) ? *reinterpret_cast<const uint4 *>(brow[ni] + (size_t)s * kStepBytes)
-                                     : make_uint4(0, 0, 0, 0);
-        __syncthreads();
-        const int koff = (kg >> 1) * kBlockWeights + 16 * (kg & 1);
+    const int koff = (kg >> 1) * kBlockWeights + 16 * (kg & 1);
+    auto compute = [&](const int8_t *lds, const v4i(&breg)[NI]) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             v4i bf[NI];
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) bf[ni] = unpack_field(b[ni], g);
+            for (int ni = 0; ni < NI; ++ni) bf[ni] = unpack_field(breg[ni], g);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const v4i a = *reinterpret_cast<const v4i *>(
-                    a_lds + (wm * TM + 16 * mi + j) * kLdsRow + koff + 32 * g);
+                    lds + (wm * TM + 16 * mi + j) * kLdsRow + koff + 32 * g);
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16(a, bf[ni], acc[mi][ni]);
             }
         }
+    };
+
+    // Software pipeline: while step s is contracted from LDS buffer s & 1,
+    // the loads of step s + 1 are in flight; they are written to the other
+    // buffer afterwards, and one barrier per step separates the two.
+    v4i areg[CH], b0[NI], b1[NI];
+    load_a(areg, 0);
+    load_b(b0, 0);
+    store_a(a_lds[0], areg);
+    __syncthreads();
+    for (int s = 0; s < nsteps; s += 2) {
+        const bool n1 = s + 1 < nsteps;
+        if (n1) {
+            load_a(areg, s + 1);
+            load_b(b1, s + 1);
+        }
+        compute(a_lds[0], b0);
+        if (n1) store_a(a_lds[1], areg);
+        __syncthreads();
+        if (!n1) break;
+        const bool n2 = s + 2 < nsteps;
+        if (n2) {
+            load_a(areg, s + 2);
+            load_b(b0, s + 2);
+        }
+        compute(a_lds[1], b1);
+        if (n2) store_a(a_lds[0], areg);
         __syncthreads();
     }
 
@@ -128,8 +161,7 @@ struct Tile {
     int BM, BN, WM, WN;
 };
 // Launch-shape table; every entry computes bit-identical results.
-constexpr Tile kTiles[] = {{128, 128, 2, 2}, {64, 128, 1, 4}, {128, 64, 2, 2},
-                           {64, 64, 2, 2},   {256, 128, 4, 2}};
+constexpr Tile kTiles[] = {{128, 128, 2, 2}, {128, 64, 2, 2}, {64, 64, 2, 2}, {64, 128, 1, 4}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 template <int BM, int BN, int WM, int WN>
@@ -156,7 +188,11 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
                        int64_t K, int64_t N, float *y, int32_t *acc,
                        int variant, hipStream_t s) {
     int v = variant;
-    if (v <= 0) v = 1;
+    if (v <= 0) {
+        // Largest tile that still gives every CU a workgroup.
+        auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+        v = tiles(128, 128) >= 256 ? 1 : tiles(128, 64) >= 256 ? 2 : 3;
+    }
 #define BL_GEMM_CASE(idx)                                                           \
     case idx:                                                                       \
         return launch_tile<kTiles[idx - 1].BM, kTiles[idx - 1].BN, kTiles[idx - 1].WM, \
@@ -166,7 +202,6 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         BL_GEMM_CASE(2)
         BL_GEMM_CASE(3)
         BL_GEMM_CASE(4)
-        BL_GEMM_CASE(5)
         default:
             return hipErrorInvalidValue;
     }

@@ -66,7 +66,7 @@ def fwd(L, x=A, p=A, s=0.02, g=A, eps=1e-6, M=1, K=256, N=256, y=A, ws=A, wsb=1 
 
 
 @pytest.mark.parametrize("M,K,N", [(0, 256, 4), (1, 100, 4), (1, 256, 0), (1, 64, 4),
-                                   (-3, 256, 4), (1, 1 << 41, 4)])
+                                   (-3, 256, 4), (1, 1 << 41, 4), (1, (1 << 22) + 128, 4)])
 def test_forward_shape_errors(L, M, K, N):
     assert fwd(L, M=M, K=K, N=N) == api.ERR_SHAPE
 

@@ -163,7 +163,7 @@ def mm_case(M, K, N, seed):
 
 MM_SHAPES = [(1, 128, 16), (1, 256, 100), (2, 384, 33), (5, 2560, 640), (16, 1024, 48),
              (17, 384, 70), (31, 256, 64), (32, 640, 129), (33, 1280, 31), (64, 2560, 256),
-             (65, 384, 300), (130, 1152, 200)]
+             (65, 384, 300), (130, 1152, 200), (16, 4096, 40), (9, 8192, 33)]
 
 
 @pytest.mark.parametrize("path", [1, 2])
@@ -296,3 +296,72 @@ def test_workload_sweep(torch, bl, orc, M):
     rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 12)]))
     cols = np.unique(np.concatenate([[0, 8191], rng.integers(0, 8192, 1000)]))
     run_linear(torch, bl, orc, work, 0, rows, cols)
+
+
+def test_graph_replay_matches_eager(torch, bl, orc):
+    """A captured HIP graph of several forwards (decode fused, decode staged,
+    prefill) replayed repeatedly, with eager work in between, gives the eager
+    bits every time."""
+    cases = [(1, 2560, 640), (8, 1024, 96), (40, 512, 130)]
+    data = []
+    for i, (M, K, N) in enumerate(cases):
+        x, w, t, g = mm_case(M, K, N, 900 + i)
+        P, s = bl.pack_i2s(dev(torch, w))
+        X, G = dev(torch, x), dev(torch, g)
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ws = bl.new_workspace(M, K)
+        data.append((X, P, s, G, N, out, ws))
+    eager = []
+    for X, P, s, G, N, out, ws in data:
+        eager.append(host(bl.forward(X, P, s, G, 1e-6, N, out=out, workspace=ws)).copy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for X, P, s, G, N, out, ws in data:
+            bl.forward(X, P, s, G, 1e-6, N, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for X, P, s, G, N, out, ws in data:
+            bl.forward(X, P, s, G, 1e-6, N, out=out, workspace=ws)
+    for rep in range(4):
+        announce("graph replay", rep)
+        for _, _, _, _, _, out, _ in data:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (X, P, s, G, N, out, ws), ref in zip(data, eager):
+            assert np.array_equal(host(out), ref), rep
+        # eager work between replays
+        bl.forward(*data[0][:4], 1e-6, data[0][4], out=torch.empty_like(data[0][5]))
+        torch.cuda.synchronize()
+
+
+def test_act_quant_order_sensitive_rows(torch, bl, orc):
+    """Rows whose fp32 sum of squares depends on the summation order (the
+    hand-derived values pinned in the oracle tests), through both GPU
+    quantisation paths (separate kernel and fused decode prologue)."""
+    K = 2048
+    rows = []
+    for idx in ([0, 1], [0, 4, 12], [0, 1, 2], [0, 256, 257], [0, 1024, 1025], [0, 512, 768]):
+        v = np.zeros(K, np.float32)
+        v[idx[0]] = 4096 if len(idx) > 2 else 2.0 ** -12
+        for i in idx[1:]:
+            v[i] = 1.0 if len(idx) > 2 else 1 + 2.0 ** -12
+        rows.append(v)
+    x = np.stack(rows)
+    g = np.ones(K, np.float32)
+    q_r, inv_r, qs_r = orc.act_quant(x, g, 1e-6)
+    q, inv, qs = bl.act_quant(dev(torch, x), dev(torch, g), 1e-6)
+    assert np.array_equal(host(q), q_r) and np.array_equal(host(qs), qs_r)
+    assert np.array_equal(host(inv).view(np.uint32), inv_r.view(np.uint32))
+    P, s = bl.pack_i2s(torch.ones((16, K), dtype=torch.float32, device="cuda"))
+    for m in range(len(rows)):
+        ws = bl.new_workspace(1, K)
+        bl.forward(dev(torch, x[m:m + 1]), P, s, dev(torch, g), 1e-6, 16, workspace=ws, path=1, fuse=1)
+        torch.cuda.synchronize()
+        qf, invf, qsf = bl.workspace_views(ws, 1, K)
+        assert np.array_equal(host(qf)[0], q_r[m]) and host(qsf)[0] == qs_r[m]
+        assert host(invf).view(np.uint32)[0] == inv_r.view(np.uint32)[m]
