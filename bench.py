@@ -75,10 +75,10 @@ class Prepared:
         torch.cuda.synchronize()
 
     def step(self, api, r: int):
-        for d in self.lin:
-            L = d["L"]
-            api.forward(d["x"], d["P"][r % self.copies], d["s"], d["g"], self.work.eps, L.N,
-                        out=d["y"], workspace=d["ws"])
+        """One step: every BitLinear of the workload, as one batched call
+        (decode-sized ones share a launch; bit-identical to single calls)."""
+        api.forward_batch([(d["x"], d["P"][r % self.copies], d["s"], d["g"], self.work.eps,
+                            d["y"], d["ws"]) for d in self.lin])
 
 
 def capture(torch, fn):
@@ -141,15 +141,26 @@ def linear_bytes(L):
     return L.N * L.K // 4 + 4 * L.M * L.K + 4 * L.K + 4 * L.M * L.N
 
 
-def traffic_from_profiles(kernel_src: str):
-    """HBM bytes per launch from the committed PMC summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_decode_layer.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "ternary_bit_linear_amd", "csrc", f)
+                  for f in ("common.hpp", "gemv.hip", "act_quant.hip", "gemm.hip")]
+
+
+def sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(name: str):
+    """HBM bytes per launch from the committed PMC summary
+    profiles/traffic_<name>.json, if it was taken on the current kernel
+    sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(kernel_src, "rb").read()
-    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("sources_sha256") != sources_sha256():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -215,6 +226,9 @@ def main():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--pmc-app", action="store_true",
+                    help="no timing: run --steps steps of the workload and a 256 MiB device "
+                         "copy (the calibration kernel for HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
@@ -230,31 +244,56 @@ def main():
 
     work = workload_by_name(args.workload)
     prep = Prepared(torch, api, work)
+    if args.pmc_app:
+        for r in range(args.steps):
+            prep.step(api, r)
+        torch.cuda.synchronize()
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")  # 256 MiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_app": work.name, "steps": args.steps, "copy_bytes": a.numel() * 4}))
+        return
     ms = time_steps(torch, api, prep, args.steps, args.warmup)
     step_bytes = sum(linear_bytes(L) for L in work.linears)
     gbs = step_bytes / (ms * 1e-3) / 1e9
     by = time_launches(torch, api, prep)
-
-    # Dominant kernel: the forward launch of the largest BitLinear shape.
-    dom_name, (dom_L, dom_s) = max(by.items(), key=lambda kv: linear_bytes(kv[1][0]))
     M = work.linears[0].M
     decode = M <= 16
-    if decode:
-        ach = linear_bytes(dom_L) / dom_s / 1e9
+    # Decode BitLinears with M == 1 and K <= 8192 take the fused kernel and a
+    # step of them is one launch (up to 8 per launch).
+    fused_all = all(L.M == 1 and L.K <= 8192 for L in work.linears)
+    launches = -(-len(work.linears) // 8)
+    if decode and fused_all:
+        avg_s = ms * 1e-3 / launches
+        ach = step_bytes / launches / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profiles(os.path.join(ROOT, "ternary_bit_linear_amd",
-                                                              "csrc", "gemv.hip")),
-                "kernel": "gemv_kernel (fused RMSNorm+quant, I2_S x int8 MFMA)",
-                "launch": f"{dom_name} M={dom_L.M} K={dom_L.K} N={dom_L.N}",
-                "avg_launch_us": round(dom_s * 1e6, 3),
-                "bytes_per_launch": linear_bytes(dom_L)}
+                "traffic": traffic_from_profiles(args.workload),
+                "kernel": "gemv_fused_kernel (RMSNorm + int8 quant + I2_S x int8 MFMA, "
+                          f"{len(work.linears)} BitLinears per launch)",
+                "launches_per_step": launches,
+                "avg_launch_us": round(avg_s * 1e6, 3),
+                "bytes_per_launch": step_bytes // launches}
     else:
-        ach = 2 * dom_L.M * dom_L.N * dom_L.K / dom_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS,
-                "unit": "TOPS", "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None,
-                "kernel": "act_quant_kernel + gemm_kernel", "launch": f"{dom_name} M={dom_L.M} "
-                f"K={dom_L.K} N={dom_L.N}", "avg_launch_us": round(dom_s * 1e6, 3)}
+        dom_name, (dom_L, dom_s) = max(by.items(), key=lambda kv: linear_bytes(kv[1][0]))
+        if decode:
+            ach = linear_bytes(dom_L) / dom_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": traffic_from_profiles(args.workload),
+                    "kernel": "act_quant + gemv (decode route)",
+                    "launch": f"{dom_name} M={dom_L.M} K={dom_L.K} N={dom_L.N}",
+                    "avg_launch_us": round(dom_s * 1e6, 3),
+                    "bytes_per_launch": linear_bytes(dom_L)}
+        else:
+            ach = 2 * dom_L.M * dom_L.N * dom_L.K / dom_s / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS,
+                    "unit": "TOPS", "frac": round(ach / INT8_PEAK_TOPS, 4),
+                    "traffic": traffic_from_profiles(args.workload),
+                    "kernel": "act_quant_kernel + gemm_kernel",
+                    "launch": f"{dom_name} M={dom_L.M} K={dom_L.K} N={dom_L.N}",
+                    "avg_launch_us": round(dom_s * 1e6, 3)}
     per_linear = {n: {"M": L.M, "K": L.K, "N": L.N, "us": round(t * 1e6, 3),
                       "GBs": round(linear_bytes(L) / t / 1e9, 1)}
                   for n, (L, t) in by.items()}
@@ -272,7 +311,7 @@ def main():
                    "algorithmic_bytes_per_step": step_bytes,
                    "weight_copies_rotated": prep.copies},
         "roofline": roof,
-        "per_linear": per_linear,
+        "per_linear_single_launch": per_linear,
     }
     del prep
     torch.cuda.empty_cache()

@@ -78,9 +78,10 @@ typedef enum {
 
 /* Launch options for bitlinear_forward_ex / bitlinear_matmul_i2s_ex.
  *   path:    a bl_path value.
- *   fuse:    forward only.  -1 = automatic; 0 = separate quantisation
- *            kernel; 1 = RMSNorm + quantisation recomputed inside every
- *            workgroup of the decode kernel (GEMV route only, M <= 4).
+ *   fuse:    forward only.  -1 = automatic (fused for M == 1 and
+ *            K <= 8192); 0 = separate quantisation kernel; 1 = RMSNorm +
+ *            quantisation recomputed inside every workgroup of the decode
+ *            kernel (GEMV route only, M <= 4 and M*K <= 32768).
  *   variant: 0 = automatic; otherwise an index into the route's table of
  *            launch shapes (1..bitlinear_num_variants(path)); every variant
  *            returns bit-identical results.
@@ -174,6 +175,33 @@ bl_status bitlinear_forward_ex(const float *x, const uint8_t *packed_w,
                                int64_t M, int64_t K, int64_t N, float *y,
                                void *workspace, size_t workspace_bytes,
                                const bl_launch *launch, void *stream);
+
+/* One BitLinear forward for bitlinear_forward_batch: the arguments of
+ * bitlinear_forward, same meaning and rules. */
+typedef struct {
+    const float *x;
+    const uint8_t *packed_w;
+    float w_scale;
+    const float *gamma;
+    float eps;
+    int64_t M, K, N;
+    float *y;
+    void *workspace;
+    size_t workspace_bytes;
+} bl_forward_desc;
+
+/* Several independent BitLinear forwards, e.g. the BitLinears of one decoder
+ * layer at decode (the survey's decode-layer launch).  Results are
+ * bit-identical to calling bitlinear_forward_ex(descs[i], launch) for each i;
+ * the decode-sized ones (M <= 4 with the fused quantisation; up to 8 per
+ * launch) share one kernel launch, the others run one by one.
+ *   descs:  HOST array of `count` descriptors (1 <= count <= 64, else
+ *           BL_ERR_INVALID_ARG); each is validated as bitlinear_forward
+ *           validates its arguments, all before anything is enqueued.
+ *   No output (y, workspace) may overlap any input or output of another
+ *   descriptor.  Asynchronous on `stream`. */
+bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
+                                  const bl_launch *launch, void *stream);
 
 /* Stage: RMSNorm + per-row absmax int8 quantisation (the first two steps of
  * bitlinear_forward, bit-identical to them).

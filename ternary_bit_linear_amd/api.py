@@ -30,6 +30,15 @@ class Launch(ctypes.Structure):
                 ("variant", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class ForwardDesc(ctypes.Structure):
+    """bl_forward_desc: the arguments of one bitlinear_forward."""
+    _fields_ = [("x", ctypes.c_void_p), ("packed_w", ctypes.c_void_p),
+                ("w_scale", ctypes.c_float), ("gamma", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("M", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("y", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 SIGNATURES = {
     "bitlinear_status_string": (ctypes.c_char_p, [_i]),
     "bitlinear_abi_version": (_i, []),
@@ -42,6 +51,7 @@ SIGNATURES = {
     "bitlinear_forward": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p, _sz, _p]),
     "bitlinear_forward_ex": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p, _sz,
                                   ctypes.POINTER(Launch), _p]),
+    "bitlinear_forward_batch": (_i, [ctypes.POINTER(ForwardDesc), _i, ctypes.POINTER(Launch), _p]),
     "bitlinear_act_quant": (_i, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
     "bitlinear_matmul_i2s": (_i, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "bitlinear_matmul_i2s_ex": (_i, [_p, _p, _p, _i64, _i64, _i64, _p,
@@ -197,6 +207,23 @@ def forward(x, packed, w_scale: float, gamma, eps: float = 1e-6, N: int | None =
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
         _launch(path, fuse, variant), _stream()), "forward")
     return out
+
+
+def forward_batch(items, path: int = PATH_AUTO, fuse: int = -1, variant: int = 0):
+    """Several independent forwards in as few launches as possible.
+    items: sequence of (x, packed, w_scale, gamma, eps, out, workspace) with
+    out fp32 [M][N] preallocated; bit-identical to forward() per item."""
+    torch = _torch()
+    arr = (ForwardDesc * len(items))()
+    for i, (x, packed, w_scale, gamma, eps, out, ws) in enumerate(items):
+        M, K = x.shape
+        N = out.shape[1]
+        arr[i] = ForwardDesc(_dev(x, torch.float32, "x"), _dev(packed, torch.uint8, "packed"),
+                             w_scale, _dev(gamma, torch.float32, "gamma"), eps, M, K, N,
+                             _dev(out, torch.float32, "out"), _dev(ws, torch.uint8, "workspace"),
+                             ws.numel())
+    _check(lib().bitlinear_forward_batch(arr, len(items), _launch(path, fuse, variant), _stream()),
+           "forward_batch")
 
 
 def workspace_views(workspace, M: int, K: int):

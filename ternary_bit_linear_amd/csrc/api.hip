@@ -76,24 +76,85 @@ Workspace carve(void *ws, int64_t M, int64_t K) {
     return w;
 }
 
-// Shared tail of forward / matmul: route choice and launch of the
-// contraction, with y (rescale epilogue) or acc (int32 epilogue).
-bl_status run_contraction(const float *x, const float *gamma, float eps,
-                          const int8_t *q, const float *inv, const int32_t *qsum,
+// Contraction with q / inv / qsum already computed: route choice and
+// launch, with y (rescale epilogue) or acc (int32 epilogue).
+bl_status run_contraction(const int8_t *q, const float *inv, const int32_t *qsum,
                           const uint8_t *packed, float w_scale, int64_t M, int64_t K,
-                          int64_t N, float *y, int32_t *acc, bool fused,
-                          const bl_launch *l, hipStream_t s) {
+                          int64_t N, float *y, int32_t *acc, const bl_launch *l, hipStream_t s) {
     int path = l ? l->path : BL_PATH_AUTO;
     if (path == BL_PATH_AUTO) path = (M <= kGemvMaxM) ? BL_PATH_GEMV : BL_PATH_GEMM;
     const int variant = l ? l->variant : 0;
     if (path == BL_PATH_GEMV) {
-        if (!fused && (M + 15) / 16 > 65535) return BL_ERR_SHAPE;
-        return hip_status(bl::launch_gemv(x, gamma, eps, q, inv, qsum, packed, w_scale, M, K,
-                                          N, y, acc, fused, variant, s));
+        if ((M + 15) / 16 > 65535) return BL_ERR_SHAPE;
+        return hip_status(bl::launch_gemv(q, inv, qsum, packed, w_scale, M, K, N, y, acc,
+                                          variant, s));
     }
     if ((M + 63) / 64 > 65535) return BL_ERR_SHAPE;
     return hip_status(bl::launch_gemm(q, inv, qsum, packed, w_scale, M, K, N, y, acc, variant, s));
 }
+
+bl_status validate_forward(const bl_forward_desc &d, const bl_launch *launch) {
+    if (bl_status st = check_mk(d.M, d.K)) return st;
+    if (bl_status st = check_nk(d.N, d.K)) return st;
+    if (bl_status st = check_mn(d.M, d.N)) return st;
+    if (!d.x || !d.packed_w || !d.gamma || !d.y || !d.workspace) return BL_ERR_INVALID_ARG;
+    if (!(d.eps > 0.0f) || !std::isfinite(d.eps) || !std::isfinite(d.w_scale))
+        return BL_ERR_INVALID_ARG;
+    if (bl_status st = check_launch(launch, true)) return st;
+    if (!aligned16(d.x) || !aligned16(d.gamma) || !aligned16(d.packed_w) || !aligned16(d.y) ||
+        !aligned16(d.workspace))
+        return BL_ERR_ALIGN;
+    if (d.workspace_bytes < bitlinear_workspace_bytes(d.M, d.K)) return BL_ERR_WORKSPACE;
+    const int path = launch ? launch->path : BL_PATH_AUTO;
+    const bool gemv = path == BL_PATH_GEMV || (path == BL_PATH_AUTO && d.M <= kGemvMaxM);
+    const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
+    if (launch && launch->fuse == 1 && !(gemv && fits)) return BL_ERR_INVALID_ARG;
+    return BL_OK;
+}
+
+// Whether a validated forward takes the fused decode kernel.  Automatic
+// choice: fused for one token with K <= 8192 (the whole row of x and gamma
+// fits in registers, one round trip); otherwise the separate quantisation
+// kernel is faster (measured on MI355X).
+bool takes_fused(const bl_forward_desc &d, const bl_launch *launch) {
+    const int path = launch ? launch->path : BL_PATH_AUTO;
+    const bool gemv = path == BL_PATH_GEMV || (path == BL_PATH_AUTO && d.M <= kGemvMaxM);
+    const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
+    if (launch && launch->fuse == 0) return false;
+    if (launch && launch->fuse == 1) return gemv && fits;
+    return gemv && fits && d.M == 1 && d.K <= 8 * 1024;
+}
+
+bl::FusedDecode fused_of(const bl_forward_desc &d) {
+    const Workspace ws = carve(d.workspace, d.M, d.K);
+    bl::FusedDecode f;
+    f.x = d.x;
+    f.gamma = d.gamma;
+    f.packed = d.packed_w;
+    f.y = d.y;
+    f.q = ws.q;
+    f.inv = ws.inv;
+    f.qsum = ws.qsum;
+    f.eps = d.eps;
+    f.w_scale = d.w_scale;
+    f.M = d.M;
+    f.K = d.K;
+    f.N = d.N;
+    return f;
+}
+
+// Enqueue one validated forward that does not take the fused kernel.
+bl_status enqueue_unfused(const bl_forward_desc &d, const bl_launch *launch, hipStream_t s) {
+    const Workspace ws = carve(d.workspace, d.M, d.K);
+    if (bl::launch_act_quant(d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum, s) !=
+        hipSuccess)
+        return BL_ERR_HIP;
+    return run_contraction(ws.q, ws.inv, ws.qsum, d.packed_w, d.w_scale, d.M, d.K, d.N, d.y,
+                           nullptr, launch, s);
+}
+
+constexpr int kMaxBatchDescs = 64;
+constexpr int kFusedPerLaunch = 8;
 
 }  // namespace
 
@@ -198,8 +259,8 @@ bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum, const ui
     if (!q || !qsum || !packed_w || !acc) return BL_ERR_INVALID_ARG;
     if (bl_status st = check_launch(launch, false)) return st;
     if (!aligned16(q) || !aligned16(packed_w)) return BL_ERR_ALIGN;
-    return run_contraction(nullptr, nullptr, 0.0f, q, nullptr, qsum, packed_w, 0.0f, M, K, N,
-                           nullptr, acc, false, launch, as_stream(stream));
+    return run_contraction(q, nullptr, qsum, packed_w, 0.0f, M, K, N, nullptr, acc, launch,
+                           as_stream(stream));
 }
 
 bl_status bitlinear_matmul_i2s(const int8_t *q, const int32_t *qsum, const uint8_t *packed_w,
@@ -211,35 +272,15 @@ bl_status bitlinear_forward_ex(const float *x, const uint8_t *packed_w, float w_
                                const float *gamma, float eps, int64_t M, int64_t K, int64_t N,
                                float *y, void *workspace, size_t workspace_bytes,
                                const bl_launch *launch, void *stream) {
-    if (bl_status st = check_mk(M, K)) return st;
-    if (bl_status st = check_nk(N, K)) return st;
-    if (bl_status st = check_mn(M, N)) return st;
-    if (!x || !packed_w || !gamma || !y || !workspace) return BL_ERR_INVALID_ARG;
-    if (!(eps > 0.0f) || !std::isfinite(eps) || !std::isfinite(w_scale)) return BL_ERR_INVALID_ARG;
-    if (bl_status st = check_launch(launch, true)) return st;
-    if (!aligned16(x) || !aligned16(gamma) || !aligned16(packed_w) || !aligned16(y) ||
-        !aligned16(workspace))
-        return BL_ERR_ALIGN;
-    if (workspace_bytes < bitlinear_workspace_bytes(M, K)) return BL_ERR_WORKSPACE;
-
-    const int path = launch ? launch->path : BL_PATH_AUTO;
-    const bool gemv = path == BL_PATH_GEMV || (path == BL_PATH_AUTO && M <= kGemvMaxM);
-    const bool fits = M <= kFuseMaxM && M * K <= kFuseMaxLds;
-    bool fused;
-    if (!launch || launch->fuse == -1)
-        fused = gemv && fits;
-    else
-        fused = launch->fuse == 1;
-    if (fused && !(gemv && fits)) return BL_ERR_INVALID_ARG;
-
+    const bl_forward_desc d{x, packed_w, w_scale, gamma, eps, M, K, N, y, workspace,
+                            workspace_bytes};
+    if (bl_status st = validate_forward(d, launch)) return st;
     hipStream_t s = as_stream(stream);
-    const Workspace ws = carve(workspace, M, K);
-    if (!fused) {
-        if (bl::launch_act_quant(x, gamma, eps, M, K, ws.q, ws.inv, ws.qsum, s) != hipSuccess)
-            return BL_ERR_HIP;
+    if (takes_fused(d, launch)) {
+        const bl::FusedDecode f = fused_of(d);
+        return hip_status(bl::launch_gemv_fused(&f, 1, launch ? launch->variant : 0, s));
     }
-    return run_contraction(x, gamma, eps, ws.q, ws.inv, ws.qsum, packed_w, w_scale, M, K, N, y,
-                           nullptr, fused, launch, s);
+    return enqueue_unfused(d, launch, s);
 }
 
 bl_status bitlinear_forward(const float *x, const uint8_t *packed_w, float w_scale,
@@ -247,6 +288,30 @@ bl_status bitlinear_forward(const float *x, const uint8_t *packed_w, float w_sca
                             float *y, void *workspace, size_t workspace_bytes, void *stream) {
     return bitlinear_forward_ex(x, packed_w, w_scale, gamma, eps, M, K, N, y, workspace,
                                 workspace_bytes, nullptr, stream);
+}
+
+bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
+                                  const bl_launch *launch, void *stream) {
+    if (!descs || count < 1 || count > kMaxBatchDescs) return BL_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i)
+        if (bl_status st = validate_forward(descs[i], launch)) return st;
+    hipStream_t s = as_stream(stream);
+    const int variant = launch ? launch->variant : 0;
+    bl::FusedDecode group[kFusedPerLaunch];
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        if (takes_fused(descs[i], launch)) {
+            group[n++] = fused_of(descs[i]);
+            if (n == kFusedPerLaunch) {
+                if (bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
+                n = 0;
+            }
+        } else if (bl_status st = enqueue_unfused(descs[i], launch, s)) {
+            return st;
+        }
+    }
+    if (n > 0 && bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
+    return BL_OK;
 }
 
 }  // extern "C"

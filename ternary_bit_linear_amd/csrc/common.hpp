@@ -396,17 +396,31 @@ hipError_t launch_act_quant(const float *x, const float *gamma, float eps,
                             int64_t M, int64_t K, int8_t *q, float *inv,
                             int32_t *qsum, hipStream_t s);
 
-// Decode route (tokens in groups of 16, int8 MFMA 16x16x64).  With y != NULL
-// the epilogue writes y = (acc - qsum) * (w_scale / inv); otherwise it writes
-// acc - qsum to `acc`.  With fused = true, q/inv/qsum are recomputed in
-// every workgroup from x, gamma, eps (M <= 4, M*K bytes of LDS) and
-// workgroup 0 writes them to q/inv/qsum (which are then outputs).
-// `variant` 0 picks a launch shape from M, K, N.
-hipError_t launch_gemv(const float *x, const float *gamma, float eps,
-                       const int8_t *q, const float *inv, const int32_t *qsum,
-                       const uint8_t *packed, float w_scale, int64_t M,
-                       int64_t K, int64_t N, float *y, int32_t *acc,
-                       bool fused, int variant, hipStream_t s);
+// Decode route, separate quantisation (q / inv / qsum already computed):
+// tokens in groups of 16 on int8 MFMA 16x16x64.  With y != NULL the
+// epilogue writes y = (acc - qsum) * (w_scale / inv); otherwise it writes
+// acc - qsum to `acc`.  `variant` 0 picks a launch shape from K.
+hipError_t launch_gemv(const int8_t *q, const float *inv, const int32_t *qsum,
+                       const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
+                       float *y, int32_t *acc, int variant, hipStream_t s);
+
+// Decode route with the RMSNorm + quantisation fused in (M <= kFuseMaxM,
+// M*K <= kFuseMaxLds): every workgroup recomputes q from x, gamma, eps; the
+// first workgroup of each problem also writes q / inv / qsum.  One launch
+// serves `count` (<= 8) independent problems.
+struct FusedDecode {
+    const float *x;
+    const float *gamma;
+    const uint8_t *packed;
+    float *y;
+    int8_t *q;
+    float *inv;
+    int32_t *qsum;
+    float eps;
+    float w_scale;
+    int64_t M, K, N;
+};
+hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipStream_t s);
 int gemv_num_variants();
 
 // Prefill route (activation tiles staged in LDS, int8 MFMA).  Same

@@ -37,6 +37,8 @@
 //    arithmetic, same order).
 //  1 staged: the token group's q rows are copied into LDS once.
 //  2 global: q fragments are loaded from global memory (L2) per batch.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace bl {
@@ -57,18 +59,47 @@ struct LdsRowSink {
     }
 };
 
-// FM (MODE 0): compile-time bound on the token rows (M <= FM); LONG
-// (MODE 0): rows longer than 8192 take the streamed normalisation.  TH:
-// token halves (1 for M <= 8, 2 for M <= 16).
+// Arguments of one contraction (one BitLinear) as seen by a workgroup.
+// The 4 waves of a workgroup work on 4 / ks tile groups at once (a set),
+// ks waves splitting each tile group's K range.  tg_first / tg_stride:
+// this workgroup's first set and the stride of its walk (its index and the
+// number of workgroups on this problem).
+struct GemvArgs {
+    const float *x;
+    const float *gamma;
+    const int8_t *q;
+    const float *inv;
+    const int32_t *qsum;
+    const uint8_t *packed;
+    float *y;
+    int32_t *acc_out;
+    int8_t *q_out;
+    float *inv_out;
+    int32_t *qsum_out;
+    float eps;
+    float w_scale;
+    int M, K, N;
+    int m0;
+    int tg_first, tg_stride;  // in units of tile-group sets (see ks)
+    int ks;                   // waves per tile group (K split): 1, 2 or 4
+};
+
+// Decode contraction of one workgroup.  FM (MODE 0): compile-time bound on
+// the token rows (M <= FM); LONG (MODE 0): rows longer than 8192 take the
+// streamed normalisation.  TH: token halves (1 for M <= 8, 2 for M <= 16).
 template <int R, int U, int MODE, bool OUT_Y, int FM, bool LONG, int TH>
-__global__ __launch_bounds__(256) void gemv_kernel(
-    const float *__restrict__ x, const float *__restrict__ gamma, float eps,
-    const int8_t *__restrict__ q, const float *__restrict__ inv,
-    const int32_t *__restrict__ qsum, const uint8_t *__restrict__ packed,
-    float w_scale, int M, int K, int N, float *__restrict__ y,
-    int32_t *__restrict__ acc_out, int8_t *__restrict__ q_out,
-    float *__restrict__ inv_out, int32_t *__restrict__ qsum_out) {
+__device__ __forceinline__ void gemv_body(const GemvArgs &A) {
     extern __shared__ __align__(16) int8_t q_lds[];
+    const float *__restrict__ x = A.x;
+    const float *__restrict__ gamma = A.gamma;
+    const int8_t *__restrict__ q = A.q;
+    const float *__restrict__ inv = A.inv;
+    const int32_t *__restrict__ qsum = A.qsum;
+    const uint8_t *__restrict__ packed = A.packed;
+    float *__restrict__ y = A.y;
+    int32_t *__restrict__ acc_out = A.acc_out;
+    const float eps = A.eps, w_scale = A.w_scale;
+    const int M = A.M, K = A.K, N = A.N;
     __shared__ float red[4];
     __shared__ float inv_sh[4];
     __shared__ int qsum_sh[4];
@@ -79,13 +110,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(
     const int wid = tid >> 6;
     const int r8 = lane & 7;    // weight row within the tile (load role)
     const int ch = lane >> 3;   // 16-byte chunk within the 128-byte step
-    const int m0 = MODE == 0 ? 0 : blockIdx.y * 16;
+    const int m0 = A.m0;
     const int mg = min(16, M - m0);  // tokens of this workgroup's group
 
     const uint32_t rowbytes = (uint32_t)K / 4;
     const int nsteps = (int)((rowbytes + kStep - 1) / kStep);
-    const int nb = (nsteps + kW * U - 1) / (kW * U);
+    const int ks = A.ks;
+    const int slots = kW / ks;                // tile groups per set
+    const int sg = wid / ks, kp = wid % ks;   // this wave's tile group slot / K part
+    const int nb = (nsteps + ks * U - 1) / (ks * U);
     const int ntg = (N + kTileRows * R - 1) / (kTileRows * R);
+    const int nset = (ntg + slots - 1) / slots;
     // MODE 2: q rows of this token group, range-checked.
     const auto rq = make_rsrc(q + (size_t)m0 * K, (uint32_t)(mg * K));
 
@@ -98,18 +133,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[g][h][r] = v4i{0, 0, 0, 0};
 
-    int tg = blockIdx.x;
+    int st = A.tg_first;  // current set
     int b = 0;
 
-    // Weights of batch b_ of tile group tg_ (wave w takes steps
-    // b_*W*U + w*U + [0, U)); rows past N and bytes past the row read zero.
-    auto load_batch = [&](v4i(&buf)[U][R], int tg_, int b_) {
-        const int n0 = tg_ * kTileRows * R;
-        const int rows = min(kTileRows * R, N - n0);
-        const auto rw = make_rsrc(packed + (size_t)n0 * rowbytes, (uint32_t)rows * rowbytes);
+    // Weights of batch b_ of this wave's tile group in set st_ (the ks
+    // waves of a tile group take steps b_*ks*U + kp*U + [0, U)); rows past
+    // N, tile groups past the last and bytes past the row read zero.
+    auto load_batch = [&](v4i(&buf)[U][R], int st_, int b_) {
+        const int n0 = (st_ * slots + sg) * kTileRows * R;
+        const int rows = max(0, min(kTileRows * R, N - n0));
+        const auto rw = make_rsrc(packed + (size_t)min(n0, N) * rowbytes, (uint32_t)rows * rowbytes);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = b_ * kW * U + wid * U + u;
+            const int s = b_ * ks * U + kp * U + u;
             const uint32_t cb = (uint32_t)s * kStep + 16u * ch;
             const bool kv = (s < nsteps) && (cb < rowbytes);
 #pragma unroll
@@ -124,7 +160,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(
         {
             LdsRowSink sink{q_lds, inv_sh, qsum_sh};
             block_act_quant_row<8, LONG>(x, gamma, eps, K, red, sink,
-                                         [&] { load_batch(bcur, tg, b); });
+                                         [&] { load_batch(bcur, st, b); });
         }
 #pragma unroll
         for (int m = 1; m < FM; ++m) {
@@ -134,37 +170,37 @@ __global__ __launch_bounds__(256) void gemv_kernel(
             }
         }
         __syncthreads();
-        if (blockIdx.x == 0) {
+        if (A.tg_first == 0) {
             for (int i = tid; i < M * K / 16; i += 256)
-                reinterpret_cast<uint4 *>(q_out)[i] = reinterpret_cast<const uint4 *>(q_lds)[i];
+                reinterpret_cast<uint4 *>(A.q_out)[i] = reinterpret_cast<const uint4 *>(q_lds)[i];
             if (tid < M) {
-                inv_out[tid] = inv_sh[tid];
-                qsum_out[tid] = qsum_sh[tid];
+                A.inv_out[tid] = inv_sh[tid];
+                A.qsum_out[tid] = qsum_sh[tid];
             }
         }
     } else if constexpr (MODE == 1) {
         const uint4 *src = reinterpret_cast<const uint4 *>(q + (size_t)m0 * K);
         for (int i = tid; i < mg * K / 16; i += 256)
             reinterpret_cast<uint4 *>(q_lds)[i] = src[i];
-        load_batch(bcur, tg, b);
+        load_batch(bcur, st, b);
         __syncthreads();
     } else {
-        load_batch(bcur, tg, b);
+        load_batch(bcur, st, b);
     }
 
     for (;;) {
-        int tg2 = tg, b2 = b + 1;
+        int st2 = st, b2 = b + 1;
         if (b2 == nb) {
-            tg2 += gridDim.x;
+            st2 += A.tg_stride;
             b2 = 0;
         }
-        const bool more = tg2 < ntg;
-        if (more) load_batch(bnxt, tg2, b2);
+        const bool more = st2 < nset;
+        if (more) load_batch(bnxt, st2, b2);
 
         // Contract the current batch.
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = b * kW * U + wid * U + u;
+            const int s = b * ks * U + kp * U + u;
             const uint32_t cb = (uint32_t)s * kStep + 16u * ch;
             const bool kv = (s < nsteps) && (cb < rowbytes);
             // k of this lane's chunk: block cb / 32, half (cb / 16) % 2.
@@ -195,7 +231,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(
         }
 
         if (b == nb - 1) {
-            // Tile group done: sum the fields, then the waves' partials.
+            // Set done: sum the fields, then the ks waves of each tile group.
 #pragma unroll
             for (int h = 0; h < TH; ++h)
 #pragma unroll
@@ -209,38 +245,40 @@ __global__ __launch_bounds__(256) void gemv_kernel(
             // D(i, j) lives in lane j + 16*(i/4), register i%4.  Useful
             // lanes: [0, 8) and [16, 24) (even chunks, rows j, tokens
             // 4*(lane/16) + c) and lane + 40 (odd chunks, same rows/tokens).
-            for (int hr = wid; hr < TH * R; hr += kW) {
-                const int h = hr / R, r = hr % R;
-                const int l = lane;
-                const bool useful = (l & 8) == 0 && l < 24;
-                if (useful) {
-                    v4i t = part[0][h][r][l] + part[0][h][r][l + 40];
+            const int tg = st * slots + sg;
+            const int l = lane;
+            if (kp == 0 && tg < ntg && (l & 8) == 0 && l < 24) {
 #pragma unroll
-                    for (int w = 1; w < kW; ++w) t += part[w][h][r][l] + part[w][h][r][l + 40];
-                    const int n = tg * kTileRows * R + kTileRows * r + (l & 7);
-                    if (n < N) {
+                for (int h = 0; h < TH; ++h)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const int mloc = 8 * h + 4 * (l >> 4) + c;
-                            if (mloc < mg) {
-                                const int m = m0 + mloc;
-                                const int qs = MODE == 0 ? qsum_sh[m] : qsum[m];
-                                const int v = t[c] - qs;
-                                if (OUT_Y) {
-                                    const float iv = MODE == 0 ? inv_sh[m] : inv[m];
-                                    y[(size_t)m * N + n] = (float)v * (w_scale / iv);
-                                } else {
-                                    acc_out[(size_t)m * N + n] = v;
+                    for (int r = 0; r < R; ++r) {
+                        v4i t = part[wid][h][r][l] + part[wid][h][r][l + 40];
+                        for (int w = 1; w < ks; ++w)
+                            t += part[wid + w][h][r][l] + part[wid + w][h][r][l + 40];
+                        const int n = tg * kTileRows * R + kTileRows * r + (l & 7);
+                        if (n < N) {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const int mloc = 8 * h + 4 * (l >> 4) + c;
+                                if (mloc < mg) {
+                                    const int m = m0 + mloc;
+                                    const int qs = MODE == 0 ? qsum_sh[m] : qsum[m];
+                                    const int v = t[c] - qs;
+                                    if (OUT_Y) {
+                                        const float iv = MODE == 0 ? inv_sh[m] : inv[m];
+                                        y[(size_t)m * N + n] = (float)v * (w_scale / iv);
+                                    } else {
+                                        acc_out[(size_t)m * N + n] = v;
+                                    }
                                 }
                             }
                         }
                     }
-                }
             }
             __syncthreads();
         }
         if (!more) break;
-        tg = tg2;
+        st = st2;
         b = b2;
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -249,11 +287,74 @@ __global__ __launch_bounds__(256) void gemv_kernel(
     }
 }
 
+// Separate-quantisation forms (MODE 1, 2): one problem, token groups on
+// blockIdx.y.
+template <int R, int U, int MODE, bool OUT_Y, int TH>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs A) {
+    A.m0 = blockIdx.y * 16;
+    A.tg_first = blockIdx.x;
+    A.tg_stride = gridDim.x;
+    gemv_body<R, U, MODE, OUT_Y, 0, false, TH>(A);
+}
+
+// Fused form (MODE 0) over a batch of independent decode BitLinears: the
+// workgroups [wg_begin, wg_begin + wg_count) serve problem i.  One launch
+// covers a whole decode step.
+constexpr int kMaxBatch = 8;
+struct FusedProblem {
+    const float *x;
+    const float *gamma;
+    const uint8_t *packed;
+    float *y;
+    int8_t *q_out;
+    float *inv_out;
+    int32_t *qsum_out;
+    float eps;
+    float w_scale;
+    int M, K, N;
+    int wg_begin, wg_count;
+    int ks;
+};
+struct FusedBatch {
+    FusedProblem p[kMaxBatch];
+    int count;
+};
+
+template <int R, int U, int FM, bool LONG>
+__global__ __launch_bounds__(256) void gemv_fused_kernel(FusedBatch B) {
+    int i = 0;
+    for (int t = 1; t < B.count; ++t)
+        if ((int)blockIdx.x >= B.p[t].wg_begin) i = t;
+    const FusedProblem &P = B.p[i];
+    GemvArgs A;
+    A.x = P.x;
+    A.gamma = P.gamma;
+    A.q = P.q_out;
+    A.inv = P.inv_out;
+    A.qsum = P.qsum_out;
+    A.packed = P.packed;
+    A.y = P.y;
+    A.acc_out = nullptr;
+    A.q_out = P.q_out;
+    A.inv_out = P.inv_out;
+    A.qsum_out = P.qsum_out;
+    A.eps = P.eps;
+    A.w_scale = P.w_scale;
+    A.M = P.M;
+    A.K = P.K;
+    A.N = P.N;
+    A.m0 = 0;
+    A.tg_first = (int)blockIdx.x - P.wg_begin;
+    A.tg_stride = P.wg_count;
+    A.ks = P.ks;
+    gemv_body<R, U, 0, true, FM, LONG, 1>(A);
+}
+
 struct Shape {
     int R, U;
 };
 // Launch-shape table; every entry computes bit-identical results.
-constexpr Shape kShapes[] = {{2, 4}, {1, 4}, {1, 2}, {2, 2}, {4, 2}, {1, 8}};
+constexpr Shape kShapes[] = {{2, 4}, {1, 4}, {1, 2}, {2, 2}, {4, 2}, {1, 8}, {2, 8}, {4, 4}};
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 
 int cu_count() {
@@ -274,53 +375,52 @@ int resident_per_cu(Kern kernel, size_t lds) {
     return n;
 }
 
-template <int R, int U, int MODE, bool OUT_Y, int FM, bool LONG, int TH>
-hipError_t launch_one(const float *x, const float *gamma, float eps, const int8_t *q,
-                      const float *inv, const int32_t *qsum, const uint8_t *packed,
-                      float w_scale, int64_t M, int64_t K, int64_t N, float *y, int32_t *acc,
-                      hipStream_t s) {
+// Smallest K split (waves per tile group) that still gives each of `wgs`
+// workgroups a set of tile groups: fewer waves per tile group means longer
+// per-wave streams and more tile groups in flight.
+int pick_ks(int64_t ntg, int64_t wgs) {
+    for (int ks = 1; ks < kW; ks *= 2)
+        if ((ntg + kW / ks - 1) / (kW / ks) >= wgs) return ks;
+    return kW;
+}
+
+template <int R, int U, int MODE, bool OUT_Y, int TH>
+hipError_t launch_sep(const int8_t *q, const float *inv, const int32_t *qsum,
+                      const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
+                      float *y, int32_t *acc, hipStream_t s) {
     const int64_t ntg = (N + kTileRows * R - 1) / (kTileRows * R);
-    const unsigned gy = MODE == 0 ? 1u : (unsigned)((M + 15) / 16);
+    const unsigned gy = (unsigned)((M + 15) / 16);
     const int64_t mg = M < 16 ? M : 16;
-    const size_t lds = MODE == 0 ? (size_t)(M * K) : MODE == 1 ? (size_t)(mg * K) : 0;
-    // One wave of co-resident workgroups walks all tile groups: per-
-    // workgroup set-up is paid once and no workgroup starts late.
-    auto kern = gemv_kernel<R, U, MODE, OUT_Y, FM, LONG, TH>;
-    const int64_t cap = (int64_t)cu_count() * resident_per_cu(kern, lds) / gy;
-    const unsigned gx = (unsigned)(ntg < cap ? ntg : (cap > 0 ? cap : 1));
-    // With MODE 0, q / inv / qsum are outputs (the caller's workspace).
-    hipLaunchKernelGGL((gemv_kernel<R, U, MODE, OUT_Y, FM, LONG, TH>), dim3(gx, gy), dim3(256),
-                       lds, s, x, gamma, eps, q, inv, qsum, packed, w_scale, (int)M, (int)K,
-                       (int)N, y, acc, const_cast<int8_t *>(q), const_cast<float *>(inv),
-                       const_cast<int32_t *>(qsum));
+    const size_t lds = MODE == 1 ? (size_t)(mg * K) : 0;
+    // One wave of co-resident workgroups walks all tile groups.
+    auto kern = gemv_kernel<R, U, MODE, OUT_Y, TH>;
+    const int64_t cap = std::max<int64_t>(1, (int64_t)cu_count() * resident_per_cu(kern, lds) / gy);
+    const int ks = pick_ks(ntg, cap);
+    const int64_t nset = (ntg + kW / ks - 1) / (kW / ks);
+    const unsigned gx = (unsigned)(nset < cap ? nset : cap);
+    GemvArgs A{};
+    A.ks = ks;
+    A.q = q;
+    A.inv = inv;
+    A.qsum = qsum;
+    A.packed = packed;
+    A.y = y;
+    A.acc_out = acc;
+    A.w_scale = w_scale;
+    A.M = (int)M;
+    A.K = (int)K;
+    A.N = (int)N;
+    hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(256), lds, s, A);
     return hipGetLastError();
 }
 
 template <int R, int U>
-hipError_t launch_shape(const float *x, const float *gamma, float eps, const int8_t *q,
-                        const float *inv, const int32_t *qsum, const uint8_t *packed,
-                        float w_scale, int64_t M, int64_t K, int64_t N, float *y, int32_t *acc,
-                        int mode, hipStream_t s) {
-    if (mode == 0) {  // forward only: y is always written; M <= 4 so TH = 1
-        const bool lng = K > 8 * 1024;
-        if (M == 1)
-            return lng ? launch_one<R, U, 0, true, 1, true, 1>(x, gamma, eps, q, inv, qsum, packed,
-                                                               w_scale, M, K, N, y, acc, s)
-                       : launch_one<R, U, 0, true, 1, false, 1>(x, gamma, eps, q, inv, qsum,
-                                                                packed, w_scale, M, K, N, y, acc,
-                                                                s);
-        return lng ? launch_one<R, U, 0, true, kFuseMaxM, true, 1>(x, gamma, eps, q, inv, qsum,
-                                                                   packed, w_scale, M, K, N, y,
-                                                                   acc, s)
-                   : launch_one<R, U, 0, true, kFuseMaxM, false, 1>(x, gamma, eps, q, inv, qsum,
-                                                                    packed, w_scale, M, K, N, y,
-                                                                    acc, s);
-    }
+hipError_t launch_shape_sep(const int8_t *q, const float *inv, const int32_t *qsum,
+                            const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
+                            float *y, int32_t *acc, int mode, hipStream_t s) {
 #define BL_ONE(MODE, TH)                                                                        \
-    return y ? launch_one<R, U, MODE, true, 0, false, TH>(x, gamma, eps, q, inv, qsum, packed,    \
-                                                          w_scale, M, K, N, y, acc, s)            \
-             : launch_one<R, U, MODE, false, 0, false, TH>(x, gamma, eps, q, inv, qsum, packed,   \
-                                                           w_scale, M, K, N, y, acc, s);
+    return y ? launch_sep<R, U, MODE, true, TH>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s) \
+             : launch_sep<R, U, MODE, false, TH>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
     const bool two = M > 8;
     if (mode == 1) {
         if (two) { BL_ONE(1, 2) }
@@ -331,38 +431,113 @@ hipError_t launch_shape(const float *x, const float *gamma, float eps, const int
 #undef BL_ONE
 }
 
+// Fused launch over `count` problems (count <= kMaxBatch): workgroups are
+// shared out in proportion to each problem's weight bytes, within the
+// number that fit on the device at once.
+template <int R, int U, int FM, bool LONG>
+hipError_t launch_fused(const FusedDecode *d, int count, hipStream_t s) {
+    int64_t max_mk = 1;
+    for (int i = 0; i < count; ++i) max_mk = std::max<int64_t>(max_mk, d[i].M * d[i].K);
+    const size_t lds = (size_t)max_mk;
+    auto kern = gemv_fused_kernel<R, U, FM, LONG>;
+    const int64_t cap = std::max<int64_t>(count, (int64_t)cu_count() * resident_per_cu(kern, lds));
+    int64_t ntg[kMaxBatch], total_tg = 0;
+    double bytes[kMaxBatch], total_bytes = 0.0;
+    for (int i = 0; i < count; ++i) {
+        ntg[i] = (d[i].N + kTileRows * R - 1) / (kTileRows * R);
+        total_tg += ntg[i];
+        bytes[i] = (double)d[i].N * (double)d[i].K;
+        total_bytes += bytes[i];
+    }
+    FusedBatch B{};
+    B.count = count;
+    int64_t begin = 0;
+    for (int i = 0; i < count; ++i) {
+        int64_t w = total_tg <= cap ? ntg[i]
+                                    : (int64_t)((double)cap * bytes[i] / total_bytes);
+        w = std::max<int64_t>(1, std::min(w, ntg[i]));
+        const int ks = pick_ks(ntg[i], w);
+        const int64_t nset = (ntg[i] + kW / ks - 1) / (kW / ks);
+        w = std::min(w, nset);
+        FusedProblem &P = B.p[i];
+        P.ks = ks;
+        P.x = d[i].x;
+        P.gamma = d[i].gamma;
+        P.packed = d[i].packed;
+        P.y = d[i].y;
+        P.q_out = d[i].q;
+        P.inv_out = d[i].inv;
+        P.qsum_out = d[i].qsum;
+        P.eps = d[i].eps;
+        P.w_scale = d[i].w_scale;
+        P.M = (int)d[i].M;
+        P.K = (int)d[i].K;
+        P.N = (int)d[i].N;
+        P.wg_begin = (int)begin;
+        P.wg_count = (int)w;
+        begin += w;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)begin), dim3(256), lds, s, B);
+    return hipGetLastError();
+}
+
+template <int R, int U>
+hipError_t launch_shape_fused(const FusedDecode *d, int count, hipStream_t s) {
+    bool lng = false;
+    int64_t max_m = 1;
+    for (int i = 0; i < count; ++i) {
+        lng = lng || d[i].K > 8 * 1024;
+        max_m = std::max<int64_t>(max_m, d[i].M);
+    }
+    if (max_m == 1)
+        return lng ? launch_fused<R, U, 1, true>(d, count, s) : launch_fused<R, U, 1, false>(d, count, s);
+    return lng ? launch_fused<R, U, kFuseMaxM, true>(d, count, s)
+               : launch_fused<R, U, kFuseMaxM, false>(d, count, s);
+}
+
 }  // namespace
 
 int gemv_num_variants() { return kNumShapes; }
 
-hipError_t launch_gemv(const float *x, const float *gamma, float eps,
-                       const int8_t *q, const float *inv, const int32_t *qsum,
-                       const uint8_t *packed, float w_scale, int64_t M,
-                       int64_t K, int64_t N, float *y, int32_t *acc,
-                       bool fused, int variant, hipStream_t s) {
-    const int64_t mg = M < 16 ? M : 16;
-    const int mode = fused ? 0 : (mg * K <= kGemvStageMaxLds ? 1 : 2);
-    int v = variant;
-    if (v <= 0) {
-        // One batch of U 128-byte steps per wave covers rows up to 4*U*128 bytes.
-        const int64_t nsteps = (K / 4 + kStep - 1) / kStep;
-        v = nsteps > 8 ? 1 : 3;
-    }
-#define BL_GEMV_CASE(idx)                                                                   \
-    case idx:                                                                               \
-        return launch_shape<kShapes[idx - 1].R, kShapes[idx - 1].U>(                        \
-            x, gamma, eps, q, inv, qsum, packed, w_scale, M, K, N, y, acc, mode, s);
-    switch (v) {
-        BL_GEMV_CASE(1)
-        BL_GEMV_CASE(2)
-        BL_GEMV_CASE(3)
-        BL_GEMV_CASE(4)
-        BL_GEMV_CASE(5)
-        BL_GEMV_CASE(6)
-        default:
-            return hipErrorInvalidValue;
-    }
-#undef BL_GEMV_CASE
+static int auto_variant(int64_t max_k) {
+    // One batch of U 128-byte steps per wave covers rows up to 4*U*128 bytes.
+    const int64_t nsteps = (max_k / 4 + kStep - 1) / kStep;
+    return nsteps > 8 ? 1 : 3;
 }
+
+#define BL_GEMV_SWITCH(CALL)                                                  \
+    switch (v) {                                                              \
+        case 1: return CALL(kShapes[0].R, kShapes[0].U);                      \
+        case 2: return CALL(kShapes[1].R, kShapes[1].U);                      \
+        case 3: return CALL(kShapes[2].R, kShapes[2].U);                      \
+        case 4: return CALL(kShapes[3].R, kShapes[3].U);                      \
+        case 5: return CALL(kShapes[4].R, kShapes[4].U);                      \
+        case 6: return CALL(kShapes[5].R, kShapes[5].U);                      \
+        case 7: return CALL(kShapes[6].R, kShapes[6].U);                      \
+        case 8: return CALL(kShapes[7].R, kShapes[7].U);                      \
+        default: return hipErrorInvalidValue;                                 \
+    }
+
+hipError_t launch_gemv(const int8_t *q, const float *inv, const int32_t *qsum,
+                       const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
+                       float *y, int32_t *acc, int variant, hipStream_t s) {
+    const int64_t mg = M < 16 ? M : 16;
+    const int mode = mg * K <= kGemvStageMaxLds ? 1 : 2;
+    const int v = variant > 0 ? variant : auto_variant(K);
+#define BL_SEP(R_, U_) launch_shape_sep<R_, U_>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, mode, s)
+    BL_GEMV_SWITCH(BL_SEP)
+#undef BL_SEP
+}
+
+hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipStream_t s) {
+    int64_t max_k = 0;
+    for (int i = 0; i < count; ++i) max_k = std::max<int64_t>(max_k, d[i].K);
+    const int v = variant > 0 ? variant : auto_variant(max_k);
+#define BL_FUSED(R_, U_) launch_shape_fused<R_, U_>(d, count, s)
+    BL_GEMV_SWITCH(BL_FUSED)
+#undef BL_FUSED
+}
+
+#undef BL_GEMV_SWITCH
 
 }  // namespace bl

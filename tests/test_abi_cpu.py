@@ -144,3 +144,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         api.lib()
+
+
+def _desc(M=1, K=256, N=16, x=A, p=A, g=A, y=A, ws=A, wsb=1 << 20, eps=1e-6):
+    return api.ForwardDesc(x, p, 0.02, g, eps, M, K, N, y, ws, wsb)
+
+
+def test_forward_batch_validation(L):
+    fb = L.bitlinear_forward_batch
+    one = (api.ForwardDesc * 1)(_desc())
+    assert fb(None, 1, None, None) == api.ERR_INVALID_ARG
+    assert fb(one, 0, None, None) == api.ERR_INVALID_ARG
+    many = (api.ForwardDesc * 65)(*[_desc() for _ in range(65)])
+    assert fb(many, 65, None, None) == api.ERR_INVALID_ARG
+    # one bad descriptor anywhere fails the whole call before any launch
+    for bad, code in [(_desc(K=100), api.ERR_SHAPE), (_desc(x=0), api.ERR_INVALID_ARG),
+                      (_desc(y=MIS), api.ERR_ALIGN), (_desc(wsb=10), api.ERR_WORKSPACE),
+                      (_desc(eps=0.0), api.ERR_INVALID_ARG)]:
+        arr = (api.ForwardDesc * 3)(_desc(), _desc(M=2, K=512), bad)
+        assert fb(arr, 3, None, None) == code
+    lp = ctypes.byref(api.Launch(api.PATH_GEMM, 1, 0, 0))
+    assert fb(one, 1, lp, None) == api.ERR_INVALID_ARG

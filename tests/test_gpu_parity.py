@@ -365,3 +365,41 @@ def test_act_quant_order_sensitive_rows(torch, bl, orc):
         qf, invf, qsf = bl.workspace_views(ws, 1, K)
         assert np.array_equal(host(qf)[0], q_r[m]) and host(qsf)[0] == qs_r[m]
         assert host(invf).view(np.uint32)[0] == inv_r.view(np.uint32)[m]
+
+
+def test_forward_batch_matches_single_calls(torch, bl, orc):
+    """A batch mixing fused decode problems (several K/N, M = 1..4), an
+    unfused decode problem and a prefill problem gives, per problem, the
+    bits of the single call; more than 8 fused problems span launches."""
+    shapes = [(1, 2560, 640), (1, 6912, 300), (3, 1024, 77), (1, 256, 16), (8, 512, 96),
+              (40, 384, 130), (1, 2560, 2560), (2, 768, 33), (1, 1024, 48), (1, 512, 1000),
+              (4, 256, 17), (1, 128, 8)]
+    items, singles, refs = [], [], []
+    for i, (M, K, N) in enumerate(shapes):
+        x, w, t, g = mm_case(M, K, N, 700 + i)
+        packed_r, s = orc.pack_i2s(w)
+        X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+        out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        ws = bl.new_workspace(M, K)
+        items.append((X, P, s, G, 1e-6, out, ws))
+        singles.append(host(bl.forward(X, P, s, G, 1e-6, N)).copy())
+        refs.append(orc.forward(x, packed_r, s, g, 1e-6, N))
+    announce("forward_batch", len(items))
+    bl.forward_batch(items)
+    torch.cuda.synchronize()
+    for (X, P, s, G, eps, out, ws), single, y64, (M, K, N) in zip(items, singles, refs, shapes):
+        assert np.array_equal(host(out), single), (M, K, N)
+        check_y(host(out), y64)
+        q, inv, qs = bl.workspace_views(ws, M, K)
+        q_r, inv_r, qs_r = orc.act_quant(host(X), host(G), 1e-6)
+        assert np.array_equal(host(q), q_r) and np.array_equal(host(inv), inv_r)
+        assert np.array_equal(host(qs), qs_r)
+    # every launch shape of the fused route gives the same bits
+    fused = [(it, single) for it, single, sh in zip(items, singles, shapes) if sh[0] <= 4]
+    for v in range(1, bl.num_variants(1) + 1):
+        for it, _ in fused:
+            it[5].fill_(float("nan"))
+        bl.forward_batch([it for it, _ in fused], path=1, variant=v)
+        torch.cuda.synchronize()
+        for it, single in fused:
+            assert np.array_equal(host(it[5]), single), v
