@@ -36,7 +36,9 @@
  *     -> BL_ERR_SHAPE; non-NULL pointers -> BL_ERR_INVALID_ARG; x, y, q,
  *     packed_w and the workspace 16-byte aligned -> BL_ERR_ALIGN.
  *   - Sizes are limited to M*K, N*K/4 and M*N below 2^40 elements, to
- *     M, N < 2^31 and to K <= 2^22 (BL_ERR_SHAPE beyond).
+ *     M, N < 2^31 and to K <= 2^22 (BL_ERR_SHAPE beyond).  Launch grids
+ *     add M <= 1048560 on the decode route and M <= 2097120 on the prefill
+ *     route (BL_ERR_SHAPE beyond).
  *
  * I2_S packed weight buffer (the persistent format) [CPPB-7]
  *   N*K/4 bytes of 2-bit codes followed by a 32-byte trailer.  Each run of

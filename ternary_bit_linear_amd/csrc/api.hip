@@ -76,20 +76,30 @@ Workspace carve(void *ws, int64_t M, int64_t K) {
     return w;
 }
 
+// The contraction route a launch takes for M tokens.
+int route_of(int64_t M, const bl_launch *l) {
+    const int path = l ? l->path : BL_PATH_AUTO;
+    if (path != BL_PATH_AUTO) return path;
+    return (M <= kGemvMaxM) ? BL_PATH_GEMV : BL_PATH_GEMM;
+}
+
+// Launch-grid row limit of a route: 16 tokens per decode workgroup row,
+// 32 per row of the smallest prefill tile, at most 65535 rows.
+bl_status check_grid(int64_t M, const bl_launch *l) {
+    const int64_t rows = route_of(M, l) == BL_PATH_GEMV ? (M + 15) / 16 : (M + 31) / 32;
+    return rows > 65535 ? BL_ERR_SHAPE : BL_OK;
+}
+
 // Contraction with q / inv / qsum already computed: route choice and
 // launch, with y (rescale epilogue) or acc (int32 epilogue).
 bl_status run_contraction(const int8_t *q, const float *inv, const int32_t *qsum,
                           const uint8_t *packed, float w_scale, int64_t M, int64_t K,
                           int64_t N, float *y, int32_t *acc, const bl_launch *l, hipStream_t s) {
-    int path = l ? l->path : BL_PATH_AUTO;
-    if (path == BL_PATH_AUTO) path = (M <= kGemvMaxM) ? BL_PATH_GEMV : BL_PATH_GEMM;
+    if (bl_status st = check_grid(M, l)) return st;
     const int variant = l ? l->variant : 0;
-    if (path == BL_PATH_GEMV) {
-        if ((M + 15) / 16 > 65535) return BL_ERR_SHAPE;
+    if (route_of(M, l) == BL_PATH_GEMV)
         return hip_status(bl::launch_gemv(q, inv, qsum, packed, w_scale, M, K, N, y, acc,
                                           variant, s));
-    }
-    if ((M + 63) / 64 > 65535) return BL_ERR_SHAPE;
     return hip_status(bl::launch_gemm(q, inv, qsum, packed, w_scale, M, K, N, y, acc, variant, s));
 }
 
@@ -105,11 +115,10 @@ bl_status validate_forward(const bl_forward_desc &d, const bl_launch *launch) {
         !aligned16(d.workspace))
         return BL_ERR_ALIGN;
     if (d.workspace_bytes < bitlinear_workspace_bytes(d.M, d.K)) return BL_ERR_WORKSPACE;
-    const int path = launch ? launch->path : BL_PATH_AUTO;
-    const bool gemv = path == BL_PATH_GEMV || (path == BL_PATH_AUTO && d.M <= kGemvMaxM);
+    const bool gemv = route_of(d.M, launch) == BL_PATH_GEMV;
     const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
     if (launch && launch->fuse == 1 && !(gemv && fits)) return BL_ERR_INVALID_ARG;
-    return BL_OK;
+    return check_grid(d.M, launch);
 }
 
 // Whether a validated forward takes the fused decode kernel.  Automatic
@@ -117,8 +126,7 @@ bl_status validate_forward(const bl_forward_desc &d, const bl_launch *launch) {
 // fits in registers, one round trip); otherwise the separate quantisation
 // kernel is faster (measured on MI355X).
 bool takes_fused(const bl_forward_desc &d, const bl_launch *launch) {
-    const int path = launch ? launch->path : BL_PATH_AUTO;
-    const bool gemv = path == BL_PATH_GEMV || (path == BL_PATH_AUTO && d.M <= kGemvMaxM);
+    const bool gemv = route_of(d.M, launch) == BL_PATH_GEMV;
     const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
     if (launch && launch->fuse == 0) return false;
     if (launch && launch->fuse == 1) return gemv && fits;

@@ -70,6 +70,20 @@ __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Same with a wave-uniform offset added in the scalar offset field.
+__device__ __forceinline__ v4i buf_load16_so(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+}
+
+// 16-byte LDS-direct buffer load: lane i's bytes land at lds + 16 i (lds is
+// wave-uniform); an out-of-range offset writes zeros.  Completion is counted
+// by vmcnt like any other vector-memory load.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off,
+                                               uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds, 16, off, soff, 0, 0);
+}
+
 __device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_float4(__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z),

@@ -6,39 +6,84 @@
 // the prompt-processing GEMM over I2_S codes and int8 activations, which
 // must write every output; codes offset by the activation sum.]
 //
-// Design.  A workgroup owns a BM x BN output tile (tokens x weight rows) and
-// walks K in stages of KSUB x 256 (two I2_S blocks per 256).  Per stage the
-// int8 activation tile (BM x 256 KSUB) is staged in LDS with coalesced 16-byte loads (rows padded
-// by 16 bytes so the 16 lanes of an MFMA row-group hit distinct banks);
-// the packed weights go straight from global memory to registers -- one
-// 16-byte load per lane per 16 weight rows, i.e. 64 weights -- and are
-// expanded there by shift+mask into the int8 B operand of
-// v_mfma_i32_16x16x64_i8 (codes 0/1/2; the activation sum is subtracted in
-// the epilogue).  Each wave computes a (BM/WM) x (BN/WN) sub-tile with
-// int32 accumulators in registers.  All loads are range-checked buffer
-// loads (ragged M, N and K tails read zeros) issued a full step ahead of
-// their use: LDS is double-buffered, one barrier per stage.
+// Design.  A workgroup of WM x WN waves owns a BM x BN output tile
+// (tokens x weight rows) and walks K in 256-k steps (two I2_S blocks).  The
+// int8 activations of a step go global -> LDS directly (LDS-direct buffer
+// loads, no register staging) into a ring of R step buffers; the packed
+// weights go global -> registers, one 16-byte load per lane per 16 weight
+// rows (64 weights per lane), and are expanded there by shift+mask into
+// the int8 B operand of v_mfma_i32_16x16x64_i8 (codes 0/1/2; the
+// activation sum is subtracted in the epilogue).  R - 1 steps are in
+// flight while one is contracted; one barrier per step.  Each wave keeps
+// its (BM/WM) x (BN/WN) sub-tile in int32 accumulators.  All loads are
+// range-checked buffer loads: ragged M, N and K tails read zeros.
+#include <utility>
+
 #include "common.hpp"
 
 namespace bl {
 namespace {
 
-// BM x BN output tile per workgroup, WM x WN waves; each pipeline stage
-// covers KSUB 256-k steps (KSUB * 256 bytes of every activation row).
-template <int BM, int BN, int WM, int WN, int KSUB, bool OUT_Y>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
+// Ring-pipelined form.  The activation tile of each 256-k step is copied
+// straight from global memory into LDS by buffer loads with the LDS-direct
+// bit (lane i of a load writes bytes [16 i, 16 i + 16) after the wave's base
+// address), into a ring of R step buffers: R - 1 steps are in flight while
+// one is contracted.  The packed weights of a step go to registers, in a
+// ring of R slots advanced with the LDS ring.
+//
+// In a step buffer a row is 256 bytes and its 16-byte chunk c sits at
+// position (c + 2 (row % 8)) % 16, which puts the 16 rows x 4 k-groups of an
+// MFMA fragment read on distinct LDS banks (the bank pattern of rows padded
+// to 288 bytes, without the padding).
+//
+// The loop runs whole turns of the ring only (R is picked to divide the step
+// count where possible; otherwise the last turn runs past K on loads that
+// read zeros), so it has no early exit: every load issued is consumed on
+// every path, the compiler can neither sink nor drop one, and the explicit
+// waits can count loads exactly.  The step buffers are distinct LDS objects
+// so that the compiler's own LDS-DMA wait tracking can tell them apart.
+template <int VMCNT>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(VMCNT >= 0 && VMCNT < 64, "vmcnt field is 6 bits");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (VMCNT & 15) | ((VMCNT >> 4) << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+template <class F, int... I>
+__device__ __forceinline__ void unroll_ic(F &&f, std::integer_sequence<int, I...>) {
+    (f(ic<I>{}), ...);
+}
+
+template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_ring_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ inv,
     const int32_t *__restrict__ qsum, const uint8_t *__restrict__ packed,
     float w_scale, int M, int K, int N, float *__restrict__ y,
     int32_t *__restrict__ acc_out) {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 16, NI = TN / 16;
-    constexpr int KST = kStepK * KSUB;            // k (= activation bytes) per stage
-    constexpr int LROW = KST + 16;                // padded LDS row
-    constexpr int CH = BM * (KST / 16) / NT;      // 16-byte A chunks per thread per stage
-    static_assert(BM * (KST / 16) % NT == 0, "A tile chunks per thread");
-    __shared__ __align__(16) int8_t a_lds[2][BM * LROW];
+    constexpr int SB = BM * kStepK;            // activation bytes of one step
+    constexpr int ND = SB / (NT * 16);         // LDS-direct loads per lane per step
+    static_assert(SB % (NT * 16) == 0, "step tile splits into whole wave loads");
+    static_assert(R >= 3 && R <= 5 && R * SB <= 160 * 1024, "ring depth");
+    __shared__ __align__(16) int8_t l0[SB], l1[SB], l2[SB], l3[R > 3 ? SB : 16],
+        l4[R > 4 ? SB : 16];
+    auto ring = [&](auto I) -> int8_t * {
+        constexpr int i = decltype(I)::value % R;
+        if constexpr (i == 0) return l0;
+        else if constexpr (i == 1) return l1;
+        else if constexpr (i == 2) return l2;
+        else if constexpr (i == 3) return l3;
+        else return l4;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -47,48 +92,61 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
     const int j = lane & 15, kg = lane >> 4;
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
-
-    const int nstages = (K + KST - 1) / KST;
+    const int nsteps = (K + kStepK - 1) / kStepK;
     const int nblocks = K / kBlockWeights;
     const uint32_t rowbytes = (uint32_t)K / 4;
-    // Range-checked views of this tile's activation rows and weight rows:
-    // rows past M or N read as zero.
     const auto rq = make_rsrc(q + (size_t)m0 * K, (uint32_t)min(BM, M - m0) * (uint32_t)K);
     const auto rw = make_rsrc(packed + (size_t)n0 * rowbytes,
                               (uint32_t)min(BN, N - n0) * rowbytes);
 
-    auto load_a = [&](v4i(&areg)[CH], int st) {
+    // Source of each of this lane's LDS-direct loads: position
+    // p = (c NW + wave) 64 + lane holds row p / 16, chunk (p % 16 - 2 row) % 16.
+    uint32_t dsrc[ND];
+    int dk[ND];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int idx = tid + c * NT;
-            const int row = idx / (KST / 16);
-            const int k = st * KST + (idx % (KST / 16)) * 16;
-            areg[c] = buf_load16(rq, k < K ? (uint32_t)row * (uint32_t)K + (uint32_t)k : kOOB);
-        }
-    };
-    auto store_a = [&](int8_t *lds, const v4i(&areg)[CH]) {
+    for (int c = 0; c < ND; ++c) {
+        const int p = (c * NW + wid) * 64 + lane;
+        const int row = p >> 4;
+        const int ch = ((p & 15) - 2 * (row & 7)) & 15;
+        dsrc[c] = (uint32_t)row * (uint32_t)K + 16u * ch;
+        dk[c] = 16 * ch;
+    }
+    // LDS byte offsets of this lane's fragment of field g (row j, logical
+    // chunk 8 (kg / 2) + kg % 2 + 2 g).
+    int aoff[4];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int idx = tid + c * NT;
-            const int row = idx / (KST / 16);
-            const int col = (idx % (KST / 16)) * 16;
-            *reinterpret_cast<v4i *>(lds + row * LROW + col) = areg[c];
-        }
-    };
-    // B of stage st: for each 256-k step t of the stage and each 16-row
-    // group ni, 16 packed bytes per lane (row j, block-pair bytes 16*kg).
-    auto load_b = [&](v4i(&breg)[KSUB][NI], int st) {
+    for (int g = 0; g < 4; ++g) {
+        const int ch = 8 * (kg >> 1) + (kg & 1) + 2 * g;
+        aoff[g] = (wm * TM + j) * kStepK + 16 * ((ch + 2 * (j & 7)) & 15);
+    }
+    // Per-lane weight offsets (row, k-group) of this wave's 16-row groups.
+    uint32_t boff[NI];
 #pragma unroll
-        for (int t = 0; t < KSUB; ++t) {
-            const int s = st * KSUB + t;
-            const bool kv = 2 * s + (kg >> 1) < nblocks;
+    for (int ni = 0; ni < NI; ++ni)
+        boff[ni] = (uint32_t)(wn * TN + 16 * ni + j) * rowbytes + 16u * kg;
+
+    // Loads of step s, activations then weights.  When K is a whole number
+    // of steps (KTAIL false) the step's k offset rides in the scalar offset
+    // and steps past the end are redirected out of range (they read zeros);
+    // otherwise each chunk past K is.
+    auto issue = [&](int8_t *buf, v4i(&breg)[NI], int s) {
+        const int kb = s * kStepK;
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                const uint32_t row = (uint32_t)(wn * TN + 16 * ni + j);
-                breg[t][ni] = buf_load16(rw, kv ? row * rowbytes + (uint32_t)s * kStepBytes + 16u * kg
-                                                : kOOB);
+        for (int c = 0; c < ND; ++c) {
+            uint32_t off, soff;
+            if constexpr (!KTAIL) {
+                off = s < nsteps ? dsrc[c] : kOOB;
+                soff = kb;
+            } else {
+                off = kb + dk[c] < K ? dsrc[c] + (uint32_t)kb : kOOB;
+                soff = 0;
             }
+            buf_load16_lds(rq, buf + (c * NW + wid) * 1024, off, soff);
         }
+        const bool kv = KTAIL ? 2 * s + (kg >> 1) < nblocks : s < nsteps;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+            breg[ni] = buf_load16_so(rw, kv ? boff[ni] : kOOB, (uint32_t)s * kStepBytes);
     };
 
     v4i acc[MI][NI];
@@ -97,60 +155,71 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4i{0, 0, 0, 0};
 
-    const int koff = (kg >> 1) * kBlockWeights + 16 * (kg & 1);
-    // One 256-k step t of a stage: the step's A fragments are read from LDS
-    // up front, then per field the B codes are expanded and the MI x NI
-    // MFMAs issued.
-    auto compute = [&](const int8_t *lds, const v4i(&breg)[KSUB][NI]) {
+    // One step: the A fragments are read from LDS up front; then the MFMAs
+    // of field g are interleaved with the expansion of field g + 1's B codes
+    // (one MFMA, then two VALU instructions), so the vector ALU works in the
+    // shadow of the matrix core.
+    auto compute = [&](const int8_t *buf, const v4i(&breg)[NI]) {
+        v4i a[4][MI];
 #pragma unroll
-        for (int t = 0; t < KSUB; ++t) {
-            v4i a[4][MI];
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+            for (int mi = 0; mi < MI; ++mi)
+                a[g][mi] = *reinterpret_cast<const v4i *>(buf + aoff[g] + 16 * mi * kStepK);
+        v4i bf[NI];
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-                    a[g][mi] = *reinterpret_cast<const v4i *>(
-                        lds + (wm * TM + 16 * mi + j) * LROW + kStepK * t + koff + 32 * g);
+        for (int ni = 0; ni < NI; ++ni) bf[ni] = unpack_field(breg[ni], 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                v4i bf[NI];
+        for (int g = 0; g < 4; ++g) {
+            v4i nb[NI];
+            if (g < 3) {
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni) bf[ni] = unpack_field(breg[t][ni], g);
+                for (int ni = 0; ni < NI; ++ni) nb[ni] = unpack_field(breg[ni], g + 1);
+            }
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < NI; ++ni)
-                        acc[mi][ni] = mfma16(a[g][mi], bf[ni], acc[mi][ni]);
+                for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16(a[g][mi], bf[ni], acc[mi][ni]);
+#pragma unroll
+            for (int k = 0; k < MI * NI; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (g < 3) {
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) bf[ni] = nb[ni];
             }
         }
     };
 
-    // Software pipeline: while stage st is contracted from one LDS buffer,
-    // the loads of stage st + 1 are in flight; they are written to the other
-    // buffer afterwards, and one barrier per stage separates the two.
-    v4i areg[CH], bcur[KSUB][NI], bnxt[KSUB][NI];
-    load_a(areg, 0);
-    load_b(bcur, 0);
-    store_a(a_lds[0], areg);
-    __syncthreads();
-    for (int st = 0; st < nstages; ++st) {
-        int8_t *cur = a_lds[st & 1];
-        int8_t *nxt = a_lds[(st & 1) ^ 1];
-        const bool more = st + 1 < nstages;
-        if (more) {
-            load_a(areg, st + 1);
-            load_b(bnxt, st + 1);
+    // Steps 0..R-2 are issued up front and step t + R - 1 at the top of
+    // step t, into the buffer and slot step t - 1 used.  At the top of step
+    // t its own loads must have landed; only steps t + 1 .. t + R - 2 may
+    // still be in flight.
+    constexpr int kPend = (R - 2) * (ND + NI);
+    v4i breg[R][NI];
+    unroll_ic([&](auto I) {
+        if constexpr (decltype(I)::value < R - 1) {
+            issue(ring(I), breg[decltype(I)::value], decltype(I)::value);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        compute(cur, bcur);
-        if (more) store_a(nxt, areg);
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < KSUB; ++t)
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) bcur[t][ni] = bnxt[t][ni];
+    }, std::make_integer_sequence<int, R>{});
+    const int turns = (nsteps + R - 1) / R;
+    int s = 0;
+    for (int t = 0; t < turns; ++t, s += R) {
+        unroll_ic([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            wait_vm_barrier<kPend>();
+            issue(ring(ic<i + R - 1>{}), breg[(i + R - 1) % R], s + i + R - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ring(I), breg[i]);
+        }, std::make_integer_sequence<int, R>{});
     }
+    // Drain the trailing loads before the workgroup's LDS is released.
+    wait_vm_barrier<0>();
 
-    // Epilogue: D(i, j) of a 16x16 tile is lane j + 16*(i/4), register i%4.
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -174,27 +243,61 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
 }
 
 struct Tile {
-    int BM, BN, WM, WN, KSUB;
+    int BM, BN, WM, WN, R;  // R == 0: ring depth picked from the step count
 };
 // Launch-shape table; every entry computes bit-identical results.
-constexpr Tile kTiles[] = {{64, 128, 1, 4, 1}, {64, 128, 1, 4, 2}, {64, 128, 1, 4, 4},
-                           {64, 64, 2, 2, 1},  {64, 64, 2, 2, 2},  {64, 64, 2, 2, 4},
-                           {128, 128, 2, 2, 1}, {128, 128, 2, 2, 2}, {32, 64, 1, 4, 4}};
+constexpr Tile kTiles[] = {{64, 256, 1, 4, 3}, {64, 128, 1, 4, 3}, {64, 64, 2, 2, 0},
+                           {32, 64, 1, 4, 0},  {32, 128, 1, 4, 0}, {128, 128, 1, 4, 3},
+                           {128, 256, 1, 4, 3}, {64, 256, 1, 4, 4}, {64, 128, 1, 4, 0},
+                           {128, 128, 2, 2, 0}, {64, 64, 2, 2, 3},  {32, 64, 1, 4, 3},
+                           {128, 256, 1, 8, 3}, {128, 256, 2, 4, 3}, {64, 512, 1, 8, 3}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int BM, int BN, int WM, int WN, int KSUB>
-hipError_t launch_tile(const int8_t *q, const float *inv, const int32_t *qsum,
-                       const uint8_t *packed, float w_scale, int64_t M, int64_t K,
-                       int64_t N, float *y, int32_t *acc, hipStream_t s) {
+// Ring depth for a tile: the deepest of 4, 5, 3 that divides the step count
+// (no padded steps), else 4.  Depths whose ring does not fit the LDS are
+// skipped.
+int pick_depth(int bm, int64_t K) {
+    const int64_t nsteps = (K + kStepK - 1) / kStepK;
+    for (int r : {4, 5, 3})
+        if (r * bm * kStepK <= 160 * 1024 && nsteps % r == 0) return r;
+    return 4;
+}
+
+template <int BM, int BN, int WM, int WN, int R>
+hipError_t launch_ring(const int8_t *q, const float *inv, const int32_t *qsum,
+                       const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
+                       float *y, int32_t *acc, hipStream_t s) {
     const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     const dim3 block(WM * WN * 64);
-    if (y)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KSUB, true>), grid, block, 0, s, q, inv,
-                           qsum, packed, w_scale, (int)M, (int)K, (int)N, y, acc);
-    else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KSUB, false>), grid, block, 0, s, q, inv,
-                           qsum, packed, w_scale, (int)M, (int)K, (int)N, y, acc);
+    const bool kt = K % kStepK != 0;
+#define BL_RING_LAUNCH(KT, OY)                                                                    \
+    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, R, KT, OY>), grid, block, 0, s, q, inv, \
+                       qsum, packed, w_scale, (int)M, (int)K, (int)N, y, acc)
+    if (y) {
+        if (kt)
+            BL_RING_LAUNCH(true, true);
+        else
+            BL_RING_LAUNCH(false, true);
+    } else {
+        if (kt)
+            BL_RING_LAUNCH(true, false);
+        else
+            BL_RING_LAUNCH(false, false);
+    }
+#undef BL_RING_LAUNCH
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int RFIX>
+hipError_t launch_tile(const int8_t *q, const float *inv, const int32_t *qsum,
+                       const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
+                       float *y, int32_t *acc, hipStream_t s) {
+    const int r = RFIX ? RFIX : pick_depth(BM, K);
+    if (r == 3) return launch_ring<BM, BN, WM, WN, 3>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+    if constexpr (5 * BM * kStepK <= 160 * 1024)
+        if (r == 5)
+            return launch_ring<BM, BN, WM, WN, 5>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+    return launch_ring<BM, BN, WM, WN, 4>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
 }
 
 }  // namespace
@@ -207,17 +310,24 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
                        int variant, hipStream_t s) {
     int v = variant;
     if (v <= 0) {
-        // Measured on MI355X: large grids prefer the 64x128 tile (two 256-k
-        // steps per stage once the grid is under ~4 waves of workgroups);
-        // smaller ones trade tile size for workgroups and a deeper stage.
+        // Picked from a sweep on MI355X: the widest tile when the grid still
+        // has two workgroups per CU, 64x128 down to one per CU, then 32-row
+        // tiles (the wider one for long K).
         auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-        v = tiles(64, 128) >= 1024 ? 1 : tiles(64, 128) >= 384 ? 2 : tiles(64, 64) >= 256 ? 5 : 9;
+        if (tiles(64, 512) >= 512)
+            v = 15;
+        else if (tiles(64, 128) >= 256)
+            v = 9;
+        else if (K > 4096 && tiles(32, 128) >= 256)
+            v = 5;
+        else
+            v = 4;
     }
-#define BL_GEMM_CASE(idx)                                                               \
-    case idx:                                                                           \
-        return launch_tile<kTiles[idx - 1].BM, kTiles[idx - 1].BN, kTiles[idx - 1].WM,  \
-                           kTiles[idx - 1].WN, kTiles[idx - 1].KSUB>(q, inv, qsum, packed, \
-                                                                     w_scale, M, K, N, y, acc, s);
+#define BL_GEMM_CASE(idx)                                                                  \
+    case idx:                                                                              \
+        return launch_tile<kTiles[idx - 1].BM, kTiles[idx - 1].BN, kTiles[idx - 1].WM,     \
+                           kTiles[idx - 1].WN, kTiles[idx - 1].R>(q, inv, qsum, packed,      \
+                                                                  w_scale, M, K, N, y, acc, s);
     switch (v) {
         BL_GEMM_CASE(1)
         BL_GEMM_CASE(2)
@@ -228,6 +338,12 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         BL_GEMM_CASE(7)
         BL_GEMM_CASE(8)
         BL_GEMM_CASE(9)
+        BL_GEMM_CASE(10)
+        BL_GEMM_CASE(11)
+        BL_GEMM_CASE(12)
+        BL_GEMM_CASE(13)
+        BL_GEMM_CASE(14)
+        BL_GEMM_CASE(15)
         default:
             return hipErrorInvalidValue;
     }

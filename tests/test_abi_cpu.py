@@ -98,6 +98,13 @@ def test_forward_bad_launch(L, launch):
     assert fwd(L, launch=lp) == api.ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("path,M", [(api.PATH_GEMV, 1048561), (api.PATH_GEMM, 2097121)])
+def test_grid_row_limits(L, path, M):
+    """M past the launch grid of a route is a shape error, not a failed launch."""
+    lp = ctypes.byref(api.Launch(path, 0, 0, 0))
+    assert fwd(L, M=M, K=128, N=4, wsb=1 << 40, launch=lp) == api.ERR_SHAPE
+
+
 def test_fused_needs_small_m(L):
     lp = ctypes.byref(api.Launch(api.PATH_GEMV, 1, 0, 0))
     assert fwd(L, M=8, wsb=1 << 20, launch=lp) == api.ERR_INVALID_ARG
