@@ -270,8 +270,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(args.workload),
-                "kernel": "gemv_fused_kernel (RMSNorm + int8 quant + I2_S x int8 MFMA, "
-                          f"{len(work.linears)} BitLinears per launch)",
+                "kernel": "gemv_shot_kernel (one-shot decode: RMSNorm + int8 quant + "
+                          f"I2_S x int8 MFMA, {len(work.linears)} BitLinears per launch)",
                 "launches_per_step": launches,
                 "avg_launch_us": round(avg_s * 1e6, 3),
                 "bytes_per_launch": step_bytes // launches}

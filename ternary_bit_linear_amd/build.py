@@ -38,9 +38,17 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+# Per-source extras.  gemv_shot.hip: its kernels take the per-problem first
+# workgroups as their eight leading int arguments, which gfx950 can preload
+# into scalar registers at wave launch.
+EXTRA = {
+    "gemv_shot.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

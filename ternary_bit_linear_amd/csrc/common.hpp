@@ -18,6 +18,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <utility>
 #include <stdint.h>
 
 namespace bl {
@@ -61,13 +64,54 @@ __device__ __forceinline__ v4i mfma16(const v4i &a, const v4i &b, const v4i &c) 
 constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    // A buffer resource lives in scalar registers.  Every resource built here
+    // is wave-uniform; readfirstlane says so to the compiler, which otherwise
+    // wraps each load in a loop over lanes whenever a field was computed by
+    // a vector instruction.
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t ua = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const int ub = __builtin_amdgcn_readfirstlane((int)bytes);
     // dword3 = 0x00020000: 32-bit data format, the raw-buffer setting on gfx9.
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ua), (short)0, ub, 0x00020000);
 }
 
 __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Compile-time index for unrolled rings: f(ic<0>{}), f(ic<1>{}), ...
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+template <class F, int... I>
+__device__ __forceinline__ void unroll_ic(F &&f, std::integer_sequence<int, I...>) {
+    (f(ic<I>{}), ...);
+}
+
+// Wait until at most VMCNT of this wave's vector-memory loads are
+// outstanding (LDS-direct loads included; lgkm and export counters
+// untouched).  Scheduling barriers keep every instruction on its side.
+template <int VMCNT>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(VMCNT >= 0 && VMCNT < 64, "vmcnt field is 6 bits");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (VMCNT & 15) | ((VMCNT >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's own LDS
+// accesses (lgkmcnt(0)) but leaves vector-memory loads in flight, unlike
+// __syncthreads, whose fence drains them.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Same with a wave-uniform offset added in the scalar offset field.
@@ -149,9 +193,9 @@ __device__ __forceinline__ float block_sumsq_finish(float p, float *red) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     p = wave_tree_sum_f(p);
     if (lane == 0) red[wid] = p;
-    __syncthreads();
+    lds_barrier();
     const float t = (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
+    lds_barrier();
     return t;
 }
 
@@ -159,9 +203,9 @@ __device__ __forceinline__ float block_max(float v, float *red) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     v = wave_max(v);
     if (lane == 0) red[wid] = v;
-    __syncthreads();
+    lds_barrier();
     const float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
+    lds_barrier();
     return t;
 }
 
@@ -170,9 +214,9 @@ __device__ __forceinline__ int block_sum_int(int v, float *red) {
     v = wave_sum_int(v);
     int *ri = reinterpret_cast<int *>(red);
     if (lane == 0) ri[wid] = v;
-    __syncthreads();
+    lds_barrier();
     const int t = ri[0] + ri[1] + ri[2] + ri[3];
-    __syncthreads();
+    lds_barrier();
     return t;
 }
 
@@ -195,10 +239,12 @@ __device__ __forceinline__ float amax4(float a, const float4 &v) {
 // Block form (256 threads): thread t owns O256 chain t, i.e. the float4
 // groups at k = 4t + 1024 i.  Rows of up to 1024 * CH elements keep x and
 // gamma in registers (one global round trip); `issued()` runs once every
-// wave of the block has issued those loads (a barrier), so loads the caller
-// issues there queue behind them and do not delay the normalisation.  LONG rows (K > 1024 * CH) are
-// streamed in chunks of CH float4 per thread, three times.
-template <int CH, bool LONG, class Sink, class Hook>
+// wave of the block has issued those loads (a barrier; with SYNC false, once
+// this wave has), so loads the caller issues there queue behind them and do
+// not delay the normalisation.  A wave skips the loads of a chunk that lies
+// wholly past K.  LONG rows (K > 1024 * CH) are streamed in chunks of CH
+// float4 per thread, three times.
+template <int CH, bool LONG, bool SYNC = true, class Sink, class Hook>
 __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
                                                     const float *__restrict__ gamma,
                                                     float eps, int K, float *red,
@@ -209,16 +255,21 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
         const auto rx = make_rsrc(x, 4u * (uint32_t)K);
         const auto rg = make_rsrc(gamma, 4u * (uint32_t)K);
         float4 xv[CH], gv[CH];
+        const int wk = 256 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int k = t4 + STRIDE * i;
             const uint32_t off = k < K ? 4u * (uint32_t)k : kOOB;
-            xv[i] = buf_load_f4(rx, off);
-            gv[i] = buf_load_f4(rg, off);
+            if (STRIDE * i + wk < K) {
+                xv[i] = buf_load_f4(rx, off);
+                gv[i] = buf_load_f4(rg, off);
+            } else {
+                xv[i] = gv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
         }
         // Every wave's x / gamma loads are issued before any load the hook
         // issues, so they do not queue behind another wave's weight misses.
-        __builtin_amdgcn_s_barrier();
+        if constexpr (SYNC) __builtin_amdgcn_s_barrier();
         issued();
         float p = 0.0f;
 #pragma unroll
@@ -435,6 +486,35 @@ struct FusedDecode {
     int64_t M, K, N;
 };
 hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipStream_t s);
+
+// One-shot decode contraction of up to 8 problems in one launch, int8
+// activations in global memory (M <= 8, M*K <= kShotMaxQ, K <= 32768).
+// y (rescaled) when every y is non-null, else acc (int32).
+constexpr int64_t kShotMaxQ = 32 * 1024;
+struct ShotDecode {
+    const int8_t *q;
+    const float *inv;
+    const int32_t *qsum;
+    const uint8_t *packed;
+    float *y;
+    int32_t *acc;
+    float w_scale;
+    int64_t M, K, N;
+};
+// shape: 1..shot_num_shapes() asks for that launch shape (taken when every
+// problem fits it), 0 picks one.
+int shot_num_shapes();
+// Rounds of workgroups the device needs for these problems in the one-shot
+// form with its own choice of launch shape (INT64_MAX: not supported).  One
+// round means every workgroup is resident at once.
+int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count);
+bool shot_supported(int64_t M, int64_t K);
+hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream_t s);
+// The same with the RMSNorm + quantisation fused in (M <= kFuseMaxM): every
+// workgroup normalises its problem's rows while its weight loads are in
+// flight; the first workgroup of each problem also writes q / inv / qsum.
+bool shot_fused_supported(int64_t M, int64_t K);
+hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hipStream_t s);
 int gemv_num_variants();
 
 // Prefill route (activation tiles staged in LDS, int8 MFMA).  Same

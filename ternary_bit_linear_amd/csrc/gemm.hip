@@ -17,8 +17,6 @@
 // flight while one is contracted; one barrier per step.  Each wave keeps
 // its (BM/WM) x (BN/WN) sub-tile in int32 accumulators.  All loads are
 // range-checked buffer loads: ragged M, N and K tails read zeros.
-#include <utility>
-
 #include "common.hpp"
 
 namespace bl {
@@ -53,14 +51,6 @@ __device__ __forceinline__ void wait_vm_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int I>
-using ic = std::integral_constant<int, I>;
-
-template <class F, int... I>
-__device__ __forceinline__ void unroll_ic(F &&f, std::integer_sequence<int, I...>) {
-    (f(ic<I>{}), ...);
-}
-
 template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_ring_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ inv,
@@ -87,7 +77,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_ring_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wid = tid >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps derived resources scalar
     const int wm = wid / WN, wn = wid % WN;
     const int j = lane & 15, kg = lane >> 4;
     const int m0 = blockIdx.y * BM;
@@ -250,7 +240,7 @@ constexpr Tile kTiles[] = {{64, 256, 1, 4, 3}, {64, 128, 1, 4, 3}, {64, 64, 2, 2
                            {32, 64, 1, 4, 0},  {32, 128, 1, 4, 0}, {128, 128, 1, 4, 3},
                            {128, 256, 1, 4, 3}, {64, 256, 1, 4, 4}, {64, 128, 1, 4, 0},
                            {128, 128, 2, 2, 0}, {64, 64, 2, 2, 3},  {32, 64, 1, 4, 3},
-                           {128, 256, 1, 8, 3}, {128, 256, 2, 4, 3}, {64, 512, 1, 8, 3}};
+                           {128, 256, 2, 4, 3}, {64, 512, 1, 8, 3}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // Ring depth for a tile: the deepest of 4, 5, 3 that divides the step count
@@ -292,12 +282,17 @@ template <int BM, int BN, int WM, int WN, int RFIX>
 hipError_t launch_tile(const int8_t *q, const float *inv, const int32_t *qsum,
                        const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
                        float *y, int32_t *acc, hipStream_t s) {
-    const int r = RFIX ? RFIX : pick_depth(BM, K);
-    if (r == 3) return launch_ring<BM, BN, WM, WN, 3>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
-    if constexpr (5 * BM * kStepK <= 160 * 1024)
-        if (r == 5)
-            return launch_ring<BM, BN, WM, WN, 5>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
-    return launch_ring<BM, BN, WM, WN, 4>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+    if constexpr (RFIX != 0) {
+        return launch_ring<BM, BN, WM, WN, RFIX>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+    } else {
+        const int r = pick_depth(BM, K);
+        if (r == 3)
+            return launch_ring<BM, BN, WM, WN, 3>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+        if constexpr (5 * BM * kStepK <= 160 * 1024)
+            if (r == 5)
+                return launch_ring<BM, BN, WM, WN, 5>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+        return launch_ring<BM, BN, WM, WN, 4>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+    }
 }
 
 }  // namespace
@@ -315,7 +310,7 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         // tiles (the wider one for long K).
         auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
         if (tiles(64, 512) >= 512)
-            v = 15;
+            v = 14;
         else if (tiles(64, 128) >= 256)
             v = 9;
         else if (K > 4096 && tiles(32, 128) >= 256)
@@ -343,7 +338,6 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         BL_GEMM_CASE(12)
         BL_GEMM_CASE(13)
         BL_GEMM_CASE(14)
-        BL_GEMM_CASE(15)
         default:
             return hipErrorInvalidValue;
     }

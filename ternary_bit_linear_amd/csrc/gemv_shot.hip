@@ -1,0 +1,562 @@
+// gemv_shot.hip -- one-shot decode contraction (gfx950).
+//
+// acc[m][n] = sum_k code(n, k) * q[m][k] - qsum[m], then optionally
+// y[m][n] = (float)acc * (w_scale / inv[m]), for M <= 8 tokens whose int8
+// activations are in global memory, or (fused form, M <= 4) whose q, inv
+// and qsum each workgroup computes from x, gamma and eps (RMSNorm + absmax
+// int8 quantisation).
+// [eejd/cpp-bitnet PR #7 "fix: I2_S ARM kernel layout + squared-ReLU FFN":
+// the vec_dot over I2_S codes and int8 activations, codes offset by the
+// activation sum; every output must be written.  HF-38087: RMSNorm on the
+// activations before their quantisation.]
+//
+// Design.  Each workgroup owns one set of weight rows (4 / ks waves' worth,
+// a wave holding R tiles of 8 consecutive rows, ks waves splitting each
+// tile group's K range) for the whole of K, and runs once: it issues every
+// load it will need at the start -- the activation block (or x and gamma)
+// and all of its weight batches, the weights as LDS-direct buffer loads
+// (lane i of a load writes bytes [16 i, 16 i + 16) after the wave's base
+// address, so no registers are held) -- then contracts batch after batch as
+// each lands, reduces the ks partial tiles through LDS, writes its outputs
+// and exits.  With no loop around the loads, a workgroup keeps its whole
+// share in flight from its first instruction.  The host picks the launch
+// shape (batches per wave, tiles per wave) so that every workgroup of the
+// launch is resident at once where it can be: a problem set that fits in
+// one round streams near the rate of a plain read of the same bytes, where
+// a persistent loop with a deep ring stays ~15% below it.  Larger sets take
+// the persistent form (gemv.hip).
+//
+// The arithmetic is the decode route's: the 16 bytes a lane copies hold,
+// per 2-bit field g, the codes of 16 consecutive k of one weight row (row
+// l % 8, chunk l / 8 of a 128-byte step); shifted and masked they are the
+// B operand of v_mfma_i32_16x16x64_i8 whose 16 columns are 8 rows x 2 chunk
+// parities, and the A operand holds the tokens in both halves of its 16 rows
+// with the matching chunk; one lane + 40 add joins the two parities.
+#include <climits>
+
+#include "common.hpp"
+
+namespace bl {
+namespace {
+
+constexpr int kW = 4;          // waves per workgroup
+constexpr int kTileRows = 8;   // weight rows per tile
+constexpr int kStep = 128;     // packed bytes of a row per step (512 k)
+constexpr int kU = 2;          // steps per batch
+constexpr int kMaxShotM = 8;
+
+struct ShotProblem {
+    const int8_t *q;       // activations (FM == 0)
+    const float *inv;
+    const int32_t *qsum;
+    const float *x;        // fused normalisation (FM > 0)
+    const float *gamma;
+    int8_t *q_out;         // fused: q / inv / qsum, written by the first workgroup
+    float *inv_out;
+    int32_t *qsum_out;
+    const uint8_t *packed;
+    float *y;
+    int32_t *acc;
+    float eps;
+    float w_scale;
+    int M, K, N;
+    int wg_begin;          // first workgroup of this problem
+    int ks_log;            // log2 of the K split: 0, 1 or 2
+};
+constexpr int kMaxShotBatch = 8;
+struct ShotBatch {
+    ShotProblem p[kMaxShotBatch];
+};
+static_assert(alignof(ShotBatch) == 8, "the batch follows eight ints in the argument segment");
+
+struct ShotRowSink {
+    int8_t *q;
+    float *inv;
+    int *qsum;
+    __device__ void store_q(int k, uint32_t v) { *reinterpret_cast<uint32_t *>(q + k) = v; }
+    __device__ void store_row(float iv, int qs) {
+        *inv = iv;
+        *qsum = qs;
+    }
+};
+
+// NB: weight batches (of kU 128-byte steps) per wave; the host picks ks so
+// that a wave's share of a row fits NB batches.  R: tiles of 8 rows per wave
+// (a wave's rows are 8 R consecutive rows; every batch holds all R tiles'
+// steps, so the activation fragments of a step serve R tiles).  FM: 0 takes q / inv / qsum
+// from global memory; FM > 0 computes them in every workgroup from x, gamma
+// and eps (M <= FM rows of K <= 1024 * CH, or streamed when LONG).
+// b0..b7: first workgroup of each problem (INT_MAX past the last); they
+// lead the argument list so that the build's kernel-argument preload puts
+// them in scalar registers at wave launch, and the lookup costs no memory
+// round trip.
+template <int NB, int R, bool OUT_Y, int FM, int CH, bool LONG>
+__global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, int b3, int b4,
+                                                        int b5, int b6, int b7, ShotBatch B) {
+    static_assert(NB >= 1 && NB <= 8, "batches per wave");
+    static_assert(R == 1 || R == 2 || R == 4, "tiles per wave");
+    static_assert(kMaxShotBatch == 8, "one leading argument per problem");
+    static_assert(kU == 2 && kW == 4, "shift forms below assume kU == 2, kW == 4");
+    static_assert(FM >= 0 && FM <= kMaxShotM, "fused token rows");
+    extern __shared__ __align__(16) int8_t q_lds[];
+    // One LDS object per batch (rows: waves), so that the compiler's own
+    // LDS-DMA tracking tells the batches apart and waits for each alone.
+    constexpr int SZ = R * kU * 1024;  // one batch of one wave
+    __shared__ __align__(16) int8_t w0[kW][SZ], w1[NB > 1 ? kW : 1][NB > 1 ? SZ : 16],
+        w2[NB > 2 ? kW : 1][NB > 2 ? SZ : 16], w3[NB > 3 ? kW : 1][NB > 3 ? SZ : 16],
+        w4[NB > 4 ? kW : 1][NB > 4 ? SZ : 16], w5[NB > 5 ? kW : 1][NB > 5 ? SZ : 16],
+        w6[NB > 6 ? kW : 1][NB > 6 ? SZ : 16], w7[NB > 7 ? kW : 1][NB > 7 ? SZ : 16];
+    __shared__ float red[4];
+    __shared__ float inv_sh[FM > 0 ? FM : 1];
+    __shared__ int qsum_sh[FM > 0 ? FM : 1];
+
+    // The batch is read in place from the kernel-argument segment (constant
+    // memory, wave-uniform addresses, so scalar loads): every field of this
+    // workgroup's problem in one round trip, all at once, before any other
+    // work (a field read where it is first used would cost a round trip of
+    // its own).
+    (void)b0;
+    const int bx = (int)blockIdx.x;
+    const int pi = (bx >= b1) + (bx >= b2) + (bx >= b3) + (bx >= b4) + (bx >= b5) + (bx >= b6) +
+                   (bx >= b7);
+    const ShotBatch *Bk = reinterpret_cast<const ShotBatch *>(
+        (const char *)__builtin_amdgcn_kernarg_segment_ptr() + 8 * sizeof(int));
+    const ShotProblem P = Bk->p[pi];
+    asm volatile("" ::"s"(P.q), "s"(P.inv), "s"(P.qsum), "s"(P.x), "s"(P.gamma), "s"(P.q_out),
+                 "s"(P.inv_out), "s"(P.qsum_out), "s"(P.packed), "s"(P.y), "s"(P.acc), "s"(P.eps),
+                 "s"(P.w_scale), "s"(P.M), "s"(P.K), "s"(P.N), "s"(P.wg_begin), "s"(P.ks_log));
+    const int M = P.M, K = P.K, N = P.N;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps derived resources scalar
+    const int r8 = lane & 7;    // weight row within the tile (load role)
+    const int ch = lane >> 3;   // 16-byte chunk within the 128-byte step
+    const uint32_t rowbytes = (uint32_t)K / 4;
+    const int nsteps = (int)((rowbytes + kStep - 1) / kStep);
+    const int kl = P.ks_log;
+    const int ks = 1 << kl;
+    const int sg = wid >> kl, kp = wid & (ks - 1);
+    const int nb = (nsteps + ks * kU - 1) >> (kl + 1);   // <= NB (kU == 2)
+    const int st = bx - P.wg_begin;                     // this workgroup's set
+    const int tg = (st << (2 - kl)) + sg;               // this wave's tile group (kW == 4)
+    const int n0 = tg * kTileRows * R;
+    auto batch = [&](auto I) -> int8_t * {
+        constexpr int b = decltype(I)::value;
+        if constexpr (b == 0) return w0[wid];
+        else if constexpr (b == 1) return w1[wid];
+        else if constexpr (b == 2) return w2[wid];
+        else if constexpr (b == 3) return w3[wid];
+        else if constexpr (b == 4) return w4[wid];
+        else if constexpr (b == 5) return w5[wid];
+        else if constexpr (b == 6) return w6[wid];
+        else return w7[wid];
+    };
+
+    // Every weight batch of this wave (past the end: range-checked to read
+    // nothing, so the count of loads is the same for every wave).
+    auto issue_weights = [&] {
+        const int rows = max(0, min(kTileRows * R, N - n0));
+        const auto rw = make_rsrc(P.packed + (size_t)min(n0, N) * rowbytes, (uint32_t)rows * rowbytes);
+        unroll_ic([&](auto I) {
+            constexpr int b = decltype(I)::value;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int s = b * ks * kU + kp * kU + u;
+                    const uint32_t cb = (uint32_t)s * kStep + 16u * ch;
+                    const bool kv = b < nb && s < nsteps && cb < rowbytes;
+                    const uint32_t off = (uint32_t)(r * kTileRows + r8) * rowbytes + cb;
+                    buf_load16_lds(rw, batch(I) + (r * kU + u) * 1024, kv ? off : kOOB, 0);
+                }
+            }
+        }, std::make_integer_sequence<int, NB>{});
+    };
+
+    // Epilogue operands of this lane's tokens (m = 4 (lane / 16) + c), read
+    // before any weight load so that no wait at the end drains behind them.
+    int qs_pre[4];
+    float iv_pre[4];
+    if constexpr (FM == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = min(4 * (lane >> 4) + c, M - 1);
+            qs_pre[c] = P.qsum[m];
+            iv_pre[c] = OUT_Y ? P.inv[m] : 1.0f;
+        }
+    }
+
+    if constexpr (FM == 0) {
+        // 1. The activation block (M rows of K int8, contiguous), 1 KB per
+        //    wave load, loads spread over the waves; 2. the weights.
+        const uint32_t qbytes = (uint32_t)(M * K);
+        const auto rq = make_rsrc(P.q, qbytes);
+        for (uint32_t c = (uint32_t)wid * 1024u; c < qbytes; c += kW * 1024u)
+            buf_load16_lds(rq, q_lds + c, c + 16u * lane, 0);
+        issue_weights();
+        // 3. Own activation loads done (only weight loads may still be in
+        //    flight), then every wave's: the block is complete in LDS.
+        wait_vmcnt<NB * R * kU>();
+        lds_barrier();
+    } else {
+        // 1. x and gamma of the first row go out first, the weights right
+        //    behind them; 2. RMSNorm + quantisation of every row into LDS
+        //    while the weights stream in.
+        {
+            ShotRowSink sink{q_lds, inv_sh, qsum_sh};
+            block_act_quant_row<CH, LONG, false>(P.x, P.gamma, P.eps, K, red, sink, issue_weights);
+        }
+#pragma unroll
+        for (int m = 1; m < FM; ++m) {
+            if (m < M) {
+                ShotRowSink sink{q_lds + m * K, inv_sh + m, qsum_sh + m};
+                block_act_quant_row<CH, LONG, false>(P.x + (size_t)m * K, P.gamma, P.eps, K, red,
+                                                     sink, [] {});
+            }
+        }
+        lds_barrier();
+        if (st == 0) {
+            for (int i = tid; i < M * K / 16; i += 256)
+                reinterpret_cast<uint4 *>(P.q_out)[i] = reinterpret_cast<const uint4 *>(q_lds)[i];
+            if (tid < M) {
+                P.inv_out[tid] = inv_sh[tid];
+                P.qsum_out[tid] = qsum_sh[tid];
+            }
+        }
+    }
+
+    // 4. Contract each batch as it lands.  The activation fragments of the
+    //    next batch are read from LDS while the current one is contracted.
+    auto read_q = [&](v4i(&a)[kU][4], int b) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int s = b * ks * kU + kp * kU + u;
+            const uint32_t cb = (uint32_t)s * kStep + 16u * ch;
+            const bool av = s < nsteps && cb < rowbytes && r8 < M;
+            // k of this lane's chunk: block cb / 32, half (cb / 16) % 2.
+            const int kb = (int)(cb / 32) * kBlockWeights + 16 * (int)((cb / 16) & 1);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                a[u][g] = av ? *reinterpret_cast<const v4i *>(q_lds + r8 * K + kb + 32 * g)
+                             : v4i{0, 0, 0, 0};
+        }
+    };
+    v4i acc[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[r][g] = v4i{0, 0, 0, 0};
+    v4i aq[2][kU][4];
+    read_q(aq[0], 0);
+    unroll_ic([&](auto I) {
+        constexpr int b = decltype(I)::value;
+        if (b >= nb) return;
+        if (b + 1 < NB) read_q(aq[(b + 1) & 1], b + 1);
+        wait_vmcnt<(NB - 1 - b) * R * kU>();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const v4i bw =
+                    *reinterpret_cast<const v4i *>(batch(I) + (r * kU + u) * 1024 + 16 * lane);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[r][g] = mfma16(aq[b & 1][u][g], unpack_field(bw, g), acc[r][g]);
+            }
+        }
+    }, std::make_integer_sequence<int, NB>{});
+
+    // 5. Sum the fields, then the ks waves of each tile group; the partial
+    //    tiles go to each wave's first weight buffer, no longer needed.
+    v4i *part = reinterpret_cast<v4i *>(&w0[0][0]);  // [kW][SZ / 16] v4i, R * 64 used
+    constexpr int PS = SZ / 16;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        part[wid * PS + r * 64 + lane] = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
+    lds_barrier();
+    // D(i, j) lives in lane j + 16*(i/4), register i%4.  Useful lanes:
+    // [0, 8) and [16, 24) (even chunks, row j, tokens 4*(lane/16) + c) and
+    // lane + 40 (odd chunks, same row and tokens).
+    const int l = lane;
+    if (kp == 0 && (l & 8) == 0 && l < 24) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int o = r * 64 + l;
+            v4i t = part[wid * PS + o] + part[wid * PS + o + 40];
+            for (int w = 1; w < ks; ++w) t += part[(wid + w) * PS + o] + part[(wid + w) * PS + o + 40];
+            const int n = n0 + r * kTileRows + (l & 7);
+            if (n < N) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int m = 4 * (l >> 4) + c;
+                    if (m < M) {
+                        const int qs = FM > 0 ? qsum_sh[m < FM ? m : 0] : qs_pre[c];
+                        const int v = t[c] - qs;
+                        if (OUT_Y) {
+                            const float iv = FM > 0 ? inv_sh[m < FM ? m : 0] : iv_pre[c];
+                            P.y[(size_t)m * N + n] = (float)v * (P.w_scale / iv);
+                        } else {
+                            P.acc[(size_t)m * N + n] = v;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Smallest K split (waves per tile group) that fits a wave's share of a
+// row into NB batches, or 0.
+int shot_ks(int64_t K, int nbmax) {
+    const int64_t nsteps = (K / 4 + kStep - 1) / kStep;
+    for (int ks = 1; ks <= kW; ks *= 2)
+        if ((nsteps + ks * kU - 1) / (ks * kU) <= nbmax) return ks;
+    return 0;
+}
+
+// Fills the batch: each problem's K split and first workgroup (begin[i];
+// INT_MAX past the last problem).  Returns the grid size; *qmax receives the
+// largest activation block (bytes).
+int64_t fill_batch(ShotBatch &B, int *begin, int count, int nb, int R, const int64_t *M,
+                   const int64_t *K, const int64_t *N, int64_t *qmax) {
+    int64_t gx = 0;
+    *qmax = 0;
+    for (int i = 0; i < count; ++i) {
+        const int ks = shot_ks(K[i], nb);
+        const int64_t ntg = (N[i] + kTileRows * R - 1) / (kTileRows * R);
+        const int64_t nset = (ntg + kW / ks - 1) / (kW / ks);
+        ShotProblem &P = B.p[i];
+        P.M = (int)M[i];
+        P.K = (int)K[i];
+        P.N = (int)N[i];
+        P.ks_log = ks == 1 ? 0 : ks == 2 ? 1 : 2;
+        P.wg_begin = (int)gx;
+        begin[i] = (int)gx;
+        gx += nset;
+        *qmax = std::max<int64_t>(*qmax, M[i] * K[i]);
+    }
+    for (int i = count; i < kMaxShotBatch; ++i) begin[i] = INT_MAX;
+    return gx;
+}
+
+template <class Kernel>
+hipError_t launch_batch(Kernel kern, const ShotBatch &B, const int *b, int64_t gx, int64_t qmax,
+                        hipStream_t s) {
+    const size_t lds = (size_t)((qmax + 1023) / 1024 * 1024);
+    if (gx < 1 || gx > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(256), lds, s, b[0], b[1], b[2], b[3], b[4],
+                       b[5], b[6], b[7], B);
+    return hipGetLastError();
+}
+
+// Launch shapes: weight batches per wave (NB) x tiles per wave (R).  A
+// workgroup holds NB * R * 8 KB of weights in LDS.
+struct ShotShape {
+    int nb, R;
+    int occupancy;  // workgroups per CU that the registers allow
+};
+constexpr ShotShape kShotShapes[] = {{3, 1, 4}, {4, 1, 4}, {8, 1, 4}, {3, 2, 3}, {4, 2, 3}, {3, 4, 3}};
+constexpr int kNumShotShapes = sizeof(kShotShapes) / sizeof(kShotShapes[0]);
+
+int device_cus() {
+    static int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        return n;
+    }();
+    return cus;
+}
+
+// Launch-shape choice.  A shape costs (in this order): the rounds of
+// workgroups the device needs to hold them all (resident workgroups per CU
+// from LDS and registers; more than one round leaves the later workgroups'
+// loads waiting for earlier ones to finish); then a score: the share of the
+// allocated weight LDS that stays unused (rows whose K share is shorter
+// than NB batches), weighted by bytes, plus small measured preferences (two
+// tiles per wave over one, one workgroup per CU the least, four tiles per
+// wave rarely).  *rounds_out receives the chosen shape's rounds.
+int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, int pref,
+               int64_t *rounds_out) {
+    auto fits = [&](int nb) {
+        for (int i = 0; i < count; ++i)
+            if (shot_ks(K[i], nb) == 0) return false;
+        return true;
+    };
+    int64_t qmax = 0;
+    for (int i = 0; i < count; ++i) qmax = std::max<int64_t>(qmax, M[i] * K[i]);
+    const int64_t q = (qmax + 1023) / 1024 * 1024;
+    const int cus = device_cus();
+    auto rounds_of = [&](const ShotShape &h) -> int64_t {
+        int64_t wgs = 0;
+        for (int i = 0; i < count; ++i) {
+            const int ks = shot_ks(K[i], h.nb);
+            const int64_t ntg = (N[i] + kTileRows * h.R - 1) / (kTileRows * h.R);
+            wgs += (ntg + kW / ks - 1) / (kW / ks);
+        }
+        const int64_t lds = (int64_t)h.nb * h.R * 8192 + q + 256;
+        const int64_t per_cu = std::min<int64_t>(h.occupancy, (160 * 1024) / lds);
+        return per_cu < 1 ? INT64_MAX : (wgs + per_cu * cus - 1) / (per_cu * cus);
+    };
+    if (pref >= 1 && pref <= kNumShotShapes && fits(kShotShapes[pref - 1].nb)) {
+        *rounds_out = rounds_of(kShotShapes[pref - 1]);
+        return pref - 1;
+    }
+    int best = -1;
+    int64_t best_rounds = 0;
+    double best_score = 0.0;
+    for (int v = 0; v < kNumShotShapes; ++v) {
+        const ShotShape &h = kShotShapes[v];
+        if (!fits(h.nb)) continue;
+        const int64_t rounds = rounds_of(h);
+        if (rounds == INT64_MAX) continue;
+        double used = 0.0, total = 0.0;
+        for (int i = 0; i < count; ++i) {
+            const int64_t nsteps = (K[i] / 4 + kStep - 1) / kStep;
+            const int ks = shot_ks(K[i], h.nb);
+            const double bytes = (double)N[i] * (double)(K[i] / 4);
+            used += bytes * ((double)nsteps / ks) / (h.nb * kU);
+            total += bytes;
+        }
+        const int64_t lds = (int64_t)h.nb * h.R * 8192 + q + 256;
+        const int64_t per_cu = std::min<int64_t>(h.occupancy, (160 * 1024) / lds);
+        double score = 100.0 * (1.0 - used / total);
+        score += h.R == 1 ? 10.0 : h.R == 4 ? 50.0 : 0.0;
+        score += per_cu == 1 ? 20.0 : 0.0;
+        if (best < 0 || rounds < best_rounds || (rounds == best_rounds && score < best_score)) {
+            best = v;
+            best_rounds = rounds;
+            best_score = score;
+        }
+    }
+    *rounds_out = best_rounds;
+    return best;
+}
+
+template <int NB, int R, bool OUT_Y>
+hipError_t launch_shot_nb(const ShotDecode *d, int count, hipStream_t s) {
+    ShotBatch B{};
+    int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
+    for (int i = 0; i < count; ++i) {
+        M[i] = d[i].M;
+        K[i] = d[i].K;
+        N[i] = d[i].N;
+        ShotProblem &P = B.p[i];
+        P.q = d[i].q;
+        P.inv = d[i].inv;
+        P.qsum = d[i].qsum;
+        P.packed = d[i].packed;
+        P.y = d[i].y;
+        P.acc = d[i].acc;
+        P.w_scale = d[i].w_scale;
+    }
+    int begin[kMaxShotBatch];
+    const int64_t gx = fill_batch(B, begin, count, NB, R, M, K, N, &qmax);
+    return launch_batch(gemv_shot_kernel<NB, R, OUT_Y, 0, 1, false>, B, begin, gx, qmax, s);
+}
+
+template <int NB, int R, int CH, bool LONG>
+hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) {
+    ShotBatch B{};
+    int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
+    for (int i = 0; i < count; ++i) {
+        M[i] = d[i].M;
+        K[i] = d[i].K;
+        N[i] = d[i].N;
+        ShotProblem &P = B.p[i];
+        P.x = d[i].x;
+        P.gamma = d[i].gamma;
+        P.q_out = d[i].q;
+        P.inv_out = d[i].inv;
+        P.qsum_out = d[i].qsum;
+        P.packed = d[i].packed;
+        P.y = d[i].y;
+        P.eps = d[i].eps;
+        P.w_scale = d[i].w_scale;
+    }
+    int begin[kMaxShotBatch];
+    const int64_t gx = fill_batch(B, begin, count, NB, R, M, K, N, &qmax);
+    return launch_batch(gemv_shot_kernel<NB, R, true, kFuseMaxM, CH, LONG>, B, begin, gx, qmax, s);
+}
+
+#define BL_SHOT_SHAPES(CALL)                                                   \
+    switch (v) {                                                               \
+        case 0: return CALL(3, 1);                                             \
+        case 1: return CALL(4, 1);                                             \
+        case 2: return CALL(8, 1);                                             \
+        case 3: return CALL(3, 2);                                             \
+        case 4: return CALL(4, 2);                                             \
+        case 5: return CALL(3, 4);                                             \
+        default: return hipErrorInvalidValue;                                  \
+    }
+
+template <int CH, bool LONG>
+hipError_t launch_fused_ch(const FusedDecode *d, int count, int v, hipStream_t s) {
+#define BL_F(NB_, R_) launch_shot_fused_nb<NB_, R_, CH, LONG>(d, count, s)
+    BL_SHOT_SHAPES(BL_F)
+#undef BL_F
+}
+
+template <bool OUT_Y>
+hipError_t launch_sep(const ShotDecode *d, int count, int v, hipStream_t s) {
+#define BL_S(NB_, R_) launch_shot_nb<NB_, R_, OUT_Y>(d, count, s)
+    BL_SHOT_SHAPES(BL_S)
+#undef BL_S
+}
+
+}  // namespace
+
+int shot_num_shapes() { return kNumShotShapes; }
+
+int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count) {
+    for (int i = 0; i < count; ++i)
+        if (!shot_supported(M[i], K[i])) return INT64_MAX;
+    int64_t rounds;
+    return pick_shape(M, K, N, count, 0, &rounds) < 0 ? INT64_MAX : rounds;
+}
+
+bool shot_supported(int64_t M, int64_t K) {
+    return M >= 1 && M <= kMaxShotM && M * K <= kShotMaxQ && shot_ks(K, 8) != 0;
+}
+
+bool shot_fused_supported(int64_t M, int64_t K) {
+    return M >= 1 && M <= kFuseMaxM && M * K <= kShotMaxQ && shot_ks(K, 8) != 0;
+}
+
+hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream_t s) {
+    if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
+    const bool y = d[0].y != nullptr;
+    int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch];
+    for (int i = 0; i < count; ++i) {
+        if (!shot_supported(d[i].M, d[i].K) || (d[i].y != nullptr) != y) return hipErrorInvalidValue;
+        M[i] = d[i].M;
+        K[i] = d[i].K;
+        N[i] = d[i].N;
+    }
+    int64_t rounds;
+    const int v = pick_shape(M, K, N, count, shape, &rounds);
+    return y ? launch_sep<true>(d, count, v, s) : launch_sep<false>(d, count, v, s);
+}
+
+hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hipStream_t s) {
+    if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
+    int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], kmax = 0;
+    for (int i = 0; i < count; ++i) {
+        if (!shot_fused_supported(d[i].M, d[i].K) || !d[i].y) return hipErrorInvalidValue;
+        M[i] = d[i].M;
+        K[i] = d[i].K;
+        N[i] = d[i].N;
+        kmax = std::max<int64_t>(kmax, d[i].K);
+    }
+    int64_t rounds;
+    const int v = pick_shape(M, K, N, count, shape, &rounds);
+    if (kmax <= 4096) return launch_fused_ch<4, false>(d, count, v, s);
+    if (kmax <= 8192) return launch_fused_ch<8, false>(d, count, v, s);
+    return launch_fused_ch<8, true>(d, count, v, s);
+}
+
+#undef BL_SHOT_SHAPES
+
+}  // namespace bl
