@@ -141,8 +141,9 @@ def linear_bytes(L):
     return L.N * L.K // 4 + 4 * L.M * L.K + 4 * L.K + 4 * L.M * L.N
 
 
+# Sources of the decode kernels (the traffic record is valid for these only).
 KERNEL_SOURCES = [os.path.join(ROOT, "ternary_bit_linear_amd", "csrc", f)
-                  for f in ("common.hpp", "gemv.hip", "act_quant.hip", "gemm.hip")]
+                  for f in ("common.hpp", "gemv.hip", "gemv_shot.hip", "act_quant.hip")]
 
 
 def sources_sha256() -> str:

@@ -70,7 +70,7 @@ typedef enum {
 } bl_status;
 
 /* Matmul route.  Both routes return bit-identical results; the choice only
- * affects speed.  AUTO takes the decode kernel for M <= 16 and the MFMA
+ * affects speed.  AUTO takes the decode kernel for M <= 4 and the MFMA
  * tile kernel above. */
 typedef enum {
     BL_PATH_AUTO = 0,
@@ -151,9 +151,11 @@ bl_status bitlinear_read_scale(const uint8_t *packed, int64_t N, int64_t K,
  *   q      = clamp(round_half_even(xn * inv_m), -128, 127)   (int8)
  *   acc    = sum_k code(n,k) * q[m][k] - sum_k q[m][k]   (int32, exact)
  *   y[m][n]= (float)acc * (w_scale / inv_m)              (fp32)
- * The sum of squares is taken in one fixed order (64 partial fp32 FMA
- * chains, chain j taking the elements k with (k/4) % 64 == j in increasing k,
- * then a halving tree over the chains), so the int8 codes are reproducible.
+ * The sum of squares is taken in one fixed order, "O256" (256 partial fp32
+ * FMA chains, chain j taking the elements k with (k/4) % 256 == j in
+ * increasing k; each group of 64 chains 64w..64w+63 reduced by a halving
+ * tree (j + 32 into j, then j + 16, ..., j + 1) to g_w; result
+ * (g_0 + g_1) + (g_2 + g_3)), so the int8 codes are reproducible.
  *   x:        device fp32 [M][K]; gamma: device fp32 [K]; eps > 0 (the
  *             pages' default is 1e-6) else BL_ERR_INVALID_ARG.
  *   packed_w: device I2_S buffer of W[N][K]; its trailer is not read:
