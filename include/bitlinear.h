@@ -196,9 +196,11 @@ typedef struct {
 
 /* Several independent BitLinear forwards, e.g. the BitLinears of one decoder
  * layer at decode (the survey's decode-layer launch).  Results are
- * bit-identical to calling bitlinear_forward_ex(descs[i], launch) for each i;
- * the decode-sized ones (M <= 4 with the fused quantisation; up to 8 per
- * launch) share one kernel launch, the others run one by one.
+ * bit-identical to calling bitlinear_forward_ex(descs[i], launch) for each i.
+ * The decode-sized ones (M <= 4 with the fused quantisation) share one
+ * kernel launch per 8; with the automatic launch shape, the prefill-sized
+ * ones with K % 256 == 0 and K <= 8192 share one quantisation launch and one
+ * tile-kernel launch per 8; the others run one by one.
  *   descs:  HOST array of `count` descriptors (1 <= count <= 64, else
  *           BL_ERR_INVALID_ARG); each is validated as bitlinear_forward
  *           validates its arguments, all before anything is enqueued.

@@ -38,11 +38,14 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-# Per-source extras.  gemv_shot.hip: its kernels take the per-problem first
-# workgroups as their eight leading int arguments, which gfx950 can preload
-# into scalar registers at wave launch.
+# Per-source extras.  The batched kernels of these files take the per-problem
+# first workgroups as their eight leading int arguments, which gfx950 can
+# preload into scalar registers at wave launch (for the other kernels the
+# preload only moves their first arguments into registers).
 EXTRA = {
     "gemv_shot.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+    "gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+    "act_quant.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
 }
 
 

@@ -12,6 +12,9 @@
 // thread, CH picked from K -- so every row is read with a single round trip
 // of fully issued loads.  HBM traffic per row: 4K (x) + 4K (gamma, L2-
 // resident after the first rows) + K (q) + 8 bytes.
+#include <algorithm>
+#include <climits>
+
 #include "common.hpp"
 
 namespace bl {
@@ -55,6 +58,44 @@ __global__ __launch_bounds__(256) void act_quant_long_kernel(
     block_act_quant_row<8, true>(x + (size_t)m * K, gamma, eps, K, red, sink, [] {});
 }
 
+// Batched form: up to 8 problems, one block per token row of any of them.
+// b0..b7: first block of each problem (INT_MAX past the last), leading the
+// argument list so that the build's kernel-argument preload puts them in
+// scalar registers at wave launch.
+struct AqProblem {
+    const float *x;
+    const float *gamma;
+    int8_t *q;
+    float *inv;
+    int32_t *qsum;
+    float eps;
+    int K;
+    int row_begin;
+};
+constexpr int kMaxAqBatch = 8;
+struct AqBatch {
+    AqProblem p[kMaxAqBatch];
+};
+
+template <int CH>
+__global__ __launch_bounds__(256) void act_quant_batch_kernel(int b0, int b1, int b2, int b3,
+                                                              int b4, int b5, int b6, int b7,
+                                                              AqBatch B) {
+    static_assert(kMaxAqBatch == 8, "one leading argument per problem");
+    __shared__ float red[4];
+    (void)b0;
+    const int bx = (int)blockIdx.x;
+    const int pi = (bx >= b1) + (bx >= b2) + (bx >= b3) + (bx >= b4) + (bx >= b5) + (bx >= b6) +
+                   (bx >= b7);
+    const AqBatch *Bk = reinterpret_cast<const AqBatch *>(
+        (const char *)__builtin_amdgcn_kernarg_segment_ptr() + 8 * sizeof(int));
+    const AqProblem P = Bk->p[pi];
+    const int m = bx - P.row_begin;
+    const int K = P.K;
+    GlobalRowSink sink{P.q + (size_t)m * K, P.inv + m, P.qsum + m};
+    block_act_quant_row<CH, false>(P.x + (size_t)m * K, P.gamma, P.eps, K, red, sink, [] {});
+}
+
 template <int CH>
 hipError_t launch_block(const float *x, const float *gamma, float eps, int64_t M, int64_t K,
                         int8_t *q, float *inv, int32_t *qsum, hipStream_t s) {
@@ -64,6 +105,37 @@ hipError_t launch_block(const float *x, const float *gamma, float eps, int64_t M
 }
 
 }  // namespace
+
+hipError_t launch_act_quant_batch(const ActQuantDesc *d, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxAqBatch) return hipErrorInvalidValue;
+    AqBatch B{};
+    int begin[kMaxAqBatch];
+    int64_t rows = 0, kmax = 0;
+    for (int i = 0; i < count; ++i) {
+        if (d[i].K > kActQuantBatchMaxK || d[i].K < 1 || d[i].M < 1) return hipErrorInvalidValue;
+        AqProblem &P = B.p[i];
+        P.x = d[i].x;
+        P.gamma = d[i].gamma;
+        P.q = d[i].q;
+        P.inv = d[i].inv;
+        P.qsum = d[i].qsum;
+        P.eps = d[i].eps;
+        P.K = (int)d[i].K;
+        P.row_begin = (int)rows;
+        begin[i] = (int)rows;
+        rows += d[i].M;
+        if (rows > INT32_MAX) return hipErrorInvalidConfiguration;
+        kmax = std::max<int64_t>(kmax, d[i].K);
+    }
+    for (int i = count; i < kMaxAqBatch; ++i) begin[i] = INT32_MAX;
+    if (kmax <= 4096)
+        hipLaunchKernelGGL(act_quant_batch_kernel<4>, dim3((unsigned)rows), dim3(256), 0, s, begin[0],
+                           begin[1], begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
+    else
+        hipLaunchKernelGGL(act_quant_batch_kernel<8>, dim3((unsigned)rows), dim3(256), 0, s, begin[0],
+                           begin[1], begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
+    return hipGetLastError();
+}
 
 hipError_t launch_act_quant(const float *x, const float *gamma, float eps,
                             int64_t M, int64_t K, int8_t *q, float *inv,

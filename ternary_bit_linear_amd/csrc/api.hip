@@ -154,6 +154,17 @@ bl::FusedDecode fused_of(const bl_forward_desc &d) {
     return f;
 }
 
+// Whether a validated forward that does not take the fused kernel can join
+// a grouped prefill launch (one batched quantisation launch, one grouped
+// tile-kernel launch): automatic launch shape, the tile route, K a whole
+// number of 256-k steps and rows that the batched quantisation holds in
+// registers.
+bool takes_group(const bl_forward_desc &d, const bl_launch *launch) {
+    if (launch && launch->variant != 0) return false;
+    return route_of(d.M, launch) == BL_PATH_GEMM && bl::gemm_group_supported(d.K) &&
+           d.K <= bl::kActQuantBatchMaxK;
+}
+
 // Enqueue one validated forward that does not take the fused kernel.
 bl_status enqueue_unfused(const bl_forward_desc &d, const bl_launch *launch, hipStream_t s) {
     const Workspace ws = carve(d.workspace, d.M, d.K);
@@ -166,6 +177,7 @@ bl_status enqueue_unfused(const bl_forward_desc &d, const bl_launch *launch, hip
 
 constexpr int kMaxBatchDescs = 64;
 constexpr int kFusedPerLaunch = 8;
+constexpr int kGroupPerLaunch = 8;
 
 }  // namespace
 
@@ -310,19 +322,37 @@ bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
     const int variant = launch ? launch->variant : 0;
     bl::FusedDecode group[kFusedPerLaunch];
     int n = 0;
+    bl::ActQuantDesc aq[kGroupPerLaunch];
+    bl::GemmDesc gd[kGroupPerLaunch];
+    int g = 0;
+    auto flush_group = [&]() -> bl_status {
+        if (g == 0) return BL_OK;
+        if (bl::launch_act_quant_batch(aq, g, s) != hipSuccess) return BL_ERR_HIP;
+        if (bl::launch_gemm_group(gd, g, s) != hipSuccess) return BL_ERR_HIP;
+        g = 0;
+        return BL_OK;
+    };
     for (int i = 0; i < count; ++i) {
-        if (takes_fused(descs[i], launch)) {
-            group[n++] = fused_of(descs[i]);
+        const bl_forward_desc &d = descs[i];
+        if (takes_fused(d, launch)) {
+            group[n++] = fused_of(d);
             if (n == kFusedPerLaunch) {
                 if (bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
                 n = 0;
             }
-        } else if (bl_status st = enqueue_unfused(descs[i], launch, s)) {
+        } else if (takes_group(d, launch)) {
+            const Workspace ws = carve(d.workspace, d.M, d.K);
+            aq[g] = bl::ActQuantDesc{d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum};
+            gd[g] = bl::GemmDesc{ws.q, ws.inv, ws.qsum, d.packed_w, d.w_scale,
+                                 d.M, d.K, d.N, d.y, nullptr};
+            if (++g == kGroupPerLaunch)
+                if (bl_status st = flush_group()) return st;
+        } else if (bl_status st = enqueue_unfused(d, launch, s)) {
             return st;
         }
     }
     if (n > 0 && bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
-    return BL_OK;
+    return flush_group();
 }
 
 }  // extern "C"

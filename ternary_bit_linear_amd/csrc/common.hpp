@@ -461,6 +461,20 @@ hipError_t launch_act_quant(const float *x, const float *gamma, float eps,
                             int64_t M, int64_t K, int8_t *q, float *inv,
                             int32_t *qsum, hipStream_t s);
 
+// Batched quantisation: up to 8 independent (x, gamma, eps, M, K) with
+// K <= 8192 each, one launch, bit-identical to launch_act_quant per problem.
+struct ActQuantDesc {
+    const float *x;
+    const float *gamma;
+    float eps;
+    int64_t M, K;
+    int8_t *q;
+    float *inv;
+    int32_t *qsum;
+};
+constexpr int64_t kActQuantBatchMaxK = 8192;
+hipError_t launch_act_quant_batch(const ActQuantDesc *d, int count, hipStream_t s);
+
 // Decode route, separate quantisation (q / inv / qsum already computed):
 // tokens in groups of 16 on int8 MFMA 16x16x64.  With y != NULL the
 // epilogue writes y = (acc - qsum) * (w_scale / inv); otherwise it writes
@@ -524,6 +538,22 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
                        int64_t K, int64_t N, float *y, int32_t *acc,
                        int variant, hipStream_t s);
 int gemm_num_variants();
+
+// Grouped prefill launch: up to 8 independent contractions (K % 256 == 0
+// each; all with y, or all with acc) in one launch, bit-identical to
+// launch_gemm per problem.
+struct GemmDesc {
+    const int8_t *q;
+    const float *inv;
+    const int32_t *qsum;
+    const uint8_t *packed;
+    float w_scale;
+    int64_t M, K, N;
+    float *y;
+    int32_t *acc;
+};
+bool gemm_group_supported(int64_t K);
+hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s);
 
 // I2_S packing: scan (codes + magnitude statistics into the trailer words),
 // then finalize (trailer = scale + 28 zero bytes).

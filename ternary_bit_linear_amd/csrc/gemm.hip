@@ -17,6 +17,9 @@
 // flight while one is contracted; one barrier per step.  Each wave keeps
 // its (BM/WM) x (BN/WN) sub-tile in int32 accumulators.  All loads are
 // range-checked buffer loads: ragged M, N and K tails read zeros.
+#include <algorithm>
+#include <climits>
+
 #include "common.hpp"
 
 namespace bl {
@@ -51,12 +54,14 @@ __device__ __forceinline__ void wait_vm_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// One BM x BN output tile at (m0, n0) of one problem, by the whole
+// workgroup.
 template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_ring_kernel(
+__device__ __forceinline__ void gemm_tile(
     const int8_t *__restrict__ q, const float *__restrict__ inv,
     const int32_t *__restrict__ qsum, const uint8_t *__restrict__ packed,
     float w_scale, int M, int K, int N, float *__restrict__ y,
-    int32_t *__restrict__ acc_out) {
+    int32_t *__restrict__ acc_out, int m0, int n0) {
     constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 16, NI = TN / 16;
@@ -80,8 +85,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_ring_kernel(
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps derived resources scalar
     const int wm = wid / WN, wn = wid % WN;
     const int j = lane & 15, kg = lane >> 4;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
     const int nsteps = (K + kStepK - 1) / kStepK;
     const int nblocks = K / kBlockWeights;
     const uint32_t rowbytes = (uint32_t)K / 4;
@@ -232,6 +235,57 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_ring_kernel(
     }
 }
 
+template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_ring_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ inv,
+    const int32_t *__restrict__ qsum, const uint8_t *__restrict__ packed,
+    float w_scale, int M, int K, int N, float *__restrict__ y,
+    int32_t *__restrict__ acc_out) {
+    gemm_tile<BM, BN, WM, WN, R, KTAIL, OUT_Y>(q, inv, qsum, packed, w_scale, M, K, N, y, acc_out,
+                                                (int)blockIdx.y * BM, (int)blockIdx.x * BN);
+}
+
+// Grouped form: up to 8 independent problems (K a whole number of steps)
+// in one launch, every tile of every problem one workgroup.
+struct GroupProblem {
+    const int8_t *q;
+    const float *inv;
+    const int32_t *qsum;
+    const uint8_t *packed;
+    float *y;
+    int32_t *acc;
+    float w_scale;
+    int M, K, N;
+    int tile_begin;  // first workgroup of this problem
+    int ntn;         // tiles along N
+};
+constexpr int kMaxGroup = 8;
+struct GroupBatch {
+    GroupProblem p[kMaxGroup];
+};
+
+// b0..b7: first workgroup of each problem (INT_MAX past the last); they
+// lead the argument list so that the build's kernel-argument preload puts
+// them in scalar registers at wave launch.  Tiles of a problem are ordered
+// N-fastest, as in the single-problem grid.
+template <int BM, int BN, int WM, int WN, int R, bool OUT_Y>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_group_kernel(int b0, int b1, int b2, int b3,
+                                                                  int b4, int b5, int b6, int b7,
+                                                                  GroupBatch B) {
+    static_assert(kMaxGroup == 8, "one leading argument per problem");
+    (void)b0;
+    const int bx = (int)blockIdx.x;
+    const int pi = (bx >= b1) + (bx >= b2) + (bx >= b3) + (bx >= b4) + (bx >= b5) + (bx >= b6) +
+                   (bx >= b7);
+    const GroupBatch *Bk = reinterpret_cast<const GroupBatch *>(
+        (const char *)__builtin_amdgcn_kernarg_segment_ptr() + 8 * sizeof(int));
+    const GroupProblem P = Bk->p[pi];
+    const int t = bx - P.tile_begin;
+    const int tm = t / P.ntn, tn = t - tm * P.ntn;
+    gemm_tile<BM, BN, WM, WN, R, false, OUT_Y>(P.q, P.inv, P.qsum, P.packed, P.w_scale, P.M, P.K,
+                                               P.N, P.y, P.acc, tm * BM, tn * BN);
+}
+
 struct Tile {
     int BM, BN, WM, WN, R;  // R == 0: ring depth picked from the step count
 };
@@ -298,6 +352,72 @@ hipError_t launch_tile(const int8_t *q, const float *inv, const int32_t *qsum,
 }  // namespace
 
 int gemm_num_variants() { return kNumTiles; }
+
+bool gemm_group_supported(int64_t K) { return K % kStepK == 0; }
+
+namespace {
+
+template <int BM, int BN, int WM, int WN, int R>
+hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
+    GroupBatch B{};
+    int begin[kMaxGroup];
+    int64_t total = 0;
+    const bool y = d[0].y != nullptr;
+    for (int i = 0; i < count; ++i) {
+        GroupProblem &P = B.p[i];
+        P.q = d[i].q;
+        P.inv = d[i].inv;
+        P.qsum = d[i].qsum;
+        P.packed = d[i].packed;
+        P.y = d[i].y;
+        P.acc = d[i].acc;
+        P.w_scale = d[i].w_scale;
+        P.M = (int)d[i].M;
+        P.K = (int)d[i].K;
+        P.N = (int)d[i].N;
+        const int64_t ntn = (d[i].N + BN - 1) / BN, ntm = (d[i].M + BM - 1) / BM;
+        P.ntn = (int)ntn;
+        P.tile_begin = (int)total;
+        begin[i] = (int)total;
+        total += ntn * ntm;
+        if (total > INT32_MAX) return hipErrorInvalidConfiguration;
+    }
+    for (int i = count; i < kMaxGroup; ++i) begin[i] = INT32_MAX;
+    const dim3 grid((unsigned)total), block(WM * WN * 64);
+    if (y)
+        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true>), grid, block, 0, s, begin[0],
+                           begin[1], begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
+    else
+        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, false>), grid, block, 0, s,
+                           begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],
+                           begin[7], B);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    const bool y = d[0].y != nullptr;
+    int64_t t64x512 = 0, t64x128 = 0, t32x128 = 0, kmax = 0;
+    for (int i = 0; i < count; ++i) {
+        if (!gemm_group_supported(d[i].K) || (d[i].y != nullptr) != y) return hipErrorInvalidValue;
+        auto tiles = [&](int bm, int bn) {
+            return ((d[i].M + bm - 1) / bm) * ((d[i].N + bn - 1) / bn);
+        };
+        t64x512 += tiles(64, 512);
+        t64x128 += tiles(64, 128);
+        t32x128 += tiles(32, 128);
+        kmax = std::max<int64_t>(kmax, d[i].K);
+    }
+    // The single-problem rule (launch_gemm) applied to the group's tile
+    // counts; one ring depth for all problems (steps past a problem's K
+    // read zeros).
+    if (t64x512 >= 512) return launch_group_tile<64, 512, 1, 8, 3>(d, count, s);
+    if (t64x128 >= 256) return launch_group_tile<64, 128, 1, 4, 4>(d, count, s);
+    if (kmax > 4096 && t32x128 >= 256) return launch_group_tile<32, 128, 1, 4, 4>(d, count, s);
+    return launch_group_tile<32, 64, 1, 4, 4>(d, count, s);
+}
 
 hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
                        const uint8_t *packed, float w_scale, int64_t M,

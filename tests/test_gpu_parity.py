@@ -403,3 +403,109 @@ def test_forward_batch_matches_single_calls(torch, bl, orc):
         torch.cuda.synchronize()
         for it, single in fused:
             assert np.array_equal(host(it[5]), single), v
+
+
+def test_forward_batch_grouped_prefill(torch, bl, orc):
+    """Prefill-sized problems of a batch (K a whole number of 256-k steps,
+    K <= 8192) go out as one batched quantisation launch and one grouped
+    tile-kernel launch per 8; each gives the bits of its single call.  The
+    batch spans two groups (10 such problems, ragged M and N, K from 256 to
+    8192) and mixes in problems that cannot join a group (K % 256 != 0,
+    K > 8192) and a fused decode problem."""
+    shapes = [(64, 256, 128), (70, 2560, 200), (130, 512, 17), (257, 768, 640), (5, 6912, 96),
+              (512, 2560, 130), (96, 8192, 64), (33, 1024, 1000), (300, 256, 33), (65, 2560, 640),
+              (40, 384, 130), (20, 8448, 48), (1, 2560, 256)]
+    items, singles, refs = [], [], []
+    for i, (M, K, N) in enumerate(shapes):
+        x, w, t, g = mm_case(M, K, N, 900 + i)
+        packed_r, s = orc.pack_i2s(w)
+        X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+        out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        ws = bl.new_workspace(M, K)
+        items.append((X, P, s, G, 1e-6, out, ws))
+        singles.append(host(bl.forward(X, P, s, G, 1e-6, N)).copy())
+        refs.append(orc.forward(x, packed_r, s, g, 1e-6, N))
+    announce("forward_batch grouped prefill", len(items))
+    bl.forward_batch(items)
+    torch.cuda.synchronize()
+    for (X, P, s, G, eps, out, ws), single, y64, (M, K, N) in zip(items, singles, refs, shapes):
+        assert np.array_equal(host(out), single), (M, K, N)
+        check_y(host(out), y64)
+        q, inv, qs = bl.workspace_views(ws, M, K)
+        q_r, inv_r, qs_r = orc.act_quant(host(X), host(G), 1e-6)
+        assert np.array_equal(host(q), q_r) and np.array_equal(host(inv), inv_r)
+        assert np.array_equal(host(qs), qs_r)
+    # the same prefill problems forced onto the tile route one by one
+    for it, single, (M, K, N) in zip(items, singles, shapes):
+        if M < 5:
+            continue
+        it[5].fill_(float("nan"))
+        bl.forward_batch([it], path=2, variant=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(it[5]), single), (M, K, N)
+
+
+def run_batch(torch, bl, orc, work, sample=None):
+    """Every BitLinear of a workload as one forward_batch call (the launch
+    configuration bench.py times); outputs checked against the oracle, on
+    sampled rows and columns when `sample` (rows, cols per linear) is set."""
+    items, data = [], []
+    for i, L in enumerate(work.linears):
+        x, w, t, g = work.inputs(i)
+        X, G = dev(torch, x), dev(torch, g)
+        P, s = bl.pack_i2s(dev(torch, w))
+        out = torch.full((L.M, L.N), float("nan"), dtype=torch.float32, device="cuda")
+        ws = bl.new_workspace(L.M, L.K)
+        items.append((X, P, s, G, work.eps, out, ws))
+        data.append((L, x, t, g, s))
+    announce("forward_batch", work.name, len(items))
+    bl.forward_batch(items)
+    torch.cuda.synchronize()
+    for i, ((X, P, s, G, eps, out, ws), (L, x, t, g, s_)) in enumerate(zip(items, data)):
+        y = host(out)
+        assert np.all(np.isfinite(y)), L.name
+        q_r, inv_r, qs_r = orc.act_quant(x, g, work.eps)
+        q, inv, qs = (host(a) for a in bl.workspace_views(ws, L.M, L.K))
+        assert np.array_equal(q, q_r) and np.array_equal(inv, inv_r) and np.array_equal(qs, qs_r)
+        rows, cols = (np.arange(L.M), np.arange(L.N)) if sample is None else sample(i, L)
+        acc = q_r[rows].astype(np.int64) @ t[cols].astype(np.int64).T
+        y64 = acc * (np.float64(s) / inv_r[rows].astype(np.float64))[:, None]
+        check_y(y[np.ix_(rows, cols)], y64)
+
+
+def test_workload_decode_layer_batched(torch, bl, orc):
+    run_batch(torch, bl, orc, wl.DECODE_LAYER)
+
+
+def test_workload_prefill_layer_batched(torch, bl, orc):
+    def sample(i, L):
+        rng = np.random.default_rng(50 + i)
+        rows = np.unique(np.concatenate([[0, L.M - 1], rng.integers(0, L.M, 14)]))
+        cols = np.unique(np.concatenate([[0, L.N - 1], rng.integers(0, L.N, 500)]))
+        return rows, cols
+    run_batch(torch, bl, orc, wl.PREFILL_LAYER, sample)
+
+
+@pytest.mark.parametrize("M,K,N", [(1024, 256, 2048), (64, 4352, 16384), (2048, 256, 8192)])
+def test_forward_batch_group_tiles(torch, bl, orc, M, K, N):
+    """The grouped tile launch with each of its larger tile shapes (64x128,
+    32x128, 64x512 by the group's tile counts): sampled outputs against the
+    oracle, all outputs bitwise against the single call."""
+    x, w, t, g = mm_case(M, K, N, 990 + M)
+    packed_r, s = orc.pack_i2s(w)
+    X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+    single = host(bl.forward(X, P, s, G, 1e-6, N)).copy()
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = bl.new_workspace(M, K)
+    announce("forward_batch group tile", M, K, N)
+    bl.forward_batch([(X, P, s, G, 1e-6, out, ws)])
+    torch.cuda.synchronize()
+    y = host(out)
+    assert np.array_equal(y, single)
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 30)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 300)]))
+    q_r, inv_r, qs_r = orc.act_quant(x, g, 1e-6)
+    acc = q_r[rows].astype(np.int64) @ t[cols].astype(np.int64).T
+    y64 = acc * (np.float64(s) / inv_r[rows].astype(np.float64))[:, None]
+    check_y(y[np.ix_(rows, cols)], y64)
