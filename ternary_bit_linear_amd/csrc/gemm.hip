@@ -294,7 +294,8 @@ constexpr Tile kTiles[] = {{64, 256, 1, 4, 3}, {64, 128, 1, 4, 3}, {64, 64, 2, 2
                            {32, 64, 1, 4, 0},  {32, 128, 1, 4, 0}, {128, 128, 1, 4, 3},
                            {128, 256, 1, 4, 3}, {64, 256, 1, 4, 4}, {64, 128, 1, 4, 0},
                            {128, 128, 2, 2, 0}, {64, 64, 2, 2, 3},  {32, 64, 1, 4, 3},
-                           {128, 256, 2, 4, 3}, {64, 512, 1, 8, 3}};
+                           {128, 256, 2, 4, 3}, {64, 512, 1, 8, 3}, {64, 512, 1, 8, 4},
+                           {64, 512, 1, 8, 5},  {64, 256, 1, 8, 4}, {32, 512, 1, 8, 4}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // Ring depth for a tile: the deepest of 4, 5, 3 that divides the step count
@@ -399,21 +400,28 @@ hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
 hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
     if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
     const bool y = d[0].y != nullptr;
-    int64_t t64x512 = 0, t64x128 = 0, t32x128 = 0, kmax = 0;
+    int64_t t64x512 = 0, t64x256 = 0, t64x128 = 0, t32x128 = 0, kmax = 0;
+    double work = 0.0, work_k = 0.0;  // int ops, and int ops x K
     for (int i = 0; i < count; ++i) {
         if (!gemm_group_supported(d[i].K) || (d[i].y != nullptr) != y) return hipErrorInvalidValue;
         auto tiles = [&](int bm, int bn) {
             return ((d[i].M + bm - 1) / bm) * ((d[i].N + bn - 1) / bn);
         };
         t64x512 += tiles(64, 512);
+        t64x256 += tiles(64, 256);
         t64x128 += tiles(64, 128);
         t32x128 += tiles(32, 128);
         kmax = std::max<int64_t>(kmax, d[i].K);
+        const double w = (double)d[i].M * (double)d[i].N * (double)d[i].K;
+        work += w;
+        work_k += w * (double)d[i].K;
     }
+    const double k_avg = work_k / work;  // K of the average int op
     // The single-problem rule (launch_gemm) applied to the group's tile
     // counts; one ring depth for all problems (steps past a problem's K
     // read zeros).
-    if (t64x512 >= 512) return launch_group_tile<64, 512, 1, 8, 3>(d, count, s);
+    if (t64x512 >= 512) return launch_group_tile<64, 512, 1, 8, 4>(d, count, s);
+    if (k_avg >= 6144.0 && t64x256 >= 256) return launch_group_tile<64, 256, 1, 8, 4>(d, count, s);
     if (t64x128 >= 256) return launch_group_tile<64, 128, 1, 4, 4>(d, count, s);
     if (kmax > 4096 && t32x128 >= 256) return launch_group_tile<32, 128, 1, 4, 4>(d, count, s);
     return launch_group_tile<32, 64, 1, 4, 4>(d, count, s);
@@ -425,12 +433,15 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
                        int variant, hipStream_t s) {
     int v = variant;
     if (v <= 0) {
-        // Picked from a sweep on MI355X: the widest tile when the grid still
-        // has two workgroups per CU, 64x128 down to one per CU, then 32-row
-        // tiles (the wider one for long K).
+        // Picked from a sweep on MI355X: the widest tiles (8 waves, a 4-step
+        // ring) when the grid still has two workgroups per CU, then 64x256
+        // (8 waves; long K only: short rows do not amortise its fill), 64x128
+        // down to one per CU, then 32-row tiles (the wider one for long K).
         auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
         if (tiles(64, 512) >= 512)
-            v = 14;
+            v = 15;
+        else if (K >= 6144 && tiles(64, 256) >= 256)
+            v = 17;
         else if (tiles(64, 128) >= 256)
             v = 9;
         else if (K > 4096 && tiles(32, 128) >= 256)
@@ -458,6 +469,10 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         BL_GEMM_CASE(12)
         BL_GEMM_CASE(13)
         BL_GEMM_CASE(14)
+        BL_GEMM_CASE(15)
+        BL_GEMM_CASE(16)
+        BL_GEMM_CASE(17)
+        BL_GEMM_CASE(18)
         default:
             return hipErrorInvalidValue;
     }

@@ -486,11 +486,12 @@ def test_workload_prefill_layer_batched(torch, bl, orc):
     run_batch(torch, bl, orc, wl.PREFILL_LAYER, sample)
 
 
-@pytest.mark.parametrize("M,K,N", [(1024, 256, 2048), (64, 4352, 16384), (2048, 256, 8192)])
+@pytest.mark.parametrize("M,K,N", [(1024, 256, 2048), (64, 4352, 16384), (2048, 256, 8192),
+                                   (512, 6144, 8192)])
 def test_forward_batch_group_tiles(torch, bl, orc, M, K, N):
     """The grouped tile launch with each of its larger tile shapes (64x128,
-    32x128, 64x512 by the group's tile counts): sampled outputs against the
-    oracle, all outputs bitwise against the single call."""
+    32x128, 64x512, 64x256 by the group's tile counts): sampled outputs
+    against the oracle, all outputs bitwise against the single call."""
     x, w, t, g = mm_case(M, K, N, 990 + M)
     packed_r, s = orc.pack_i2s(w)
     X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
