@@ -303,6 +303,7 @@ bl_status bitlinear_forward_ex(const float *x, const uint8_t *packed_w, float w_
         const bl::FusedDecode f = fused_of(d);
         return hip_status(bl::launch_gemv_fused(&f, 1, launch ? launch->variant : 0, s));
     }
+    if (takes_group(d, launch)) return bitlinear_forward_batch(&d, 1, launch, stream);
     return enqueue_unfused(d, launch, s);
 }
 

@@ -420,11 +420,26 @@ hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
     // The single-problem rule (launch_gemm) applied to the group's tile
     // counts; one ring depth for all problems (steps past a problem's K
     // read zeros).
+    // Ring depth (4 or 5) with the fewest padded steps, weighted by work: a
+    // problem's last ring turn runs past its K on loads that read zeros.
+    double pad4 = 0.0, pad5 = 0.0;
+    for (int i = 0; i < count; ++i) {
+        const double w = (double)d[i].M * (double)d[i].N * (double)d[i].K;
+        const int64_t ns = d[i].K / kStepK;
+        pad4 += w * (double)((4 - ns % 4) % 4) / (double)ns;
+        pad5 += w * (double)((5 - ns % 5) % 5) / (double)ns;
+    }
+    const bool r5 = pad5 < pad4;
     if (t64x512 >= 512) return launch_group_tile<64, 512, 1, 8, 4>(d, count, s);
     if (k_avg >= 6144.0 && t64x256 >= 256) return launch_group_tile<64, 256, 1, 8, 4>(d, count, s);
-    if (t64x128 >= 256) return launch_group_tile<64, 128, 1, 4, 4>(d, count, s);
-    if (kmax > 4096 && t32x128 >= 256) return launch_group_tile<32, 128, 1, 4, 4>(d, count, s);
-    return launch_group_tile<32, 64, 1, 4, 4>(d, count, s);
+    if (t64x128 >= 256)
+        return r5 ? launch_group_tile<64, 128, 1, 4, 5>(d, count, s)
+                  : launch_group_tile<64, 128, 1, 4, 4>(d, count, s);
+    if (kmax > 4096 && t32x128 >= 256)
+        return r5 ? launch_group_tile<32, 128, 1, 4, 5>(d, count, s)
+                  : launch_group_tile<32, 128, 1, 4, 4>(d, count, s);
+    return r5 ? launch_group_tile<32, 64, 1, 4, 5>(d, count, s)
+              : launch_group_tile<32, 64, 1, 4, 4>(d, count, s);
 }
 
 hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,

@@ -267,41 +267,58 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
         }
     }, std::make_integer_sequence<int, NB>{});
 
-    // 5. Sum the fields, then the ks waves of each tile group; the partial
-    //    tiles go to each wave's first weight buffer, no longer needed.
+    // 5. Sum the fields, then the ks waves of each tile group.
+    //    D(i, j) lives in lane j + 16*(i/4), register i%4.  Useful lanes:
+    //    [0, 8) and [16, 24) (even chunks, row j, tokens 4*(lane/16) + c) and
+    //    lane + 40 (odd chunks, same row and tokens).
+    const int l = lane;
+    auto store = [&](int r, const v4i &t) {
+        const int n = n0 + r * kTileRows + (l & 7);
+        if (n >= N) return;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = 4 * (l >> 4) + c;
+            if (m < M) {
+                const int qs = FM > 0 ? qsum_sh[m < FM ? m : 0] : qs_pre[c];
+                const int v = t[c] - qs;
+                if (OUT_Y) {
+                    const float iv = FM > 0 ? inv_sh[m < FM ? m : 0] : iv_pre[c];
+                    P.y[(size_t)m * N + n] = (float)v * (P.w_scale / iv);
+                } else {
+                    P.acc[(size_t)m * N + n] = v;
+                }
+            }
+        }
+    };
+    if (ks == 1) {
+        // Each wave owns whole tiles (ks is uniform over the workgroup):
+        // the parity halves meet by a lane permute, no LDS, no barrier.
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const v4i s4 = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
+            v4i t;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                t[c] = s4[c] + __builtin_amdgcn_ds_bpermute(((l + 40) & 63) << 2, s4[c]);
+            if ((l & 8) == 0 && l < 24) store(r, t);
+        }
+        return;
+    }
+    // ks > 1: the partial tiles go to each wave's first weight buffer, no
+    // longer needed, and the first wave of each group sums them.
     v4i *part = reinterpret_cast<v4i *>(&w0[0][0]);  // [kW][SZ / 16] v4i, R * 64 used
     constexpr int PS = SZ / 16;
 #pragma unroll
     for (int r = 0; r < R; ++r)
         part[wid * PS + r * 64 + lane] = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
     lds_barrier();
-    // D(i, j) lives in lane j + 16*(i/4), register i%4.  Useful lanes:
-    // [0, 8) and [16, 24) (even chunks, row j, tokens 4*(lane/16) + c) and
-    // lane + 40 (odd chunks, same row and tokens).
-    const int l = lane;
     if (kp == 0 && (l & 8) == 0 && l < 24) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int o = r * 64 + l;
             v4i t = part[wid * PS + o] + part[wid * PS + o + 40];
             for (int w = 1; w < ks; ++w) t += part[(wid + w) * PS + o] + part[(wid + w) * PS + o + 40];
-            const int n = n0 + r * kTileRows + (l & 7);
-            if (n < N) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int m = 4 * (l >> 4) + c;
-                    if (m < M) {
-                        const int qs = FM > 0 ? qsum_sh[m < FM ? m : 0] : qs_pre[c];
-                        const int v = t[c] - qs;
-                        if (OUT_Y) {
-                            const float iv = FM > 0 ? inv_sh[m < FM ? m : 0] : iv_pre[c];
-                            P.y[(size_t)m * N + n] = (float)v * (P.w_scale / iv);
-                        } else {
-                            P.acc[(size_t)m * N + n] = v;
-                        }
-                    }
-                }
-            }
+            store(r, t);
         }
     }
 }
