@@ -43,7 +43,7 @@ template <int CH>
 __global__ __launch_bounds__(256) void act_quant_block_kernel(
     const float *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
     int8_t *__restrict__ q, float *__restrict__ inv, int32_t *__restrict__ qsum) {
-    __shared__ float red[4];
+    __shared__ float red[kRedWords];
     const int m = blockIdx.x;
     GlobalRowSink sink{q + (size_t)m * K, inv + m, qsum + m};
     block_act_quant_row<CH, false>(x + (size_t)m * K, gamma, eps, K, red, sink, [] {});
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void act_quant_block_kernel(
 __global__ __launch_bounds__(256) void act_quant_long_kernel(
     const float *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
     int8_t *__restrict__ q, float *__restrict__ inv, int32_t *__restrict__ qsum) {
-    __shared__ float red[4];
+    __shared__ float red[kRedWords];
     const int m = blockIdx.x;
     GlobalRowSink sink{q + (size_t)m * K, inv + m, qsum + m};
     block_act_quant_row<8, true>(x + (size_t)m * K, gamma, eps, K, red, sink, [] {});
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void act_quant_batch_kernel(int b0, int b1, in
                                                               int b4, int b5, int b6, int b7,
                                                               AqBatch B) {
     static_assert(kMaxAqBatch == 8, "one leading argument per problem");
-    __shared__ float red[4];
+    __shared__ float red[kRedWords];
     (void)b0;
     const int bx = (int)blockIdx.x;
     const int pi = (bx >= b1) + (bx >= b2) + (bx >= b3) + (bx >= b4) + (bx >= b5) + (bx >= b6) +

@@ -51,6 +51,31 @@ __device__ __forceinline__ v4i unpack_field(const v4i &p, int g) {
     return r;
 }
 
+// Field g of a 16-byte packed chunk, each code scaled by 2^kFieldShift[g]:
+// the code bits are masked where they sit (fields 1..3) or shifted down
+// (field 0), 5 instructions per dword instead of 7.  Byte values: field 0 code,
+// field 1 16 code, field 2 4 code, field 3 code -- all within int8.  A sum of
+// int8 products over field g is then an exact multiple of 2^kFieldShift[g];
+// an arithmetic right shift by it restores the sum of codes times
+// activations.
+constexpr int kFieldShift[4] = {0, 4, 2, 0};
+__device__ __forceinline__ v4i unpack_scaled(const v4i &p, int g) {
+    v4i r;
+    if (g == 0) {
+        r.x = (int)(((uint32_t)p.x >> 6) & 0x03030303u);
+        r.y = (int)(((uint32_t)p.y >> 6) & 0x03030303u);
+        r.z = (int)(((uint32_t)p.z >> 6) & 0x03030303u);
+        r.w = (int)(((uint32_t)p.w >> 6) & 0x03030303u);
+    } else {
+        const uint32_t mask = g == 1 ? 0x30303030u : g == 2 ? 0x0C0C0C0Cu : 0x03030303u;
+        r.x = (int)((uint32_t)p.x & mask);
+        r.y = (int)((uint32_t)p.y & mask);
+        r.z = (int)((uint32_t)p.z & mask);
+        r.w = (int)((uint32_t)p.w & mask);
+    }
+    return r;
+}
+
 // D[16][16] += A[16][64] * B[64][16] (int8 -> int32).  Lane l supplies
 // A row (l % 16) and B column (l % 16), 16 bytes each for its k-group
 // l / 16; D element (i, j) lives in lane j + 16 * (i / 4), register i % 4.
@@ -181,6 +206,9 @@ __device__ __forceinline__ uint32_t pack_char4(int a, int b, int c, int d) {
 
 // Block-wide reductions over exactly 256 threads (4 waves).  `red` is 4
 // words of shared memory; the caller's block must reach these uniformly.
+// Each takes one barrier: a caller that runs several reductions gives each
+// its own 4 words (or separates reuses of the same words by another
+// barrier), so no trailing barrier is needed.
 //
 // Sum of squares of one row in the library's fixed order "O256": thread t
 // owns the elements k with (k / 4) % 256 == t and accumulates their squares
@@ -194,9 +222,7 @@ __device__ __forceinline__ float block_sumsq_finish(float p, float *red) {
     p = wave_tree_sum_f(p);
     if (lane == 0) red[wid] = p;
     lds_barrier();
-    const float t = (red[0] + red[1]) + (red[2] + red[3]);
-    lds_barrier();
-    return t;
+    return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 __device__ __forceinline__ float block_max(float v, float *red) {
@@ -204,9 +230,7 @@ __device__ __forceinline__ float block_max(float v, float *red) {
     v = wave_max(v);
     if (lane == 0) red[wid] = v;
     lds_barrier();
-    const float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    lds_barrier();
-    return t;
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 __device__ __forceinline__ int block_sum_int(int v, float *red) {
@@ -215,10 +239,12 @@ __device__ __forceinline__ int block_sum_int(int v, float *red) {
     int *ri = reinterpret_cast<int *>(red);
     if (lane == 0) ri[wid] = v;
     lds_barrier();
-    const int t = ri[0] + ri[1] + ri[2] + ri[3];
-    lds_barrier();
-    return t;
+    return ri[0] + ri[1] + ri[2] + ri[3];
 }
+
+// Shared-memory words the block reductions of one row take (three
+// reductions of 4 words each).
+constexpr int kRedWords = 12;
 
 __device__ __forceinline__ float4 xn4(const float4 &x, const float4 &g, float r) {
     return make_float4((x.x * r) * g.x, (x.y * r) * g.y, (x.z * r) * g.z, (x.w * r) * g.w);
@@ -271,34 +297,43 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
         // issues, so they do not queue behind another wave's weight misses.
         if constexpr (SYNC) __builtin_amdgcn_s_barrier();
         issued();
+        // Chunks wholly past K hold zeros, which leave the sum of squares and
+        // the max unchanged: the wave skips them (a wave-uniform test).
         float p = 0.0f;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            p = __builtin_fmaf(xv[i].x, xv[i].x, p);
-            p = __builtin_fmaf(xv[i].y, xv[i].y, p);
-            p = __builtin_fmaf(xv[i].z, xv[i].z, p);
-            p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+            if (STRIDE * i + wk < K) {
+                p = __builtin_fmaf(xv[i].x, xv[i].x, p);
+                p = __builtin_fmaf(xv[i].y, xv[i].y, p);
+                p = __builtin_fmaf(xv[i].z, xv[i].z, p);
+                p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+            }
         }
         const float ss = block_sumsq_finish(p, red);
         const float r = 1.0f / sqrtf(ss / (float)K + eps);
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) amax = amax4(amax, xn4(xv[i], gv[i], r));
-        amax = block_max(amax, red);
+        for (int i = 0; i < CH; ++i) {
+            if (STRIDE * i + wk < K) {
+                xv[i] = xn4(xv[i], gv[i], r);  // x is not needed again: keep xn
+                amax = amax4(amax, xv[i]);
+            }
+        }
+        amax = block_max(amax, red + 4);
         const float inv = 127.0f / fmaxf(amax, 1e-5f);
         int qs = 0;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int k = t4 + STRIDE * i;
             if (k < K) {
-                const float4 v = xn4(xv[i], gv[i], r);
+                const float4 v = xv[i];
                 const int a = quant_one(v.x, inv), b = quant_one(v.y, inv);
                 const int c = quant_one(v.z, inv), d = quant_one(v.w, inv);
                 qs += a + b + c + d;
                 sink.store_q(k, pack_char4(a, b, c, d));
             }
         }
-        qs = block_sum_int(qs, red);
+        qs = block_sum_int(qs, red + 8);
         if (threadIdx.x == 0) sink.store_row(inv, qs);
         return;
     } else {
@@ -333,7 +368,7 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
 #pragma unroll
         for (int i = 0; i < CH; ++i) amax = amax4(amax, xn4(xv[i], gv[i], r));
     }
-    amax = block_max(amax, red);
+    amax = block_max(amax, red + 4);
     const float inv = 127.0f / fmaxf(amax, 1e-5f);
     int qs = 0;
     for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
@@ -355,7 +390,7 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
             }
         }
     }
-    qs = block_sum_int(qs, red);
+    qs = block_sum_int(qs, red + 8);
     if (threadIdx.x == 0) sink.store_row(inv, qs);
     }
 }

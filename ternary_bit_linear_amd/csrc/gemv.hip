@@ -100,7 +100,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &A) {
     int32_t *__restrict__ acc_out = A.acc_out;
     const float eps = A.eps, w_scale = A.w_scale;
     const int M = A.M, K = A.K, N = A.N;
-    __shared__ float red[4];
+    __shared__ float red[kRedWords];
     __shared__ float inv_sh[4];
     __shared__ int qsum_sh[4];
     __shared__ v4i part[kW][TH][R][64];
@@ -322,7 +322,7 @@ __device__ __forceinline__ void gemv_ring_body(const GemvArgs &A) {
     int32_t *__restrict__ acc_out = A.acc_out;
     const float eps = A.eps, w_scale = A.w_scale;
     const int M = A.M, K = A.K, N = A.N;
-    __shared__ float red[4];
+    __shared__ float red[kRedWords];
     __shared__ float inv_sh[16];
     __shared__ int qsum_sh[16];
     __shared__ v4i part[kW][TH][R][64];

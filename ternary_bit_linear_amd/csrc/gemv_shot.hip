@@ -69,16 +69,36 @@ struct ShotBatch {
 };
 static_assert(alignof(ShotBatch) == 8, "the batch follows eight ints in the argument segment");
 
+// q / inv / qsum of one token row into LDS and, for the problem's first
+// workgroup (gq non-null), also into global memory -- straight from
+// registers, so that no LDS read of them has to wait for the weight loads
+// in flight.
 struct ShotRowSink {
     int8_t *q;
     float *inv;
     int *qsum;
-    __device__ void store_q(int k, uint32_t v) { *reinterpret_cast<uint32_t *>(q + k) = v; }
+    int8_t *gq;
+    float *ginv;
+    int32_t *gqsum;
+    __device__ void store_q(int k, uint32_t v) {
+        *reinterpret_cast<uint32_t *>(q + k) = v;
+        if (gq) *reinterpret_cast<uint32_t *>(gq + k) = v;
+    }
     __device__ void store_row(float iv, int qs) {
         *inv = iv;
         *qsum = qs;
+        if (gq) {
+            *ginv = iv;
+            *gqsum = qs;
+        }
     }
 };
+
+// Sum over the four fields of per-field accumulators of scaled codes
+// (unpack_scaled): each is an exact multiple of its scale.
+__device__ __forceinline__ v4i field_sum(const v4i (&a)[4]) {
+    return (a[0] + (a[1] >> kFieldShift[1])) + ((a[2] >> kFieldShift[2]) + a[3]);
+}
 
 // NB: weight batches (of kU 128-byte steps) per wave; the host picks ks so
 // that a wave's share of a row fits NB batches.  R: tiles of 8 rows per wave
@@ -106,7 +126,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
         w2[NB > 2 ? kW : 1][NB > 2 ? SZ : 16], w3[NB > 3 ? kW : 1][NB > 3 ? SZ : 16],
         w4[NB > 4 ? kW : 1][NB > 4 ? SZ : 16], w5[NB > 5 ? kW : 1][NB > 5 ? SZ : 16],
         w6[NB > 6 ? kW : 1][NB > 6 ? SZ : 16], w7[NB > 7 ? kW : 1][NB > 7 ? SZ : 16];
-    __shared__ float red[4];
+    __shared__ float red[kRedWords];
     __shared__ float inv_sh[FM > 0 ? FM : 1];
     __shared__ int qsum_sh[FM > 0 ? FM : 1];
 
@@ -204,26 +224,21 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
         //    behind them; 2. RMSNorm + quantisation of every row into LDS
         //    while the weights stream in.
         {
-            ShotRowSink sink{q_lds, inv_sh, qsum_sh};
+            ShotRowSink sink{q_lds, inv_sh, qsum_sh, st == 0 ? P.q_out : nullptr, P.inv_out,
+                             P.qsum_out};
             block_act_quant_row<CH, LONG, false>(P.x, P.gamma, P.eps, K, red, sink, issue_weights);
         }
 #pragma unroll
         for (int m = 1; m < FM; ++m) {
             if (m < M) {
-                ShotRowSink sink{q_lds + m * K, inv_sh + m, qsum_sh + m};
+                ShotRowSink sink{q_lds + m * K, inv_sh + m, qsum_sh + m,
+                                 st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m,
+                                 P.qsum_out + m};
                 block_act_quant_row<CH, LONG, false>(P.x + (size_t)m * K, P.gamma, P.eps, K, red,
                                                      sink, [] {});
             }
         }
         lds_barrier();
-        if (st == 0) {
-            for (int i = tid; i < M * K / 16; i += 256)
-                reinterpret_cast<uint4 *>(P.q_out)[i] = reinterpret_cast<const uint4 *>(q_lds)[i];
-            if (tid < M) {
-                P.inv_out[tid] = inv_sh[tid];
-                P.qsum_out[tid] = qsum_sh[tid];
-            }
-        }
     }
 
     // 4. Contract each batch as it lands.  The activation fragments of the
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
                     *reinterpret_cast<const v4i *>(batch(I) + (r * kU + u) * 1024 + 16 * lane);
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    acc[r][g] = mfma16(aq[b & 1][u][g], unpack_field(bw, g), acc[r][g]);
+                    acc[r][g] = mfma16(aq[b & 1][u][g], unpack_scaled(bw, g), acc[r][g]);
             }
         }
     }, std::make_integer_sequence<int, NB>{});
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
         // the parity halves meet by a lane permute, no LDS, no barrier.
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const v4i s4 = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
+            const v4i s4 = field_sum(acc[r]);
             v4i t;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
@@ -310,7 +325,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
     constexpr int PS = SZ / 16;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        part[wid * PS + r * 64 + lane] = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
+        part[wid * PS + r * 64 + lane] = field_sum(acc[r]);
     lds_barrier();
     if (kp == 0 && (l & 8) == 0 && l < 24) {
 #pragma unroll
@@ -474,7 +489,7 @@ hipError_t launch_shot_nb(const ShotDecode *d, int count, hipStream_t s) {
     return launch_batch(gemv_shot_kernel<NB, R, OUT_Y, 0, 1, false>, B, begin, gx, qmax, s);
 }
 
-template <int NB, int R, int CH, bool LONG>
+template <int NB, int R, int FM, int CH, bool LONG>
 hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) {
     ShotBatch B{};
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
@@ -495,7 +510,7 @@ hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) 
     }
     int begin[kMaxShotBatch];
     const int64_t gx = fill_batch(B, begin, count, NB, R, M, K, N, &qmax);
-    return launch_batch(gemv_shot_kernel<NB, R, true, kFuseMaxM, CH, LONG>, B, begin, gx, qmax, s);
+    return launch_batch(gemv_shot_kernel<NB, R, true, FM, CH, LONG>, B, begin, gx, qmax, s);
 }
 
 #define BL_SHOT_SHAPES(CALL)                                                   \
@@ -509,9 +524,9 @@ hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) 
         default: return hipErrorInvalidValue;                                  \
     }
 
-template <int CH, bool LONG>
+template <int FM, int CH, bool LONG>
 hipError_t launch_fused_ch(const FusedDecode *d, int count, int v, hipStream_t s) {
-#define BL_F(NB_, R_) launch_shot_fused_nb<NB_, R_, CH, LONG>(d, count, s)
+#define BL_F(NB_, R_) launch_shot_fused_nb<NB_, R_, FM, CH, LONG>(d, count, s)
     BL_SHOT_SHAPES(BL_F)
 #undef BL_F
 }
@@ -559,19 +574,27 @@ hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream
 
 hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hipStream_t s) {
     if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
-    int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], kmax = 0;
+    int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], kmax = 0, mmax = 0;
     for (int i = 0; i < count; ++i) {
         if (!shot_fused_supported(d[i].M, d[i].K) || !d[i].y) return hipErrorInvalidValue;
         M[i] = d[i].M;
         K[i] = d[i].K;
         N[i] = d[i].N;
         kmax = std::max<int64_t>(kmax, d[i].K);
+        mmax = std::max<int64_t>(mmax, d[i].M);
     }
     int64_t rounds;
     const int v = pick_shape(M, K, N, count, shape, &rounds);
-    if (kmax <= 4096) return launch_fused_ch<4, false>(d, count, v, s);
-    if (kmax <= 8192) return launch_fused_ch<8, false>(d, count, v, s);
-    return launch_fused_ch<8, true>(d, count, v, s);
+    // One token everywhere (the decode case): the kernel that normalises a
+    // single row, whose code is a quarter of the general one's.
+    if (mmax == 1) {
+        if (kmax <= 4096) return launch_fused_ch<1, 4, false>(d, count, v, s);
+        if (kmax <= 8192) return launch_fused_ch<1, 8, false>(d, count, v, s);
+        return launch_fused_ch<1, 8, true>(d, count, v, s);
+    }
+    if (kmax <= 4096) return launch_fused_ch<kFuseMaxM, 4, false>(d, count, v, s);
+    if (kmax <= 8192) return launch_fused_ch<kFuseMaxM, 8, false>(d, count, v, s);
+    return launch_fused_ch<kFuseMaxM, 8, true>(d, count, v, s);
 }
 
 #undef BL_SHOT_SHAPES
