@@ -69,11 +69,9 @@ struct AqProblem {
     float *inv;
     int32_t *qsum;
     float eps;
-    int M, K;
-    int blk_begin;  // first block of this problem
-    int rows4;      // 1: four rows per block, one per wave; 0: one row per block
+    int K;
+    int row_begin;
 };
-constexpr int kWaveRowMaxK = 3 * 1024;  // rows a single wave holds in registers
 constexpr int kMaxAqBatch = 8;
 struct AqBatch {
     AqProblem p[kMaxAqBatch];
@@ -92,17 +90,8 @@ __global__ __launch_bounds__(256) void act_quant_batch_kernel(int b0, int b1, in
     const AqBatch *Bk = reinterpret_cast<const AqBatch *>(
         (const char *)__builtin_amdgcn_kernarg_segment_ptr() + 8 * sizeof(int));
     const AqProblem P = Bk->p[pi];
+    const int m = bx - P.row_begin;
     const int K = P.K;
-    if (P.rows4) {
-        // Short rows: one wave per row, whole row in registers, no barrier
-        // (the same bits as the block form).
-        const int m = 4 * (bx - P.blk_begin) + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-        if (m >= P.M) return;
-        GlobalRowSink sink{P.q + (size_t)m * K, P.inv + m, P.qsum + m};
-        wave_act_quant_row<3>(P.x + (size_t)m * K, P.gamma, P.eps, K, sink);
-        return;
-    }
-    const int m = bx - P.blk_begin;
     GlobalRowSink sink{P.q + (size_t)m * K, P.inv + m, P.qsum + m};
     block_act_quant_row<CH, false>(P.x + (size_t)m * K, P.gamma, P.eps, K, red, sink, [] {});
 }
@@ -131,14 +120,12 @@ hipError_t launch_act_quant_batch(const ActQuantDesc *d, int count, hipStream_t 
         P.inv = d[i].inv;
         P.qsum = d[i].qsum;
         P.eps = d[i].eps;
-        P.M = (int)d[i].M;
         P.K = (int)d[i].K;
-        P.rows4 = d[i].K <= kWaveRowMaxK ? 1 : 0;
-        P.blk_begin = (int)rows;
+        P.row_begin = (int)rows;
         begin[i] = (int)rows;
-        rows += P.rows4 ? (d[i].M + 3) / 4 : d[i].M;
+        rows += d[i].M;
         if (rows > INT32_MAX) return hipErrorInvalidConfiguration;
-        if (!P.rows4) kmax = std::max<int64_t>(kmax, d[i].K);
+        kmax = std::max<int64_t>(kmax, d[i].K);
     }
     for (int i = count; i < kMaxAqBatch; ++i) begin[i] = INT32_MAX;
     if (kmax <= 4096)
