@@ -141,9 +141,10 @@ def linear_bytes(L):
     return L.N * L.K // 4 + 4 * L.M * L.K + 4 * L.K + 4 * L.M * L.N
 
 
-# Sources of the decode kernels (the traffic record is valid for these only).
+# Sources of the batched decode kernel (the traffic record is valid for
+# these only).
 KERNEL_SOURCES = [os.path.join(ROOT, "ternary_bit_linear_amd", "csrc", f)
-                  for f in ("common.hpp", "gemv.hip", "gemv_shot.hip", "act_quant.hip")]
+                  for f in ("common.hpp", "gemv_shot.hip")]
 
 
 def sources_sha256() -> str:
