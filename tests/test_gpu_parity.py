@@ -510,3 +510,46 @@ def test_forward_batch_group_tiles(torch, bl, orc, M, K, N):
     acc = q_r[rows].astype(np.int64) @ t[cols].astype(np.int64).T
     y64 = acc * (np.float64(s) / inv_r[rows].astype(np.float64))[:, None]
     check_y(y[np.ix_(rows, cols)], y64)
+
+
+def test_graph_replay_forward_batch_new_inputs(torch, bl, orc):
+    """forward_batch captured once in a HIP graph (one-shot decode launch plus
+    a grouped prefill launch pair) and replayed with new activations copied
+    into the same buffers between replays: every replay matches the eager
+    batch on those inputs and the oracle, so no launch keeps state from an
+    earlier one."""
+    shapes = [(1, 2560, 640), (1, 6912, 256), (2, 1024, 96), (64, 2560, 200), (130, 512, 96)]
+    data = []
+    for i, (M, K, N) in enumerate(shapes):
+        x, w, t, g = mm_case(M, K, N, 1500 + i)
+        packed_r, s = orc.pack_i2s(w)
+        X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        data.append([X, P, s, G, out, bl.new_workspace(M, K), packed_r, g])
+    items = lambda: [(d[0], d[1], d[2], d[3], 1e-6, d[4], d[5]) for d in data]  # noqa: E731
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bl.forward_batch(items())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bl.forward_batch(items())
+    for rep in range(3):
+        announce("graph replay forward_batch", rep)
+        xs = [wl.activations(1600 + 10 * rep + i, M, K, 0.01) for i, (M, K, N) in enumerate(shapes)]
+        for d, x in zip(data, xs):
+            d[0].copy_(torch.from_numpy(x))
+            d[4].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [host(d[4]).copy() for d in data]
+        # eager batch on the same inputs
+        outs = [torch.full_like(d[4], float("nan")) for d in data]
+        bl.forward_batch([(d[0], d[1], d[2], d[3], 1e-6, o, d[5]) for d, o in zip(data, outs)])
+        torch.cuda.synchronize()
+        for d, x, y, o, (M, K, N) in zip(data, xs, got, outs, shapes):
+            assert np.array_equal(y, host(o)), (rep, M, K, N)
+            check_y(y, orc.forward(x, d[6], d[2], d[7], 1e-6, N))
