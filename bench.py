@@ -232,6 +232,32 @@ def secondary_prefill(torch, api, steps, warmup):
                             "frac_of_int8_peak": round(tops_sq / INT8_PEAK_TOPS, 4)}}
 
 
+def secondary_pack(torch, api, reps=5):
+    """I2_S packing of the packing workload (fp32 ternary x 0.02, N = 8192 x
+    K = 28672; seeded on the device): GB/s of algorithmic bytes (4NK read +
+    NK/4 + 32 written) over the whole synchronous bitlinear_pack_i2s call."""
+    from ternary_bit_linear_amd import workloads as wl
+    N, K = wl.PACK_SHAPE
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5000)
+    t = torch.randint(-1, 2, (N, K), generator=gen, device="cuda", dtype=torch.int8)
+    w = t.to(torch.float32).mul_(0.02)
+    del t
+    api.pack_i2s(w)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        api.pack_i2s(w)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / reps
+    nbytes = 4 * N * K + N * K // 4 + 32
+    del w
+    torch.cuda.empty_cache()
+    return {"workload": f"I2_S pack, N={N} x K={K}", "metric": "pack GB/s (whole call)",
+            "value": round(nbytes / sec / 1e9, 1), "unit": "GB/s", "us_per_call": round(sec * 1e6, 1),
+            "frac_of_hbm_peak": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +364,7 @@ def main():
     if not args.no_secondary and args.workload == "decode":
         out["secondary"] = secondary_prefill(torch, api, max(20, args.steps // 4), 5)
         torch.cuda.empty_cache()
+        out["secondary"]["pack"] = secondary_pack(torch, api)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work)
     print(json.dumps(out), flush=True)

@@ -35,8 +35,8 @@ bl_status check_mk(int64_t M, int64_t K) {
 bl_status check_nk(int64_t N, int64_t K) {
     if (N < 1 || K < 1 || K % bl::kBlockWeights != 0 || K > kMaxK) return BL_ERR_SHAPE;
     if (N > kMaxDim || K > kMaxDim || N * K >= kMaxElems) return BL_ERR_SHAPE;
-    // grids of the pack kernels: N*K/64 chunks in 256-thread blocks
-    if ((N * (K / 64) + 255) / 256 > kMaxDim) return BL_ERR_SHAPE;
+    // grids of the pack kernels: N*K/16 words in 256-thread blocks
+    if ((N * (K / 16) + 255) / 256 > kMaxDim) return BL_ERR_SHAPE;
     return BL_OK;
 }
 

@@ -32,47 +32,54 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// One thread per 16-byte output chunk: bytes [16h, 16h+16) of block b of row
-// n hold, in field g, the weights 128b + 32g + 16h + [0, 16).
+// One thread per 4-byte output word: word s (0..7) of block b of row n
+// holds, in byte i and field g, the code of weight 128b + 32g + 4s + i.  The
+// eight threads of a block read, per field g, the 32 consecutive weights
+// 128b + 32g + [0, 32) as eight float4: every load instruction of a wave
+// reads whole 128-byte lines (8 blocks x 128 bytes), and the wave writes
+// 256 consecutive output bytes.
 __global__ __launch_bounds__(256) void pack_scan_kernel(const float *__restrict__ w,
-                                                         int64_t chunks, int64_t chunks_per_row,
+                                                         int64_t words, int64_t words_per_row,
                                                          int64_t K, uint8_t *__restrict__ packed,
                                                          uint32_t *__restrict__ stats) {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     uint32_t mn = 0xffffffffu, mx = 0u;
-    if (c < chunks) {
-        const int64_t n = c / chunks_per_row;
-        const int64_t cc = c % chunks_per_row;
-        const float *src = w + n * K + (cc >> 1) * kBlockWeights + 16 * (cc & 1);
-        uint32_t d[4] = {0u, 0u, 0u, 0u};
+    if (u < words) {
+        const int64_t n = u / words_per_row;
+        const int64_t r = u - n * words_per_row;
+        const float *src = w + n * K + (r >> 3) * kBlockWeights + 4 * (r & 7);
+        float4 v[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) v[g] = *reinterpret_cast<const float4 *>(src + 32 * g);
+        uint32_t word = 0u;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int sh = 6 - 2 * g;
+            const float e[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
-                const float4 v = *reinterpret_cast<const float4 *>(src + 32 * g + 4 * t4);
-                const float e[4] = {v.x, v.y, v.z, v.w};
-                uint32_t word = 0u;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t code = e[i] > 0.0f ? 2u : (e[i] < 0.0f ? 0u : 1u);
-                    word |= code << (8 * i + sh);
-                    const uint32_t bits = __float_as_uint(e[i]) & 0x7fffffffu;
-                    if (bits != 0u) {
-                        mn = min(mn, bits);
-                        mx = max(mx, bits);
-                    }
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t code = e[i] > 0.0f ? 2u : (e[i] < 0.0f ? 0u : 1u);
+                word |= code << (8 * i + sh);
+                const uint32_t bits = __float_as_uint(e[i]) & 0x7fffffffu;
+                if (bits != 0u) {
+                    mn = min(mn, bits);
+                    mx = max(mx, bits);
                 }
-                d[t4] |= word;
             }
         }
-        *reinterpret_cast<uint4 *>(packed + 16 * c) = make_uint4(d[0], d[1], d[2], d[3]);
+        reinterpret_cast<uint32_t *>(packed)[u] = word;
     }
     mn = wave_min_u32(mn);
     mx = wave_max_u32(mx);
+    // Fold into the trailer words only where this wave can improve them.
+    // The words only ever move towards their final values, so a stale read
+    // can at worst cause a needless atomic, never skip a needed one; on
+    // valid input (one magnitude) nearly every wave skips both.
     if ((threadIdx.x & 63) == 0) {
-        if (mn != 0xffffffffu) atomicMin(stats + 0, mn);
-        if (mx != 0u) atomicMax(stats + 1, mx);
+        const uint32_t cur_mn = __hip_atomic_load(stats + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t cur_mx = __hip_atomic_load(stats + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (mn < cur_mn) atomicMin(stats + 0, mn);
+        if (mx > cur_mx) atomicMax(stats + 1, mx);
     }
 }
 
@@ -86,31 +93,29 @@ __global__ void pack_finalize_kernel(uint32_t *trailer, float scale) {
     if (t < 8) trailer[t] = (t == 0) ? __float_as_uint(scale) : 0u;
 }
 
-// One thread per 16-byte chunk: 64 weights w = (code - 1) * scale.
+// One thread per 4-byte packed word (16 weights w = (code - 1) * scale):
+// the mirror of pack_scan_kernel's mapping, so the float4 stores of a wave
+// fill whole 128-byte lines.
 __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__ packed,
-                                                      int64_t chunks, int64_t chunks_per_row,
+                                                      int64_t words, int64_t words_per_row,
                                                       int64_t K, const float *__restrict__ scale_p,
                                                       float *__restrict__ w) {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= chunks) return;
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= words) return;
     const float s = *scale_p;
-    const uint4 p = *reinterpret_cast<const uint4 *>(packed + 16 * c);
-    const uint32_t d[4] = {p.x, p.y, p.z, p.w};
-    const int64_t n = c / chunks_per_row;
-    const int64_t cc = c % chunks_per_row;
-    float *dst = w + n * K + (cc >> 1) * kBlockWeights + 16 * (cc & 1);
+    const uint32_t d = reinterpret_cast<const uint32_t *>(packed)[u];
+    const int64_t n = u / words_per_row;
+    const int64_t r = u - n * words_per_row;
+    float *dst = w + n * K + (r >> 3) * kBlockWeights + 4 * (r & 7);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const int sh = 6 - 2 * g;
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-            float4 v;
-            v.x = (float)((int)((d[t4] >> sh) & 3u) - 1) * s;
-            v.y = (float)((int)((d[t4] >> (sh + 8)) & 3u) - 1) * s;
-            v.z = (float)((int)((d[t4] >> (sh + 16)) & 3u) - 1) * s;
-            v.w = (float)((int)((d[t4] >> (sh + 24)) & 3u) - 1) * s;
-            *reinterpret_cast<float4 *>(dst + 32 * g + 4 * t4) = v;
-        }
+        float4 v;
+        v.x = (float)((int)((d >> sh) & 3u) - 1) * s;
+        v.y = (float)((int)((d >> (sh + 8)) & 3u) - 1) * s;
+        v.z = (float)((int)((d >> (sh + 16)) & 3u) - 1) * s;
+        v.w = (float)((int)((d >> (sh + 24)) & 3u) - 1) * s;
+        *reinterpret_cast<float4 *>(dst + 32 * g) = v;
     }
 }
 
@@ -124,12 +129,12 @@ hipError_t launch_pack_init(uint8_t *trailer, hipStream_t s) {
 
 hipError_t launch_pack_scan(const float *w, int64_t N, int64_t K, uint8_t *packed,
                             hipStream_t s) {
-    const int64_t cpr = K / 64;
-    const int64_t chunks = N * cpr;
-    const int64_t blocks = (chunks + 255) / 256;
+    const int64_t wpr = K / 16;
+    const int64_t words = N * wpr;
+    const int64_t blocks = (words + 255) / 256;
     uint32_t *stats = reinterpret_cast<uint32_t *>(packed + N * (K / 4));
-    hipLaunchKernelGGL(pack_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, chunks,
-                       cpr, K, packed, stats);
+    hipLaunchKernelGGL(pack_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, words,
+                       wpr, K, packed, stats);
     return hipGetLastError();
 }
 
@@ -141,12 +146,12 @@ hipError_t launch_pack_finalize(uint8_t *trailer, float scale, hipStream_t s) {
 
 hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, float *w,
                          hipStream_t s) {
-    const int64_t cpr = K / 64;
-    const int64_t chunks = N * cpr;
-    const int64_t blocks = (chunks + 255) / 256;
+    const int64_t wpr = K / 16;
+    const int64_t words = N * wpr;
+    const int64_t blocks = (words + 255) / 256;
     const float *scale_p = reinterpret_cast<const float *>(packed + N * (K / 4));
-    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, chunks,
-                       cpr, K, scale_p, w);
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, words,
+                       wpr, K, scale_p, w);
     return hipGetLastError();
 }
 
