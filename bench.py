@@ -16,7 +16,7 @@ not from the 256 MB last-level cache.
 Prints one JSON line (see the "metric" of the workload).  Options:
   --gpus N (only 1 is supported), --steps K, --warmup W,
   --workload decode|prefill|ffn70b-1|ffn70b-16|sweep-M,
-  --no-cpu-baseline, --no-secondary.
+  --no-cpu-baseline, --no-secondary, --pack-only.
 """
 from __future__ import annotations
 
@@ -266,6 +266,8 @@ def main():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--pack-only", action="store_true",
+                    help="time only the I2_S packer over --steps calls and print its line")
     ap.add_argument("--pmc-app", action="store_true",
                     help="no timing: run --steps steps of the workload and a 256 MiB device "
                          "copy (the calibration kernel for HBM byte counters), then exit")
@@ -282,6 +284,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.pack_only:
+        print(json.dumps(secondary_pack(torch, api, reps=max(1, args.steps))), flush=True)
+        return
     work = workload_by_name(args.workload)
     prep = Prepared(torch, api, work)
     if args.pmc_app:

@@ -32,35 +32,45 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// One thread per 4-byte output word: word s (0..7) of block b of row n
-// holds, in byte i and field g, the code of weight 128b + 32g + 4s + i.  The
-// eight threads of a block read, per field g, the 32 consecutive weights
-// 128b + 32g + [0, 32) as eight float4: every load instruction of a wave
-// reads whole 128-byte lines (8 blocks x 128 bytes), and the wave writes
-// 256 consecutive output bytes.
-__global__ __launch_bounds__(256) void pack_scan_kernel(const float *__restrict__ w,
-                                                         int64_t words, int64_t words_per_row,
-                                                         int64_t K, uint8_t *__restrict__ packed,
+// Word s (0..7) of block b of row n holds, in byte i and field g, the code
+// of weight 128b + 32g + 4s + i.  A thread builds one word per loop trip:
+// the eight threads of a block read, per field g, the 32 consecutive
+// weights 128b + 32g + [0, 32) as eight float4, so every load instruction
+// of a wave reads whole 128-byte lines (8 blocks x 128 bytes) and the wave
+// writes 256 consecutive output bytes.  The grid is capped and strides over
+// the words, so the minimum and maximum stay in registers for many words
+// and each workgroup touches the trailer words at most once: one hot
+// address read by every wave of a one-word-per-thread grid serialises at
+// the memory channel that owns it.  I is 32-bit whenever the word count
+// fits, which keeps the row division cheap.
+template <typename I>
+__global__ __launch_bounds__(256) void pack_scan_kernel(const float *__restrict__ w, I words,
+                                                         I words_per_row, I K,
+                                                         uint8_t *__restrict__ packed,
                                                          uint32_t *__restrict__ stats) {
-    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    typedef float f4v __attribute__((ext_vector_type(4)));
     uint32_t mn = 0xffffffffu, mx = 0u;
-    if (u < words) {
-        const int64_t n = u / words_per_row;
-        const int64_t r = u - n * words_per_row;
-        const float *src = w + n * K + (r >> 3) * kBlockWeights + 4 * (r & 7);
-        float4 v[4];
+    const I stride = (I)gridDim.x * blockDim.x;
+    for (I u = (I)blockIdx.x * blockDim.x + threadIdx.x; u < words; u += stride) {
+        const I n = u / words_per_row;
+        const I r = u - n * words_per_row;
+        const float *src = w + (int64_t)n * K + (int64_t)(r >> 3) * kBlockWeights + 4 * (r & 7);
+        // W is read once: non-temporal loads keep it from displacing
+        // cached lines (measured about 10% faster than plain loads).
+        f4v v[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) v[g] = *reinterpret_cast<const float4 *>(src + 32 * g);
+        for (int g = 0; g < 4; ++g)
+            v[g] = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(src + 32 * g));
         uint32_t word = 0u;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int sh = 6 - 2 * g;
-            const float e[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t code = e[i] > 0.0f ? 2u : (e[i] < 0.0f ? 0u : 1u);
+                const float e = v[g][i];
+                const uint32_t code = e > 0.0f ? 2u : (e < 0.0f ? 0u : 1u);
                 word |= code << (8 * i + sh);
-                const uint32_t bits = __float_as_uint(e[i]) & 0x7fffffffu;
+                const uint32_t bits = __float_as_uint(e) & 0x7fffffffu;
                 if (bits != 0u) {
                     mn = min(mn, bits);
                     mx = max(mx, bits);
@@ -71,11 +81,23 @@ __global__ __launch_bounds__(256) void pack_scan_kernel(const float *__restrict_
     }
     mn = wave_min_u32(mn);
     mx = wave_max_u32(mx);
-    // Fold into the trailer words only where this wave can improve them.
-    // The words only ever move towards their final values, so a stale read
-    // can at worst cause a needless atomic, never skip a needed one; on
-    // valid input (one magnitude) nearly every wave skips both.
+    __shared__ uint32_t part[2][4];
+    const int wv = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
+        part[0][wv] = mn;
+        part[1][wv] = mx;
+    }
+    __syncthreads();
+    // Fold into the trailer words only where this workgroup can improve
+    // them.  The words only ever move towards their final values, so a
+    // stale read can at worst cause a needless atomic, never skip a needed
+    // one.
+    if (threadIdx.x == 0) {
+        const int nw = (blockDim.x + 63) >> 6;
+        for (int i = 1; i < nw; ++i) {
+            mn = min(mn, part[0][i]);
+            mx = max(mx, part[1][i]);
+        }
         const uint32_t cur_mn = __hip_atomic_load(stats + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t cur_mx = __hip_atomic_load(stats + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (mn < cur_mn) atomicMin(stats + 0, mn);
@@ -131,10 +153,19 @@ hipError_t launch_pack_scan(const float *w, int64_t N, int64_t K, uint8_t *packe
                             hipStream_t s) {
     const int64_t wpr = K / 16;
     const int64_t words = N * wpr;
-    const int64_t blocks = (words + 255) / 256;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
+    // Four 256-thread workgroups per CU: measured as fast as more.
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((words + 255) / 256, 4 * (int64_t)cus));
     uint32_t *stats = reinterpret_cast<uint32_t *>(packed + N * (K / 4));
-    hipLaunchKernelGGL(pack_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, words,
-                       wpr, K, packed, stats);
+    if (words + 256 * blocks < (int64_t)UINT32_MAX)
+        hipLaunchKernelGGL(pack_scan_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           w, (uint32_t)words, (uint32_t)wpr, (uint32_t)K, packed, stats);
+    else
+        hipLaunchKernelGGL(pack_scan_kernel<int64_t>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           w, words, wpr, K, packed, stats);
     return hipGetLastError();
 }
 
