@@ -213,7 +213,9 @@ int oracle_rmsnorm(const float *x, const float *gamma, float eps, int64_t M,
  * sum is kept for the code offset):
  *   amax = max |xn|; inv = 127 / max(amax, 1e-5);
  *   q = clamp(rint(xn * inv), -128, 127) with round-half-to-even;
- *   qsum = sum q.  xn_scratch holds K floats per thread. */
+ *   qsum = sum q.  xn_scratch holds K floats per row.
+ * gamma == NULL is the layer without RMSNorm [HF-38087, "What does this PR
+ * do?": use_rms_norm, off by default]: xn = x and eps is not used. */
 int oracle_act_quant(const float *x, const float *gamma, float eps, int64_t M,
                      int64_t K, int8_t *q, float *inv, int32_t *qsum,
                      float *xn_scratch) {
@@ -221,7 +223,10 @@ int oracle_act_quant(const float *x, const float *gamma, float eps, int64_t M,
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         float *xn = xn_scratch + m * K;
-        rmsnorm_row(x + m * K, gamma, eps, K, xn);
+        if (gamma)
+            rmsnorm_row(x + m * K, gamma, eps, K, xn);
+        else
+            for (int64_t k = 0; k < K; ++k) xn[k] = x[m * K + k];
         float amax = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
             float a = fabsf(xn[k]);

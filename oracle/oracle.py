@@ -48,8 +48,7 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
+        build()  # compiles only when the library is missing or older than oracle.c
         L = ctypes.CDLL(_LIB)
         i64, p = ctypes.c_int64, ctypes.c_void_p
         L.oracle_packed_bytes.restype = i64
@@ -142,16 +141,18 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     return xn
 
 
-def act_quant(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-6):
-    """-> (q int8[M][K], inv fp32[M], qsum int32[M])."""
+def act_quant(x: np.ndarray, gamma, eps: float = 1e-6):
+    """-> (q int8[M][K], inv fp32[M], qsum int32[M]).  gamma None: the layer
+    without RMSNorm (x is quantised as it is)."""
     x = _f32(np.atleast_2d(x))
-    gamma = _f32(gamma)
+    gamma = None if gamma is None else _f32(gamma)
     M, K = x.shape
     q = np.empty((M, K), dtype=np.int8)
     inv = np.empty(M, dtype=np.float32)
     qsum = np.empty(M, dtype=np.int32)
     xn = np.empty((M, K), dtype=np.float32)
-    st = lib().oracle_act_quant(_ptr(x), _ptr(gamma), ctypes.c_float(eps), M, K,
+    gp = ctypes.c_void_p(None) if gamma is None else _ptr(gamma)
+    st = lib().oracle_act_quant(_ptr(x), gp, ctypes.c_float(eps), M, K,
                                 _ptr(q), _ptr(inv), _ptr(qsum), _ptr(xn))
     if st != OK:
         raise OracleError(st, "act_quant")
@@ -182,9 +183,9 @@ def rescale(acc: np.ndarray, inv: np.ndarray, w_scale: float) -> np.ndarray:
     return y
 
 
-def forward(x: np.ndarray, packed: np.ndarray, w_scale: float, gamma: np.ndarray,
+def forward(x: np.ndarray, packed: np.ndarray, w_scale: float, gamma,
             eps: float, N: int) -> np.ndarray:
-    """Whole forward; returns fp64 y[M][N]."""
+    """Whole forward; returns fp64 y[M][N].  gamma None: no RMSNorm."""
     q, inv, qsum = act_quant(x, gamma, eps)
     acc = matmul_i2s(q, qsum, packed, N)
     return rescale(acc, inv, w_scale)

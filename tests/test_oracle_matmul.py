@@ -132,3 +132,16 @@ def test_packed_rows_sampling(orc):
     rows = [0, 5, 11]
     sub = orc.matmul_i2s(q, qsum, orc.packed_rows(p, K, rows), len(rows))
     assert np.array_equal(sub, full[:, rows])
+
+
+def test_forward_without_norm_reproduces_integer_rows(orc):
+    """The layer without RMSNorm on x[m][k] = integers in [-127, 0] with
+    amax 127: inv = 1, q = x exactly, and W = s I gives y = s x exactly.
+    Any normalisation applied by mistake would change y."""
+    K = 128
+    x = np.stack([np.arange(K, dtype=np.float32) - 127,
+                  -np.arange(K, dtype=np.float32)[::-1].copy()])
+    x[1, 5] = 127.0
+    packed, s = orc.pack_i2s(np.eye(K, dtype=np.float32) * np.float32(0.25))
+    y = orc.forward(x, packed, s, None, 1e-6, K)
+    assert np.array_equal(y, x.astype(np.float64) * 0.25)

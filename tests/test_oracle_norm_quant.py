@@ -185,3 +185,53 @@ def test_quant_vs_fp64_pipeline(orc, K):
     assert np.all(~diff | near)
     assert diff.sum() <= 1e-4 * q.size + 1
     assert np.abs(q.astype(np.float64) - ref).max() <= 1
+
+
+# --- the layer without RMSNorm (gamma None: use_rms_norm off) -------------
+
+def test_quant_without_norm_hand_values(orc):
+    """amax = 2 gives inv = 63.5 exactly and every product x * 63.5 below is
+    exact in fp32, so the codes follow by hand: 31.75 -> 32, 15.875 -> 16,
+    63.5 -> 64 (tie to even), -47.625 -> -48, 7.9375 -> 8, 95.25 -> 95."""
+    x = np.array([[0.5, -2.0, 0.25, 0.0, 1.0, -0.75, 0.125, 1.5]], np.float32)
+    q, inv, qsum = orc.act_quant(x, None, 1e-6)
+    assert inv[0] == np.float32(63.5)
+    assert q[0].tolist() == [32, -127, 16, 0, 64, -48, 8, 95]
+    assert qsum[0] == 40
+    # amax = 1: inv = 127 and 0.5 * 127 = 63.5 ties to 64
+    x = np.array([[1.0, 0.5, -0.5, 0.25]], np.float32)
+    q, inv, qsum = orc.act_quant(x, None, 1e-6)
+    assert inv[0] == np.float32(127.0)
+    assert q[0].tolist() == [127, 64, -64, 32] and qsum[0] == 159
+
+
+def test_quant_without_norm_ignores_eps_and_is_not_normalised(orc):
+    """With no RMSNorm the result depends on x alone: eps is unused, and a
+    power-of-two scaling of x leaves q and qsum unchanged while inv scales
+    inversely (all exact in fp32).  The normalised form differs from it on
+    a row whose RMS is not 1."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((4, 512)) * 3).astype(np.float32)
+    q, inv, qsum = orc.act_quant(x, None, 1e-6)
+    q2, inv2, qsum2 = orc.act_quant(x, None, 0.5)
+    assert np.array_equal(q, q2) and np.array_equal(inv, inv2)
+    q4, inv4, qsum4 = orc.act_quant(x * np.float32(4.0), None, 1e-6)
+    assert np.array_equal(q4, q) and np.array_equal(qsum4, qsum)
+    assert np.array_equal(inv4, inv / np.float32(4.0))
+    assert np.array_equal(inv, np.float32(127.0) / np.abs(x).max(axis=1))
+    qn, invn, _ = orc.act_quant(x, np.ones(512, np.float32), 1e-6)
+    assert not np.array_equal(invn, inv)
+
+
+def test_quant_without_norm_vs_fp64(orc):
+    """q = round(x * 127 / amax) from fp64 except within 1e-4 of a tie."""
+    rng = np.random.default_rng(12)
+    M, K = 32, 2560
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    q, inv, qsum = orc.act_quant(x, None, 1e-6)
+    v = x.astype(np.float64) * (127.0 / np.abs(x.astype(np.float64)).max(axis=1, keepdims=True))
+    ref = np.round(v)
+    near = np.abs(np.abs(v - np.floor(v)) - 0.5) < 1e-4
+    diff = q.astype(np.float64) != ref
+    assert np.all(~diff | near)
+    assert np.array_equal(qsum, q.astype(np.int64).sum(axis=1))
