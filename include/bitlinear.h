@@ -158,6 +158,9 @@ bl_status bitlinear_read_scale(const uint8_t *packed, int64_t N, int64_t K,
  * (g_0 + g_1) + (g_2 + g_3)), so the int8 codes are reproducible.
  *   x:        device fp32 [M][K]; gamma: device fp32 [K]; eps > 0 (the
  *             pages' default is 1e-6) else BL_ERR_INVALID_ARG.
+ *   gamma == NULL selects the layer without RMSNorm [HF-38087 "What does
+ *             this PR do?": use_rms_norm, off by default]: xn = x, no sum
+ *             of squares, and eps is ignored (not validated).
  *   packed_w: device I2_S buffer of W[N][K]; its trailer is not read:
  *             w_scale is the scale (from bitlinear_pack_i2s or
  *             bitlinear_read_scale).
@@ -210,7 +213,8 @@ bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
                                   const bl_launch *launch, void *stream);
 
 /* Stage: RMSNorm + per-row absmax int8 quantisation (the first two steps of
- * bitlinear_forward, bit-identical to them).
+ * bitlinear_forward, bit-identical to them; gamma == NULL: no RMSNorm, eps
+ * ignored, as there).
  *   q: device int8 [M][K] (16-byte aligned); inv: device fp32 [M];
  *   qsum: device int32 [M].  Asynchronous on `stream`. */
 bl_status bitlinear_act_quant(const float *x, const float *gamma, float eps,

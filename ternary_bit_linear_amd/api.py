@@ -109,6 +109,12 @@ def _dev(t, dtype, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _gamma(g):
+    """gamma tensor, or None for the layer without RMSNorm (NULL pointer)."""
+    torch = _torch()
+    return ctypes.c_void_p(None) if g is None else _dev(g, torch.float32, "gamma")
+
+
 def _launch(path, fuse, variant):
     if path == PATH_AUTO and fuse == -1 and variant == 0:
         return None
@@ -160,13 +166,13 @@ def read_scale(packed, N: int, K: int) -> float:
 
 
 def act_quant(x, gamma, eps: float = 1e-6):
-    """-> (q int8 [M][K], inv fp32 [M], qsum int32 [M])."""
+    """-> (q int8 [M][K], inv fp32 [M], qsum int32 [M]); gamma None: no RMSNorm."""
     torch = _torch()
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     inv = torch.empty(M, dtype=torch.float32, device=x.device)
     qsum = torch.empty(M, dtype=torch.int32, device=x.device)
-    _check(lib().bitlinear_act_quant(_dev(x, torch.float32, "x"), _dev(gamma, torch.float32, "gamma"),
+    _check(lib().bitlinear_act_quant(_dev(x, torch.float32, "x"), _gamma(gamma),
                                      eps, M, K, ctypes.c_void_p(q.data_ptr()),
                                      ctypes.c_void_p(inv.data_ptr()),
                                      ctypes.c_void_p(qsum.data_ptr()), _stream()), "act_quant")
@@ -192,7 +198,8 @@ def new_workspace(M: int, K: int, device="cuda"):
 
 def forward(x, packed, w_scale: float, gamma, eps: float = 1e-6, N: int | None = None,
             out=None, workspace=None, path: int = PATH_AUTO, fuse: int = -1, variant: int = 0):
-    """y = BitLinear(x) with I2_S weights; x fp32 [M][K] -> y fp32 [M][N]."""
+    """y = BitLinear(x) with I2_S weights; x fp32 [M][K] -> y fp32 [M][N].
+    gamma None: the layer without RMSNorm (x is quantised as it is)."""
     torch = _torch()
     M, K = x.shape
     if N is None:
@@ -203,7 +210,7 @@ def forward(x, packed, w_scale: float, gamma, eps: float = 1e-6, N: int | None =
         workspace = new_workspace(M, K, x.device)
     _check(lib().bitlinear_forward_ex(
         _dev(x, torch.float32, "x"), _dev(packed, torch.uint8, "packed"), w_scale,
-        _dev(gamma, torch.float32, "gamma"), eps, M, K, N, _dev(out, torch.float32, "out"),
+        _gamma(gamma), eps, M, K, N, _dev(out, torch.float32, "out"),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
         _launch(path, fuse, variant), _stream()), "forward")
     return out
@@ -219,7 +226,7 @@ def forward_batch(items, path: int = PATH_AUTO, fuse: int = -1, variant: int = 0
         M, K = x.shape
         N = out.shape[1]
         arr[i] = ForwardDesc(_dev(x, torch.float32, "x"), _dev(packed, torch.uint8, "packed"),
-                             w_scale, _dev(gamma, torch.float32, "gamma"), eps, M, K, N,
+                             w_scale, _gamma(gamma), eps, M, K, N,
                              _dev(out, torch.float32, "out"), _dev(ws, torch.uint8, "workspace"),
                              ws.numel())
     _check(lib().bitlinear_forward_batch(arr, len(items), _launch(path, fuse, variant), _stream()),

@@ -110,8 +110,9 @@ bl_status validate_forward(const bl_forward_desc &d, const bl_launch *launch) {
     if (bl_status st = check_mk(d.M, d.K)) return st;
     if (bl_status st = check_nk(d.N, d.K)) return st;
     if (bl_status st = check_mn(d.M, d.N)) return st;
-    if (!d.x || !d.packed_w || !d.gamma || !d.y || !d.workspace) return BL_ERR_INVALID_ARG;
-    if (!(d.eps > 0.0f) || !std::isfinite(d.eps) || !std::isfinite(d.w_scale))
+    // gamma == nullptr: no RMSNorm, and eps is not used.
+    if (!d.x || !d.packed_w || !d.y || !d.workspace) return BL_ERR_INVALID_ARG;
+    if ((d.gamma && (!(d.eps > 0.0f) || !std::isfinite(d.eps))) || !std::isfinite(d.w_scale))
         return BL_ERR_INVALID_ARG;
     if (bl_status st = check_launch(launch, true)) return st;
     if (!aligned16(d.x) || !aligned16(d.gamma) || !aligned16(d.packed_w) || !aligned16(d.y) ||
@@ -267,8 +268,8 @@ bl_status bitlinear_read_scale(const uint8_t *packed, int64_t N, int64_t K, floa
 bl_status bitlinear_act_quant(const float *x, const float *gamma, float eps, int64_t M,
                               int64_t K, int8_t *q, float *inv, int32_t *qsum, void *stream) {
     if (bl_status st = check_mk(M, K)) return st;
-    if (!x || !gamma || !q || !inv || !qsum) return BL_ERR_INVALID_ARG;
-    if (!(eps > 0.0f) || !std::isfinite(eps)) return BL_ERR_INVALID_ARG;
+    if (!x || !q || !inv || !qsum) return BL_ERR_INVALID_ARG;
+    if (gamma && (!(eps > 0.0f) || !std::isfinite(eps))) return BL_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(gamma) || !aligned16(q)) return BL_ERR_ALIGN;
     return hip_status(bl::launch_act_quant(x, gamma, eps, M, K, q, inv, qsum, as_stream(stream)));
 }

@@ -250,6 +250,17 @@ __device__ __forceinline__ float4 xn4(const float4 &x, const float4 &g, float r)
     return make_float4((x.x * r) * g.x, (x.y * r) * g.y, (x.z * r) * g.z, (x.w * r) * g.w);
 }
 
+// gamma == nullptr selects the layer without RMSNorm (HF-38087: use_rms_norm
+// off, the activations are quantised as they come): r = 1 and gamma = 1, so
+// xn4 returns x exactly.  The gamma descriptor then has no records, so no
+// load through it touches memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gamma_rsrc(const float *gamma, int K) {
+    return make_rsrc(gamma, gamma ? 4u * (uint32_t)K : 0u);
+}
+__device__ __forceinline__ float4 gamma_f4(__amdgpu_buffer_rsrc_t rg, uint32_t off, bool norm) {
+    return norm ? buf_load_f4(rg, off) : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+}
+
 __device__ __forceinline__ float amax4(float a, const float4 &v) {
     return fmaxf(fmaxf(fmaxf(a, fabsf(v.x)), fmaxf(fabsf(v.y), fabsf(v.z))), fabsf(v.w));
 }
@@ -260,6 +271,7 @@ __device__ __forceinline__ float amax4(float a, const float4 &v) {
 //   r = 1 / sqrt(sumsq / K + eps)      (O256 order, IEEE division and root)
 //   xn = (x * r) * gamma,  inv = 127 / max(max |xn|, 1e-5)
 //   q = clamp(rint(xn * inv), -128, 127),  qsum = sum q.
+// With gamma == nullptr there is no RMSNorm: xn = x (no sum of squares).
 // Sink receives store_q(k, 4 packed int8) and store_row(inv, qsum).
 
 // Block form (256 threads): thread t owns O256 chain t, i.e. the float4
@@ -278,8 +290,9 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
     const int t4 = 4 * threadIdx.x;
     constexpr int STRIDE = 1024;
     if constexpr (!LONG) {  // K <= 1024 * CH
+        const bool norm = gamma != nullptr;
         const auto rx = make_rsrc(x, 4u * (uint32_t)K);
-        const auto rg = make_rsrc(gamma, 4u * (uint32_t)K);
+        const auto rg = gamma_rsrc(gamma, K);
         float4 xv[CH], gv[CH];
         const int wk = 256 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 #pragma unroll
@@ -288,7 +301,7 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
             const uint32_t off = k < K ? 4u * (uint32_t)k : kOOB;
             if (STRIDE * i + wk < K) {
                 xv[i] = buf_load_f4(rx, off);
-                gv[i] = buf_load_f4(rg, off);
+                gv[i] = gamma_f4(rg, off, norm);
             } else {
                 xv[i] = gv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
@@ -299,18 +312,21 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
         issued();
         // Chunks wholly past K hold zeros, which leave the sum of squares and
         // the max unchanged: the wave skips them (a wave-uniform test).
-        float p = 0.0f;
+        float r = 1.0f;
+        if (norm) {
+            float p = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            if (STRIDE * i + wk < K) {
-                p = __builtin_fmaf(xv[i].x, xv[i].x, p);
-                p = __builtin_fmaf(xv[i].y, xv[i].y, p);
-                p = __builtin_fmaf(xv[i].z, xv[i].z, p);
-                p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+            for (int i = 0; i < CH; ++i) {
+                if (STRIDE * i + wk < K) {
+                    p = __builtin_fmaf(xv[i].x, xv[i].x, p);
+                    p = __builtin_fmaf(xv[i].y, xv[i].y, p);
+                    p = __builtin_fmaf(xv[i].z, xv[i].z, p);
+                    p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+                }
             }
+            const float ss = block_sumsq_finish(p, red);
+            r = 1.0f / sqrtf(ss / (float)K + eps);
         }
-        const float ss = block_sumsq_finish(p, red);
-        const float r = 1.0f / sqrtf(ss / (float)K + eps);
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
@@ -339,31 +355,35 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
     } else {
     issued();
     // Long rows: three streamed passes.
+    const bool norm = gamma != nullptr;
     const auto rx = make_rsrc(x, 4u * (uint32_t)K);
-    const auto rg = make_rsrc(gamma, 4u * (uint32_t)K);
+    const auto rg = gamma_rsrc(gamma, K);
     auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
-    float p = 0.0f;
-    for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
-        float4 xv[CH];
+    float r = 1.0f;
+    if (norm) {
+        float p = 0.0f;
+        for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
+            float4 xv[CH];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
+            for (int i = 0; i < CH; ++i) xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            p = __builtin_fmaf(xv[i].x, xv[i].x, p);
-            p = __builtin_fmaf(xv[i].y, xv[i].y, p);
-            p = __builtin_fmaf(xv[i].z, xv[i].z, p);
-            p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+            for (int i = 0; i < CH; ++i) {
+                p = __builtin_fmaf(xv[i].x, xv[i].x, p);
+                p = __builtin_fmaf(xv[i].y, xv[i].y, p);
+                p = __builtin_fmaf(xv[i].z, xv[i].z, p);
+                p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+            }
         }
+        const float ss = block_sumsq_finish(p, red);
+        r = 1.0f / sqrtf(ss / (float)K + eps);
     }
-    const float ss = block_sumsq_finish(p, red);
-    const float r = 1.0f / sqrtf(ss / (float)K + eps);
     float amax = 0.0f;
     for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
         float4 xv[CH], gv[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
-            gv[i] = buf_load_f4(rg, off_of(c0 + t4 + STRIDE * i));
+            gv[i] = gamma_f4(rg, off_of(c0 + t4 + STRIDE * i), norm);
         }
 #pragma unroll
         for (int i = 0; i < CH; ++i) amax = amax4(amax, xn4(xv[i], gv[i], r));
@@ -376,7 +396,7 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
-            gv[i] = buf_load_f4(rg, off_of(c0 + t4 + STRIDE * i));
+            gv[i] = gamma_f4(rg, off_of(c0 + t4 + STRIDE * i), norm);
         }
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
@@ -406,8 +426,9 @@ __device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
                                                    const float *__restrict__ gamma,
                                                    float eps, int K, Sink &sink) {
     const int lane = threadIdx.x & 63;
+    const bool norm = gamma != nullptr;
     const auto rx = make_rsrc(x, 4u * (uint32_t)K);
-    const auto rg = make_rsrc(gamma, 4u * (uint32_t)K);
+    const auto rg = gamma_rsrc(gamma, K);
     auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
     float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const bool in_regs = K <= 1024 * CI;
@@ -419,7 +440,7 @@ __device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
             for (int w = 0; w < 4; ++w) {
                 const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
                 xv[i][w] = buf_load_f4(rx, off);
-                if (in_regs) gv[i][w] = buf_load_f4(rg, off);
+                if (in_regs) gv[i][w] = gamma_f4(rg, off, norm);
             }
 #pragma unroll
         for (int i = 0; i < CI; ++i)
@@ -431,10 +452,13 @@ __device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
                 p[w] = __builtin_fmaf(xv[i][w].w, xv[i][w].w, p[w]);
             }
     }
+    float r = 1.0f;
+    if (norm) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) p[w] = wave_tree_sum_f(p[w]);
-    const float ss = (p[0] + p[1]) + (p[2] + p[3]);
-    const float r = 1.0f / sqrtf(ss / (float)K + eps);
+        for (int w = 0; w < 4; ++w) p[w] = wave_tree_sum_f(p[w]);
+        const float ss = (p[0] + p[1]) + (p[2] + p[3]);
+        r = 1.0f / sqrtf(ss / (float)K + eps);
+    }
     float amax = 0.0f;
     for (int c0 = 0; c0 < K; c0 += 1024 * CI) {
         if (!in_regs) {
@@ -444,7 +468,7 @@ __device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
                     xv[i][w] = buf_load_f4(rx, off);
-                    gv[i][w] = buf_load_f4(rg, off);
+                    gv[i][w] = gamma_f4(rg, off, norm);
                 }
         }
 #pragma unroll
@@ -463,7 +487,7 @@ __device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
                     xv[i][w] = buf_load_f4(rx, off);
-                    gv[i][w] = buf_load_f4(rg, off);
+                    gv[i][w] = gamma_f4(rg, off, norm);
                 }
         }
 #pragma unroll

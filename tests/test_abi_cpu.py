@@ -71,9 +71,17 @@ def test_forward_shape_errors(L, M, K, N):
     assert fwd(L, M=M, K=K, N=N) == api.ERR_SHAPE
 
 
-@pytest.mark.parametrize("which", ["x", "p", "g", "y", "ws"])
+@pytest.mark.parametrize("which", ["x", "p", "y", "ws"])
 def test_forward_null(L, which):
     assert fwd(L, **{which: 0}) == api.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.0, float("nan")])
+def test_forward_null_gamma_is_the_layer_without_norm(L, eps):
+    """gamma NULL selects the layer without RMSNorm and eps is then not
+    validated: the call gets past both checks to the alignment check (a
+    misaligned y stops it there, before anything is enqueued)."""
+    assert fwd(L, g=0, eps=eps, y=MIS) == api.ERR_ALIGN
 
 
 @pytest.mark.parametrize("which", ["x", "p", "g", "y", "ws"])
@@ -125,7 +133,9 @@ def test_pack_errors(L):
 def test_stage_errors(L):
     aq = L.bitlinear_act_quant
     assert aq(F(A), F(A), 1e-6, 2, 200, F(A), F(A), F(A), None) == api.ERR_SHAPE
-    assert aq(F(A), F(0), 1e-6, 2, 256, F(A), F(A), F(A), None) == api.ERR_INVALID_ARG
+    assert aq(F(0), F(A), 1e-6, 2, 256, F(A), F(A), F(A), None) == api.ERR_INVALID_ARG
+    # gamma NULL (no RMSNorm) with eps 0 passes validation up to the alignment check
+    assert aq(F(A), F(0), 0.0, 2, 256, F(MIS), F(A), F(A), None) == api.ERR_ALIGN
     assert aq(F(A), F(A), 0.0, 2, 256, F(A), F(A), F(A), None) == api.ERR_INVALID_ARG
     assert aq(F(A), F(A), 1e-6, 2, 256, F(MIS), F(A), F(A), None) == api.ERR_ALIGN
     mm = L.bitlinear_matmul_i2s_ex

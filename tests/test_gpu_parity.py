@@ -553,3 +553,112 @@ def test_graph_replay_forward_batch_new_inputs(torch, bl, orc):
         for d, x, y, o, (M, K, N) in zip(data, xs, got, outs, shapes):
             assert np.array_equal(y, host(o)), (rep, M, K, N)
             check_y(y, orc.forward(x, d[6], d[2], d[7], 1e-6, N))
+
+
+# ---------------------------------------------------------------- no RMSNorm
+
+NONORM_AQ = [(1, 128), (3, 1024), (4, 2560), (16, 8192), (2, 28672), (33, 640)]
+
+
+@pytest.mark.parametrize("M,K", NONORM_AQ)
+def test_act_quant_without_norm_parity(torch, bl, orc, M, K):
+    """gamma None (use_rms_norm off): x is quantised as it is; the one-wave,
+    block and streamed-row forms all match the oracle bit for bit."""
+    announce("act_quant no-norm", M, K)
+    x = wl.activations(900 + M + K, M, K, 0.01)
+    x[0] *= np.float32(1e-3)
+    q_r, inv_r, qs_r = orc.act_quant(x, None, 1e-6)
+    q, inv, qs = bl.act_quant(dev(torch, x), None, 0.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), q_r)
+    assert np.array_equal(host(inv).view(np.uint32), inv_r.view(np.uint32))
+    assert np.array_equal(host(qs), qs_r)
+
+
+def test_act_quant_without_norm_hand_values(torch, bl):
+    announce("act_quant no-norm hand values")
+    x = np.zeros((2, 128), np.float32)
+    x[0, :8] = [0.5, -2.0, 0.25, 0.0, 1.0, -0.75, 0.125, 1.5]
+    x[1, :4] = [1.0, 0.5, -0.5, 0.25]
+    q, inv, qs = bl.act_quant(dev(torch, x), None, 1e-6)
+    torch.cuda.synchronize()
+    q, inv, qs = host(q), host(inv), host(qs)
+    assert inv[0] == np.float32(63.5) and inv[1] == np.float32(127.0)
+    assert q[0, :8].tolist() == [32, -127, 16, 0, 64, -48, 8, 95] and qs[0] == 40
+    assert q[1, :4].tolist() == [127, 64, -64, 32] and qs[1] == 159
+    assert np.all(q[0, 8:] == 0) and np.all(q[1, 4:] == 0)
+
+
+NONORM_FWD = [(1, 2560, 640), (1, 6912, 300), (3, 1024, 77), (4, 8192, 64), (1, 28672, 64),
+              (17, 256, 64), (64, 1024, 200)]
+
+
+@pytest.mark.parametrize("M,K,N", NONORM_FWD)
+def test_forward_without_norm_parity(torch, bl, orc, M, K, N):
+    """The layer without RMSNorm through every route, fusion and launch
+    shape: the same bits each time, within 1e-5 of the oracle."""
+    announce("forward no-norm", M, K, N)
+    x, w, t, g = mm_case(M, K, N, 950 + M + K)
+    packed_r, s = orc.pack_i2s(w)
+    y64 = orc.forward(x, packed_r, s, None, 1e-6, N)
+    X, P = dev(torch, x), dev(torch, packed_r)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = bl.new_workspace(M, K)
+    y = bl.forward(X, P, s, None, 1e-6, N, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    check_y(host(y), y64)
+    q_r, inv_r, qs_r = orc.act_quant(x, None, 1e-6)
+    q, inv, qs = bl.workspace_views(ws, M, K)
+    assert np.array_equal(host(q), q_r) and np.array_equal(host(inv), inv_r)
+    assert np.array_equal(host(qs), qs_r)
+    ref = host(y).copy()
+    opts = [(1, 0, 0), (2, 0, 0)] + [(2, 0, v) for v in range(1, bl.num_variants(2) + 1)]
+    opts += [(1, 0, v) for v in range(1, bl.num_variants(1) + 1)]
+    if M <= 4 and M * K <= 32768:
+        opts += [(1, 1, v) for v in range(1, bl.num_variants(1) + 1)]
+    for path, fuse, v in opts:
+        out.fill_(float("nan"))
+        y2 = bl.forward(X, P, s, None, 1e-6, N, out=out, workspace=ws, path=path, fuse=fuse,
+                        variant=v)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y2), ref), (path, fuse, v)
+
+
+def test_forward_without_norm_identity_exact(torch, bl, orc):
+    """Integer rows with amax 127 through W = s I: y = s x exactly, on the
+    fused decode route (M = 1) and the tile route (M = 64)."""
+    K = 128
+    packed_r, s = orc.pack_i2s(np.eye(K, dtype=np.float32) * np.float32(0.25))
+    P = dev(torch, packed_r)
+    for M in (1, 64):
+        announce("forward no-norm identity", M)
+        x = (np.arange(M * K, dtype=np.int64).reshape(M, K) % 255 - 127).astype(np.float32)
+        x[:, 0] = -127.0
+        y = host(bl.forward(dev(torch, x), P, s, None, 1e-6, K))
+        torch.cuda.synchronize()
+        assert np.array_equal(y, x * np.float32(0.25))
+
+
+def test_forward_batch_mixes_norm_and_no_norm(torch, bl, orc):
+    """A batch where some problems have RMSNorm and some not, on the fused
+    decode launch and the grouped prefill launches: each matches its single
+    call and the oracle."""
+    shapes = [(1, 2560, 640, True), (1, 2560, 640, False), (1, 6912, 256, False),
+              (64, 2560, 256, False), (64, 2560, 256, True), (32, 1024, 96, False)]
+    items, singles, refs = [], [], []
+    for i, (M, K, N, norm) in enumerate(shapes):
+        x, w, t, g = mm_case(M, K, N, 980 + i)
+        packed_r, s = orc.pack_i2s(w)
+        X, P = dev(torch, x), dev(torch, packed_r)
+        G = dev(torch, g) if norm else None
+        out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        ws = bl.new_workspace(M, K)
+        items.append((X, P, s, G, 1e-6, out, ws))
+        singles.append(host(bl.forward(X, P, s, G, 1e-6, N)).copy())
+        refs.append(orc.forward(x, packed_r, s, g if norm else None, 1e-6, N))
+    announce("forward_batch norm/no-norm", len(items))
+    bl.forward_batch(items)
+    torch.cuda.synchronize()
+    for it, single, y64, sh in zip(items, singles, refs, shapes):
+        assert np.array_equal(host(it[5]), single), sh
+        check_y(host(it[5]), y64)
