@@ -37,6 +37,13 @@
  *     q = clamp(round-half-even(xn * inv), -128, 127), qsum = sum(q).
  *   - y = acc * (w_scale / inv), computed here in fp64 from the exact int32
  *     accumulator.
+ *   - use_rms_norm off (gamma NULL): the activations are quantised as they
+ *     come, with no RMSNorm.
+ *   - FFN block: each projection is a BitLinear; the sub-norm is the down
+ *     projection's RMSNorm; the gate/up outputs are fp32 values
+ *     (float)acc * (w_scale / inv) and a = (relu(g) * relu(g)) * u in fp32,
+ *     so the down projection's int8 codes are decided from the same fp32
+ *     values the product computes.
  *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -fopenmp -shared
  * -fPIC.  The fp32 steps must not be contracted or reassociated: they decide
@@ -45,6 +52,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* Status values (the oracle's own; the product library defines its own). */
@@ -292,4 +300,76 @@ int oracle_forward(const float *x, const uint8_t *packed, float w_scale,
     st = oracle_matmul_i2s(q, qsum, packed, M, K, N, acc);
     if (st) return st;
     return oracle_rescale(acc, inv, w_scale, M, N, y);
+}
+
+/* BitLinear output in fp32, the precision the product returns it in:
+ * y32 = (float)acc * (w_scale / inv[m]), one IEEE division and one
+ * multiplication.  Used where a BitLinear output feeds another step whose
+ * integer codes depend on it (the FFN block below), so that both sides take
+ * those decisions from the same fp32 values. */
+int oracle_rescale_f32(const int32_t *acc, const float *inv, float w_scale,
+                       int64_t M, int64_t N, float *y) {
+    if (M < 1 || N < 1) return ORC_ERR_SHAPE;
+    for (int64_t m = 0; m < M; ++m) {
+        const float c = w_scale / inv[m];
+        for (int64_t n = 0; n < N; ++n) y[m * N + n] = (float)acc[m * N + n] * c;
+    }
+    return ORC_OK;
+}
+
+/* One BitLinear with fp32 output (act_quant -> contraction -> rescale_f32);
+ * gamma NULL: no RMSNorm.  Scratch is allocated here. */
+static int bitlinear_f32(const float *x, const float *gamma, float eps, int64_t M,
+                         int64_t K, int64_t N, const uint8_t *packed, float w_scale,
+                         float *y) {
+    float *xn = malloc(sizeof(float) * (size_t)(M * K));
+    int8_t *q = malloc((size_t)(M * K));
+    float *inv = malloc(sizeof(float) * (size_t)M);
+    int32_t *qsum = malloc(sizeof(int32_t) * (size_t)M);
+    int32_t *acc = malloc(sizeof(int32_t) * (size_t)(M * N));
+    int st = ORC_ERR_SHAPE;
+    if (xn && q && inv && qsum && acc) {
+        st = oracle_act_quant(x, gamma, eps, M, K, q, inv, qsum, xn);
+        if (!st) st = oracle_matmul_i2s(q, qsum, packed, M, K, N, acc);
+        if (!st) st = oracle_rescale_f32(acc, inv, w_scale, M, N, y);
+    }
+    free(xn); free(q); free(inv); free(qsum); free(acc);
+    return st;
+}
+
+/* BitNet FFN block [HF-38087, the BitNetMLP excerpt in the review thread:
+ * down(ffn_sub_norm(act(gate(x)) * up(x))); CPPB-7 summary bullet and the
+ * commit on the bitnet-b1.58 graph: the 2B4T activation is squared ReLU,
+ * not SiLU].  Every projection is a BitLinear (RMSNorm with its gamma, or
+ * none when the gamma is NULL, then int8 quantisation and the ternary
+ * contraction); the sub-norm is the down projection's own RMSNorm:
+ *   g = BitLinear(x; gate, gamma_in)      [M][F] fp32
+ *   u = BitLinear(x; up,   gamma_in)      [M][F] fp32
+ *   a = (max(g, 0) * max(g, 0)) * u       [M][F] fp32, this order
+ *   y = BitLinear(a; down, gamma_sub)     [M][H] fp64 (oracle_forward's rescale)
+ * Shapes: x [M][H]; gate, up packed from [F][H]; down packed from [H][F];
+ * gamma_in [H], gamma_sub [F].  g, u, a are returned for inspection. */
+int oracle_ffn(const float *x, const float *gamma_in, float eps, int64_t M, int64_t H,
+               int64_t F, const uint8_t *p_gate, float s_gate, const uint8_t *p_up,
+               float s_up, const uint8_t *p_down, float s_down, const float *gamma_sub,
+               float *g, float *u, float *a, double *y) {
+    if (M < 1 || H < 1 || F < 1 || H % ORC_BLOCK_WEIGHTS || F % ORC_BLOCK_WEIGHTS)
+        return ORC_ERR_SHAPE;
+    int st = bitlinear_f32(x, gamma_in, eps, M, H, F, p_gate, s_gate, g);
+    if (!st) st = bitlinear_f32(x, gamma_in, eps, M, H, F, p_up, s_up, u);
+    if (st) return st;
+    for (int64_t i = 0; i < M * F; ++i) {
+        const float r = g[i] > 0.0f ? g[i] : 0.0f;
+        a[i] = (r * r) * u[i];
+    }
+    float *xn = malloc(sizeof(float) * (size_t)(M * F));
+    int8_t *q = malloc((size_t)(M * F));
+    float *inv = malloc(sizeof(float) * (size_t)M);
+    int32_t *qsum = malloc(sizeof(int32_t) * (size_t)M);
+    int32_t *acc = malloc(sizeof(int32_t) * (size_t)(M * H));
+    st = ORC_ERR_SHAPE;
+    if (xn && q && inv && qsum && acc)
+        st = oracle_forward(a, p_down, s_down, gamma_sub, eps, M, F, H, y, xn, q, inv, qsum, acc);
+    free(xn); free(q); free(inv); free(qsum); free(acc);
+    return st;
 }

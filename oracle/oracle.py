@@ -11,8 +11,10 @@ builds it with gcc when no build is present and marshals numpy arrays.
 
 Sources: huggingface/transformers PR #38087 "Add optional RMSNorm support to
 BitNet quantization (config + layers)" (RMSNorm before quantisation, eps
-1e-6); eejd/cpp-bitnet PR #7 "fix: I2_S ARM kernel layout + squared-ReLU FFN"
-(I2_S layout, code offset, per-tensor scale, trailer, K % 128).
+1e-6, use_rms_norm; the BitNetMLP excerpt of the review thread for the FFN
+block); eejd/cpp-bitnet PR #7 "fix: I2_S ARM kernel layout + squared-ReLU
+FFN" (I2_S layout, code offset, per-tensor scale, trailer, K % 128; squared
+ReLU as the 2B4T FFN activation).
 """
 from __future__ import annotations
 
@@ -71,6 +73,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_matmul_i2s.argtypes = [p, p, p, i64, i64, i64, p]
         L.oracle_rescale.restype = ctypes.c_int
         L.oracle_rescale.argtypes = [p, p, ctypes.c_float, i64, i64, p]
+        L.oracle_rescale_f32.restype = ctypes.c_int
+        L.oracle_rescale_f32.argtypes = [p, p, ctypes.c_float, i64, i64, p]
+        f = ctypes.c_float
+        L.oracle_ffn.restype = ctypes.c_int
+        L.oracle_ffn.argtypes = [p, p, f, i64, i64, i64, p, f, p, f, p, f, p, p, p, p, p]
         _lib = L
     return _lib
 
@@ -189,6 +196,44 @@ def forward(x: np.ndarray, packed: np.ndarray, w_scale: float, gamma,
     q, inv, qsum = act_quant(x, gamma, eps)
     acc = matmul_i2s(q, qsum, packed, N)
     return rescale(acc, inv, w_scale)
+
+
+def rescale_f32(acc: np.ndarray, inv: np.ndarray, w_scale: float) -> np.ndarray:
+    """fp32 BitLinear output (float)acc * (w_scale / inv[m])."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    inv = _f32(inv)
+    M, N = acc.shape
+    y = np.empty((M, N), dtype=np.float32)
+    st = lib().oracle_rescale_f32(_ptr(acc), _ptr(inv), ctypes.c_float(w_scale), M, N, _ptr(y))
+    if st != OK:
+        raise OracleError(st, "rescale_f32")
+    return y
+
+
+def ffn(x: np.ndarray, gamma_in, eps: float, gate, up, down, gamma_sub):
+    """BitNet FFN block y = down(sub_norm(relu(g)^2 * u)), g / u = gate / up(x).
+    gate, up, down: (packed, scale) pairs, packed from [F][H], [F][H], [H][F].
+    gamma_in [H] / gamma_sub [F], or None for no RMSNorm.
+    Returns (y fp64 [M][H], g, u, a fp32 [M][F])."""
+    x = _f32(np.atleast_2d(x))
+    M, H = x.shape
+    (pg, sg), (pu, su), (pd, sd) = gate, up, down
+    pg, pu, pd = (np.ascontiguousarray(p, dtype=np.uint8) for p in (pg, pu, pd))
+    F = (pg.size - 32) * 4 // H
+    gi = None if gamma_in is None else _f32(gamma_in)
+    gs = None if gamma_sub is None else _f32(gamma_sub)
+    g = np.empty((M, F), np.float32)
+    u = np.empty((M, F), np.float32)
+    a = np.empty((M, F), np.float32)
+    y = np.empty((M, H), np.float64)
+    null = ctypes.c_void_p(None)
+    st = lib().oracle_ffn(_ptr(x), null if gi is None else _ptr(gi), ctypes.c_float(eps), M, H, F,
+                          _ptr(pg), ctypes.c_float(sg), _ptr(pu), ctypes.c_float(su),
+                          _ptr(pd), ctypes.c_float(sd), null if gs is None else _ptr(gs),
+                          _ptr(g), _ptr(u), _ptr(a), _ptr(y))
+    if st != OK:
+        raise OracleError(st, "ffn")
+    return y, g, u, a
 
 
 def packed_rows(packed: np.ndarray, K: int, rows) -> np.ndarray:
