@@ -337,6 +337,18 @@ static int bitlinear_f32(const float *x, const float *gamma, float eps, int64_t 
     return st;
 }
 
+/* Squared-ReLU gate of the FFN block [CPPB-7 summary bullet: the 2B4T
+ * activation is relu2; HF-38087 BitNetMLP: act(gate) * up]:
+ * a = (max(g, 0) * max(g, 0)) * u, element by element, fp32, this order. */
+int oracle_relu2_mul(const float *g, const float *u, int64_t n, float *a) {
+    if (n < 1) return ORC_ERR_SHAPE;
+    for (int64_t i = 0; i < n; ++i) {
+        const float r = g[i] > 0.0f ? g[i] : 0.0f;
+        a[i] = (r * r) * u[i];
+    }
+    return ORC_OK;
+}
+
 /* BitNet FFN block [HF-38087, the BitNetMLP excerpt in the review thread:
  * down(ffn_sub_norm(act(gate(x)) * up(x))); CPPB-7 summary bullet and the
  * commit on the bitnet-b1.58 graph: the 2B4T activation is squared ReLU,
@@ -358,10 +370,7 @@ int oracle_ffn(const float *x, const float *gamma_in, float eps, int64_t M, int6
     int st = bitlinear_f32(x, gamma_in, eps, M, H, F, p_gate, s_gate, g);
     if (!st) st = bitlinear_f32(x, gamma_in, eps, M, H, F, p_up, s_up, u);
     if (st) return st;
-    for (int64_t i = 0; i < M * F; ++i) {
-        const float r = g[i] > 0.0f ? g[i] : 0.0f;
-        a[i] = (r * r) * u[i];
-    }
+    oracle_relu2_mul(g, u, M * F, a);
     float *xn = malloc(sizeof(float) * (size_t)(M * F));
     int8_t *q = malloc((size_t)(M * F));
     float *inv = malloc(sizeof(float) * (size_t)M);

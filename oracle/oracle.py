@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_rescale_f32.restype = ctypes.c_int
         L.oracle_rescale_f32.argtypes = [p, p, ctypes.c_float, i64, i64, p]
         f = ctypes.c_float
+        L.oracle_relu2_mul.restype = ctypes.c_int
+        L.oracle_relu2_mul.argtypes = [p, p, i64, p]
         L.oracle_ffn.restype = ctypes.c_int
         L.oracle_ffn.argtypes = [p, p, f, i64, i64, i64, p, f, p, f, p, f, p, p, p, p, p]
         _lib = L
@@ -208,6 +210,16 @@ def rescale_f32(acc: np.ndarray, inv: np.ndarray, w_scale: float) -> np.ndarray:
     if st != OK:
         raise OracleError(st, "rescale_f32")
     return y
+
+
+def relu2_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """a = (max(g, 0)^2) * u in fp32 (the FFN block's gate)."""
+    g, u = _f32(g), _f32(u)
+    a = np.empty_like(g)
+    st = lib().oracle_relu2_mul(_ptr(g), _ptr(u), g.size, _ptr(a))
+    if st != OK:
+        raise OracleError(st, "relu2_mul")
+    return a
 
 
 def ffn(x: np.ndarray, gamma_in, eps: float, gate, up, down, gamma_sub):

@@ -131,3 +131,18 @@ def test_ffn_random_vs_fp64_pipeline(orc):
     assert rows.sum() >= 2
     assert np.allclose(g[rows], g64[rows], rtol=1e-5, atol=1e-7)
     assert np.allclose(y[rows], y64[rows], rtol=1e-4, atol=1e-6 * np.abs(y64).max())
+
+
+def test_relu2_mul_values(orc):
+    """Hand values: negative and zero gates give exactly 0, positive gates
+    are squared and multiply the up value; the product is taken after the
+    square."""
+    g = np.array([-3.0, 0.0, 0.5, 2.0, 3.0, -0.0], np.float32)
+    u = np.array([5.0, 7.0, 4.0, -0.25, 1.0, 9.0], np.float32)
+    a = orc.relu2_mul(g, u)
+    assert a.tolist() == [0.0, 0.0, 1.0, -1.0, 9.0, 0.0]
+    # (r * r) * u, not r * (r * u): 3 * 3 = 9 exactly, then 9 * (1 + 2^-23)
+    # rounds differently from 3 * (3 * (1 + 2^-23))
+    g = np.array([3.0], np.float32)
+    u = np.array([1 + 2.0 ** -23], np.float32)
+    assert orc.relu2_mul(g, u)[0] == np.float32(9.0) * np.float32(1 + 2.0 ** -23)
