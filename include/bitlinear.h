@@ -235,6 +235,53 @@ bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum,
                                   int64_t K, int64_t N, int32_t *acc,
                                   const bl_launch *launch, void *stream);
 
+/* BitNet FFN block [HF-38087, the BitNetMLP excerpt of the review thread:
+ * y = down(ffn_sub_norm(act(gate(x)) * up(x))); CPPB-7 summary bullet and
+ * the bitnet-b1.58 graph commit: the 2B4T activation is squared ReLU].
+ * Each projection is a BitLinear as in bitlinear_forward; the sub-norm is
+ * the down projection's own RMSNorm:
+ *   g = BitLinear(x; gate, gamma_in), u = BitLinear(x; up, gamma_in)   fp32 [M][F]
+ *   a = (max(g, 0) * max(g, 0)) * u                                    fp32 [M][F]
+ *   y = BitLinear(a; down, gamma_sub)                                  fp32 [M][H]
+ * a is never stored: the down projection's quantisation forms it from g and
+ * u as it reads them.  At M = 1 with F <= 8192 the block is two launches
+ * (gate and up in one, the down projection with its quantisation in the
+ * other); otherwise gate and up take bitlinear_forward_batch's launches and
+ * the down projection one quantisation and one contraction launch.
+ *   x: device fp32 [M][H]; y: device fp32 [M][H] (every element written).
+ *   packed_gate / packed_up: I2_S of W [F][H]; packed_down: I2_S of W [H][F]
+ *             (H and F multiples of 128); s_*: their per-tensor scales.
+ *   gamma_in: device fp32 [H] or NULL (no RMSNorm before gate / up);
+ *   gamma_sub: device fp32 [F] (the sub-norm's weight) or NULL.
+ *   eps: > 0 and finite when either gamma is non-NULL.
+ *   workspace: device, >= bitlinear_ffn_workspace_bytes(M, H, F) bytes,
+ *             16-byte aligned; after the call it holds g at offset 0 and u
+ *             at offset align256(4*M*F) (fp32 [M][F] each), then the three
+ *             projections' q / inv / qsum.
+ *   No output may overlap an input.  Errors as bitlinear_forward; all
+ *   checks run before anything is enqueued.  Asynchronous on `stream`. */
+typedef struct {
+    const float *x;
+    const float *gamma_in;
+    const uint8_t *packed_gate;
+    float s_gate;
+    const uint8_t *packed_up;
+    float s_up;
+    const uint8_t *packed_down;
+    float s_down;
+    const float *gamma_sub;
+    float eps;
+    int64_t M, H, F;
+    float *y;
+    void *workspace;
+    size_t workspace_bytes;
+} bl_ffn_desc;
+
+/* Workspace bytes of bitlinear_ffn_forward (0 if a size is invalid). */
+size_t bitlinear_ffn_workspace_bytes(int64_t M, int64_t H, int64_t F);
+
+bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,8 @@ allocated here and their pointers passed down) and the stream
 missing, loading it raises.
 
 Functions mirror the C entry points: :func:`pack_i2s`, :func:`unpack_i2s`,
-:func:`read_scale`, :func:`forward`, :func:`act_quant`, :func:`matmul_i2s`.
+:func:`read_scale`, :func:`forward`, :func:`forward_batch`,
+:func:`ffn_forward`, :func:`act_quant`, :func:`matmul_i2s`.
 """
 from __future__ import annotations
 
@@ -39,6 +40,18 @@ class ForwardDesc(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+class FfnDesc(ctypes.Structure):
+    """bl_ffn_desc: the arguments of one bitlinear_ffn_forward."""
+    _fields_ = [("x", ctypes.c_void_p), ("gamma_in", ctypes.c_void_p),
+                ("packed_gate", ctypes.c_void_p), ("s_gate", ctypes.c_float),
+                ("packed_up", ctypes.c_void_p), ("s_up", ctypes.c_float),
+                ("packed_down", ctypes.c_void_p), ("s_down", ctypes.c_float),
+                ("gamma_sub", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("M", ctypes.c_int64), ("H", ctypes.c_int64), ("F", ctypes.c_int64),
+                ("y", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 SIGNATURES = {
     "bitlinear_status_string": (ctypes.c_char_p, [_i]),
     "bitlinear_abi_version": (_i, []),
@@ -53,6 +66,8 @@ SIGNATURES = {
                                   ctypes.POINTER(Launch), _p]),
     "bitlinear_forward_batch": (_i, [ctypes.POINTER(ForwardDesc), _i, ctypes.POINTER(Launch), _p]),
     "bitlinear_act_quant": (_i, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
+    "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_ffn_forward": (_i, [ctypes.POINTER(FfnDesc), _p]),
     "bitlinear_matmul_i2s": (_i, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "bitlinear_matmul_i2s_ex": (_i, [_p, _p, _p, _i64, _i64, _i64, _p,
                                      ctypes.POINTER(Launch), _p]),
@@ -243,3 +258,36 @@ def workspace_views(workspace, M: int, K: int):
     o += a(4 * M)
     qsum = workspace[o: o + 4 * M].view(torch.int32)
     return q, inv, qsum
+
+
+def ffn_workspace_bytes(M: int, H: int, F: int) -> int:
+    return int(lib().bitlinear_ffn_workspace_bytes(M, H, F))
+
+
+def ffn_forward(x, gamma_in, eps: float, gate, up, down, gamma_sub, out=None, workspace=None):
+    """BitNet FFN block y = down(sub_norm(relu(g)^2 * u)), g / u = gate / up(x).
+    gate, up, down: (packed, scale) pairs (packed from [F][H], [F][H], [H][F]);
+    gamma_in [H] / gamma_sub [F] or None (no RMSNorm).  x fp32 [M][H] -> y fp32 [M][H]."""
+    torch = _torch()
+    M, H = x.shape
+    (pg, sg), (pu, su), (pd, sd) = gate, up, down
+    F = (pg.numel() - 32) * 4 // H
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(ffn_workspace_bytes(M, H, F), dtype=torch.uint8, device=x.device)
+    d = FfnDesc(_dev(x, torch.float32, "x"), _gamma(gamma_in), _dev(pg, torch.uint8, "gate"), sg,
+                _dev(pu, torch.uint8, "up"), su, _dev(pd, torch.uint8, "down"), sd,
+                _gamma(gamma_sub), eps, M, H, F, _dev(out, torch.float32, "out"),
+                _dev(workspace, torch.uint8, "workspace"), workspace.numel())
+    _check(lib().bitlinear_ffn_forward(ctypes.byref(d), _stream()), "ffn_forward")
+    return out
+
+
+def ffn_workspace_views(workspace, M: int, F: int):
+    """(g, u) fp32 [M][F] views of an FFN workspace after the call."""
+    torch = _torch()
+    gb = (4 * M * F + 255) // 256 * 256
+    g = workspace[: 4 * M * F].view(torch.float32).view(M, F)
+    u = workspace[gb: gb + 4 * M * F].view(torch.float32).view(M, F)
+    return g, u

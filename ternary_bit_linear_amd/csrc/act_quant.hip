@@ -58,6 +58,21 @@ __global__ __launch_bounds__(256) void act_quant_long_kernel(
     block_act_quant_row<8, true>(x + (size_t)m * K, gamma, eps, K, red, sink, [] {});
 }
 
+// The FFN's down-projection input: the row is relu2_mul(g, u) of the gate
+// and up rows, normalised (gamma: the sub-norm) and quantised.  Rows of up
+// to 1024 * CH in registers, longer ones streamed.
+template <int CH, bool LONG>
+__global__ __launch_bounds__(256) void act_quant_glu_kernel(
+    const float *__restrict__ g, const float *__restrict__ u, const float *__restrict__ gamma,
+    float eps, int K, int8_t *__restrict__ q, float *__restrict__ inv,
+    int32_t *__restrict__ qsum) {
+    __shared__ float red[kRedWords];
+    const int m = blockIdx.x;
+    GlobalRowSink sink{q + (size_t)m * K, inv + m, qsum + m};
+    block_act_quant_row<CH, LONG, true, true>(g + (size_t)m * K, gamma, eps, K, red, sink, [] {},
+                                              u + (size_t)m * K);
+}
+
 // Batched form: up to 8 problems, one block per token row of any of them.
 // b0..b7: first block of each problem (INT_MAX past the last), leading the
 // argument list so that the build's kernel-argument preload puts them in
@@ -134,6 +149,22 @@ hipError_t launch_act_quant_batch(const ActQuantDesc *d, int count, hipStream_t 
     else
         hipLaunchKernelGGL(act_quant_batch_kernel<8>, dim3((unsigned)rows), dim3(256), 0, s, begin[0],
                            begin[1], begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_quant_glu(const float *g, const float *u, const float *gamma, float eps,
+                                int64_t M, int64_t K, int8_t *q, float *inv, int32_t *qsum,
+                                hipStream_t s) {
+    const dim3 grid((unsigned)M), block(256);
+    if (K <= 4 * 1024)
+        hipLaunchKernelGGL((act_quant_glu_kernel<4, false>), grid, block, 0, s, g, u, gamma, eps,
+                           (int)K, q, inv, qsum);
+    else if (K <= 8 * 1024)
+        hipLaunchKernelGGL((act_quant_glu_kernel<8, false>), grid, block, 0, s, g, u, gamma, eps,
+                           (int)K, q, inv, qsum);
+    else
+        hipLaunchKernelGGL((act_quant_glu_kernel<8, true>), grid, block, 0, s, g, u, gamma, eps,
+                           (int)K, q, inv, qsum);
     return hipGetLastError();
 }
 

@@ -176,6 +176,29 @@ bl_status enqueue_unfused(const bl_forward_desc &d, const bl_launch *launch, hip
                            nullptr, launch, s);
 }
 
+// FFN block workspace: g, u (fp32 [M][F] each), then the gate, up and down
+// projections' own forward workspaces.
+struct FfnWorkspace {
+    float *g, *u;
+    void *ws_gate, *ws_up, *ws_down;
+    size_t b_gate, b_down;
+};
+
+FfnWorkspace carve_ffn(void *ws, int64_t M, int64_t H, int64_t F) {
+    uint8_t *p = static_cast<uint8_t *>(ws);
+    FfnWorkspace w;
+    const size_t gb = align256((size_t)(M * F) * 4);
+    w.g = reinterpret_cast<float *>(p);
+    w.u = reinterpret_cast<float *>(p + gb);
+    p += 2 * gb;
+    w.b_gate = align256(bitlinear_workspace_bytes(M, H));
+    w.b_down = align256(bitlinear_workspace_bytes(M, F));
+    w.ws_gate = p;
+    w.ws_up = p + w.b_gate;
+    w.ws_down = p + 2 * w.b_gate;
+    return w;
+}
+
 constexpr int kMaxBatchDescs = 64;
 constexpr int kFusedPerLaunch = 8;
 constexpr int kGroupPerLaunch = 8;
@@ -313,6 +336,69 @@ bl_status bitlinear_forward(const float *x, const uint8_t *packed_w, float w_sca
                             float *y, void *workspace, size_t workspace_bytes, void *stream) {
     return bitlinear_forward_ex(x, packed_w, w_scale, gamma, eps, M, K, N, y, workspace,
                                 workspace_bytes, nullptr, stream);
+}
+
+size_t bitlinear_ffn_workspace_bytes(int64_t M, int64_t H, int64_t F) {
+    if (check_mk(M, H) || check_mk(M, F) || check_mn(M, F) || check_mn(M, H)) return 0;
+    return 2 * align256((size_t)(M * F) * 4) + 2 * align256(bitlinear_workspace_bytes(M, H)) +
+           align256(bitlinear_workspace_bytes(M, F));
+}
+
+bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
+    if (!desc) return BL_ERR_INVALID_ARG;
+    const bl_ffn_desc &d = *desc;
+    const int64_t M = d.M, H = d.H, F = d.F;
+    if (bl_status st = check_mk(M, H)) return st;
+    if (bl_status st = check_mk(M, F)) return st;
+    if (bl_status st = check_nk(F, H)) return st;
+    if (bl_status st = check_nk(H, F)) return st;
+    if (bl_status st = check_mn(M, F)) return st;
+    if (bl_status st = check_mn(M, H)) return st;
+    if (!d.x || !d.packed_gate || !d.packed_up || !d.packed_down || !d.y || !d.workspace)
+        return BL_ERR_INVALID_ARG;
+    if ((d.gamma_in || d.gamma_sub) && (!(d.eps > 0.0f) || !std::isfinite(d.eps)))
+        return BL_ERR_INVALID_ARG;
+    if (!std::isfinite(d.s_gate) || !std::isfinite(d.s_up) || !std::isfinite(d.s_down))
+        return BL_ERR_INVALID_ARG;
+    if (!aligned16(d.x) || !aligned16(d.gamma_in) || !aligned16(d.gamma_sub) ||
+        !aligned16(d.packed_gate) || !aligned16(d.packed_up) || !aligned16(d.packed_down) ||
+        !aligned16(d.y) || !aligned16(d.workspace))
+        return BL_ERR_ALIGN;
+    if (d.workspace_bytes < bitlinear_ffn_workspace_bytes(M, H, F)) return BL_ERR_WORKSPACE;
+    if (bl_status st = check_grid(M, nullptr)) return st;
+    const FfnWorkspace w = carve_ffn(d.workspace, M, H, F);
+    // 1. gate and up: two BitLinears over the same x.
+    const bl_forward_desc gu[2] = {
+        {d.x, d.packed_gate, d.s_gate, d.gamma_in, d.eps, M, H, F, w.g, w.ws_gate, w.b_gate},
+        {d.x, d.packed_up, d.s_up, d.gamma_in, d.eps, M, H, F, w.u, w.ws_up, w.b_gate}};
+    if (bl_status st = bitlinear_forward_batch(gu, 2, nullptr, stream)) return st;
+    // 2. down over relu2_mul(g, u), formed while its quantisation reads g, u.
+    hipStream_t s = as_stream(stream);
+    const Workspace wd = carve(w.ws_down, M, F);
+    const int64_t Ms[1] = {M}, Ks[1] = {F}, Ns[1] = {H};
+    if (M == 1 && F <= 8 * 1024 && bl::shot_fused_supported(M, F) &&
+        bl::shot_rounds(Ms, Ks, Ns, 1) == 1) {
+        bl::FusedDecode f;
+        f.x = w.g;
+        f.gamma = d.gamma_sub;
+        f.packed = d.packed_down;
+        f.y = d.y;
+        f.q = wd.q;
+        f.inv = wd.inv;
+        f.qsum = wd.qsum;
+        f.eps = d.eps;
+        f.w_scale = d.s_down;
+        f.M = M;
+        f.K = F;
+        f.N = H;
+        f.u = w.u;
+        return hip_status(bl::launch_gemv_shot_fused(&f, 1, 0, s));
+    }
+    if (bl::launch_act_quant_glu(w.g, w.u, d.gamma_sub, d.eps, M, F, wd.q, wd.inv, wd.qsum, s) !=
+        hipSuccess)
+        return BL_ERR_HIP;
+    return run_contraction(wd.q, wd.inv, wd.qsum, d.packed_down, d.s_down, M, F, H, d.y, nullptr,
+                           nullptr, s);
 }
 
 bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,

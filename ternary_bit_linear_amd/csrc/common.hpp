@@ -261,6 +261,19 @@ __device__ __forceinline__ float4 gamma_f4(__amdgpu_buffer_rsrc_t rg, uint32_t o
     return norm ? buf_load_f4(rg, off) : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
 }
 
+// Squared-ReLU gated input of the BitNet FFN's down projection
+// (HF-38087 BitNetMLP: down(sub_norm(act(gate) * up)); CPPB-7: the 2B4T
+// activation is squared ReLU): a = (max(g, 0) * max(g, 0)) * u, in fp32, in
+// this order.
+__device__ __forceinline__ float relu2_mul(float g, float u) {
+    const float r = g > 0.0f ? g : 0.0f;
+    return (r * r) * u;
+}
+__device__ __forceinline__ float4 relu2_mul4(const float4 &g, const float4 &u) {
+    return make_float4(relu2_mul(g.x, u.x), relu2_mul(g.y, u.y), relu2_mul(g.z, u.z),
+                       relu2_mul(g.w, u.w));
+}
+
 __device__ __forceinline__ float amax4(float a, const float4 &v) {
     return fmaxf(fmaxf(fmaxf(a, fabsf(v.x)), fmaxf(fabsf(v.y), fabsf(v.z))), fabsf(v.w));
 }
@@ -272,6 +285,8 @@ __device__ __forceinline__ float amax4(float a, const float4 &v) {
 //   xn = (x * r) * gamma,  inv = 127 / max(max |xn|, 1e-5)
 //   q = clamp(rint(xn * inv), -128, 127),  qsum = sum q.
 // With gamma == nullptr there is no RMSNorm: xn = x (no sum of squares).
+// GLU: the row is not read from x but formed as relu2_mul(x, u) from the
+// gate row x and the up row u (the FFN's down projection input).
 // Sink receives store_q(k, 4 packed int8) and store_row(inv, qsum).
 
 // Block form (256 threads): thread t owns O256 chain t, i.e. the float4
@@ -282,18 +297,20 @@ __device__ __forceinline__ float amax4(float a, const float4 &v) {
 // not delay the normalisation.  A wave skips the loads of a chunk that lies
 // wholly past K.  LONG rows (K > 1024 * CH) are streamed in chunks of CH
 // float4 per thread, three times.
-template <int CH, bool LONG, bool SYNC = true, class Sink, class Hook>
+template <int CH, bool LONG, bool SYNC = true, bool GLU = false, class Sink, class Hook>
 __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
                                                     const float *__restrict__ gamma,
                                                     float eps, int K, float *red,
-                                                    Sink &sink, Hook &&issued) {
+                                                    Sink &sink, Hook &&issued,
+                                                    const float *__restrict__ u = nullptr) {
     const int t4 = 4 * threadIdx.x;
     constexpr int STRIDE = 1024;
     if constexpr (!LONG) {  // K <= 1024 * CH
         const bool norm = gamma != nullptr;
         const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+        const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
         const auto rg = gamma_rsrc(gamma, K);
-        float4 xv[CH], gv[CH];
+        float4 xv[CH], gv[CH], uv[GLU ? CH : 1];
         const int wk = 256 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
@@ -301,15 +318,21 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
             const uint32_t off = k < K ? 4u * (uint32_t)k : kOOB;
             if (STRIDE * i + wk < K) {
                 xv[i] = buf_load_f4(rx, off);
+                if constexpr (GLU) uv[i] = buf_load_f4(ru, off);
                 gv[i] = gamma_f4(rg, off, norm);
             } else {
                 xv[i] = gv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if constexpr (GLU) uv[i] = xv[i];
             }
         }
         // Every wave's x / gamma loads are issued before any load the hook
         // issues, so they do not queue behind another wave's weight misses.
         if constexpr (SYNC) __builtin_amdgcn_s_barrier();
         issued();
+        if constexpr (GLU) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) xv[i] = relu2_mul4(xv[i], uv[i]);
+        }
         // Chunks wholly past K hold zeros, which leave the sum of squares and
         // the max unchanged: the wave skips them (a wave-uniform test).
         float r = 1.0f;
@@ -357,15 +380,22 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
     // Long rows: three streamed passes.
     const bool norm = gamma != nullptr;
     const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+    const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
     const auto rg = gamma_rsrc(gamma, K);
     auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
+    // x of one chunk (GLU: formed from the gate and up rows)
+    auto load_x = [&](int k) -> float4 {
+        const float4 v = buf_load_f4(rx, off_of(k));
+        if constexpr (GLU) return relu2_mul4(v, buf_load_f4(ru, off_of(k)));
+        else return v;
+    };
     float r = 1.0f;
     if (norm) {
         float p = 0.0f;
         for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
             float4 xv[CH];
 #pragma unroll
-            for (int i = 0; i < CH; ++i) xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
+            for (int i = 0; i < CH; ++i) xv[i] = load_x(c0 + t4 + STRIDE * i);
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
                 p = __builtin_fmaf(xv[i].x, xv[i].x, p);
@@ -382,7 +412,7 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
         float4 xv[CH], gv[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
+            xv[i] = load_x(c0 + t4 + STRIDE * i);
             gv[i] = gamma_f4(rg, off_of(c0 + t4 + STRIDE * i), norm);
         }
 #pragma unroll
@@ -395,7 +425,7 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
         float4 xv[CH], gv[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            xv[i] = buf_load_f4(rx, off_of(c0 + t4 + STRIDE * i));
+            xv[i] = load_x(c0 + t4 + STRIDE * i);
             gv[i] = gamma_f4(rg, off_of(c0 + t4 + STRIDE * i), norm);
         }
 #pragma unroll
@@ -520,6 +550,13 @@ hipError_t launch_act_quant(const float *x, const float *gamma, float eps,
                             int64_t M, int64_t K, int8_t *q, float *inv,
                             int32_t *qsum, hipStream_t s);
 
+// Quantisation of the FFN down projection's input relu2_mul(g, u) (rows of
+// g and u: [M][K], gamma the sub-norm or nullptr); same codes as
+// launch_act_quant over that product.
+hipError_t launch_act_quant_glu(const float *g, const float *u, const float *gamma, float eps,
+                                int64_t M, int64_t K, int8_t *q, float *inv, int32_t *qsum,
+                                hipStream_t s);
+
 // Batched quantisation: up to 8 independent (x, gamma, eps, M, K) with
 // K <= 8192 each, one launch, bit-identical to launch_act_quant per problem.
 struct ActQuantDesc {
@@ -557,6 +594,10 @@ struct FusedDecode {
     float eps;
     float w_scale;
     int64_t M, K, N;
+    // Non-null: the input row is relu2_mul(x, u) (the FFN's down projection
+    // over the gate rows x and up rows u).  One-shot route with M == 1 only;
+    // every problem of a launch has it or none does.
+    const float *u = nullptr;
 };
 hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipStream_t s);
 

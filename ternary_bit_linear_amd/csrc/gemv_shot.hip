@@ -62,6 +62,7 @@ struct ShotProblem {
     int M, K, N;
     int wg_begin;          // first workgroup of this problem
     int ks_log;            // log2 of the K split: 0, 1 or 2
+    const float *u;        // GLU: up rows (the input row is relu2_mul(x, u))
 };
 constexpr int kMaxShotBatch = 8;
 struct ShotBatch {
@@ -110,7 +111,7 @@ __device__ __forceinline__ v4i field_sum(const v4i (&a)[4]) {
 // lead the argument list so that the build's kernel-argument preload puts
 // them in scalar registers at wave launch, and the lookup costs no memory
 // round trip.
-template <int NB, int R, bool OUT_Y, int FM, int CH, bool LONG>
+template <int NB, int R, bool OUT_Y, int FM, int CH, bool LONG, bool GLU = false>
 __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, int b3, int b4,
                                                         int b5, int b6, int b7, ShotBatch B) {
     static_assert(NB >= 1 && NB <= 8, "batches per wave");
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
     asm volatile("" ::"s"(P.q), "s"(P.inv), "s"(P.qsum), "s"(P.x), "s"(P.gamma), "s"(P.q_out),
                  "s"(P.inv_out), "s"(P.qsum_out), "s"(P.packed), "s"(P.y), "s"(P.acc), "s"(P.eps),
                  "s"(P.w_scale), "s"(P.M), "s"(P.K), "s"(P.N), "s"(P.wg_begin), "s"(P.ks_log));
+    if constexpr (GLU) asm volatile("" ::"s"(P.u));
     const int M = P.M, K = P.K, N = P.N;
 
     const int tid = threadIdx.x;
@@ -226,7 +228,8 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
         {
             ShotRowSink sink{q_lds, inv_sh, qsum_sh, st == 0 ? P.q_out : nullptr, P.inv_out,
                              P.qsum_out};
-            block_act_quant_row<CH, LONG, false>(P.x, P.gamma, P.eps, K, red, sink, issue_weights);
+            block_act_quant_row<CH, LONG, false, GLU>(P.x, P.gamma, P.eps, K, red, sink,
+                                                      issue_weights, P.u);
         }
 #pragma unroll
         for (int m = 1; m < FM; ++m) {
@@ -234,8 +237,9 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
                 ShotRowSink sink{q_lds + m * K, inv_sh + m, qsum_sh + m,
                                  st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m,
                                  P.qsum_out + m};
-                block_act_quant_row<CH, LONG, false>(P.x + (size_t)m * K, P.gamma, P.eps, K, red,
-                                                     sink, [] {});
+                block_act_quant_row<CH, LONG, false, GLU>(P.x + (size_t)m * K, P.gamma, P.eps, K,
+                                                          red, sink, [] {},
+                                                          GLU ? P.u + (size_t)m * K : nullptr);
             }
         }
         lds_barrier();
@@ -489,7 +493,7 @@ hipError_t launch_shot_nb(const ShotDecode *d, int count, hipStream_t s) {
     return launch_batch(gemv_shot_kernel<NB, R, OUT_Y, 0, 1, false>, B, begin, gx, qmax, s);
 }
 
-template <int NB, int R, int FM, int CH, bool LONG>
+template <int NB, int R, int FM, int CH, bool LONG, bool GLU>
 hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) {
     ShotBatch B{};
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
@@ -507,10 +511,11 @@ hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) 
         P.y = d[i].y;
         P.eps = d[i].eps;
         P.w_scale = d[i].w_scale;
+        P.u = d[i].u;
     }
     int begin[kMaxShotBatch];
     const int64_t gx = fill_batch(B, begin, count, NB, R, M, K, N, &qmax);
-    return launch_batch(gemv_shot_kernel<NB, R, true, FM, CH, LONG>, B, begin, gx, qmax, s);
+    return launch_batch(gemv_shot_kernel<NB, R, true, FM, CH, LONG, GLU>, B, begin, gx, qmax, s);
 }
 
 #define BL_SHOT_SHAPES(CALL)                                                   \
@@ -524,9 +529,9 @@ hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) 
         default: return hipErrorInvalidValue;                                  \
     }
 
-template <int FM, int CH, bool LONG>
+template <int FM, int CH, bool LONG, bool GLU = false>
 hipError_t launch_fused_ch(const FusedDecode *d, int count, int v, hipStream_t s) {
-#define BL_F(NB_, R_) launch_shot_fused_nb<NB_, R_, FM, CH, LONG>(d, count, s)
+#define BL_F(NB_, R_) launch_shot_fused_nb<NB_, R_, FM, CH, LONG, GLU>(d, count, s)
     BL_SHOT_SHAPES(BL_F)
 #undef BL_F
 }
@@ -575,8 +580,10 @@ hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream
 hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hipStream_t s) {
     if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], kmax = 0, mmax = 0;
+    const bool glu = d[0].u != nullptr;
     for (int i = 0; i < count; ++i) {
         if (!shot_fused_supported(d[i].M, d[i].K) || !d[i].y) return hipErrorInvalidValue;
+        if ((d[i].u != nullptr) != glu || (glu && d[i].M != 1)) return hipErrorInvalidValue;
         M[i] = d[i].M;
         K[i] = d[i].K;
         N[i] = d[i].N;
@@ -587,6 +594,11 @@ hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hi
     const int v = pick_shape(M, K, N, count, shape, &rounds);
     // One token everywhere (the decode case): the kernel that normalises a
     // single row, whose code is a quarter of the general one's.
+    if (glu) {
+        if (kmax <= 4096) return launch_fused_ch<1, 4, false, true>(d, count, v, s);
+        if (kmax <= 8192) return launch_fused_ch<1, 8, false, true>(d, count, v, s);
+        return launch_fused_ch<1, 8, true, true>(d, count, v, s);
+    }
     if (mmax == 1) {
         if (kmax <= 4096) return launch_fused_ch<1, 4, false>(d, count, v, s);
         if (kmax <= 8192) return launch_fused_ch<1, 8, false>(d, count, v, s);

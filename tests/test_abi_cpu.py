@@ -182,3 +182,37 @@ def test_forward_batch_validation(L):
         assert fb(arr, 3, None, None) == code
     lp = ctypes.byref(api.Launch(api.PATH_GEMM, 1, 0, 0))
     assert fb(one, 1, lp, None) == api.ERR_INVALID_ARG
+
+
+def _ffn(x=A, gi=A, pg=A, pu=A, pd=A, gs=A, eps=1e-6, M=1, H=256, F=512, y=A, ws=A,
+         wsb=1 << 24, sg=0.02, su=0.02, sd=0.02):
+    return api.FfnDesc(x, gi, pg, sg, pu, su, pd, sd, gs, eps, M, H, F, y, ws, wsb)
+
+
+def test_ffn_workspace_bytes(L):
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    M, H, F = 4, 256, 640
+    expect = 2 * al(4 * M * F) + 2 * al(L.bitlinear_workspace_bytes(M, H)) + \
+        al(L.bitlinear_workspace_bytes(M, F))
+    assert L.bitlinear_ffn_workspace_bytes(M, H, F) == expect
+    assert L.bitlinear_ffn_workspace_bytes(0, H, F) == 0
+    assert L.bitlinear_ffn_workspace_bytes(M, 100, F) == 0
+    assert L.bitlinear_ffn_workspace_bytes(M, H, 100) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"M": 0}, api.ERR_SHAPE), ({"H": 200}, api.ERR_SHAPE), ({"F": 130}, api.ERR_SHAPE),
+    ({"x": 0}, api.ERR_INVALID_ARG), ({"pg": 0}, api.ERR_INVALID_ARG),
+    ({"pu": 0}, api.ERR_INVALID_ARG), ({"pd": 0}, api.ERR_INVALID_ARG),
+    ({"y": 0}, api.ERR_INVALID_ARG), ({"ws": 0}, api.ERR_INVALID_ARG),
+    ({"eps": 0.0}, api.ERR_INVALID_ARG), ({"eps": float("nan")}, api.ERR_INVALID_ARG),
+    ({"sd": float("inf")}, api.ERR_INVALID_ARG),
+    ({"x": MIS}, api.ERR_ALIGN), ({"gi": MIS}, api.ERR_ALIGN), ({"gs": MIS}, api.ERR_ALIGN),
+    ({"pd": MIS}, api.ERR_ALIGN), ({"y": MIS}, api.ERR_ALIGN), ({"ws": MIS}, api.ERR_ALIGN),
+    ({"wsb": 1000}, api.ERR_WORKSPACE),
+    # no RMSNorm anywhere: eps is not checked, the call reaches the alignment check
+    ({"gi": 0, "gs": 0, "eps": 0.0, "y": MIS}, api.ERR_ALIGN)])
+def test_ffn_validation(L, kw, code):
+    d = _ffn(**kw)
+    assert L.bitlinear_ffn_forward(ctypes.byref(d), None) == code
+    assert L.bitlinear_ffn_forward(None, None) == api.ERR_INVALID_ARG

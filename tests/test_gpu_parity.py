@@ -662,3 +662,166 @@ def test_forward_batch_mixes_norm_and_no_norm(torch, bl, orc):
     for it, single, y64, sh in zip(items, singles, refs, shapes):
         assert np.array_equal(host(it[5]), single), sh
         check_y(host(it[5]), y64)
+
+
+# ---------------------------------------------------------------- FFN block
+
+def ffn_case(seed, M, H, F, norm=True):
+    x = wl.activations(seed, M, H, 0.01)
+    gi = wl.gamma(seed + 1, H, "u0.8-1.2") if norm else None
+    gs = wl.gamma(seed + 2, F, "u0.8-1.2") if norm else None
+    wg, _ = wl.ternary(seed + 3, F, H, 1 / 3, 0.02)
+    wu, _ = wl.ternary(seed + 4, F, H, 1 / 3, 0.015)
+    wd, _ = wl.ternary(seed + 5, H, F, 1 / 3, 0.025)
+    return x, gi, gs, wg, wu, wd
+
+
+# (M, H, F, norm): M = 1 with F <= 8192 takes the two-launch form (the down
+# projection's quantisation inside the one-shot kernel); F > 8192 and M > 1
+# take the separate gated quantisation; M = 64 the tile kernel.
+FFN_SHAPES = [(1, 2560, 6912, True), (1, 256, 384, False), (1, 1024, 9216, True),
+              (3, 512, 1280, True), (17, 256, 384, True), (64, 1024, 2816, True),
+              (64, 256, 640, False)]
+
+
+@pytest.mark.parametrize("M,H,F,norm", FFN_SHAPES)
+def test_ffn_parity(torch, bl, orc, M, H, F, norm):
+    """Gate / up outputs and the down projection's int8 codes bit for bit,
+    y within 1e-5 of the oracle's fp64 block."""
+    announce("ffn", M, H, F, norm)
+    x, gi, gs, wg, wu, wd = ffn_case(1000 + M + F, M, H, F, norm)
+    gate, up, down = orc.pack_i2s(wg), orc.pack_i2s(wu), orc.pack_i2s(wd)
+    y64, g_r, u_r, a_r = orc.ffn(x, gi, 1e-6, gate, up, down, gs)
+    dv = lambda a: None if a is None else dev(torch, a)  # noqa: E731
+    D = [(dev(torch, p), s) for p, s in (gate, up, down)]
+    ws = torch.empty(bl.ffn_workspace_bytes(M, H, F), dtype=torch.uint8, device="cuda")
+    out = torch.full((M, H), float("nan"), dtype=torch.float32, device="cuda")
+    y = bl.ffn_forward(dev(torch, x), dv(gi), 1e-6, D[0], D[1], D[2], dv(gs), out=out,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    g, u = bl.ffn_workspace_views(ws, M, F)
+    assert np.array_equal(host(g).view(np.uint32), g_r.view(np.uint32))
+    assert np.array_equal(host(u).view(np.uint32), u_r.view(np.uint32))
+    check_y(host(y), y64)
+    # the same call again gives the same bits
+    out2 = bl.ffn_forward(dev(torch, x), dv(gi), 1e-6, D[0], D[1], D[2], dv(gs))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out2), host(y))
+
+
+def test_ffn_down_codes_match_oracle(torch, bl, orc):
+    """The down projection's q / inv / qsum (formed from g and u inside its
+    quantisation, never stored as a) equal the oracle's quantisation of
+    relu2_mul(g, u), on both down routes."""
+    for M, H, F in ((1, 2560, 6912), (5, 512, 1280)):
+        announce("ffn down codes", M, H, F)
+        x, gi, gs, wg, wu, wd = ffn_case(1100 + M, M, H, F)
+        gate, up, down = orc.pack_i2s(wg), orc.pack_i2s(wu), orc.pack_i2s(wd)
+        _, g_r, u_r, a_r = orc.ffn(x, gi, 1e-6, gate, up, down, gs)
+        assert np.array_equal(orc.relu2_mul(g_r, u_r), a_r)
+        D = [(dev(torch, p), s) for p, s in (gate, up, down)]
+        ws = torch.empty(bl.ffn_workspace_bytes(M, H, F), dtype=torch.uint8, device="cuda")
+        bl.ffn_forward(dev(torch, x), dev(torch, gi), 1e-6, D[0], D[1], D[2], dev(torch, gs),
+                       workspace=ws)
+        torch.cuda.synchronize()
+        al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+        off = 2 * al(4 * M * F) + 2 * al(bl.workspace_bytes(M, H))
+        q, inv, qs = bl.workspace_views(ws[off:], M, F)
+        q_r, inv_r, qs_r = orc.act_quant(a_r, gs, 1e-6)
+        assert np.array_equal(host(q), q_r)
+        assert np.array_equal(host(inv).view(np.uint32), inv_r.view(np.uint32))
+        assert np.array_equal(host(qs), qs_r)
+
+
+def test_ffn_structured_closed_form(torch, bl, orc):
+    """The selector-weight block of the oracle's pins, on the device."""
+    from tests.test_oracle_ffn import structured_case
+    for M, H, F, ni, ns in ((2, 128, 256, True, True), (1, 128, 384, False, True)):
+        announce("ffn structured", M, H, F)
+        x, gi, gs, _, (wg, wu, wd), _, _ = structured_case(40 + M + H, M, H, F, ni, ns)
+        gate, up, down = orc.pack_i2s(wg), orc.pack_i2s(wu), orc.pack_i2s(wd)
+        y64 = orc.ffn(x, gi, 1e-6, gate, up, down, gs)[0]
+        dv = lambda a: None if a is None else dev(torch, a)  # noqa: E731
+        D = [(dev(torch, p), s) for p, s in (gate, up, down)]
+        y = bl.ffn_forward(dev(torch, x), dv(gi), 1e-6, D[0], D[1], D[2], dv(gs))
+        torch.cuda.synchronize()
+        check_y(host(y), y64)
+
+
+def test_ffn_70b_shapes_sampled(torch, bl, orc):
+    """The 70B FFN (H = 8192, F = 28672) at M = 1 and 16: gate / up outputs
+    checked on sampled columns (the oracle over the sampled weight rows),
+    the down projection's codes against the oracle's quantisation of the
+    device's g and u, and y on sampled outputs."""
+    H, F = 8192, 28672
+    rng = np.random.default_rng(5)
+    cols = np.sort(rng.choice(F, 24, replace=False))
+    outs = np.sort(rng.choice(H, 24, replace=False))
+    for M in (1, 16):
+        announce("ffn 70b sampled", M)
+        x = wl.activations(1200 + M, M, H, 0.01)
+        gi = wl.gamma(1201, H, "u0.8-1.2")
+        gs = wl.gamma(1202, F, "u0.8-1.2")
+        gen = torch.Generator(device="cuda")
+        packs = []
+        for i, (n, k, sc) in enumerate(((F, H, 0.02), (F, H, 0.015), (H, F, 0.025))):
+            gen.manual_seed(1203 + i)
+            t = torch.randint(-1, 2, (n, k), generator=gen, device="cuda", dtype=torch.int8)
+            w = t.to(torch.float32).mul_(sc)
+            del t
+            p, s = bl.pack_i2s(w)
+            del w
+            packs.append((p, s))
+        torch.cuda.synchronize()
+        ws = torch.empty(bl.ffn_workspace_bytes(M, H, F), dtype=torch.uint8, device="cuda")
+        y = host(bl.ffn_forward(dev(torch, x), dev(torch, gi), 1e-6, packs[0], packs[1],
+                                packs[2], dev(torch, gs), workspace=ws))
+        torch.cuda.synchronize()
+        g, u = (host(t) for t in bl.ffn_workspace_views(ws, M, F))
+        # gate / up on sampled columns: fp32 outputs, bit for bit
+        q, inv, qs = orc.act_quant(x, gi, 1e-6)
+        for (p, s), full in ((packs[0], g), (packs[1], u)):
+            sub = orc.packed_rows(host(p), H, cols)
+            acc = orc.matmul_i2s(q, qs, sub, cols.size)
+            assert np.array_equal(orc.rescale_f32(acc, inv, s), full[:, cols])
+        # down: codes of relu2_mul(g, u) and sampled outputs
+        a = orc.relu2_mul(g, u)
+        qa, inva, qsa = orc.act_quant(a, gs, 1e-6)
+        sub = orc.packed_rows(host(packs[2][0]), F, outs)
+        y64 = orc.rescale(orc.matmul_i2s(qa, qsa, sub, outs.size), inva, packs[2][1])
+        check_y(y[:, outs], y64)
+        del packs, ws
+        torch.cuda.empty_cache()
+
+
+def test_ffn_graph_replay(torch, bl, orc):
+    """The block captured in a HIP graph and replayed with new inputs
+    matches the eager call each time."""
+    M, H, F = 1, 2560, 6912
+    x, gi, gs, wg, wu, wd = ffn_case(1300, M, H, F)
+    gate, up, down = orc.pack_i2s(wg), orc.pack_i2s(wu), orc.pack_i2s(wd)
+    D = [(dev(torch, p), s) for p, s in (gate, up, down)]
+    X, GI, GS = dev(torch, x), dev(torch, gi), dev(torch, gs)
+    ws = torch.empty(bl.ffn_workspace_bytes(M, H, F), dtype=torch.uint8, device="cuda")
+    out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bl.ffn_forward(X, GI, 1e-6, D[0], D[1], D[2], GS, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bl.ffn_forward(X, GI, 1e-6, D[0], D[1], D[2], GS, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    announce("ffn graph replay")
+    for r in range(3):
+        xr = wl.activations(1310 + r, M, H, 0.01)
+        X.copy_(dev(torch, xr))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(out).copy()
+        eager = host(bl.ffn_forward(dev(torch, xr), GI, 1e-6, D[0], D[1], D[2], GS))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager), r
+        check_y(got, orc.ffn(xr, gi, 1e-6, gate, up, down, gs)[0])
