@@ -16,7 +16,7 @@ not from the 256 MB last-level cache.
 Prints one JSON line (see the "metric" of the workload).  Options:
   --gpus N (only 1 is supported), --steps K, --warmup W,
   --workload decode|prefill|ffn70b-1|ffn70b-16|sweep-M,
-  --no-cpu-baseline, --no-secondary, --pack-only.
+  --no-cpu-baseline, --no-secondary, --pack-only, --ffn-only.
 """
 from __future__ import annotations
 
@@ -232,6 +232,85 @@ def secondary_prefill(torch, api, steps, warmup):
                             "frac_of_int8_peak": round(tops_sq / INT8_PEAK_TOPS, 4)}}
 
 
+def secondary_ffn(torch, api, steps, warmup):
+    """The BitNet FFN block (gate, up, squared-ReLU product, down with its
+    sub-norm) as one bitlinear_ffn_forward call per step, on the 2B4T
+    shapes (H = 2560, F = 6912) at decode (M = 1, GB/s of algorithmic
+    bytes) and prefill (M = 512, int8 TOPS), and the 70B shapes (H = 8192,
+    F = 28672) at M = 1.  Beside it the same block from the plain entry
+    points (gate and up in one forward_batch call, relu(g)^2 * u in torch,
+    then the down forward).  Weights: seeded ternary x scale generated on
+    the device, packed copies rotated past the last-level cache."""
+    from ternary_bit_linear_amd import workloads as wl
+    res = {}
+    for name, M, H, F in (("2b4t_decode", 1, 2560, 6912), ("2b4t_prefill", 512, 2560, 6912),
+                          ("70b_decode", 1, 8192, 28672)):
+        gen = torch.Generator(device="cuda")
+        packs = []
+        for i, (n, k, sc) in enumerate(((F, H, 0.02), (F, H, 0.015), (H, F, 0.025))):
+            gen.manual_seed(6000 + i)
+            t = torch.randint(-1, 2, (n, k), generator=gen, device="cuda", dtype=torch.int8)
+            w = t.to(torch.float32).mul_(sc)
+            del t
+            packs.append(api.pack_i2s(w))
+            del w
+        wbytes = 3 * H * F // 4
+        copies = max(2, -(-ROTATE_BYTES // wbytes))
+        rot = [[(p.clone() if c else p, sc) for p, sc in packs] for c in range(copies)]
+        x = torch.from_numpy(wl.activations(6100, M, H, 0.01)).cuda()
+        gi = torch.from_numpy(wl.gamma(6101, H, "u0.8-1.2")).cuda()
+        gs = torch.from_numpy(wl.gamma(6102, F, "u0.8-1.2")).cuda()
+        y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        ws = torch.empty(api.ffn_workspace_bytes(M, H, F), dtype=torch.uint8, device="cuda")
+        g_t = torch.empty((M, F), dtype=torch.float32, device="cuda")
+        u_t = torch.empty_like(g_t)
+        a_t = torch.empty_like(g_t)
+        ws_g, ws_u = api.new_workspace(M, H), api.new_workspace(M, H)
+        ws_d = api.new_workspace(M, F)
+
+        def fused(r):
+            gp, up, dp = rot[r % copies]
+            api.ffn_forward(x, gi, 1e-6, gp, up, dp, gs, out=y, workspace=ws)
+
+        def plain(r):
+            (gp, sg), (up, su), (dp, sd) = rot[r % copies]
+            api.forward_batch([(x, gp, sg, gi, 1e-6, g_t, ws_g), (x, up, su, gi, 1e-6, u_t, ws_u)])
+            torch.mul(torch.relu(g_t).square_(), u_t, out=a_t)
+            api.forward(a_t, dp, sd, gs, 1e-6, H, out=y, workspace=ws_d)
+
+        def timed(fn):
+            gw = capture(torch, lambda: [fn(r) for r in range(max(1, warmup))])
+            gt = capture(torch, lambda: [fn(warmup + r) for r in range(steps)])
+            gw.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gt.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            del gw, gt
+            return e0.elapsed_time(e1) * 1e-3 / steps  # s per step
+
+        t_f = timed(fused)
+        t_p = timed(plain)
+        nbytes = wbytes + 4 * M * H + 4 * H + 4 * F + 4 * M * H
+        ops = 2 * M * 3 * H * F
+        r = {"M": M, "H": H, "F": F, "us": round(t_f * 1e6, 2),
+             "plain_entry_points_us": round(t_p * 1e6, 2),
+             "speedup_vs_plain": round(t_p / t_f, 3)}
+        if M <= 16:
+            r.update({"GBs": round(nbytes / t_f / 1e9, 1),
+                      "frac_of_hbm_peak": round(nbytes / t_f / 1e9 / HBM_PEAK_GBS, 4),
+                      "algorithmic_bytes": nbytes})
+        else:
+            r.update({"TOPS": round(ops / t_f / 1e12, 1),
+                      "frac_of_int8_peak": round(ops / t_f / 1e12 / INT8_PEAK_TOPS, 4)})
+        res[name] = r
+        del rot, packs, x, gi, gs, y, ws, g_t, u_t, a_t, ws_g, ws_u, ws_d
+        torch.cuda.empty_cache()
+    return {"workload": "BitNet FFN block: down(sub_norm(relu(gate(x))^2 * up(x)))", **res}
+
+
 def secondary_pack(torch, api, reps=5):
     """I2_S packing of the packing workload (fp32 ternary x 0.02, N = 8192 x
     K = 28672; seeded on the device): GB/s of algorithmic bytes (4NK read +
@@ -268,6 +347,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--pack-only", action="store_true",
                     help="time only the I2_S packer over --steps calls and print its line")
+    ap.add_argument("--ffn-only", action="store_true",
+                    help="time only the FFN block legs (--steps steps each) and print their line")
     ap.add_argument("--pmc-app", action="store_true",
                     help="no timing: run --steps steps of the workload and a 256 MiB device "
                          "copy (the calibration kernel for HBM byte counters), then exit")
@@ -286,6 +367,9 @@ def main():
 
     if args.pack_only:
         print(json.dumps(secondary_pack(torch, api, reps=max(1, args.steps))), flush=True)
+        return
+    if args.ffn_only:
+        print(json.dumps(secondary_ffn(torch, api, max(1, args.steps), args.warmup)), flush=True)
         return
     work = workload_by_name(args.workload)
     prep = Prepared(torch, api, work)
@@ -370,6 +454,8 @@ def main():
         out["secondary"] = secondary_prefill(torch, api, max(20, args.steps // 4), 5)
         torch.cuda.empty_cache()
         out["secondary"]["pack"] = secondary_pack(torch, api)
+        torch.cuda.empty_cache()
+        out["secondary"]["ffn"] = secondary_ffn(torch, api, max(20, args.steps // 4), 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work)
     print(json.dumps(out), flush=True)

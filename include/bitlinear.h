@@ -243,11 +243,13 @@ bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum,
  *   g = BitLinear(x; gate, gamma_in), u = BitLinear(x; up, gamma_in)   fp32 [M][F]
  *   a = (max(g, 0) * max(g, 0)) * u                                    fp32 [M][F]
  *   y = BitLinear(a; down, gamma_sub)                                  fp32 [M][H]
- * a is never stored: the down projection's quantisation forms it from g and
- * u as it reads them.  At M = 1 with F <= 8192 the block is two launches
- * (gate and up in one, the down projection with its quantisation in the
- * other); otherwise gate and up take bitlinear_forward_batch's launches and
- * the down projection one quantisation and one contraction launch.
+ * For F <= 8192, a is never stored: the down projection's quantisation
+ * forms it from g and u as it reads them.  At M = 1 with F <= 8192 the
+ * block is two launches (gate and up in one, the down projection with its
+ * quantisation in the other); otherwise gate and up take
+ * bitlinear_forward_batch's launches and the down projection one
+ * quantisation and one contraction launch (for F > 8192, after one
+ * elementwise launch that stores a in the workspace).
  *   x: device fp32 [M][H]; y: device fp32 [M][H] (every element written).
  *   packed_gate / packed_up: I2_S of W [F][H]; packed_down: I2_S of W [H][F]
  *             (H and F multiples of 128); s_*: their per-tensor scales.
@@ -257,7 +259,7 @@ bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum,
  *   workspace: device, >= bitlinear_ffn_workspace_bytes(M, H, F) bytes,
  *             16-byte aligned; after the call it holds g at offset 0 and u
  *             at offset align256(4*M*F) (fp32 [M][F] each), then the three
- *             projections' q / inv / qsum.
+ *             projections' q / inv / qsum (and a, when F > 8192).
  *   No output may overlap an input.  Errors as bitlinear_forward; all
  *   checks run before anything is enqueued.  Asynchronous on `stream`. */
 typedef struct {

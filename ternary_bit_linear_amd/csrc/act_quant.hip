@@ -73,6 +73,16 @@ __global__ __launch_bounds__(256) void act_quant_glu_kernel(
                                               u + (size_t)m * K);
 }
 
+// a = relu2_mul(g, u) over n elements (n % 4 == 0), float4 per thread, for
+// rows too long for the gated quantisation to hold in registers.
+__global__ __launch_bounds__(256) void relu2_mul_kernel(const float4 *__restrict__ g,
+                                                        const float4 *__restrict__ u,
+                                                        float4 *__restrict__ a, int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        a[i] = relu2_mul4(g[i], u[i]);
+}
+
 // Batched form: up to 8 problems, one block per token row of any of them.
 // b0..b7: first block of each problem (INT_MAX past the last), leading the
 // argument list so that the build's kernel-argument preload puts them in
@@ -165,6 +175,15 @@ hipError_t launch_act_quant_glu(const float *g, const float *u, const float *gam
     else
         hipLaunchKernelGGL((act_quant_glu_kernel<8, true>), grid, block, 0, s, g, u, gamma, eps,
                            (int)K, q, inv, qsum);
+    return hipGetLastError();
+}
+
+hipError_t launch_relu2_mul(const float *g, const float *u, float *a, int64_t n, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n4 + 255) / 256, 4096));
+    hipLaunchKernelGGL(relu2_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(g), reinterpret_cast<const float4 *>(u),
+                       reinterpret_cast<float4 *>(a), n4);
     return hipGetLastError();
 }
 

@@ -557,6 +557,10 @@ hipError_t launch_act_quant_glu(const float *g, const float *u, const float *gam
                                 int64_t M, int64_t K, int8_t *q, float *inv, int32_t *qsum,
                                 hipStream_t s);
 
+// a = relu2_mul(g, u) elementwise over n floats (n % 4 == 0, 16-byte
+// aligned arrays).
+hipError_t launch_relu2_mul(const float *g, const float *u, float *a, int64_t n, hipStream_t s);
+
 // Batched quantisation: up to 8 independent (x, gamma, eps, M, K) with
 // K <= 8192 each, one launch, bit-identical to launch_act_quant per problem.
 struct ActQuantDesc {

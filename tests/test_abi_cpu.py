@@ -195,6 +195,11 @@ def test_ffn_workspace_bytes(L):
     expect = 2 * al(4 * M * F) + 2 * al(L.bitlinear_workspace_bytes(M, H)) + \
         al(L.bitlinear_workspace_bytes(M, F))
     assert L.bitlinear_ffn_workspace_bytes(M, H, F) == expect
+    # rows longer than 8192 also hold a = relu(g)^2 * u
+    F = 9216
+    expect = 3 * al(4 * M * F) + 2 * al(L.bitlinear_workspace_bytes(M, H)) + \
+        al(L.bitlinear_workspace_bytes(M, F))
+    assert L.bitlinear_ffn_workspace_bytes(M, H, F) == expect
     assert L.bitlinear_ffn_workspace_bytes(0, H, F) == 0
     assert L.bitlinear_ffn_workspace_bytes(M, 100, F) == 0
     assert L.bitlinear_ffn_workspace_bytes(M, H, 100) == 0
