@@ -380,7 +380,7 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
     const Workspace wd = carve(w.ws_down, M, F);
     const int64_t Ms[1] = {M}, Ks[1] = {F}, Ns[1] = {H};
     if (M == 1 && F <= 8 * 1024 && bl::shot_fused_supported(M, F) &&
-        bl::shot_rounds(Ms, Ks, Ns, 1) == 1) {
+        bl::shot_rounds(Ms, Ks, Ns, 1, true) == 1) {
         bl::FusedDecode f;
         f.x = w.g;
         f.gamma = d.gamma_sub;

@@ -625,7 +625,7 @@ int shot_num_shapes();
 // Rounds of workgroups the device needs for these problems in the one-shot
 // form with its own choice of launch shape (INT64_MAX: not supported).  One
 // round means every workgroup is resident at once.
-int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count);
+int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count, bool fused);
 bool shot_supported(int64_t M, int64_t K);
 hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream_t s);
 // The same with the RMSNorm + quantisation fused in (M <= kFuseMaxM): every

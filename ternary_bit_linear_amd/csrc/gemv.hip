@@ -826,7 +826,10 @@ static bool is_shot(int variant) {
 
 // Automatic choice of the persistent form's launch shape (measured best on
 // the decode shapes of 2560- to 28672-wide layers).
-static int auto_variant(int64_t) { return 1; }
+// Persistent-form shape for M tokens: one tile per wave for one token, two
+// up to 4 tokens, four beyond (each tile's activation fragments serve more
+// rows as M grows; measured at K = 16384..28672).
+static int auto_variant(int64_t M) { return M <= 1 ? 1 : M <= 4 ? 6 : 8; }
 
 #define BL_GEMV_SWITCH(CALL)                                                  \
     switch (v) {                                                              \
@@ -846,15 +849,18 @@ hipError_t launch_gemv(const int8_t *q, const float *inv, const int32_t *qsum,
                        float *y, int32_t *acc, int variant, hipStream_t s) {
     const int64_t mg = M < 16 ? M : 16;
     const int mode = mg * K <= kGemvStageMaxLds ? 1 : 2;
-    // Automatic: the one-shot form when all of its workgroups fit on the
-    // device at once, else the persistent form.
+    // Automatic: the one-shot form for rows up to 16384, also when its
+    // workgroups take several rounds of the device (measured faster than the
+    // persistent form there, by up to 1.4x at N = 28672); the persistent
+    // form for longer rows (faster at K = 28672).
     const bool shot = is_shot(variant) ? shot_supported(M, K)
-                                       : variant == 0 && shot_rounds(&M, &K, &N, 1) == 1;
+                                       : variant == 0 && shot_supported(M, K) && K <= 16384 &&
+                                             shot_rounds(&M, &K, &N, 1, false) != INT64_MAX;
     if (shot) {
         const ShotDecode d{q, inv, qsum, packed, y, acc, w_scale, M, K, N};
         return launch_gemv_shot(&d, 1, is_shot(variant) ? shot_shape_of(variant) : 0, s);
     }
-    const int v = variant > 0 && variant <= kNumShapes ? variant : auto_variant(K);
+    const int v = variant > 0 && variant <= kNumShapes ? variant : auto_variant(M);
 #define BL_SEP(R_, U_, D_) \
     launch_shape_sep<R_, U_, D_>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, mode, s)
     BL_GEMV_SWITCH(BL_SEP)
@@ -862,11 +868,9 @@ hipError_t launch_gemv(const int8_t *q, const float *inv, const int32_t *qsum,
 }
 
 hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipStream_t s) {
-    int64_t max_k = 0;
     bool fits = true;
     int64_t M[8], K[8], N[8];
     for (int i = 0; i < count; ++i) {
-        max_k = std::max<int64_t>(max_k, d[i].K);
         fits = fits && shot_fused_supported(d[i].M, d[i].K);
         if (i < 8) {
             M[i] = d[i].M;
@@ -877,10 +881,11 @@ hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipSt
     // Automatic: the one-shot form when all of its workgroups fit on the
     // device at once, else the persistent form.
     const bool shot = fits && count <= 8 &&
-                      (is_shot(variant) || (variant == 0 && shot_rounds(M, K, N, count) == 1));
+                      (is_shot(variant) || (variant == 0 && shot_rounds(M, K, N, count, true) == 1));
     if (shot)
         return launch_gemv_shot_fused(d, count, is_shot(variant) ? shot_shape_of(variant) : 0, s);
-    const int v = variant > 0 && variant <= kNumShapes ? variant : auto_variant(max_k);
+    // (fused: one tile per wave, the shape measured for one token)
+    const int v = variant > 0 && variant <= kNumShapes ? variant : 1;
 #define BL_FUSED(R_, U_, D_) launch_shape_fused<R_, U_, D_>(d, count, s)
     BL_GEMV_SWITCH(BL_FUSED)
 #undef BL_FUSED

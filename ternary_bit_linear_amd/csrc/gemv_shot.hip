@@ -411,11 +411,14 @@ int device_cus() {
 // from LDS and registers; more than one round leaves the later workgroups'
 // loads waiting for earlier ones to finish); then a score: the share of the
 // allocated weight LDS that stays unused (rows whose K share is shorter
-// than NB batches), weighted by bytes, plus small measured preferences (two
-// tiles per wave over one, one workgroup per CU the least, four tiles per
-// wave rarely).  *rounds_out receives the chosen shape's rounds.
+// than NB batches), weighted by bytes, plus small measured preferences.
+// With the quantisation fused in, two tiles per wave beat one (half the
+// workgroups repeat the quantisation); over q from global memory one tile
+// per wave is the faster (measured on MI355X, M = 1..4, K = 2560..8192: up
+// to 1.4x).  One workgroup per CU costs extra, four tiles per wave more.
+// *rounds_out receives the chosen shape's rounds.
 int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, int pref,
-               int64_t *rounds_out) {
+               int64_t *rounds_out, bool fused) {
     auto fits = [&](int nb) {
         for (int i = 0; i < count; ++i)
             if (shot_ks(K[i], nb) == 0) return false;
@@ -459,7 +462,10 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
         const int64_t lds = (int64_t)h.nb * h.R * 8192 + q + 256;
         const int64_t per_cu = std::min<int64_t>(h.occupancy, (160 * 1024) / lds);
         double score = 100.0 * (1.0 - used / total);
-        score += h.R == 1 ? 10.0 : h.R == 4 ? 50.0 : 0.0;
+        if (fused)
+            score += h.R == 1 ? 10.0 : h.R == 4 ? 50.0 : 0.0;
+        else
+            score += h.R == 2 ? 10.0 : h.R == 4 ? 50.0 : 0.0;
         score += per_cu == 1 ? 20.0 : 0.0;
         if (best < 0 || rounds < best_rounds || (rounds == best_rounds && score < best_score)) {
             best = v;
@@ -547,11 +553,11 @@ hipError_t launch_sep(const ShotDecode *d, int count, int v, hipStream_t s) {
 
 int shot_num_shapes() { return kNumShotShapes; }
 
-int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count) {
+int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count, bool fused) {
     for (int i = 0; i < count; ++i)
         if (!shot_supported(M[i], K[i])) return INT64_MAX;
     int64_t rounds;
-    return pick_shape(M, K, N, count, 0, &rounds) < 0 ? INT64_MAX : rounds;
+    return pick_shape(M, K, N, count, 0, &rounds, fused) < 0 ? INT64_MAX : rounds;
 }
 
 bool shot_supported(int64_t M, int64_t K) {
@@ -573,7 +579,7 @@ hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream
         N[i] = d[i].N;
     }
     int64_t rounds;
-    const int v = pick_shape(M, K, N, count, shape, &rounds);
+    const int v = pick_shape(M, K, N, count, shape, &rounds, false);
     return y ? launch_sep<true>(d, count, v, s) : launch_sep<false>(d, count, v, s);
 }
 
@@ -591,7 +597,7 @@ hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hi
         mmax = std::max<int64_t>(mmax, d[i].M);
     }
     int64_t rounds;
-    const int v = pick_shape(M, K, N, count, shape, &rounds);
+    const int v = pick_shape(M, K, N, count, shape, &rounds, true);
     // One token everywhere (the decode case): the kernel that normalises a
     // single row, whose code is a quarter of the general one's.
     if (glu) {
