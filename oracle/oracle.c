@@ -382,3 +382,31 @@ int oracle_ffn(const float *x, const float *gamma_in, float eps, int64_t M, int6
     free(xn); free(q); free(inv); free(qsum); free(acc);
     return st;
 }
+
+/* bf16 <-> fp32 for the bf16 activation I/O variant (the pages fix no
+ * half-precision format; the reading is the IEEE-style bfloat16: the top 16
+ * bits of an fp32, rounded to nearest with ties to even).
+ *   to fp32: exact (the 16 bits become the high half of the fp32 word).
+ *   from fp32: round to nearest even on the 16 dropped bits; NaN stays a
+ *   quiet NaN with its sign. */
+int oracle_bf16_to_f32(const uint16_t *in, int64_t n, float *out) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u = (uint32_t)in[i] << 16;
+        memcpy(out + i, &u, 4);
+    }
+    return ORC_OK;
+}
+
+int oracle_f32_to_bf16(const float *in, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u = float_bits(in[i]);
+        if ((u & 0x7fffffffu) > 0x7f800000u) {
+            out[i] = (uint16_t)((u >> 16) | 0x0040u);
+            continue;
+        }
+        const uint32_t lsb = (u >> 16) & 1u;
+        u += 0x7fffu + lsb;
+        out[i] = (uint16_t)(u >> 16);
+    }
+    return ORC_OK;
+}

@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_rescale_f32.restype = ctypes.c_int
         L.oracle_rescale_f32.argtypes = [p, p, ctypes.c_float, i64, i64, p]
         f = ctypes.c_float
+        L.oracle_bf16_to_f32.restype = ctypes.c_int
+        L.oracle_bf16_to_f32.argtypes = [p, i64, p]
+        L.oracle_f32_to_bf16.restype = ctypes.c_int
+        L.oracle_f32_to_bf16.argtypes = [p, i64, p]
         L.oracle_relu2_mul.restype = ctypes.c_int
         L.oracle_relu2_mul.argtypes = [p, p, i64, p]
         L.oracle_ffn.restype = ctypes.c_int
@@ -210,6 +214,58 @@ def rescale_f32(acc: np.ndarray, inv: np.ndarray, w_scale: float) -> np.ndarray:
     if st != OK:
         raise OracleError(st, "rescale_f32")
     return y
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> fp32, exact."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float32)
+    lib().oracle_bf16_to_f32(_ptr(bits), bits.size, _ptr(out))
+    return out
+
+
+def f32_to_bf16(v: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    v = _f32(v)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_f32_to_bf16(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Activations of the given I/O type to fp32 (exact for every type)."""
+    if dtype == "f32":
+        return _f32(x)
+    if dtype == "bf16":
+        return bf16_to_f32(x)
+    if dtype == "f16":
+        return np.asarray(x, np.float16).astype(np.float32)
+    raise ValueError(dtype)
+
+
+def from_f32(y: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 outputs rounded to the I/O type (nearest, ties to even): bf16 as
+    uint16 bit patterns, f16 by numpy's IEEE conversion."""
+    if dtype == "f32":
+        return _f32(y)
+    if dtype == "bf16":
+        return f32_to_bf16(y)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):  # beyond 65504 rounds to inf, as IEEE says
+            return _f32(y).astype(np.float16)
+    raise ValueError(dtype)
+
+
+def forward_io(x: np.ndarray, x_dtype: str, packed: np.ndarray, w_scale: float, gamma,
+               eps: float, N: int, y_dtype: str) -> np.ndarray:
+    """Forward with half-precision activation I/O: x of x_dtype (bf16 as
+    uint16 bits) is widened exactly to fp32, the fp32 path runs as in
+    forward(), and the fp32 output (float)acc * (w_scale / inv) is rounded
+    to y_dtype."""
+    xf = to_f32(np.atleast_2d(x), x_dtype)
+    q, inv, qsum = act_quant(xf, gamma, eps)
+    acc = matmul_i2s(q, qsum, packed, N)
+    return from_f32(rescale_f32(acc, inv, w_scale), y_dtype)
 
 
 def relu2_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
