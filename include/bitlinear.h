@@ -235,6 +235,31 @@ bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum,
                                   int64_t K, int64_t N, int32_t *acc,
                                   const bl_launch *launch, void *stream);
 
+/* Activation storage types of bitlinear_forward_io. */
+typedef enum { BL_F32 = 0, BL_BF16 = 1, BL_F16 = 2 } bl_dtype;
+
+/* Workspace bytes of bitlinear_forward_io: the forward workspace of (M, K)
+ * followed by an int32 accumulator [M][N] (0 if a size is invalid). */
+size_t bitlinear_io_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* bitlinear_forward with the activations stored as x_dtype and the output
+ * as y_dtype (bl_dtype) [HF-38087 "What does this PR do?": the same layer;
+ * the page fixes no storage type].  x is widened exactly to fp32 as it is
+ * loaded, the fp32 path runs unchanged (same q, inv, qsum, acc), and
+ * y = (float)acc * (w_scale / inv) is rounded to y_dtype to nearest with
+ * ties to even (bf16: the high 16 bits of the fp32 word after rounding;
+ * fp16: IEEE binary16, overflow to inf).  With both types BL_F32 the bits
+ * equal bitlinear_forward's.  Three launches: quantisation, contraction to
+ * the int32 accumulator in the workspace, rescale.
+ *   x: device [M][K] of x_dtype; y: device [M][N] of y_dtype; both 16-byte
+ *   aligned.  Other arguments and errors as bitlinear_forward; an unknown
+ *   dtype is BL_ERR_INVALID_ARG.  workspace: >=
+ *   bitlinear_io_workspace_bytes(M, K, N).  Asynchronous on `stream`. */
+bl_status bitlinear_forward_io(const void *x, int x_dtype, const uint8_t *packed_w,
+                               float w_scale, const float *gamma, float eps, int64_t M,
+                               int64_t K, int64_t N, void *y, int y_dtype, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* BitNet FFN block [HF-38087, the BitNetMLP excerpt of the review thread:
  * y = down(ffn_sub_norm(act(gate(x)) * up(x))); CPPB-7 summary bullet and
  * the bitnet-b1.58 graph commit: the 2B4T activation is squared ReLU].

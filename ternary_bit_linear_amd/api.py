@@ -67,6 +67,8 @@ SIGNATURES = {
     "bitlinear_forward_batch": (_i, [ctypes.POINTER(ForwardDesc), _i, ctypes.POINTER(Launch), _p]),
     "bitlinear_act_quant": (_i, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
     "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_io_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_forward_io": (_i, [_p, _i, _p, _f, _p, _f, _i64, _i64, _i64, _p, _i, _p, _sz, _p]),
     "bitlinear_ffn_forward": (_i, [ctypes.POINTER(FfnDesc), _p]),
     "bitlinear_matmul_i2s": (_i, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "bitlinear_matmul_i2s_ex": (_i, [_p, _p, _p, _i64, _i64, _i64, _p,
@@ -291,3 +293,37 @@ def ffn_workspace_views(workspace, M: int, F: int):
     g = workspace[: 4 * M * F].view(torch.float32).view(M, F)
     u = workspace[gb: gb + 4 * M * F].view(torch.float32).view(M, F)
     return g, u
+
+
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
+
+
+def _io_dtype(t):
+    torch = _torch()
+    m = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+    if t not in m:
+        raise TypeError(f"unsupported activation type {t}")
+    return m[t]
+
+
+def forward_io(x, packed, w_scale: float, gamma, eps: float = 1e-6, N: int | None = None,
+               y_dtype=None, out=None, workspace=None):
+    """forward() with x and y in float32 / bfloat16 / float16 (x's dtype is
+    read from the tensor; y_dtype defaults to x's)."""
+    torch = _torch()
+    M, K = x.shape
+    if N is None:
+        N = (packed.numel() - 32) * 4 // K
+    if out is None:
+        out = torch.empty((M, N), dtype=y_dtype or x.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib().bitlinear_io_workspace_bytes(M, K, N)),
+                                dtype=torch.uint8, device=x.device)
+    if not (x.is_cuda and x.is_contiguous() and out.is_cuda and out.is_contiguous()):
+        raise ValueError("x and out must be contiguous HIP tensors")
+    _check(lib().bitlinear_forward_io(
+        ctypes.c_void_p(x.data_ptr()), _io_dtype(x.dtype), _dev(packed, torch.uint8, "packed"),
+        w_scale, _gamma(gamma), eps, M, K, N, ctypes.c_void_p(out.data_ptr()),
+        _io_dtype(out.dtype), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream()), "forward_io")
+    return out

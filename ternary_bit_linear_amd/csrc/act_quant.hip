@@ -31,31 +31,102 @@ struct GlobalRowSink {
     }
 };
 
+// XT: the activations' storage type (float, bf16_t, _Float16), widened to
+// fp32 as they are loaded.
+template <typename XT = float>
 __global__ __launch_bounds__(64) void act_quant_wave_kernel(
-    const float *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
+    const XT *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
     int8_t *__restrict__ q, float *__restrict__ inv, int32_t *__restrict__ qsum) {
     const int m = blockIdx.x;
     GlobalRowSink sink{q + (size_t)m * K, inv + m, qsum + m};
-    wave_act_quant_row<1>(x + (size_t)m * K, gamma, eps, K, sink);
+    wave_act_quant_row<1, XT>(x + (size_t)m * K, gamma, eps, K, sink);
 }
 
-template <int CH>
+template <int CH, typename XT = float>
 __global__ __launch_bounds__(256) void act_quant_block_kernel(
-    const float *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
+    const XT *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
     int8_t *__restrict__ q, float *__restrict__ inv, int32_t *__restrict__ qsum) {
     __shared__ float red[kRedWords];
     const int m = blockIdx.x;
     GlobalRowSink sink{q + (size_t)m * K, inv + m, qsum + m};
-    block_act_quant_row<CH, false>(x + (size_t)m * K, gamma, eps, K, red, sink, [] {});
+    block_act_quant_row<CH, false, true, false, XT>(x + (size_t)m * K, gamma, eps, K, red, sink,
+                                                    [] {});
 }
 
+template <typename XT = float>
 __global__ __launch_bounds__(256) void act_quant_long_kernel(
-    const float *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
+    const XT *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
     int8_t *__restrict__ q, float *__restrict__ inv, int32_t *__restrict__ qsum) {
     __shared__ float red[kRedWords];
     const int m = blockIdx.x;
     GlobalRowSink sink{q + (size_t)m * K, inv + m, qsum + m};
-    block_act_quant_row<8, true>(x + (size_t)m * K, gamma, eps, K, red, sink, [] {});
+    block_act_quant_row<8, true, true, false, XT>(x + (size_t)m * K, gamma, eps, K, red, sink,
+                                                  [] {});
+}
+
+// y[m][n] = (float)acc[m][n] * (w_scale / inv[m]) rounded to the output
+// type YT (bf16_t, _Float16: to nearest, ties to even, NaN kept quiet).
+// Two outputs per thread.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// fp32 -> IEEE binary16 bits, nearest even, by integer operations (exact
+// rounding for subnormal results too, whatever the fp16 denormal mode):
+// NaN stays a quiet NaN, from 65520 up the result is inf.
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return (uint16_t)(sign | 0x7E00u | ((a >> 13) & 0x3FFu));
+    if (a >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);  // >= 65520
+    if (a >= 0x38800000u) {                                    // >= 2^-14: normal
+        const uint32_t r = a - 0x38000000u;                    // rebias 127 -> 15
+        return (uint16_t)(sign | ((r + 0xFFFu + ((r >> 13) & 1u)) >> 13));
+    }
+    // subnormal or zero: units of 2^-24; the scaling is exact, rintf rounds
+    // to nearest even (1024 units is the smallest normal, encoded alike)
+    const float v = __uint_as_float(a) * 16777216.0f;
+    return (uint16_t)(sign | (uint32_t)rintf(v));
+}
+
+template <typename YT>
+__device__ __forceinline__ uint16_t to_half_bits(float v) {
+    if constexpr (std::is_same<YT, bf16_t>::value) return f32_to_bf16_rne(v);
+    else return f32_to_f16_rne(v);
+}
+
+template <typename YT>
+__global__ __launch_bounds__(256) void rescale_kernel(const int32_t *__restrict__ acc,
+                                                      const float *__restrict__ inv, float w_scale,
+                                                      int64_t M, int64_t N, YT *__restrict__ y) {
+    const int64_t total = M * N;
+    const int64_t pairs = total / 2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = t; i < pairs; i += stride) {
+        const int64_t e = 2 * i;
+        const int64_t m0 = e / N, m1 = (e + 1) / N;  // a pair may straddle two rows
+        const float c0 = w_scale / inv[m0];
+        const float c1 = m1 == m0 ? c0 : w_scale / inv[m1];
+        const int2 a = *reinterpret_cast<const int2 *>(acc + e);
+        const float v0 = (float)a.x * c0, v1 = (float)a.y * c1;
+        if constexpr (std::is_same<YT, float>::value) {
+            *reinterpret_cast<float2 *>(y + e) = make_float2(v0, v1);
+        } else {
+            *reinterpret_cast<uint32_t *>(y + e) =
+                (uint32_t)to_half_bits<YT>(v0) | ((uint32_t)to_half_bits<YT>(v1) << 16);
+        }
+    }
+    if ((total & 1) && t == 0) {  // odd element count: the last one alone
+        const int64_t e = total - 1;
+        const float v = (float)acc[e] * (w_scale / inv[e / N]);
+        if constexpr (std::is_same<YT, float>::value)
+            y[e] = v;
+        else
+            reinterpret_cast<uint16_t *>(y)[e] = to_half_bits<YT>(v);
+    }
 }
 
 // The FFN's down-projection input: the row is relu2_mul(g, u) of the gate
@@ -121,11 +192,39 @@ __global__ __launch_bounds__(256) void act_quant_batch_kernel(int b0, int b1, in
     block_act_quant_row<CH, false>(P.x + (size_t)m * K, P.gamma, P.eps, K, red, sink, [] {});
 }
 
-template <int CH>
-hipError_t launch_block(const float *x, const float *gamma, float eps, int64_t M, int64_t K,
+template <int CH, typename XT>
+hipError_t launch_block(const XT *x, const float *gamma, float eps, int64_t M, int64_t K,
                         int8_t *q, float *inv, int32_t *qsum, hipStream_t s) {
-    hipLaunchKernelGGL(act_quant_block_kernel<CH>, dim3((unsigned)M), dim3(256), 0, s, x, gamma,
+    hipLaunchKernelGGL((act_quant_block_kernel<CH, XT>), dim3((unsigned)M), dim3(256), 0, s, x,
+                       gamma, eps, (int)K, q, inv, qsum);
+    return hipGetLastError();
+}
+
+template <typename XT>
+hipError_t launch_act_quant_t(const XT *x, const float *gamma, float eps, int64_t M, int64_t K,
+                              int8_t *q, float *inv, int32_t *qsum, hipStream_t s) {
+    if (K <= 1024) {
+        hipLaunchKernelGGL((act_quant_wave_kernel<XT>), dim3((unsigned)M), dim3(64), 0, s, x,
+                           gamma, eps, (int)K, q, inv, qsum);
+        return hipGetLastError();
+    }
+    if (K <= 4 * 1024) return launch_block<4>(x, gamma, eps, M, K, q, inv, qsum, s);
+    if (K <= 8 * 1024) return launch_block<8>(x, gamma, eps, M, K, q, inv, qsum, s);
+    if (K <= 16 * 1024) return launch_block<16>(x, gamma, eps, M, K, q, inv, qsum, s);
+    if (K <= 32 * 1024) return launch_block<32>(x, gamma, eps, M, K, q, inv, qsum, s);
+    // Rows beyond 32768: streamed in three passes.
+    hipLaunchKernelGGL((act_quant_long_kernel<XT>), dim3((unsigned)M), dim3(256), 0, s, x, gamma,
                        eps, (int)K, q, inv, qsum);
+    return hipGetLastError();
+}
+
+template <typename YT>
+hipError_t launch_rescale_t(const int32_t *acc, const float *inv, float w_scale, int64_t M,
+                            int64_t N, YT *y, hipStream_t s) {
+    const int64_t pairs = (M * N + 1) / 2;
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((pairs + 255) / 256, 4096));
+    hipLaunchKernelGGL((rescale_kernel<YT>), dim3((unsigned)blocks), dim3(256), 0, s, acc, inv,
+                       w_scale, M, N, y);
     return hipGetLastError();
 }
 
@@ -190,19 +289,36 @@ hipError_t launch_relu2_mul(const float *g, const float *u, float *a, int64_t n,
 hipError_t launch_act_quant(const float *x, const float *gamma, float eps,
                             int64_t M, int64_t K, int8_t *q, float *inv,
                             int32_t *qsum, hipStream_t s) {
-    if (K <= 1024) {
-        hipLaunchKernelGGL(act_quant_wave_kernel, dim3((unsigned)M), dim3(64), 0, s, x, gamma,
-                           eps, (int)K, q, inv, qsum);
-        return hipGetLastError();
+    return launch_act_quant_t(x, gamma, eps, M, K, q, inv, qsum, s);
+}
+
+hipError_t launch_act_quant_io(const void *x, int xtype, const float *gamma, float eps, int64_t M,
+                               int64_t K, int8_t *q, float *inv, int32_t *qsum, hipStream_t s) {
+    switch (xtype) {
+        case kIoF32:
+            return launch_act_quant_t(static_cast<const float *>(x), gamma, eps, M, K, q, inv,
+                                      qsum, s);
+        case kIoBf16:
+            return launch_act_quant_t(static_cast<const bf16_t *>(x), gamma, eps, M, K, q, inv,
+                                      qsum, s);
+        case kIoF16:
+            return launch_act_quant_t(static_cast<const _Float16 *>(x), gamma, eps, M, K, q, inv,
+                                      qsum, s);
+        default: return hipErrorInvalidValue;
     }
-    if (K <= 4 * 1024) return launch_block<4>(x, gamma, eps, M, K, q, inv, qsum, s);
-    if (K <= 8 * 1024) return launch_block<8>(x, gamma, eps, M, K, q, inv, qsum, s);
-    if (K <= 16 * 1024) return launch_block<16>(x, gamma, eps, M, K, q, inv, qsum, s);
-    if (K <= 32 * 1024) return launch_block<32>(x, gamma, eps, M, K, q, inv, qsum, s);
-    // Rows beyond 32768: streamed in three passes.
-    hipLaunchKernelGGL((act_quant_long_kernel), dim3((unsigned)M), dim3(256), 0, s, x, gamma, eps,
-                       (int)K, q, inv, qsum);
-    return hipGetLastError();
+}
+
+hipError_t launch_rescale_io(const int32_t *acc, const float *inv, float w_scale, int64_t M,
+                             int64_t N, void *y, int ytype, hipStream_t s) {
+    switch (ytype) {
+        case kIoF32:
+            return launch_rescale_t(acc, inv, w_scale, M, N, static_cast<float *>(y), s);
+        case kIoBf16:
+            return launch_rescale_t(acc, inv, w_scale, M, N, static_cast<bf16_t *>(y), s);
+        case kIoF16:
+            return launch_rescale_t(acc, inv, w_scale, M, N, static_cast<_Float16 *>(y), s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace bl

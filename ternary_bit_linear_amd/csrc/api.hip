@@ -340,6 +340,41 @@ bl_status bitlinear_forward(const float *x, const uint8_t *packed_w, float w_sca
                                 workspace_bytes, nullptr, stream);
 }
 
+size_t bitlinear_io_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (check_mk(M, K) || N < 1 || N > kMaxDim || check_mn(M, N)) return 0;
+    return align256(bitlinear_workspace_bytes(M, K)) + align256((size_t)(M * N) * 4);
+}
+
+bl_status bitlinear_forward_io(const void *x, int x_dtype, const uint8_t *packed_w, float w_scale,
+                               const float *gamma, float eps, int64_t M, int64_t K, int64_t N,
+                               void *y, int y_dtype, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    if (bl_status st = check_mk(M, K)) return st;
+    if (bl_status st = check_nk(N, K)) return st;
+    if (bl_status st = check_mn(M, N)) return st;
+    if (!x || !packed_w || !y || !workspace) return BL_ERR_INVALID_ARG;
+    auto known = [](int t) { return t == BL_F32 || t == BL_BF16 || t == BL_F16; };
+    if (!known(x_dtype) || !known(y_dtype)) return BL_ERR_INVALID_ARG;
+    if ((gamma && (!(eps > 0.0f) || !std::isfinite(eps))) || !std::isfinite(w_scale))
+        return BL_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(packed_w) || !aligned16(y) ||
+        !aligned16(workspace))
+        return BL_ERR_ALIGN;
+    if (workspace_bytes < bitlinear_io_workspace_bytes(M, K, N)) return BL_ERR_WORKSPACE;
+    if (bl_status st = check_grid(M, nullptr)) return st;
+    hipStream_t s = as_stream(stream);
+    const Workspace ws = carve(workspace, M, K);
+    int32_t *acc = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) +
+                                               align256(bitlinear_workspace_bytes(M, K)));
+    if (bl::launch_act_quant_io(x, x_dtype, gamma, eps, M, K, ws.q, ws.inv, ws.qsum, s) !=
+        hipSuccess)
+        return BL_ERR_HIP;
+    if (bl_status st = run_contraction(ws.q, ws.inv, ws.qsum, packed_w, w_scale, M, K, N, nullptr,
+                                       acc, nullptr, s))
+        return st;
+    return hip_status(bl::launch_rescale_io(acc, ws.inv, w_scale, M, N, y, y_dtype, s));
+}
+
 size_t bitlinear_ffn_workspace_bytes(int64_t M, int64_t H, int64_t F) {
     if (check_mk(M, H) || check_mk(M, F) || check_mn(M, F) || check_mn(M, H)) return 0;
     const size_t gb = align256((size_t)(M * F) * 4);

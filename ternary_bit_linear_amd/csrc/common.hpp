@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 #include <stdint.h>
 
@@ -157,6 +158,48 @@ __device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t
     const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_float4(__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z),
                        __int_as_float(v.w));
+}
+
+// Activation storage types.  bf16 is carried as its bit pattern; widening
+// to fp32 is exact for every type (bf16: the 16 bits become the high half
+// of the fp32 word; fp16: f16_bits_to_f32 below).
+struct bf16_t {
+    uint16_t bits;
+};
+template <typename XT>
+constexpr uint32_t kXBytes = sizeof(XT);
+
+// Four consecutive activations at byte offset `off` (out of range: zeros).
+template <typename XT>
+__device__ __forceinline__ float4 load_x4(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ float4 load_x4<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return buf_load_f4(r, off);
+}
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+template <>
+__device__ __forceinline__ float4 load_x4<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+}
+// IEEE binary16 bits -> fp32 by integer operations: exact for every input,
+// subnormals included, whatever the hardware's fp16 denormal mode.
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    const uint32_t sign = (h & 0x8000u) << 16;
+    const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+    if (e == 0) {  // zero or subnormal: m * 2^-24, exact in fp32
+        const float v = (float)m * 5.9604644775390625e-8f;
+        return __uint_as_float(__float_as_uint(v) | sign);
+    }
+    if (e == 31) return __uint_as_float(sign | 0x7F800000u | (m << 13));
+    return __uint_as_float(sign | ((e + 112u) << 23) | (m << 13));
+}
+template <>
+__device__ __forceinline__ float4 load_x4<_Float16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_float4(f16_bits_to_f32(v.x & 0xFFFFu), f16_bits_to_f32(v.x >> 16),
+                       f16_bits_to_f32(v.y & 0xFFFFu), f16_bits_to_f32(v.y >> 16));
 }
 
 // Halving-tree reduction of the 64 lanes of a wave into lane 0:
@@ -297,17 +340,20 @@ __device__ __forceinline__ float amax4(float a, const float4 &v) {
 // not delay the normalisation.  A wave skips the loads of a chunk that lies
 // wholly past K.  LONG rows (K > 1024 * CH) are streamed in chunks of CH
 // float4 per thread, three times.
-template <int CH, bool LONG, bool SYNC = true, bool GLU = false, class Sink, class Hook>
-__device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
+template <int CH, bool LONG, bool SYNC = true, bool GLU = false, typename XT = float, class Sink,
+          class Hook>
+__device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                                                     const float *__restrict__ gamma,
                                                     float eps, int K, float *red,
                                                     Sink &sink, Hook &&issued,
                                                     const float *__restrict__ u = nullptr) {
+    static_assert(!GLU || std::is_same<XT, float>::value, "the gated input is fp32");
+    constexpr uint32_t XB = kXBytes<XT>;
     const int t4 = 4 * threadIdx.x;
     constexpr int STRIDE = 1024;
     if constexpr (!LONG) {  // K <= 1024 * CH
         const bool norm = gamma != nullptr;
-        const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+        const auto rx = make_rsrc(x, XB * (uint32_t)K);
         const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
         const auto rg = gamma_rsrc(gamma, K);
         float4 xv[CH], gv[CH], uv[GLU ? CH : 1];
@@ -317,7 +363,7 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
             const int k = t4 + STRIDE * i;
             const uint32_t off = k < K ? 4u * (uint32_t)k : kOOB;
             if (STRIDE * i + wk < K) {
-                xv[i] = buf_load_f4(rx, off);
+                xv[i] = load_x4<XT>(rx, k < K ? XB * (uint32_t)k : kOOB);
                 if constexpr (GLU) uv[i] = buf_load_f4(ru, off);
                 gv[i] = gamma_f4(rg, off, norm);
             } else {
@@ -379,13 +425,13 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
     issued();
     // Long rows: three streamed passes.
     const bool norm = gamma != nullptr;
-    const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+    const auto rx = make_rsrc(x, XB * (uint32_t)K);
     const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
     const auto rg = gamma_rsrc(gamma, K);
     auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
     // x of one chunk (GLU: formed from the gate and up rows)
     auto load_x = [&](int k) -> float4 {
-        const float4 v = buf_load_f4(rx, off_of(k));
+        const float4 v = load_x4<XT>(rx, k < K ? XB * (uint32_t)k : kOOB);
         if constexpr (GLU) return relu2_mul4(v, buf_load_f4(ru, off_of(k)));
         else return v;
     };
@@ -451,15 +497,17 @@ __device__ __forceinline__ void block_act_quant_row(const float *__restrict__ x,
 // same halving tree (wave_tree_sum_f) and the four totals are added as
 // (g0 + g1) + (g2 + g3) -- the same bits as the block form.  Rows of up to
 // 1024 * CI elements stay in registers; longer rows take three passes.
-template <int CI, class Sink>
-__device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
+template <int CI, typename XT = float, class Sink>
+__device__ __forceinline__ void wave_act_quant_row(const XT *__restrict__ x,
                                                    const float *__restrict__ gamma,
                                                    float eps, int K, Sink &sink) {
+    constexpr uint32_t XB = kXBytes<XT>;
     const int lane = threadIdx.x & 63;
     const bool norm = gamma != nullptr;
-    const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+    const auto rx = make_rsrc(x, XB * (uint32_t)K);
     const auto rg = gamma_rsrc(gamma, K);
     auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
+    auto xoff_of = [&](int k) -> uint32_t { return k < K ? XB * (uint32_t)k : kOOB; };
     float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const bool in_regs = K <= 1024 * CI;
     float4 xv[CI][4], gv[CI][4];
@@ -468,8 +516,9 @@ __device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
         for (int i = 0; i < CI; ++i)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
-                xv[i][w] = buf_load_f4(rx, off);
+                const int k = c0 + 1024 * i + 256 * w + 4 * lane;
+                const uint32_t off = off_of(k);
+                xv[i][w] = load_x4<XT>(rx, xoff_of(k));
                 if (in_regs) gv[i][w] = gamma_f4(rg, off, norm);
             }
 #pragma unroll
@@ -496,8 +545,9 @@ __device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
             for (int i = 0; i < CI; ++i)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
-                    xv[i][w] = buf_load_f4(rx, off);
+                    const int k = c0 + 1024 * i + 256 * w + 4 * lane;
+                    const uint32_t off = off_of(k);
+                    xv[i][w] = load_x4<XT>(rx, xoff_of(k));
                     gv[i][w] = gamma_f4(rg, off, norm);
                 }
         }
@@ -515,8 +565,9 @@ __device__ __forceinline__ void wave_act_quant_row(const float *__restrict__ x,
             for (int i = 0; i < CI; ++i)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const uint32_t off = off_of(c0 + 1024 * i + 256 * w + 4 * lane);
-                    xv[i][w] = buf_load_f4(rx, off);
+                    const int k = c0 + 1024 * i + 256 * w + 4 * lane;
+                    const uint32_t off = off_of(k);
+                    xv[i][w] = load_x4<XT>(rx, xoff_of(k));
                     gv[i][w] = gamma_f4(rg, off, norm);
                 }
         }
@@ -556,6 +607,19 @@ hipError_t launch_act_quant(const float *x, const float *gamma, float eps,
 hipError_t launch_act_quant_glu(const float *g, const float *u, const float *gamma, float eps,
                                 int64_t M, int64_t K, int8_t *q, float *inv, int32_t *qsum,
                                 hipStream_t s);
+
+// Activation I/O types of the typed forward (the values of bl_dtype).
+constexpr int kIoF32 = 0, kIoBf16 = 1, kIoF16 = 2;
+
+// launch_act_quant over x stored as xtype (widened to fp32 on load; the
+// same codes as launch_act_quant over the widened values).
+hipError_t launch_act_quant_io(const void *x, int xtype, const float *gamma, float eps, int64_t M,
+                               int64_t K, int8_t *q, float *inv, int32_t *qsum, hipStream_t s);
+
+// y = (float)acc * (w_scale / inv[m]) stored as ytype (rounded to nearest
+// even).
+hipError_t launch_rescale_io(const int32_t *acc, const float *inv, float w_scale, int64_t M,
+                             int64_t N, void *y, int ytype, hipStream_t s);
 
 // a = relu2_mul(g, u) elementwise over n floats (n % 4 == 0, 16-byte
 // aligned arrays).

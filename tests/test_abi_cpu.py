@@ -221,3 +221,28 @@ def test_ffn_validation(L, kw, code):
     d = _ffn(**kw)
     assert L.bitlinear_ffn_forward(ctypes.byref(d), None) == code
     assert L.bitlinear_ffn_forward(None, None) == api.ERR_INVALID_ARG
+
+
+def test_io_workspace_bytes(L):
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert L.bitlinear_io_workspace_bytes(3, 256, 77) == al(L.bitlinear_workspace_bytes(3, 256)) + al(4 * 3 * 77)
+    assert L.bitlinear_io_workspace_bytes(0, 256, 4) == 0
+    assert L.bitlinear_io_workspace_bytes(2, 100, 4) == 0
+
+
+def fio(L, x=A, xd=1, p=A, s=0.02, g=A, eps=1e-6, M=1, K=256, N=256, y=A, yd=1, ws=A,
+        wsb=1 << 20):
+    return L.bitlinear_forward_io(F(x), xd, F(p), s, F(g), eps, M, K, N, F(y), yd, F(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"M": 0}, api.ERR_SHAPE), ({"K": 100}, api.ERR_SHAPE), ({"N": 0}, api.ERR_SHAPE),
+    ({"x": 0}, api.ERR_INVALID_ARG), ({"p": 0}, api.ERR_INVALID_ARG),
+    ({"y": 0}, api.ERR_INVALID_ARG), ({"ws": 0}, api.ERR_INVALID_ARG),
+    ({"xd": 3}, api.ERR_INVALID_ARG), ({"yd": -1}, api.ERR_INVALID_ARG),
+    ({"eps": 0.0}, api.ERR_INVALID_ARG), ({"s": float("nan")}, api.ERR_INVALID_ARG),
+    ({"x": MIS}, api.ERR_ALIGN), ({"y": MIS}, api.ERR_ALIGN), ({"g": MIS}, api.ERR_ALIGN),
+    ({"wsb": 100}, api.ERR_WORKSPACE),
+    ({"g": 0, "eps": 0.0, "y": MIS}, api.ERR_ALIGN)])
+def test_forward_io_validation(L, kw, code):
+    assert fio(L, **kw) == code

@@ -825,3 +825,106 @@ def test_ffn_graph_replay(torch, bl, orc):
         torch.cuda.synchronize()
         assert np.array_equal(got, eager), r
         check_y(got, orc.ffn(xr, gi, 1e-6, gate, up, down, gs)[0])
+
+
+# ---------------------------------------------------------------- half-precision I/O
+
+IO_SHAPES = [(1, 2560, 640), (3, 1024, 77), (17, 256, 63), (64, 1024, 200), (2, 28672, 48)]
+IO_TYPES = [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f32")]
+
+
+def torch_io(torch, a, dt):
+    """numpy oracle-side representation -> device tensor of the I/O type."""
+    if dt == "bf16":
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    if dt == "f16":
+        return torch.from_numpy(np.ascontiguousarray(a, np.float16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def bits16(torch, t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("xd,yd", IO_TYPES)
+@pytest.mark.parametrize("M,K,N", IO_SHAPES)
+def test_forward_io_parity(torch, bl, orc, M, K, N, xd, yd):
+    """x widened exactly, the int8 codes of the widened x, and y rounded
+    once from the fp32 output: bit for bit against the oracle."""
+    announce("forward_io", M, K, N, xd, yd)
+    x32, w, t, g = mm_case(M, K, N, 1400 + M + N)
+    x = orc.from_f32(x32, xd)
+    packed_r, s = orc.pack_i2s(w)
+    y_r = orc.forward_io(x, xd, packed_r, s, g, 1e-6, N, yd)
+    X = torch_io(torch, x, xd)
+    ydt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[yd]
+    ws = torch.empty(bl.lib().bitlinear_io_workspace_bytes(M, K, N), dtype=torch.uint8,
+                     device="cuda")
+    y = bl.forward_io(X, dev(torch, packed_r), s, dev(torch, g), 1e-6, N, y_dtype=ydt, workspace=ws)
+    torch.cuda.synchronize()
+    if yd == "f32":
+        assert np.array_equal(host(y).view(np.uint32), y_r.view(np.uint32))
+    else:
+        assert np.array_equal(bits16(torch, y), np.asarray(y_r).view(np.uint16))
+    q_r, inv_r, qs_r = orc.act_quant(orc.to_f32(x, xd), g, 1e-6)
+    q, inv, qs = bl.workspace_views(ws, M, K)
+    assert np.array_equal(host(q), q_r) and np.array_equal(host(inv), inv_r)
+    assert np.array_equal(host(qs), qs_r)
+
+
+def test_forward_io_f32_equals_forward(torch, bl, orc):
+    """With fp32 in and out the typed entry point gives forward()'s bits,
+    with and without RMSNorm."""
+    for M, K, N in ((1, 2560, 640), (40, 512, 130)):
+        x, w, t, g = mm_case(M, K, N, 1450 + M)
+        packed_r, s = orc.pack_i2s(w)
+        X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+        for gg in (G, None):
+            announce("forward_io f32", M, K, N, gg is None)
+            a = host(bl.forward(X, P, s, gg, 1e-6, N))
+            b = host(bl.forward_io(X, P, s, gg, 1e-6, N))
+            torch.cuda.synchronize()
+            assert np.array_equal(a, b)
+
+
+def test_forward_io_identity_exact(torch, bl, orc):
+    """bf16 x = integers / 64 (exact), no norm, W = 0.5 I: y = x / 2 exactly
+    in bf16 and fp16."""
+    K = 128
+    m = (np.arange(2 * K).reshape(2, K) % 255 - 127).astype(np.float32)
+    m[:, 0] = -127.0
+    xf = m / np.float32(64.0)
+    packed_r, s = orc.pack_i2s(np.eye(K, dtype=np.float32) * np.float32(0.5))
+    for dt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        announce("forward_io identity", dt)
+        X = torch_io(torch, orc.from_f32(xf, dt), dt)
+        y = bl.forward_io(X, dev(torch, packed_r), s, None, 1e-6, K)
+        torch.cuda.synchronize()
+        assert y.dtype == tdt
+        assert np.array_equal(y.float().cpu().numpy(), xf / np.float32(2.0))
+
+
+def test_forward_io_f16_subnormals_exact(torch, bl, orc):
+    """fp16 subnormal inputs and outputs keep their exact values: x = m *
+    2^-20 (subnormal below |m| = 16) widens exactly, so q = m; with
+    W = s I, y = s x exactly: m * 2^-24 (all subnormal) for s = 2^-4 and
+    m * 2^-10 (normal) for s = 2^10; the device's bits are checked against
+    the oracle's."""
+    K = 128
+    m = (np.arange(2 * K).reshape(2, K) % 255 - 127).astype(np.float32)
+    m[:, 0] = -127.0
+    xf = m * np.float32(2.0 ** -20)
+    x = orc.from_f32(xf, "f16")
+    assert np.array_equal(orc.to_f32(x, "f16"), xf)  # exact in fp16, subnormals included
+    for s_w in (2.0 ** -4, 2.0 ** 10):
+        packed_r, s = orc.pack_i2s(np.eye(K, dtype=np.float32) * np.float32(s_w))
+        y_r = orc.forward_io(x, "f16", packed_r, s, None, 1e-6, K, "f16")
+        assert np.array_equal(y_r.astype(np.float32), xf * np.float32(s_w))
+        sub = (y_r != 0) & (np.abs(y_r.astype(np.float32)) < 2.0 ** -14)
+        assert sub.any() == (s_w < 1)
+        announce("forward_io f16 subnormals", s_w)
+        y = bl.forward_io(torch_io(torch, x, "f16"), dev(torch, packed_r), s, None, 1e-6, K)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits16(torch, y), y_r.view(np.uint16))
+        q, inv, qs = orc.act_quant(orc.to_f32(x, "f16"), None, 1e-6)
+        assert np.array_equal(q.astype(np.float32), m)
