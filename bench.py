@@ -16,7 +16,7 @@ not from the 256 MB last-level cache.
 Prints one JSON line (see the "metric" of the workload).  Options:
   --gpus N (only 1 is supported), --steps K, --warmup W,
   --workload decode|prefill|ffn70b-1|ffn70b-16|sweep-M,
-  --no-cpu-baseline, --no-secondary, --pack-only, --ffn-only.
+  --no-cpu-baseline, --no-secondary, --pack-only, --ffn-only, --io-only.
 """
 from __future__ import annotations
 
@@ -311,6 +311,50 @@ def secondary_ffn(torch, api, steps, warmup):
     return {"workload": "BitNet FFN block: down(sub_norm(relu(gate(x))^2 * up(x)))", **res}
 
 
+def secondary_io(torch, api, steps, warmup):
+    """The decoder layer's BitLinears with bf16 activations in and out, as
+    one bitlinear_forward_io_batch call per step (decode: one one-shot
+    launch; prefill: typed quantisation, contraction, rescale per
+    BitLinear), beside the fp32 step."""
+    from ternary_bit_linear_amd import workloads as wl
+    res = {}
+    for key, work in (("decode_bf16", wl.DECODE_LAYER), ("prefill_bf16", wl.PREFILL_LAYER)):
+        prep = Prepared(torch, api, work)
+        io = []
+        for d in prep.lin:
+            L = d["L"]
+            io.append({"x": d["x"].to(torch.bfloat16),
+                       "y": torch.empty((L.M, L.N), dtype=torch.bfloat16, device="cuda"),
+                       "ws": torch.empty(int(api.lib().bitlinear_io_workspace_bytes(L.M, L.K, L.N)),
+                                         dtype=torch.uint8, device="cuda")})
+
+        def step(r):
+            api.forward_io_batch([(b["x"], d["P"][r % prep.copies], d["s"], d["g"], work.eps,
+                                   b["y"], b["ws"]) for d, b in zip(prep.lin, io)])
+        gw = capture(torch, lambda: [step(r) for r in range(max(1, warmup))])
+        gt = capture(torch, lambda: [step(warmup + r) for r in range(steps)])
+        gw.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gt.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / steps
+        del gw, gt
+        t32 = time_steps(torch, api, prep, steps, warmup) * 1e-3
+        nbytes = sum(L.N * L.K // 4 + 2 * L.M * L.K + 4 * L.K + 2 * L.M * L.N for L in work.linears)
+        r = {"us": round(t * 1e6, 2), "fp32_step_us": round(t32 * 1e6, 2)}
+        if work.linears[0].M <= 16:
+            r["GBs"] = round(nbytes / t / 1e9, 1)
+        else:
+            r["TOPS"] = round(work.int_ops() / t / 1e12, 1)
+        res[key] = r
+        del prep, io
+        torch.cuda.empty_cache()
+    return {"workload": "decoder-layer BitLinears with bf16 activation I/O", **res}
+
+
 def secondary_pack(torch, api, reps=5):
     """I2_S packing of the packing workload (fp32 ternary x 0.02, N = 8192 x
     K = 28672; seeded on the device): GB/s of algorithmic bytes (4NK read +
@@ -347,6 +391,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--pack-only", action="store_true",
                     help="time only the I2_S packer over --steps calls and print its line")
+    ap.add_argument("--io-only", action="store_true",
+                    help="time only the bf16-I/O legs (--steps steps each) and print their line")
     ap.add_argument("--ffn-only", action="store_true",
                     help="time only the FFN block legs (--steps steps each) and print their line")
     ap.add_argument("--pmc-app", action="store_true",
@@ -367,6 +413,9 @@ def main():
 
     if args.pack_only:
         print(json.dumps(secondary_pack(torch, api, reps=max(1, args.steps))), flush=True)
+        return
+    if args.io_only:
+        print(json.dumps(secondary_io(torch, api, max(1, args.steps), args.warmup)), flush=True)
         return
     if args.ffn_only:
         print(json.dumps(secondary_ffn(torch, api, max(1, args.steps), args.warmup)), flush=True)
@@ -456,6 +505,8 @@ def main():
         out["secondary"]["pack"] = secondary_pack(torch, api)
         torch.cuda.empty_cache()
         out["secondary"]["ffn"] = secondary_ffn(torch, api, max(20, args.steps // 4), 5)
+        torch.cuda.empty_cache()
+        out["secondary"]["io"] = secondary_io(torch, api, max(20, args.steps // 4), 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work)
     print(json.dumps(out), flush=True)

@@ -249,8 +249,11 @@ size_t bitlinear_io_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * y = (float)acc * (w_scale / inv) is rounded to y_dtype to nearest with
  * ties to even (bf16: the high 16 bits of the fp32 word after rounding;
  * fp16: IEEE binary16, overflow to inf).  With both types BL_F32 the bits
- * equal bitlinear_forward's.  Three launches: quantisation, contraction to
- * the int32 accumulator in the workspace, rescale.
+ * equal bitlinear_forward's.  One token with K <= 8192 and x_dtype ==
+ * y_dtype: one launch (the one-shot decode kernel with the quantisation and
+ * the rescale inside) when its workgroups fit on the device at once;
+ * otherwise three launches: quantisation, contraction to the int32
+ * accumulator in the workspace, rescale.
  *   x: device [M][K] of x_dtype; y: device [M][N] of y_dtype; both 16-byte
  *   aligned.  Other arguments and errors as bitlinear_forward; an unknown
  *   dtype is BL_ERR_INVALID_ARG.  workspace: >=
@@ -259,6 +262,36 @@ bl_status bitlinear_forward_io(const void *x, int x_dtype, const uint8_t *packed
                                float w_scale, const float *gamma, float eps, int64_t M,
                                int64_t K, int64_t N, void *y, int y_dtype, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* One forward of bitlinear_forward_io_batch: the arguments of
+ * bitlinear_forward_io, same meaning and rules. */
+typedef struct {
+    const void *x;
+    int x_dtype;
+    const uint8_t *packed_w;
+    float w_scale;
+    const float *gamma;
+    float eps;
+    int64_t M, K, N;
+    void *y;
+    int y_dtype;
+    void *workspace;
+    size_t workspace_bytes;
+} bl_forward_io_desc;
+
+/* Several independent typed forwards (e.g. a decoder layer's BitLinears
+ * with bf16 activations); per descriptor bit-identical to
+ * bitlinear_forward_io.  Those with M = 1, K <= 8192 and x_dtype ==
+ * y_dtype share one one-shot launch per 8 and per type (quantisation and
+ * rescale inside it) when their workgroups fit on the device at once; the
+ * prefill-sized ones (M > 4, K % 256 == 0, K <= 8192) share one typed
+ * quantisation launch and one tile-kernel launch (rounding y in its
+ * epilogue) per 8 of one (x_dtype, y_dtype) pair; the others run as
+ * bitlinear_forward_io does.
+ *   descs: HOST array, 1 <= count <= 64, each validated as
+ *   bitlinear_forward_io validates its arguments, all before anything is
+ *   enqueued.  Asynchronous on `stream`. */
+bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count, void *stream);
 
 /* BitNet FFN block [HF-38087, the BitNetMLP excerpt of the review thread:
  * y = down(ffn_sub_norm(act(gate(x)) * up(x))); CPPB-7 summary bullet and

@@ -52,6 +52,15 @@ class FfnDesc(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+class IoDesc(ctypes.Structure):
+    """bl_forward_io_desc: the arguments of one bitlinear_forward_io."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int), ("packed_w", ctypes.c_void_p),
+                ("w_scale", ctypes.c_float), ("gamma", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("y", ctypes.c_void_p), ("y_dtype", ctypes.c_int), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 SIGNATURES = {
     "bitlinear_status_string": (ctypes.c_char_p, [_i]),
     "bitlinear_abi_version": (_i, []),
@@ -69,6 +78,7 @@ SIGNATURES = {
     "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bitlinear_io_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bitlinear_forward_io": (_i, [_p, _i, _p, _f, _p, _f, _i64, _i64, _i64, _p, _i, _p, _sz, _p]),
+    "bitlinear_forward_io_batch": (_i, [ctypes.POINTER(IoDesc), _i, _p]),
     "bitlinear_ffn_forward": (_i, [ctypes.POINTER(FfnDesc), _p]),
     "bitlinear_matmul_i2s": (_i, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "bitlinear_matmul_i2s_ex": (_i, [_p, _p, _p, _i64, _i64, _i64, _p,
@@ -327,3 +337,26 @@ def forward_io(x, packed, w_scale: float, gamma, eps: float = 1e-6, N: int | Non
         _io_dtype(out.dtype), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream()), "forward_io")
     return out
+
+
+def io_workspace(M: int, K: int, N: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(int(lib().bitlinear_io_workspace_bytes(M, K, N)), dtype=torch.uint8,
+                       device=device)
+
+
+def forward_io_batch(items):
+    """Several typed forwards: items of (x, packed, w_scale, gamma, eps, out,
+    workspace) with x / out float32, bfloat16 or float16 tensors; per item
+    bit-identical to forward_io()."""
+    torch = _torch()
+    arr = (IoDesc * len(items))()
+    for i, (x, packed, w_scale, gamma, eps, out, ws) in enumerate(items):
+        M, K = x.shape
+        N = out.shape[1]
+        if not (x.is_cuda and x.is_contiguous() and out.is_cuda and out.is_contiguous()):
+            raise ValueError("x and out must be contiguous HIP tensors")
+        arr[i] = IoDesc(x.data_ptr(), _io_dtype(x.dtype), _dev(packed, torch.uint8, "packed"),
+                        w_scale, _gamma(gamma), eps, M, K, N, out.data_ptr(), _io_dtype(out.dtype),
+                        _dev(ws, torch.uint8, "workspace"), ws.numel())
+    _check(lib().bitlinear_forward_io_batch(arr, len(items), _stream()), "forward_io_batch")

@@ -67,36 +67,6 @@ __global__ __launch_bounds__(256) void act_quant_long_kernel(
 // y[m][n] = (float)acc[m][n] * (w_scale / inv[m]) rounded to the output
 // type YT (bf16_t, _Float16: to nearest, ties to even, NaN kept quiet).
 // Two outputs per thread.
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-// fp32 -> IEEE binary16 bits, nearest even, by integer operations (exact
-// rounding for subnormal results too, whatever the fp16 denormal mode):
-// NaN stays a quiet NaN, from 65520 up the result is inf.
-__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return (uint16_t)(sign | 0x7E00u | ((a >> 13) & 0x3FFu));
-    if (a >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);  // >= 65520
-    if (a >= 0x38800000u) {                                    // >= 2^-14: normal
-        const uint32_t r = a - 0x38000000u;                    // rebias 127 -> 15
-        return (uint16_t)(sign | ((r + 0xFFFu + ((r >> 13) & 1u)) >> 13));
-    }
-    // subnormal or zero: units of 2^-24; the scaling is exact, rintf rounds
-    // to nearest even (1024 units is the smallest normal, encoded alike)
-    const float v = __uint_as_float(a) * 16777216.0f;
-    return (uint16_t)(sign | (uint32_t)rintf(v));
-}
-
-template <typename YT>
-__device__ __forceinline__ uint16_t to_half_bits(float v) {
-    if constexpr (std::is_same<YT, bf16_t>::value) return f32_to_bf16_rne(v);
-    else return f32_to_f16_rne(v);
-}
-
 template <typename YT>
 __global__ __launch_bounds__(256) void rescale_kernel(const int32_t *__restrict__ acc,
                                                       const float *__restrict__ inv, float w_scale,
@@ -159,7 +129,7 @@ __global__ __launch_bounds__(256) void relu2_mul_kernel(const float4 *__restrict
 // argument list so that the build's kernel-argument preload puts them in
 // scalar registers at wave launch.
 struct AqProblem {
-    const float *x;
+    const void *x;
     const float *gamma;
     int8_t *q;
     float *inv;
@@ -173,7 +143,7 @@ struct AqBatch {
     AqProblem p[kMaxAqBatch];
 };
 
-template <int CH>
+template <int CH, typename XT = float>
 __global__ __launch_bounds__(256) void act_quant_batch_kernel(int b0, int b1, int b2, int b3,
                                                               int b4, int b5, int b6, int b7,
                                                               AqBatch B) {
@@ -189,7 +159,8 @@ __global__ __launch_bounds__(256) void act_quant_batch_kernel(int b0, int b1, in
     const int m = bx - P.row_begin;
     const int K = P.K;
     GlobalRowSink sink{P.q + (size_t)m * K, P.inv + m, P.qsum + m};
-    block_act_quant_row<CH, false>(P.x + (size_t)m * K, P.gamma, P.eps, K, red, sink, [] {});
+    block_act_quant_row<CH, false, true, false, XT>(static_cast<const XT *>(P.x) + (size_t)m * K,
+                                                    P.gamma, P.eps, K, red, sink, [] {});
 }
 
 template <int CH, typename XT>
@@ -236,7 +207,8 @@ hipError_t launch_act_quant_batch(const ActQuantDesc *d, int count, hipStream_t 
     int begin[kMaxAqBatch];
     int64_t rows = 0, kmax = 0;
     for (int i = 0; i < count; ++i) {
-        if (d[i].K > kActQuantBatchMaxK || d[i].K < 1 || d[i].M < 1) return hipErrorInvalidValue;
+        if (d[i].K > kActQuantBatchMaxK || d[i].K < 1 || d[i].M < 1 || d[i].io != d[0].io)
+            return hipErrorInvalidValue;
         AqProblem &P = B.p[i];
         P.x = d[i].x;
         P.gamma = d[i].gamma;
@@ -252,13 +224,21 @@ hipError_t launch_act_quant_batch(const ActQuantDesc *d, int count, hipStream_t 
         kmax = std::max<int64_t>(kmax, d[i].K);
     }
     for (int i = count; i < kMaxAqBatch; ++i) begin[i] = INT32_MAX;
-    if (kmax <= 4096)
-        hipLaunchKernelGGL(act_quant_batch_kernel<4>, dim3((unsigned)rows), dim3(256), 0, s, begin[0],
-                           begin[1], begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
-    else
-        hipLaunchKernelGGL(act_quant_batch_kernel<8>, dim3((unsigned)rows), dim3(256), 0, s, begin[0],
-                           begin[1], begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
-    return hipGetLastError();
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(256), 0, s, begin[0], begin[1],
+                           begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
+        return hipGetLastError();
+    };
+    const bool small = kmax <= 4096;
+    switch (d[0].io) {
+        case kIoF32: return small ? go(act_quant_batch_kernel<4>) : go(act_quant_batch_kernel<8>);
+        case kIoBf16:
+            return small ? go(act_quant_batch_kernel<4, bf16_t>) : go(act_quant_batch_kernel<8, bf16_t>);
+        case kIoF16:
+            return small ? go(act_quant_batch_kernel<4, _Float16>)
+                         : go(act_quant_batch_kernel<8, _Float16>);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_act_quant_glu(const float *g, const float *u, const float *gamma, float eps,

@@ -205,6 +205,83 @@ constexpr int kMaxBatchDescs = 64;
 constexpr int kFusedPerLaunch = 8;
 constexpr int kGroupPerLaunch = 8;
 
+bl_status validate_io(const bl_forward_io_desc &d) {
+    const int64_t M = d.M, K = d.K, N = d.N;
+    if (bl_status st = check_mk(M, K)) return st;
+    if (bl_status st = check_nk(N, K)) return st;
+    if (bl_status st = check_mn(M, N)) return st;
+    if (!d.x || !d.packed_w || !d.y || !d.workspace) return BL_ERR_INVALID_ARG;
+    auto known = [](int t) { return t == BL_F32 || t == BL_BF16 || t == BL_F16; };
+    if (!known(d.x_dtype) || !known(d.y_dtype)) return BL_ERR_INVALID_ARG;
+    if ((d.gamma && (!(d.eps > 0.0f) || !std::isfinite(d.eps))) || !std::isfinite(d.w_scale))
+        return BL_ERR_INVALID_ARG;
+    if (!aligned16(d.x) || !aligned16(d.gamma) || !aligned16(d.packed_w) || !aligned16(d.y) ||
+        !aligned16(d.workspace))
+        return BL_ERR_ALIGN;
+    if (d.workspace_bytes < bitlinear_io_workspace_bytes(M, K, N)) return BL_ERR_WORKSPACE;
+    return check_grid(M, nullptr);
+}
+
+// Whether a validated typed forward joins a one-shot fused launch.
+bool io_fusable(const bl_forward_io_desc &d) {
+    return d.M == 1 && d.K <= 8 * 1024 && d.x_dtype == d.y_dtype &&
+           bl::shot_fused_supported(d.M, d.K);
+}
+
+bl::FusedDecode fused_io_of(const bl_forward_io_desc &d) {
+    const Workspace ws = carve(d.workspace, d.M, d.K);
+    bl::FusedDecode f;
+    f.x = static_cast<const float *>(d.x);  // of type io, as the kernel reads it
+    f.gamma = d.gamma;
+    f.packed = d.packed_w;
+    f.y = static_cast<float *>(d.y);
+    f.q = ws.q;
+    f.inv = ws.inv;
+    f.qsum = ws.qsum;
+    f.eps = d.eps;
+    f.w_scale = d.w_scale;
+    f.M = d.M;
+    f.K = d.K;
+    f.N = d.N;
+    f.io = d.x_dtype;
+    return f;
+}
+
+// The three-launch form: typed quantisation, contraction to the int32
+// accumulator, typed rescale.
+bl_status enqueue_io_staged(const bl_forward_io_desc &d, hipStream_t s) {
+    const Workspace ws = carve(d.workspace, d.M, d.K);
+    int32_t *acc = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(d.workspace) +
+                                               align256(bitlinear_workspace_bytes(d.M, d.K)));
+    if (bl::launch_act_quant_io(d.x, d.x_dtype, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum,
+                                s) != hipSuccess)
+        return BL_ERR_HIP;
+    if (bl_status st = run_contraction(ws.q, ws.inv, ws.qsum, d.packed_w, d.w_scale, d.M, d.K,
+                                       d.N, nullptr, acc, nullptr, s))
+        return st;
+    return hip_status(bl::launch_rescale_io(acc, ws.inv, d.w_scale, d.M, d.N, d.y, d.y_dtype, s));
+}
+
+// Fused launches of up to 8 same-type problems when their workgroups fit on
+// the device at once; else each one staged.
+bl_status flush_io_group(const bl_forward_io_desc *const *g, int n, hipStream_t s) {
+    if (n == 0) return BL_OK;
+    int64_t Ms[8], Ks[8], Ns[8];
+    bl::FusedDecode f[8];
+    for (int i = 0; i < n; ++i) {
+        Ms[i] = g[i]->M;
+        Ks[i] = g[i]->K;
+        Ns[i] = g[i]->N;
+        f[i] = fused_io_of(*g[i]);
+    }
+    if (bl::shot_rounds(Ms, Ks, Ns, n, true) == 1)
+        return hip_status(bl::launch_gemv_shot_fused(f, n, 0, s));
+    for (int i = 0; i < n; ++i)
+        if (bl_status st = enqueue_io_staged(*g[i], s)) return st;
+    return BL_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -345,34 +422,72 @@ size_t bitlinear_io_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return align256(bitlinear_workspace_bytes(M, K)) + align256((size_t)(M * N) * 4);
 }
 
+bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count, void *stream) {
+    if (!descs || count < 1 || count > kMaxBatchDescs) return BL_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i)
+        if (bl_status st = validate_io(descs[i])) return st;
+    hipStream_t s = as_stream(stream);
+    const bl_forward_io_desc *grp[3][8];
+    int n[3] = {0, 0, 0};
+    // Prefill-sized problems: one batched typed quantisation and one grouped
+    // tile launch (typed epilogue) per 8 of one (x type, y type) pair.
+    struct PrefillGroup {
+        bl::ActQuantDesc aq[kGroupPerLaunch];
+        bl::GemmDesc gd[kGroupPerLaunch];
+        int n = 0;
+    };
+    PrefillGroup pg[3][3];
+    auto flush_pg = [&](PrefillGroup &G) -> bl_status {
+        if (G.n == 0) return BL_OK;
+        if (bl::launch_act_quant_batch(G.aq, G.n, s) != hipSuccess) return BL_ERR_HIP;
+        if (bl::launch_gemm_group(G.gd, G.n, s) != hipSuccess) return BL_ERR_HIP;
+        G.n = 0;
+        return BL_OK;
+    };
+    for (int i = 0; i < count; ++i) {
+        const bl_forward_io_desc &d = descs[i];
+        if (!io_fusable(d)) {
+            if (route_of(d.M, nullptr) == BL_PATH_GEMM && bl::gemm_group_supported(d.K) &&
+                d.K <= bl::kActQuantBatchMaxK) {
+                PrefillGroup &G = pg[d.x_dtype][d.y_dtype];
+                const Workspace ws = carve(d.workspace, d.M, d.K);
+                bl::ActQuantDesc &a = G.aq[G.n];
+                a = bl::ActQuantDesc{d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum};
+                a.io = d.x_dtype;
+                bl::GemmDesc &g = G.gd[G.n];
+                g = bl::GemmDesc{ws.q, ws.inv, ws.qsum, d.packed_w, d.w_scale, d.M, d.K, d.N,
+                                 static_cast<float *>(d.y), nullptr};
+                g.io = d.y_dtype;
+                if (++G.n == kGroupPerLaunch)
+                    if (bl_status st = flush_pg(G)) return st;
+            } else if (bl_status st = enqueue_io_staged(d, s)) {
+                return st;
+            }
+            continue;
+        }
+        const int t = d.x_dtype;
+        grp[t][n[t]++] = &d;
+        if (n[t] == 8) {
+            if (bl_status st = flush_io_group(grp[t], 8, s)) return st;
+            n[t] = 0;
+        }
+    }
+    for (int t = 0; t < 3; ++t)
+        if (bl_status st = flush_io_group(grp[t], n[t], s)) return st;
+    for (int xt = 0; xt < 3; ++xt)
+        for (int yt = 0; yt < 3; ++yt)
+            if (bl_status st = flush_pg(pg[xt][yt])) return st;
+    return BL_OK;
+}
+
 bl_status bitlinear_forward_io(const void *x, int x_dtype, const uint8_t *packed_w, float w_scale,
                                const float *gamma, float eps, int64_t M, int64_t K, int64_t N,
                                void *y, int y_dtype, void *workspace, size_t workspace_bytes,
                                void *stream) {
-    if (bl_status st = check_mk(M, K)) return st;
-    if (bl_status st = check_nk(N, K)) return st;
-    if (bl_status st = check_mn(M, N)) return st;
-    if (!x || !packed_w || !y || !workspace) return BL_ERR_INVALID_ARG;
-    auto known = [](int t) { return t == BL_F32 || t == BL_BF16 || t == BL_F16; };
-    if (!known(x_dtype) || !known(y_dtype)) return BL_ERR_INVALID_ARG;
-    if ((gamma && (!(eps > 0.0f) || !std::isfinite(eps))) || !std::isfinite(w_scale))
-        return BL_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(gamma) || !aligned16(packed_w) || !aligned16(y) ||
-        !aligned16(workspace))
-        return BL_ERR_ALIGN;
-    if (workspace_bytes < bitlinear_io_workspace_bytes(M, K, N)) return BL_ERR_WORKSPACE;
-    if (bl_status st = check_grid(M, nullptr)) return st;
-    hipStream_t s = as_stream(stream);
-    const Workspace ws = carve(workspace, M, K);
-    int32_t *acc = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) +
-                                               align256(bitlinear_workspace_bytes(M, K)));
-    if (bl::launch_act_quant_io(x, x_dtype, gamma, eps, M, K, ws.q, ws.inv, ws.qsum, s) !=
-        hipSuccess)
-        return BL_ERR_HIP;
-    if (bl_status st = run_contraction(ws.q, ws.inv, ws.qsum, packed_w, w_scale, M, K, N, nullptr,
-                                       acc, nullptr, s))
-        return st;
-    return hip_status(bl::launch_rescale_io(acc, ws.inv, w_scale, M, N, y, y_dtype, s));
+    const bl_forward_io_desc d{x,   x_dtype, packed_w, w_scale, gamma,          eps,
+                               M,   K,       N,        y,       y_dtype,        workspace,
+                               workspace_bytes};
+    return bitlinear_forward_io_batch(&d, 1, stream);
 }
 
 size_t bitlinear_ffn_workspace_bytes(int64_t M, int64_t H, int64_t F) {

@@ -202,6 +202,44 @@ __device__ __forceinline__ float4 load_x4<_Float16>(__amdgpu_buffer_rsrc_t r, ui
                        f16_bits_to_f32(v.y & 0xFFFFu), f16_bits_to_f32(v.y >> 16));
 }
 
+// fp32 -> bf16 bits, nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// fp32 -> IEEE binary16 bits, nearest even, by integer operations (exact
+// rounding for subnormal results too, whatever the fp16 denormal mode):
+// NaN stays a quiet NaN, from 65520 up the result is inf.
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return (uint16_t)(sign | 0x7E00u | ((a >> 13) & 0x3FFu));
+    if (a >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);  // >= 65520
+    if (a >= 0x38800000u) {                                    // >= 2^-14: normal
+        const uint32_t r = a - 0x38000000u;                    // rebias 127 -> 15
+        return (uint16_t)(sign | ((r + 0xFFFu + ((r >> 13) & 1u)) >> 13));
+    }
+    // subnormal or zero: units of 2^-24; the scaling is exact, rintf rounds
+    // to nearest even (1024 units is the smallest normal, encoded alike)
+    const float v = __uint_as_float(a) * 16777216.0f;
+    return (uint16_t)(sign | (uint32_t)rintf(v));
+}
+
+template <typename YT>
+__device__ __forceinline__ uint16_t to_half_bits(float v) {
+    if constexpr (std::is_same<YT, bf16_t>::value) return f32_to_bf16_rne(v);
+    else return f32_to_f16_rne(v);
+}
+
+// One output element of type YT.
+template <typename YT>
+__device__ __forceinline__ void store_out(YT *y, size_t i, float v) {
+    if constexpr (std::is_same<YT, float>::value) y[i] = v;
+    else reinterpret_cast<uint16_t *>(y)[i] = to_half_bits<YT>(v);
+}
+
 // Halving-tree reduction of the 64 lanes of a wave into lane 0:
 // level s = 32, 16, 8, 4, 2, 1 adds lane j + s into lane j (j < s).  Lane
 // 0's result is exactly the tree the pinned sum-of-squares order defines.
@@ -628,13 +666,14 @@ hipError_t launch_relu2_mul(const float *g, const float *u, float *a, int64_t n,
 // Batched quantisation: up to 8 independent (x, gamma, eps, M, K) with
 // K <= 8192 each, one launch, bit-identical to launch_act_quant per problem.
 struct ActQuantDesc {
-    const float *x;
+    const void *x;  // of type io (widened to fp32 as it is loaded)
     const float *gamma;
     float eps;
     int64_t M, K;
     int8_t *q;
     float *inv;
     int32_t *qsum;
+    int io = 0;     // kIoF32 / kIoBf16 / kIoF16; one type per launch
 };
 constexpr int64_t kActQuantBatchMaxK = 8192;
 hipError_t launch_act_quant_batch(const ActQuantDesc *d, int count, hipStream_t s);
@@ -666,6 +705,10 @@ struct FusedDecode {
     // over the gate rows x and up rows u).  One-shot route with M == 1 only;
     // every problem of a launch has it or none does.
     const float *u = nullptr;
+    // Storage type of x and y (kIoF32 / kIoBf16 / kIoF16; x and y point to
+    // that type).  Half types: one-shot route, M == 1, K <= 8192, no GLU,
+    // one type per launch.
+    int io = 0;
 };
 hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipStream_t s);
 
@@ -717,8 +760,9 @@ struct GemmDesc {
     const uint8_t *packed;
     float w_scale;
     int64_t M, K, N;
-    float *y;
+    float *y;    // of type io (rounded to nearest even) when not fp32
     int32_t *acc;
+    int io = 0;  // kIoF32 / kIoBf16 / kIoF16; one type per launch
 };
 bool gemm_group_supported(int64_t K);
 hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s);

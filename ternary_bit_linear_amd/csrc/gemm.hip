@@ -56,11 +56,12 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 // One BM x BN output tile at (m0, n0) of one problem, by the whole
 // workgroup.
-template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y>
+// YT: storage type of y (float, bf16_t, _Float16; rounded to nearest even).
+template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y, typename YT = float>
 __device__ __forceinline__ void gemm_tile(
     const int8_t *__restrict__ q, const float *__restrict__ inv,
     const int32_t *__restrict__ qsum, const uint8_t *__restrict__ packed,
-    float w_scale, int M, int K, int N, float *__restrict__ y,
+    float w_scale, int M, int K, int N, YT *__restrict__ y,
     int32_t *__restrict__ acc_out, int m0, int n0) {
     constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -227,7 +228,7 @@ __device__ __forceinline__ void gemm_tile(
                 if (n >= N) continue;
                 const int v = acc[mi][ni][c] - qs;
                 if (OUT_Y)
-                    y[(size_t)m * N + n] = (float)v * sc;
+                    store_out(y, (size_t)m * N + n, (float)v * sc);
                 else
                     acc_out[(size_t)m * N + n] = v;
             }
@@ -268,7 +269,7 @@ struct GroupBatch {
 // lead the argument list so that the build's kernel-argument preload puts
 // them in scalar registers at wave launch.  Tiles of a problem are ordered
 // N-fastest, as in the single-problem grid.
-template <int BM, int BN, int WM, int WN, int R, bool OUT_Y>
+template <int BM, int BN, int WM, int WN, int R, bool OUT_Y, typename YT = float>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_group_kernel(int b0, int b1, int b2, int b3,
                                                                   int b4, int b5, int b6, int b7,
                                                                   GroupBatch B) {
@@ -282,8 +283,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_group_kernel(int b0, int b1
     const GroupProblem P = Bk->p[pi];
     const int t = bx - P.tile_begin;
     const int tm = t / P.ntn, tn = t - tm * P.ntn;
-    gemm_tile<BM, BN, WM, WN, R, false, OUT_Y>(P.q, P.inv, P.qsum, P.packed, P.w_scale, P.M, P.K,
-                                               P.N, P.y, P.acc, tm * BM, tn * BN);
+    gemm_tile<BM, BN, WM, WN, R, false, OUT_Y, YT>(P.q, P.inv, P.qsum, P.packed, P.w_scale, P.M,
+                                                   P.K, P.N, reinterpret_cast<YT *>(P.y), P.acc,
+                                                   tm * BM, tn * BN);
 }
 
 struct Tile {
@@ -385,7 +387,16 @@ hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
     }
     for (int i = count; i < kMaxGroup; ++i) begin[i] = INT32_MAX;
     const dim3 grid((unsigned)total), block(WM * WN * 64);
-    if (y)
+    const int io = d[0].io;
+    if (y && io == kIoBf16)
+        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true, bf16_t>), grid, block, 0, s,
+                           begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],
+                           begin[7], B);
+    else if (y && io == kIoF16)
+        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true, _Float16>), grid, block, 0,
+                           s, begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],
+                           begin[7], B);
+    else if (y)
         hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true>), grid, block, 0, s, begin[0],
                            begin[1], begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
     else
@@ -403,7 +414,8 @@ hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
     int64_t t64x512 = 0, t64x256 = 0, t64x128 = 0, t32x128 = 0, kmax = 0;
     double work = 0.0, work_k = 0.0;  // int ops, and int ops x K
     for (int i = 0; i < count; ++i) {
-        if (!gemm_group_supported(d[i].K) || (d[i].y != nullptr) != y) return hipErrorInvalidValue;
+        if (!gemm_group_supported(d[i].K) || (d[i].y != nullptr) != y || d[i].io != d[0].io)
+            return hipErrorInvalidValue;
         auto tiles = [&](int bm, int bn) {
             return ((d[i].M + bm - 1) / bm) * ((d[i].N + bn - 1) / bn);
         };

@@ -884,6 +884,9 @@ hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipSt
                       (is_shot(variant) || (variant == 0 && shot_rounds(M, K, N, count, true) == 1));
     if (shot)
         return launch_gemv_shot_fused(d, count, is_shot(variant) ? shot_shape_of(variant) : 0, s);
+    // The persistent form reads and writes fp32 activations only.
+    for (int i = 0; i < count; ++i)
+        if (d[i].io != kIoF32 || d[i].u) return hipErrorInvalidValue;
     // (fused: one tile per wave, the shape measured for one token)
     const int v = variant > 0 && variant <= kNumShapes ? variant : 1;
 #define BL_FUSED(R_, U_, D_) launch_shape_fused<R_, U_, D_>(d, count, s)

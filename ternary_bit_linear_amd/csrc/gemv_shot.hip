@@ -111,7 +111,11 @@ __device__ __forceinline__ v4i field_sum(const v4i (&a)[4]) {
 // lead the argument list so that the build's kernel-argument preload puts
 // them in scalar registers at wave launch, and the lookup costs no memory
 // round trip.
-template <int NB, int R, bool OUT_Y, int FM, int CH, bool LONG, bool GLU = false>
+// IO: storage type of x and y with the fused quantisation (float, bf16_t,
+// _Float16): x is widened to fp32 as it is loaded, y rounded as it is
+// stored.
+template <int NB, int R, bool OUT_Y, int FM, int CH, bool LONG, bool GLU = false,
+          typename IO = float>
 __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, int b3, int b4,
                                                         int b5, int b6, int b7, ShotBatch B) {
     static_assert(NB >= 1 && NB <= 8, "batches per wave");
@@ -228,8 +232,9 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
         {
             ShotRowSink sink{q_lds, inv_sh, qsum_sh, st == 0 ? P.q_out : nullptr, P.inv_out,
                              P.qsum_out};
-            block_act_quant_row<CH, LONG, false, GLU>(P.x, P.gamma, P.eps, K, red, sink,
-                                                      issue_weights, P.u);
+            block_act_quant_row<CH, LONG, false, GLU, IO>(reinterpret_cast<const IO *>(P.x),
+                                                          P.gamma, P.eps, K, red, sink,
+                                                          issue_weights, P.u);
         }
 #pragma unroll
         for (int m = 1; m < FM; ++m) {
@@ -237,9 +242,9 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
                 ShotRowSink sink{q_lds + m * K, inv_sh + m, qsum_sh + m,
                                  st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m,
                                  P.qsum_out + m};
-                block_act_quant_row<CH, LONG, false, GLU>(P.x + (size_t)m * K, P.gamma, P.eps, K,
-                                                          red, sink, [] {},
-                                                          GLU ? P.u + (size_t)m * K : nullptr);
+                block_act_quant_row<CH, LONG, false, GLU, IO>(
+                    reinterpret_cast<const IO *>(P.x) + (size_t)m * K, P.gamma, P.eps, K, red,
+                    sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr);
             }
         }
         lds_barrier();
@@ -302,7 +307,8 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
                 const int v = t[c] - qs;
                 if (OUT_Y) {
                     const float iv = FM > 0 ? inv_sh[m < FM ? m : 0] : iv_pre[c];
-                    P.y[(size_t)m * N + n] = (float)v * (P.w_scale / iv);
+                    store_out(reinterpret_cast<IO *>(P.y), (size_t)m * N + n,
+                              (float)v * (P.w_scale / iv));
                 } else {
                     P.acc[(size_t)m * N + n] = v;
                 }
@@ -499,7 +505,7 @@ hipError_t launch_shot_nb(const ShotDecode *d, int count, hipStream_t s) {
     return launch_batch(gemv_shot_kernel<NB, R, OUT_Y, 0, 1, false>, B, begin, gx, qmax, s);
 }
 
-template <int NB, int R, int FM, int CH, bool LONG, bool GLU>
+template <int NB, int R, int FM, int CH, bool LONG, bool GLU, typename IO>
 hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) {
     ShotBatch B{};
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
@@ -521,7 +527,8 @@ hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) 
     }
     int begin[kMaxShotBatch];
     const int64_t gx = fill_batch(B, begin, count, NB, R, M, K, N, &qmax);
-    return launch_batch(gemv_shot_kernel<NB, R, true, FM, CH, LONG, GLU>, B, begin, gx, qmax, s);
+    return launch_batch(gemv_shot_kernel<NB, R, true, FM, CH, LONG, GLU, IO>, B, begin, gx, qmax,
+                        s);
 }
 
 #define BL_SHOT_SHAPES(CALL)                                                   \
@@ -535,9 +542,9 @@ hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) 
         default: return hipErrorInvalidValue;                                  \
     }
 
-template <int FM, int CH, bool LONG, bool GLU = false>
+template <int FM, int CH, bool LONG, bool GLU = false, typename IO = float>
 hipError_t launch_fused_ch(const FusedDecode *d, int count, int v, hipStream_t s) {
-#define BL_F(NB_, R_) launch_shot_fused_nb<NB_, R_, FM, CH, LONG, GLU>(d, count, s)
+#define BL_F(NB_, R_) launch_shot_fused_nb<NB_, R_, FM, CH, LONG, GLU, IO>(d, count, s)
     BL_SHOT_SHAPES(BL_F)
 #undef BL_F
 }
@@ -587,9 +594,13 @@ hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hi
     if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], kmax = 0, mmax = 0;
     const bool glu = d[0].u != nullptr;
+    const int io = d[0].io;
     for (int i = 0; i < count; ++i) {
         if (!shot_fused_supported(d[i].M, d[i].K) || !d[i].y) return hipErrorInvalidValue;
         if ((d[i].u != nullptr) != glu || (glu && d[i].M != 1)) return hipErrorInvalidValue;
+        // half-precision I/O: one token, rows held in registers, one type
+        if (d[i].io != io || (io != kIoF32 && (glu || d[i].M != 1 || d[i].K > 8192)))
+            return hipErrorInvalidValue;
         M[i] = d[i].M;
         K[i] = d[i].K;
         N[i] = d[i].N;
@@ -600,6 +611,14 @@ hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hi
     const int v = pick_shape(M, K, N, count, shape, &rounds, true);
     // One token everywhere (the decode case): the kernel that normalises a
     // single row, whose code is a quarter of the general one's.
+    if (io == kIoBf16) {
+        if (kmax <= 4096) return launch_fused_ch<1, 4, false, false, bf16_t>(d, count, v, s);
+        return launch_fused_ch<1, 8, false, false, bf16_t>(d, count, v, s);
+    }
+    if (io == kIoF16) {
+        if (kmax <= 4096) return launch_fused_ch<1, 4, false, false, _Float16>(d, count, v, s);
+        return launch_fused_ch<1, 8, false, false, _Float16>(d, count, v, s);
+    }
     if (glu) {
         if (kmax <= 4096) return launch_fused_ch<1, 4, false, true>(d, count, v, s);
         if (kmax <= 8192) return launch_fused_ch<1, 8, false, true>(d, count, v, s);

@@ -246,3 +246,16 @@ def fio(L, x=A, xd=1, p=A, s=0.02, g=A, eps=1e-6, M=1, K=256, N=256, y=A, yd=1, 
     ({"g": 0, "eps": 0.0, "y": MIS}, api.ERR_ALIGN)])
 def test_forward_io_validation(L, kw, code):
     assert fio(L, **kw) == code
+
+
+def test_forward_io_batch_validation(L):
+    fb = L.bitlinear_forward_io_batch
+    good = api.IoDesc(A, 1, A, 0.02, A, 1e-6, 1, 256, 16, A, 1, A, 1 << 20)
+    bad = api.IoDesc(A, 7, A, 0.02, A, 1e-6, 1, 256, 16, A, 1, A, 1 << 20)
+    assert fb(None, 1, None) == api.ERR_INVALID_ARG
+    assert fb((api.IoDesc * 1)(good), 0, None) == api.ERR_INVALID_ARG
+    assert fb((api.IoDesc * 65)(*[good] * 65), 65, None) == api.ERR_INVALID_ARG
+    # one bad descriptor fails the whole call before anything is enqueued
+    assert fb((api.IoDesc * 3)(good, good, bad), 3, None) == api.ERR_INVALID_ARG
+    mis = api.IoDesc(A, 1, A, 0.02, A, 1e-6, 1, 256, 16, MIS, 1, A, 1 << 20)
+    assert fb((api.IoDesc * 2)(good, mis), 2, None) == api.ERR_ALIGN

@@ -928,3 +928,40 @@ def test_forward_io_f16_subnormals_exact(torch, bl, orc):
         assert np.array_equal(bits16(torch, y), y_r.view(np.uint16))
         q, inv, qs = orc.act_quant(orc.to_f32(x, "f16"), None, 1e-6)
         assert np.array_equal(q.astype(np.float32), m)
+
+
+def test_forward_io_batch_mixed(torch, bl, orc):
+    """A typed batch mixing bf16, fp16 and fp32 decode problems (fused per
+    type), prefill problems (grouped per type pair) and staged ones (mixed
+    types, M = 2..4, K > 8192): each equals its single forward_io call and
+    the oracle, bit for bit."""
+    cases = [(1, 2560, 640, "bf16", "bf16"), (1, 6912, 256, "bf16", "bf16"),
+             (1, 2560, 96, "f16", "f16"), (1, 1024, 48, "f32", "f32"),
+             (1, 2560, 64, "bf16", "f32"), (5, 512, 33, "bf16", "bf16"),
+             (1, 9216, 40, "f16", "f16"), (1, 256, 16, "bf16", "bf16"),
+             (64, 2560, 256, "bf16", "bf16"), (40, 512, 130, "f16", "bf16"),
+             (96, 1024, 64, "bf16", "f32"), (33, 768, 50, "bf16", "bf16"),
+             (70, 256, 40, "f32", "f16")]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    items, refs, singles = [], [], []
+    for i, (M, K, N, xd, yd) in enumerate(cases):
+        x32, w, t, g = mm_case(M, K, N, 1500 + i)
+        x = orc.from_f32(x32, xd)
+        packed_r, s = orc.pack_i2s(w)
+        refs.append(orc.forward_io(x, xd, packed_r, s, g, 1e-6, N, yd))
+        X, P, G = torch_io(torch, x, xd), dev(torch, packed_r), dev(torch, g)
+        out = torch.empty((M, N), dtype=tdt[yd], device="cuda")
+        ws = bl.io_workspace(M, K, N)
+        items.append((X, P, s, G, 1e-6, out, ws))
+        singles.append(bl.forward_io(X, P, s, G, 1e-6, N, y_dtype=tdt[yd]).clone())
+    announce("forward_io_batch", len(items))
+    bl.forward_io_batch(items)
+    torch.cuda.synchronize()
+    for it, single, ref, c in zip(items, singles, refs, cases):
+        out = it[5]
+        if c[4] == "f32":
+            assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32)), c
+            assert torch.equal(out, single), c
+        else:
+            assert np.array_equal(bits16(torch, out), np.asarray(ref).view(np.uint16)), c
+            assert np.array_equal(bits16(torch, out), bits16(torch, single)), c
