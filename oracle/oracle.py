@@ -268,6 +268,12 @@ def forward_io(x: np.ndarray, x_dtype: str, packed: np.ndarray, w_scale: float, 
     return from_f32(rescale_f32(acc, inv, w_scale), y_dtype)
 
 
+def dequant_i2s(packed: np.ndarray, N: int, K: int, dtype: str) -> np.ndarray:
+    """The to_float direction in a dense type: unpack (code - 1) * scale in
+    fp32, then round to dtype (bf16 as uint16 bit patterns)."""
+    return from_f32(unpack_i2s(packed, N, K), dtype)
+
+
 def relu2_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     """a = (max(g, 0)^2) * u in fp32 (the FFN block's gate)."""
     g, u = _f32(g), _f32(u)

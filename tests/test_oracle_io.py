@@ -96,3 +96,20 @@ def test_forward_io_with_norm_matches_rounded_f32(orc):
     y = orc.to_f32(orc.forward_io(x, "bf16", packed, s, g, 1e-6, N, "bf16"), "bf16")
     y64 = orc.forward(orc.to_f32(x, "bf16"), packed, s, g, 1e-6, N)
     assert np.all(np.abs(y - y64) <= 2.0 ** -8 * np.abs(y64) * (1 + 1e-5))
+
+
+def test_dequant_hand_values(orc):
+    """(code - 1) * s rounded once: s = 0.1 (fp32 0x3DCCCCCD) is 0x3DCD in
+    bf16 (dropped half 0xCCCD > 0x8000 rounds up) and 0x2E66 in fp16."""
+    t = np.array([[1, 0, -1, 1] * 32, [0, -1, 0, 1] * 32], np.float32)
+    w = t * np.float32(0.1)
+    packed, s = orc.pack_i2s(w)
+    assert s == np.float32(0.1)
+    b = orc.dequant_i2s(packed, 2, 128, "bf16")
+    expect_b = np.where(t > 0, 0x3DCD, np.where(t < 0, 0xBDCD, 0)).astype(np.uint16)
+    assert np.array_equal(b, expect_b)
+    h = orc.dequant_i2s(packed, 2, 128, "f16").view(np.uint16)
+    expect_h = np.where(t > 0, 0x2E66, np.where(t < 0, 0xAE66, 0)).astype(np.uint16)
+    assert np.array_equal(h, expect_h)
+    f = orc.dequant_i2s(packed, 2, 128, "f32")
+    assert np.array_equal(f, w)
