@@ -16,7 +16,8 @@ not from the 256 MB last-level cache.
 Prints one JSON line (see the "metric" of the workload).  Options:
   --gpus N (only 1 is supported), --steps K, --warmup W,
   --workload decode|prefill|ffn70b-1|ffn70b-16|sweep-M,
-  --no-cpu-baseline, --no-secondary, --pack-only, --ffn-only, --io-only.
+  --no-cpu-baseline, --no-secondary, --pack-only, --ffn-only, --io-only,
+  --dense-only.
 """
 from __future__ import annotations
 
@@ -355,6 +356,53 @@ def secondary_io(torch, api, steps, warmup):
     return {"workload": "decoder-layer BitLinears with bf16 activation I/O", **res}
 
 
+def secondary_dense(torch, api, steps, warmup):
+    """Comparison: the decoder layer run the way the pages' BLAS route runs
+    a prompt batch -- weights dequantised once (bitlinear_dequant_i2s, to
+    bf16) and a library GEMM per BitLinear (torch.mm on bf16, no activation
+    quantisation) -- beside the I2_S path, at decode and prefill.  The dense
+    weights are rotated past the last-level cache like the packed ones."""
+    from ternary_bit_linear_amd import workloads as wl
+    res = {}
+    for key, work in (("decode", wl.DECODE_LAYER), ("prefill", wl.PREFILL_LAYER)):
+        prep = Prepared(torch, api, work)
+        dense_bytes = sum(2 * L.N * L.K for L in work.linears)
+        copies = max(2, -(-ROTATE_BYTES // dense_bytes))
+        mats = []
+        for d in prep.lin:
+            L = d["L"]
+            w = api.dequant_i2s(d["P"][0], L.N, L.K, torch.bfloat16)
+            wt = w.t().contiguous()  # [K][N]: a plain (non-transposed) right operand
+            del w
+            mats.append({"x": d["x"].to(torch.bfloat16), "wt": [wt] + [wt.clone() for _ in range(copies - 1)],
+                         "y": torch.empty((L.M, L.N), dtype=torch.bfloat16, device="cuda")})
+        torch.cuda.synchronize()
+
+        def step(r):
+            for m in mats:
+                torch.mm(m["x"], m["wt"][r % copies], out=m["y"])
+        gw = capture(torch, lambda: [step(r) for r in range(max(1, warmup))])
+        gt = capture(torch, lambda: [step(warmup + r) for r in range(steps)])
+        gw.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gt.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / steps
+        del gw, gt
+        t_i2s = time_steps(torch, api, prep, steps, warmup) * 1e-3
+        res[key] = {"dense_bf16_library_us": round(t * 1e6, 2), "i2s_us": round(t_i2s * 1e6, 2),
+                    "i2s_speedup": round(t / t_i2s, 3),
+                    "dense_weight_bytes": dense_bytes,
+                    "packed_weight_bytes": sum(L.N * L.K // 4 for L in work.linears)}
+        del prep, mats
+        torch.cuda.empty_cache()
+    return {"workload": "decoder-layer BitLinears: dequantised bf16 weights + library GEMM "
+                        "(torch.mm) against the I2_S path", **res}
+
+
 def secondary_pack(torch, api, reps=5):
     """I2_S packing of the packing workload (fp32 ternary x 0.02, N = 8192 x
     K = 28672; seeded on the device): GB/s of algorithmic bytes (4NK read +
@@ -391,6 +439,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--pack-only", action="store_true",
                     help="time only the I2_S packer over --steps calls and print its line")
+    ap.add_argument("--dense-only", action="store_true",
+                    help="time only the dequantised-bf16 library comparison and print its line")
     ap.add_argument("--io-only", action="store_true",
                     help="time only the bf16-I/O legs (--steps steps each) and print their line")
     ap.add_argument("--ffn-only", action="store_true",
@@ -413,6 +463,9 @@ def main():
 
     if args.pack_only:
         print(json.dumps(secondary_pack(torch, api, reps=max(1, args.steps))), flush=True)
+        return
+    if args.dense_only:
+        print(json.dumps(secondary_dense(torch, api, max(1, args.steps), args.warmup)), flush=True)
         return
     if args.io_only:
         print(json.dumps(secondary_io(torch, api, max(1, args.steps), args.warmup)), flush=True)
@@ -507,6 +560,8 @@ def main():
         out["secondary"]["ffn"] = secondary_ffn(torch, api, max(20, args.steps // 4), 5)
         torch.cuda.empty_cache()
         out["secondary"]["io"] = secondary_io(torch, api, max(20, args.steps // 4), 5)
+        torch.cuda.empty_cache()
+        out["secondary"]["dense_comparison"] = secondary_dense(torch, api, max(20, args.steps // 4), 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work)
     print(json.dumps(out), flush=True)

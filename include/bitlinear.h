@@ -235,8 +235,19 @@ bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum,
                                   int64_t K, int64_t N, int32_t *acc,
                                   const bl_launch *launch, void *stream);
 
-/* Activation storage types of bitlinear_forward_io. */
+/* Activation storage types of bitlinear_forward_io (and weight types of
+ * bitlinear_dequant_i2s). */
 typedef enum { BL_F32 = 0, BL_BF16 = 1, BL_F16 = 2 } bl_dtype;
+
+/* Dequantisation of an I2_S tensor to a dense float type [CPPB-7,
+ * dequantize_row_i2_s, the to_float the BLAS route of the pages runs before
+ * a library GEMM]: w_out[n][k] = (code(n,k) - 1) * s in fp32, rounded to
+ * w_dtype to nearest with ties to even (BL_F32: bitlinear_unpack_i2s's
+ * values).  For comparison with the I2_S path and for callers that run a
+ * dense GEMM.  w_out: device [N][K] of w_dtype, 16-byte aligned; an unknown
+ * dtype is BL_ERR_INVALID_ARG.  Asynchronous on `stream`. */
+bl_status bitlinear_dequant_i2s(const uint8_t *packed, int64_t N, int64_t K, void *w_out,
+                                int w_dtype, void *stream);
 
 /* Workspace bytes of bitlinear_forward_io: the forward workspace of (M, K)
  * followed by an int32 accumulator [M][N] (0 if a size is invalid). */

@@ -77,6 +77,7 @@ SIGNATURES = {
     "bitlinear_act_quant": (_i, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
     "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bitlinear_io_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_dequant_i2s": (_i, [_p, _i64, _i64, _p, _i, _p]),
     "bitlinear_forward_io": (_i, [_p, _i, _p, _f, _p, _f, _i64, _i64, _i64, _p, _i, _p, _sz, _p]),
     "bitlinear_forward_io_batch": (_i, [ctypes.POINTER(IoDesc), _i, _p]),
     "bitlinear_ffn_forward": (_i, [ctypes.POINTER(FfnDesc), _p]),
@@ -360,3 +361,14 @@ def forward_io_batch(items):
                         w_scale, _gamma(gamma), eps, M, K, N, out.data_ptr(), _io_dtype(out.dtype),
                         _dev(ws, torch.uint8, "workspace"), ws.numel())
     _check(lib().bitlinear_forward_io_batch(arr, len(items), _stream()), "forward_io_batch")
+
+
+def dequant_i2s(packed, N: int, K: int, dtype=None):
+    """Dense W [N][K] = (code - 1) * scale in float32 / bfloat16 / float16."""
+    torch = _torch()
+    dtype = dtype or torch.float32
+    w = torch.empty((N, K), dtype=dtype, device=packed.device)
+    _check(lib().bitlinear_dequant_i2s(_dev(packed, torch.uint8, "packed"), N, K,
+                                       ctypes.c_void_p(w.data_ptr()), _io_dtype(dtype), _stream()),
+           "dequant_i2s")
+    return w

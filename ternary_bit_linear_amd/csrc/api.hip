@@ -354,6 +354,15 @@ bl_status bitlinear_unpack_i2s(const uint8_t *packed, int64_t N, int64_t K, floa
     return hip_status(bl::launch_unpack(packed, N, K, w_out, as_stream(stream)));
 }
 
+bl_status bitlinear_dequant_i2s(const uint8_t *packed, int64_t N, int64_t K, void *w_out,
+                                int w_dtype, void *stream) {
+    if (bl_status st = check_nk(N, K)) return st;
+    if (!packed || !w_out) return BL_ERR_INVALID_ARG;
+    if (w_dtype != BL_F32 && w_dtype != BL_BF16 && w_dtype != BL_F16) return BL_ERR_INVALID_ARG;
+    if (!aligned16(packed) || !aligned16(w_out)) return BL_ERR_ALIGN;
+    return hip_status(bl::launch_dequant(packed, N, K, w_out, w_dtype, as_stream(stream)));
+}
+
 bl_status bitlinear_read_scale(const uint8_t *packed, int64_t N, int64_t K, float *out_host,
                                void *stream) {
     if (bl_status st = check_nk(N, K)) return st;

@@ -773,6 +773,10 @@ hipError_t launch_pack_scan(const float *w, int64_t N, int64_t K,
                             uint8_t *packed, hipStream_t s);
 hipError_t launch_pack_init(uint8_t *trailer, hipStream_t s);
 hipError_t launch_pack_finalize(uint8_t *trailer, float scale, hipStream_t s);
+// Dequantisation to wtype (kIoF32 / kIoBf16 / kIoF16): (code - 1) * scale,
+// rounded to nearest even for the half types.
+hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, void *w, int wtype,
+                          hipStream_t s);
 hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K,
                          float *w, hipStream_t s);
 

@@ -116,28 +116,39 @@ __global__ void pack_finalize_kernel(uint32_t *trailer, float scale) {
 }
 
 // One thread per 4-byte packed word (16 weights w = (code - 1) * scale):
-// the mirror of pack_scan_kernel's mapping, so the float4 stores of a wave
-// fill whole 128-byte lines.
+// the mirror of pack_scan_kernel's mapping, so the stores of a wave fill
+// whole 128-byte lines (64 for the half types).  OT: the output type; the
+// fp32 value (code - 1) * scale is rounded to it to nearest even.
+template <typename OT>
+__device__ __forceinline__ void store4(OT *dst, float a, float b, float c, float d) {
+    if constexpr (std::is_same<OT, float>::value) {
+        *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
+    } else {
+        const uint32_t lo = (uint32_t)to_half_bits<OT>(a) | ((uint32_t)to_half_bits<OT>(b) << 16);
+        const uint32_t hi = (uint32_t)to_half_bits<OT>(c) | ((uint32_t)to_half_bits<OT>(d) << 16);
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+    }
+}
+
+template <typename OT = float>
 __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__ packed,
                                                       int64_t words, int64_t words_per_row,
                                                       int64_t K, const float *__restrict__ scale_p,
-                                                      float *__restrict__ w) {
+                                                      OT *__restrict__ w) {
     const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (u >= words) return;
     const float s = *scale_p;
     const uint32_t d = reinterpret_cast<const uint32_t *>(packed)[u];
     const int64_t n = u / words_per_row;
     const int64_t r = u - n * words_per_row;
-    float *dst = w + n * K + (r >> 3) * kBlockWeights + 4 * (r & 7);
+    OT *dst = w + n * K + (r >> 3) * kBlockWeights + 4 * (r & 7);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const int sh = 6 - 2 * g;
-        float4 v;
-        v.x = (float)((int)((d >> sh) & 3u) - 1) * s;
-        v.y = (float)((int)((d >> (sh + 8)) & 3u) - 1) * s;
-        v.z = (float)((int)((d >> (sh + 16)) & 3u) - 1) * s;
-        v.w = (float)((int)((d >> (sh + 24)) & 3u) - 1) * s;
-        *reinterpret_cast<float4 *>(dst + 32 * g) = v;
+        store4(dst + 32 * g, (float)((int)((d >> sh) & 3u) - 1) * s,
+               (float)((int)((d >> (sh + 8)) & 3u) - 1) * s,
+               (float)((int)((d >> (sh + 16)) & 3u) - 1) * s,
+               (float)((int)((d >> (sh + 24)) & 3u) - 1) * s);
     }
 }
 
@@ -177,12 +188,31 @@ hipError_t launch_pack_finalize(uint8_t *trailer, float scale, hipStream_t s) {
 
 hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, float *w,
                          hipStream_t s) {
+    return launch_dequant(packed, N, K, w, kIoF32, s);
+}
+
+hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, void *w, int wtype,
+                          hipStream_t s) {
     const int64_t wpr = K / 16;
     const int64_t words = N * wpr;
     const int64_t blocks = (words + 255) / 256;
     const float *scale_p = reinterpret_cast<const float *>(packed + N * (K / 4));
-    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, words,
-                       wpr, K, scale_p, w);
+    const dim3 grid((unsigned)blocks), block(256);
+    switch (wtype) {
+        case kIoF32:
+            hipLaunchKernelGGL(unpack_kernel<float>, grid, block, 0, s, packed, words, wpr, K,
+                               scale_p, static_cast<float *>(w));
+            break;
+        case kIoBf16:
+            hipLaunchKernelGGL(unpack_kernel<bf16_t>, grid, block, 0, s, packed, words, wpr, K,
+                               scale_p, static_cast<bf16_t *>(w));
+            break;
+        case kIoF16:
+            hipLaunchKernelGGL(unpack_kernel<_Float16>, grid, block, 0, s, packed, words, wpr, K,
+                               scale_p, static_cast<_Float16 *>(w));
+            break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -259,3 +259,12 @@ def test_forward_io_batch_validation(L):
     assert fb((api.IoDesc * 3)(good, good, bad), 3, None) == api.ERR_INVALID_ARG
     mis = api.IoDesc(A, 1, A, 0.02, A, 1e-6, 1, 256, 16, MIS, 1, A, 1 << 20)
     assert fb((api.IoDesc * 2)(good, mis), 2, None) == api.ERR_ALIGN
+
+
+def test_dequant_validation(L):
+    dq = L.bitlinear_dequant_i2s
+    assert dq(F(A), 4, 100, F(A), 1, None) == api.ERR_SHAPE
+    assert dq(F(0), 4, 128, F(A), 1, None) == api.ERR_INVALID_ARG
+    assert dq(F(A), 4, 128, F(0), 1, None) == api.ERR_INVALID_ARG
+    assert dq(F(A), 4, 128, F(A), 5, None) == api.ERR_INVALID_ARG
+    assert dq(F(A), 4, 128, F(MIS), 2, None) == api.ERR_ALIGN

@@ -965,3 +965,23 @@ def test_forward_io_batch_mixed(torch, bl, orc):
         else:
             assert np.array_equal(bits16(torch, out), np.asarray(ref).view(np.uint16)), c
             assert np.array_equal(bits16(torch, out), bits16(torch, single)), c
+
+
+# ---------------------------------------------------------------- dequantisation
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("N,K", [(1, 128), (17, 384), (640, 2560), (2560, 6912)])
+def test_dequant_parity(torch, bl, orc, N, K, dt):
+    """Dense W in each type, bit for bit against the oracle's unpack
+    rounded once."""
+    announce("dequant", N, K, dt)
+    w, _ = wl.ternary(1600 + N, N, K, 1 / 3, 0.0137)
+    packed_r, s = orc.pack_i2s(w)
+    ref = orc.dequant_i2s(packed_r, N, K, dt)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
+    got = bl.dequant_i2s(dev(torch, packed_r), N, K, tdt)
+    torch.cuda.synchronize()
+    if dt == "f32":
+        assert np.array_equal(host(got).view(np.uint32), ref.view(np.uint32))
+    else:
+        assert np.array_equal(bits16(torch, got), np.asarray(ref).view(np.uint16))
