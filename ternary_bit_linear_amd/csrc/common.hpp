@@ -274,15 +274,24 @@ __device__ __forceinline__ int wave_sum_int(int v) {
     return wave_tree_i(v, [](int a, int b) { return a + b; });
 }
 
+// q = clamp(rint(xn * inv), -128, 127).  The clamp never acts, so it is not
+// evaluated: |xn| <= amax' = max(amax, 1e-5) and inv = fl(127 / amax') <=
+// (127 / amax') (1 + 2^-24), so |fl(xn * inv)| <= 127 (1 + 2^-24)^2 < 127.5
+// and rint gives |q| <= 127 (finite inputs; others are unspecified).
 __device__ __forceinline__ int quant_one(float xn, float inv) {
-    float t = rintf(xn * inv);
-    t = fminf(fmaxf(t, -128.0f), 127.0f);
-    return (int)t;
+    return (int)rintf(xn * inv);
 }
 
 __device__ __forceinline__ uint32_t pack_char4(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) |
-           ((uint32_t)(c & 0xff) << 16) | ((uint32_t)(d & 0xff) << 24);
+    // byte 0 of each: v_perm picks [a0 b0] and [c0 d0], a third joins them
+    const uint32_t ab = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0C0C0400u);
+    const uint32_t cd = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0C0C0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Sum of the four signed bytes of a packed word, added to acc (exact).
+__device__ __forceinline__ int sum_char4(uint32_t v, int acc) {
+    return __builtin_amdgcn_sdot4((int)v, 0x01010101, acc, false);
 }
 
 // Block-wide reductions over exactly 256 threads (4 waves).  `red` is 4
@@ -355,8 +364,10 @@ __device__ __forceinline__ float4 relu2_mul4(const float4 &g, const float4 &u) {
                        relu2_mul(g.w, u.w));
 }
 
+// Running max of |v| (exact and order-free for finite values; the chain
+// form lets the compiler use three-operand max with abs modifiers).
 __device__ __forceinline__ float amax4(float a, const float4 &v) {
-    return fmaxf(fmaxf(fmaxf(a, fabsf(v.x)), fmaxf(fabsf(v.y), fabsf(v.z))), fabsf(v.w));
+    return fmaxf(fmaxf(fmaxf(fmaxf(a, fabsf(v.x)), fabsf(v.y)), fabsf(v.z)), fabsf(v.w));
 }
 
 // RMSNorm + absmax int8 quantisation of one token row (HF-38087: RMSNorm on
@@ -400,13 +411,12 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
         for (int i = 0; i < CH; ++i) {
             const int k = t4 + STRIDE * i;
             const uint32_t off = k < K ? 4u * (uint32_t)k : kOOB;
+            // Chunks wholly past K (wave-uniform) are never read below: no
+            // load and no initialisation.
             if (STRIDE * i + wk < K) {
                 xv[i] = load_x4<XT>(rx, k < K ? XB * (uint32_t)k : kOOB);
                 if constexpr (GLU) uv[i] = buf_load_f4(ru, off);
                 gv[i] = gamma_f4(rg, off, norm);
-            } else {
-                xv[i] = gv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                if constexpr (GLU) uv[i] = xv[i];
             }
         }
         // Every wave's x / gamma loads are issued before any load the hook
@@ -415,10 +425,12 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
         issued();
         if constexpr (GLU) {
 #pragma unroll
-            for (int i = 0; i < CH; ++i) xv[i] = relu2_mul4(xv[i], uv[i]);
+            for (int i = 0; i < CH; ++i)
+                if (STRIDE * i + wk < K) xv[i] = relu2_mul4(xv[i], uv[i]);
         }
-        // Chunks wholly past K hold zeros, which leave the sum of squares and
-        // the max unchanged: the wave skips them (a wave-uniform test).
+        // Chunks wholly past K are skipped by the wave (a wave-uniform
+        // test); in the others, lanes past K loaded zeros, which leave the
+        // sum of squares and the max unchanged.
         float r = 1.0f;
         if (norm) {
             float p = 0.0f;
@@ -452,8 +464,9 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                 const float4 v = xv[i];
                 const int a = quant_one(v.x, inv), b = quant_one(v.y, inv);
                 const int c = quant_one(v.z, inv), d = quant_one(v.w, inv);
-                qs += a + b + c + d;
-                sink.store_q(k, pack_char4(a, b, c, d));
+                const uint32_t w = pack_char4(a, b, c, d);
+                qs = sum_char4(w, qs);
+                sink.store_q(k, w);
             }
         }
         qs = block_sum_int(qs, red + 8);
@@ -519,8 +532,9 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                 const float4 v = xn4(xv[i], gv[i], r);
                 const int a = quant_one(v.x, inv), b = quant_one(v.y, inv);
                 const int c = quant_one(v.z, inv), d = quant_one(v.w, inv);
-                qs += a + b + c + d;
-                sink.store_q(k, pack_char4(a, b, c, d));
+                const uint32_t w = pack_char4(a, b, c, d);
+                qs = sum_char4(w, qs);
+                sink.store_q(k, w);
             }
         }
     }
@@ -618,8 +632,9 @@ __device__ __forceinline__ void wave_act_quant_row(const XT *__restrict__ x,
                     const float4 v = xn4(xv[i][w], gv[i][w], r);
                     const int a = quant_one(v.x, inv), b = quant_one(v.y, inv);
                     const int c = quant_one(v.z, inv), d = quant_one(v.w, inv);
-                    qs += a + b + c + d;
-                    sink.store_q(k, pack_char4(a, b, c, d));
+                    const uint32_t w = pack_char4(a, b, c, d);
+                    qs = sum_char4(w, qs);
+                    sink.store_q(k, w);
                 }
             }
     }
