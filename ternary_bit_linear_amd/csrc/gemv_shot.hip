@@ -252,25 +252,29 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
 
     // 4. Contract each batch as it lands.  The activation fragments of the
     //    next batch are read from LDS while the current one is contracted.
+    // A lane whose token row r8 is past M reads row M - 1 instead: those A
+    // rows only reach D rows of tokens >= M, which are never stored.  A
+    // chunk past K reads the row's first chunk: its weight bytes were loaded
+    // as zeros (codes 0), so it adds nothing.  Every read is in bounds and
+    // no fragment is cleared first.
+    const int qrow = min(r8, M - 1) * K;
     auto read_q = [&](v4i(&a)[kU][4], int b) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int s = b * ks * kU + kp * kU + u;
             const uint32_t cb = (uint32_t)s * kStep + 16u * ch;
-            const bool av = s < nsteps && cb < rowbytes && r8 < M;
+            const bool kv = s < nsteps && cb < rowbytes;
             // k of this lane's chunk: block cb / 32, half (cb / 16) % 2.
-            const int kb = (int)(cb / 32) * kBlockWeights + 16 * (int)((cb / 16) & 1);
+            const int kb = kv ? (int)(cb / 32) * kBlockWeights + 16 * (int)((cb / 16) & 1) : 0;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                a[u][g] = av ? *reinterpret_cast<const v4i *>(q_lds + r8 * K + kb + 32 * g)
-                             : v4i{0, 0, 0, 0};
+                a[u][g] = *reinterpret_cast<const v4i *>(q_lds + qrow + kb + 32 * g);
         }
     };
+    // The accumulators start at the first MFMAs (batch 0, step 0, which
+    // every wave runs) with a zero addend, so no register is cleared on the
+    // way from the quantisation to the first MFMA.
     v4i acc[R][4];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) acc[r][g] = v4i{0, 0, 0, 0};
     v4i aq[2][kU][4];
     read_q(aq[0], 0);
     unroll_ic([&](auto I) {
@@ -286,7 +290,8 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
                     *reinterpret_cast<const v4i *>(batch(I) + (r * kU + u) * 1024 + 16 * lane);
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    acc[r][g] = mfma16(aq[b & 1][u][g], unpack_scaled(bw, g), acc[r][g]);
+                    acc[r][g] = mfma16(aq[b & 1][u][g], unpack_scaled(bw, g),
+                                       b == 0 && u == 0 ? v4i{0, 0, 0, 0} : acc[r][g]);
             }
         }
     }, std::make_integer_sequence<int, NB>{});
