@@ -410,11 +410,14 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int k = t4 + STRIDE * i;
-            const uint32_t off = k < K ? 4u * (uint32_t)k : kOOB;
+            // Offsets past the row fall outside the resources (exactly K
+            // elements each; k and K are multiples of 4), so they read zeros
+            // with no select.
+            const uint32_t off = 4u * (uint32_t)k;
             // Chunks wholly past K (wave-uniform) are never read below: no
             // load and no initialisation.
             if (STRIDE * i + wk < K) {
-                xv[i] = load_x4<XT>(rx, k < K ? XB * (uint32_t)k : kOOB);
+                xv[i] = load_x4<XT>(rx, XB * (uint32_t)k);
                 if constexpr (GLU) uv[i] = buf_load_f4(ru, off);
                 gv[i] = gamma_f4(rg, off, norm);
             }
@@ -479,10 +482,11 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
     const auto rx = make_rsrc(x, XB * (uint32_t)K);
     const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
     const auto rg = gamma_rsrc(gamma, K);
-    auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
+    // (offsets past the row read zeros: the resources end at the row)
+    auto off_of = [&](int k) -> uint32_t { return 4u * (uint32_t)k; };
     // x of one chunk (GLU: formed from the gate and up rows)
     auto load_x = [&](int k) -> float4 {
-        const float4 v = load_x4<XT>(rx, k < K ? XB * (uint32_t)k : kOOB);
+        const float4 v = load_x4<XT>(rx, XB * (uint32_t)k);
         if constexpr (GLU) return relu2_mul4(v, buf_load_f4(ru, off_of(k)));
         else return v;
     };
@@ -558,8 +562,9 @@ __device__ __forceinline__ void wave_act_quant_row(const XT *__restrict__ x,
     const bool norm = gamma != nullptr;
     const auto rx = make_rsrc(x, XB * (uint32_t)K);
     const auto rg = gamma_rsrc(gamma, K);
-    auto off_of = [&](int k) -> uint32_t { return k < K ? 4u * (uint32_t)k : kOOB; };
-    auto xoff_of = [&](int k) -> uint32_t { return k < K ? XB * (uint32_t)k : kOOB; };
+    // (offsets past the row read zeros: the resources end at the row)
+    auto off_of = [&](int k) -> uint32_t { return 4u * (uint32_t)k; };
+    auto xoff_of = [&](int k) -> uint32_t { return XB * (uint32_t)k; };
     float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const bool in_regs = K <= 1024 * CI;
     float4 xv[CI][4], gv[CI][4];
