@@ -424,9 +424,10 @@ int device_cus() {
 // allocated weight LDS that stays unused (rows whose K share is shorter
 // than NB batches), weighted by bytes, plus small measured preferences.
 // With the quantisation fused in, two tiles per wave beat one (half the
-// workgroups repeat the quantisation); over q from global memory one tile
-// per wave is the faster (measured on MI355X, M = 1..4, K = 2560..8192: up
-// to 1.4x).  One workgroup per CU costs extra, four tiles per wave more.
+// workgroups repeat the quantisation) unless the device would be left
+// underfilled; over q from global memory one tile per wave is the faster
+// (measured on MI355X, M = 1..4, K = 2560..8192: up to 1.4x).  One
+// workgroup per CU costs extra, four tiles per wave more.
 // *rounds_out receives the chosen shape's rounds.
 int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, int pref,
                int64_t *rounds_out, bool fused) {
@@ -439,13 +440,17 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
     for (int i = 0; i < count; ++i) qmax = std::max<int64_t>(qmax, M[i] * K[i]);
     const int64_t q = (qmax + 1023) / 1024 * 1024;
     const int cus = device_cus();
-    auto rounds_of = [&](const ShotShape &h) -> int64_t {
+    auto wgs_of = [&](const ShotShape &h) -> int64_t {
         int64_t wgs = 0;
         for (int i = 0; i < count; ++i) {
             const int ks = shot_ks(K[i], h.nb);
             const int64_t ntg = (N[i] + kTileRows * h.R - 1) / (kTileRows * h.R);
             wgs += (ntg + kW / ks - 1) / (kW / ks);
         }
+        return wgs;
+    };
+    auto rounds_of = [&](const ShotShape &h) -> int64_t {
+        const int64_t wgs = wgs_of(h);
         const int64_t lds = (int64_t)h.nb * h.R * 8192 + q + 256;
         const int64_t per_cu = std::min<int64_t>(h.occupancy, (160 * 1024) / lds);
         return per_cu < 1 ? INT64_MAX : (wgs + per_cu * cus - 1) / (per_cu * cus);
@@ -477,6 +482,11 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
             score += h.R == 1 ? 10.0 : h.R == 4 ? 50.0 : 0.0;
         else
             score += h.R == 2 ? 10.0 : h.R == 4 ? 50.0 : 0.0;
+        // Fewer workgroups than CUs leave CUs without weights to stream:
+        // with the quantisation fused in this outweighs the tile
+        // preference (one BitLinear of N = 2560 at K = 6912: one tile per
+        // wave 5.7 us against two tiles 7.2 us, measured).
+        if (fused) score += 60.0 * std::max(0.0, 1.0 - (double)wgs_of(h) / cus);
         score += per_cu == 1 ? 20.0 : 0.0;
         if (best < 0 || rounds < best_rounds || (rounds == best_rounds && score < best_score)) {
             best = v;
