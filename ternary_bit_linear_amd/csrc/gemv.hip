@@ -209,14 +209,19 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &A) {
 #pragma unroll
             for (int h = 0; h < TH; ++h) {
                 const int t = 8 * h + r8;  // token (group-relative)
-                const bool av = kv && t < mg;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     if constexpr (MODE == 2) {
+                        const bool av = kv && t < mg;
                         a[h][g] = buf_load16(rq, av ? (uint32_t)(t * K + kb + 32 * g) : kOOB);
                     } else {
-                        a[h][g] = av ? *reinterpret_cast<const v4i *>(q_lds + t * K + kb + 32 * g)
-                                     : v4i{0, 0, 0, 0};
+                        // In-bounds LDS rows without zero-fill: tokens past
+                        // the group read its last row (their D rows are never
+                        // stored), chunks past K read chunk 0 (their weight
+                        // bytes are zeros).
+                        const int tc = min(t, mg - 1);
+                        a[h][g] = *reinterpret_cast<const v4i *>(q_lds + tc * K + (kv ? kb : 0) +
+                                                                 32 * g);
                     }
                 }
             }
@@ -455,12 +460,12 @@ __device__ __forceinline__ void gemv_ring_body(const GemvArgs &A) {
             v4i a[TH][4];
 #pragma unroll
             for (int h = 0; h < TH; ++h) {
-                const int t = 8 * h + r8;
-                const bool av = kv && t < mg;
+                // (in-bounds rows, no zero-fill: as in the register form)
+                const int tc = min(8 * h + r8, mg - 1);
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    a[h][g] = av ? *reinterpret_cast<const v4i *>(q_lds + t * K + kb + 32 * g)
-                                 : v4i{0, 0, 0, 0};
+                    a[h][g] = *reinterpret_cast<const v4i *>(q_lds + tc * K + (kv ? kb : 0) +
+                                                             32 * g);
             }
 #pragma unroll
             for (int g = 0; g < 4; ++g)

@@ -488,7 +488,18 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
         // wave 5.7 us against two tiles 7.2 us, measured).
         if (fused) score += 60.0 * std::max(0.0, 1.0 - (double)wgs_of(h) / cus);
         score += per_cu == 1 ? 20.0 : 0.0;
-        if (best < 0 || rounds < best_rounds || (rounds == best_rounds && score < best_score)) {
+        // Over q from global memory: more resident workgroups per CU keep
+        // more weight loads in flight.
+        if (!fused) score += 5.0 * (double)(4 - std::min<int64_t>(per_cu, 4));
+        // Fused: a later round repeats the quantisation chain, so rounds come
+        // first.  Over q from global memory the score comes first: more
+        // resident waves per CU beat fewer rounds (N = 28672, K = 8192:
+        // 4 batches x 1 tile over 3 rounds 12.4 us, 8 x 1 over 2 rounds
+        // 15.6 us, measured).
+        const bool better =
+            fused ? (rounds < best_rounds || (rounds == best_rounds && score < best_score))
+                  : (score < best_score || (score == best_score && rounds < best_rounds));
+        if (best < 0 || better) {
             best = v;
             best_rounds = rounds;
             best_score = score;
