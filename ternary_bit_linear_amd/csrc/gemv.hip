@@ -703,7 +703,11 @@ hipError_t launch_sep(const int8_t *q, const float *inv, const int32_t *qsum,
     const int64_t cap = std::max<int64_t>(1, (int64_t)cu_count() * resident_per_cu(kern, lds) / gy);
     const int ks = pick_ks(ntg, cap);
     const int64_t nset = (ntg + kW / ks - 1) / (kW / ks);
-    const unsigned gx = (unsigned)(nset < cap ? nset : cap);
+    // Every workgroup walks the same number of sets: a grid of cap with a
+    // few workgroups taking one set more leaves the device underused for
+    // that last set.
+    const int64_t per = (nset + cap - 1) / cap;
+    const unsigned gx = (unsigned)((nset + per - 1) / per);
     GemvArgs A{};
     A.ks = ks;
     A.q = q;
