@@ -356,6 +356,37 @@ def secondary_io(torch, api, steps, warmup):
     return {"workload": "decoder-layer BitLinears with bf16 activation I/O", **res}
 
 
+def secondary_nonorm(torch, api, steps, warmup):
+    """The decoder layer's BitLinears without RMSNorm (gamma NULL: the layer
+    with use_rms_norm off), one forward_batch call per step, beside the
+    step with RMSNorm."""
+    from ternary_bit_linear_amd import workloads as wl
+    work = wl.DECODE_LAYER
+    prep = Prepared(torch, api, work)
+
+    def step(r):
+        api.forward_batch([(d["x"], d["P"][r % prep.copies], d["s"], None, work.eps, d["y"],
+                            d["ws"]) for d in prep.lin])
+    gw = capture(torch, lambda: [step(r) for r in range(max(1, warmup))])
+    gt = capture(torch, lambda: [step(warmup + r) for r in range(steps)])
+    gw.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gt.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    del gw, gt
+    t_norm = time_steps(torch, api, prep, steps, warmup) * 1e-3
+    nbytes = sum(L.N * L.K // 4 + 4 * L.M * L.K + 4 * L.M * L.N for L in work.linears)
+    del prep
+    torch.cuda.empty_cache()
+    return {"workload": "decoder-layer BitLinears at decode without RMSNorm (gamma NULL)",
+            "us": round(t * 1e6, 2), "with_rmsnorm_us": round(t_norm * 1e6, 2),
+            "GBs": round(nbytes / t / 1e9, 1)}
+
+
 def secondary_dense(torch, api, steps, warmup):
     """Comparison: the decoder layer run the way the pages' BLAS route runs
     a prompt batch -- weights dequantised once (bitlinear_dequant_i2s, to
@@ -562,6 +593,8 @@ def main():
         out["secondary"]["io"] = secondary_io(torch, api, max(20, args.steps // 4), 5)
         torch.cuda.empty_cache()
         out["secondary"]["dense_comparison"] = secondary_dense(torch, api, max(20, args.steps // 4), 5)
+        torch.cuda.empty_cache()
+        out["secondary"]["no_rmsnorm"] = secondary_nonorm(torch, api, max(20, args.steps // 4), 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work)
     print(json.dumps(out), flush=True)
