@@ -268,7 +268,9 @@ size_t bitlinear_io_workspace_bytes(int64_t M, int64_t K, int64_t N);
  *   x: device [M][K] of x_dtype; y: device [M][N] of y_dtype; both 16-byte
  *   aligned.  Other arguments and errors as bitlinear_forward; an unknown
  *   dtype is BL_ERR_INVALID_ARG.  workspace: >=
- *   bitlinear_io_workspace_bytes(M, K, N).  Asynchronous on `stream`. */
+ *   bitlinear_io_workspace_bytes(M, K, N); after the call it holds q, inv
+ *   and qsum as bitlinear_forward's does (the accumulator region only on
+ *   the three-launch route).  Asynchronous on `stream`. */
 bl_status bitlinear_forward_io(const void *x, int x_dtype, const uint8_t *packed_w,
                                float w_scale, const float *gamma, float eps, int64_t M,
                                int64_t K, int64_t N, void *y, int y_dtype, void *workspace,
@@ -301,7 +303,8 @@ typedef struct {
  * bitlinear_forward_io does.
  *   descs: HOST array, 1 <= count <= 64, each validated as
  *   bitlinear_forward_io validates its arguments, all before anything is
- *   enqueued.  Asynchronous on `stream`. */
+ *   enqueued.  No output (y, workspace) may overlap any input or output of
+ *   another descriptor.  Asynchronous on `stream`. */
 bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count, void *stream);
 
 /* BitNet FFN block [HF-38087, the BitNetMLP excerpt of the review thread:
