@@ -331,7 +331,9 @@ bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count,
  *   workspace: device, >= bitlinear_ffn_workspace_bytes(M, H, F) bytes,
  *             16-byte aligned; after the call it holds g at offset 0 and u
  *             at offset align256(4*M*F) (fp32 [M][F] each), then the three
- *             projections' q / inv / qsum (and a, when F > 8192).
+ *             projections' q / inv / qsum (and a, when F > 8192); on the
+ *             grouped prefill route x is quantised once, into the gate's
+ *             part, which both contractions read.
  *   No output may overlap an input.  Errors as bitlinear_forward; all
  *   checks run before anything is enqueued.  Asynchronous on `stream`. */
 typedef struct {

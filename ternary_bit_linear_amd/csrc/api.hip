@@ -530,12 +530,25 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
     if (bl_status st = check_grid(M, nullptr)) return st;
     const FfnWorkspace w = carve_ffn(d.workspace, M, H, F);
     // 1. gate and up: two BitLinears over the same x.
+    hipStream_t s = as_stream(stream);
     const bl_forward_desc gu[2] = {
         {d.x, d.packed_gate, d.s_gate, d.gamma_in, d.eps, M, H, F, w.g, w.ws_gate, w.b_gate},
         {d.x, d.packed_up, d.s_up, d.gamma_in, d.eps, M, H, F, w.u, w.ws_up, w.b_gate}};
-    if (bl_status st = bitlinear_forward_batch(gu, 2, nullptr, stream)) return st;
+    if (!takes_fused(gu[0], nullptr) && takes_group(gu[0], nullptr)) {
+        // Prefill: x is quantised once (into the gate's workspace) and both
+        // contractions read that q in one grouped tile launch.
+        const Workspace wq = carve(w.ws_gate, M, H);
+        const bl::ActQuantDesc aq{d.x, d.gamma_in, d.eps, M, H, wq.q, wq.inv, wq.qsum};
+        const bl::GemmDesc gd[2] = {
+            {wq.q, wq.inv, wq.qsum, d.packed_gate, d.s_gate, M, H, F, w.g, nullptr},
+            {wq.q, wq.inv, wq.qsum, d.packed_up, d.s_up, M, H, F, w.u, nullptr}};
+        if (bl::launch_act_quant_batch(&aq, 1, s) != hipSuccess ||
+            bl::launch_gemm_group(gd, 2, s) != hipSuccess)
+            return BL_ERR_HIP;
+    } else if (bl_status st = bitlinear_forward_batch(gu, 2, nullptr, stream)) {
+        return st;
+    }
     // 2. down over relu2_mul(g, u), formed while its quantisation reads g, u.
-    hipStream_t s = as_stream(stream);
     const Workspace wd = carve(w.ws_down, M, F);
     const int64_t Ms[1] = {M}, Ks[1] = {F}, Ns[1] = {H};
     if (M == 1 && F <= 8 * 1024 && bl::shot_fused_supported(M, F) &&
