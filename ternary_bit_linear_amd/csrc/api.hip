@@ -281,7 +281,6 @@ bl_status flush_io_group(const bl_forward_io_desc *const *g, int n, hipStream_t 
     return BL_OK;
 }
 
-
 }  // namespace
 
 extern "C" {
