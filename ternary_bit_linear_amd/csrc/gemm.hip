@@ -297,7 +297,9 @@ constexpr Tile kTiles[] = {{64, 256, 1, 4, 3}, {64, 128, 1, 4, 3}, {64, 64, 2, 2
                            {128, 256, 1, 4, 3}, {64, 256, 1, 4, 4}, {64, 128, 1, 4, 0},
                            {128, 128, 2, 2, 0}, {64, 64, 2, 2, 3},  {32, 64, 1, 4, 3},
                            {128, 256, 2, 4, 3}, {64, 512, 1, 8, 3}, {64, 512, 1, 8, 4},
-                           {64, 512, 1, 8, 5},  {64, 256, 1, 8, 4}, {32, 512, 1, 8, 4}};
+                           {64, 512, 1, 8, 5},  {64, 256, 1, 8, 4}, {32, 512, 1, 8, 4},
+                           {16, 256, 1, 4, 0},  {16, 128, 1, 4, 0}, {32, 32, 2, 2, 0},
+                           {16, 32, 1, 2, 0},   {16, 64, 1, 4, 0}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // Ring depth for a tile: the deepest of 4, 5, 3 that divides the step count
@@ -411,7 +413,8 @@ hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
 hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
     if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
     const bool y = d[0].y != nullptr;
-    int64_t t64x512 = 0, t64x256 = 0, t64x128 = 0, t32x128 = 0, kmax = 0;
+    int64_t t64x512 = 0, t64x256 = 0, t64x128 = 0, t32x128 = 0, t16x128 = 0, t16x64 = 0, kmax = 0,
+            mmax = 0;
     double work = 0.0, work_k = 0.0;  // int ops, and int ops x K
     for (int i = 0; i < count; ++i) {
         if (!gemm_group_supported(d[i].K) || (d[i].y != nullptr) != y || d[i].io != d[0].io)
@@ -423,7 +426,10 @@ hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
         t64x256 += tiles(64, 256);
         t64x128 += tiles(64, 128);
         t32x128 += tiles(32, 128);
+        t16x128 += tiles(16, 128);
+        t16x64 += tiles(16, 64);
         kmax = std::max<int64_t>(kmax, d[i].K);
+        mmax = std::max<int64_t>(mmax, d[i].M);
         const double w = (double)d[i].M * (double)d[i].N * (double)d[i].K;
         work += w;
         work_k += w * (double)d[i].K;
@@ -442,6 +448,17 @@ hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
         pad5 += w * (double)((5 - ns % 5) % 5) / (double)ns;
     }
     const bool r5 = pad5 < pad4;
+    if (mmax <= 32) {
+        // Few tokens: 16-row tiles, as for a single problem.
+        if (t16x128 >= 200)
+            return r5 ? launch_group_tile<16, 128, 1, 4, 5>(d, count, s)
+                      : launch_group_tile<16, 128, 1, 4, 4>(d, count, s);
+        if (t16x64 >= 200)
+            return r5 ? launch_group_tile<16, 64, 1, 4, 5>(d, count, s)
+                      : launch_group_tile<16, 64, 1, 4, 4>(d, count, s);
+        return r5 ? launch_group_tile<16, 32, 1, 2, 5>(d, count, s)
+                  : launch_group_tile<16, 32, 1, 2, 4>(d, count, s);
+    }
     if (t64x512 >= 512) return launch_group_tile<64, 512, 1, 8, 4>(d, count, s);
     if (k_avg >= 6144.0 && t64x256 >= 256) return launch_group_tile<64, 256, 1, 8, 4>(d, count, s);
     if (t64x128 >= 256)
@@ -469,7 +486,12 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         // (8 waves; long K only: short rows do not amortise its fill), 64x128
         // down to one per CU, then 32-row tiles (the wider one for long K).
         auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-        if (tiles(64, 512) >= 512)
+        if (M <= 32)
+            // Few tokens: 16-row tiles, the widest that still gives about one
+            // tile per CU (M = 16, K = 8192: N = 8192 16x32 8.8 us against
+            // 32x64 10.3 us; N = 28672 16x128; measured).
+            v = tiles(16, 128) >= 200 ? 20 : tiles(16, 64) >= 200 ? 23 : 22;
+        else if (tiles(64, 512) >= 512)
             v = 15;
         else if (K >= 6144 && tiles(64, 256) >= 256)
             v = 17;
@@ -504,6 +526,11 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         BL_GEMM_CASE(16)
         BL_GEMM_CASE(17)
         BL_GEMM_CASE(18)
+        BL_GEMM_CASE(19)
+        BL_GEMM_CASE(20)
+        BL_GEMM_CASE(21)
+        BL_GEMM_CASE(22)
+        BL_GEMM_CASE(23)
         default:
             return hipErrorInvalidValue;
     }

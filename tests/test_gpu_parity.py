@@ -985,3 +985,30 @@ def test_dequant_parity(torch, bl, orc, N, K, dt):
         assert np.array_equal(host(got).view(np.uint32), ref.view(np.uint32))
     else:
         assert np.array_equal(bits16(torch, got), np.asarray(ref).view(np.uint16))
+
+
+def test_forward_batch_few_token_tiles(torch, bl, orc):
+    """Prefill-route problems of 5..32 tokens take 16-row tiles (grouped and
+    single, each width): the oracle's outputs within 1e-5, the single calls'
+    bits."""
+    shapes = [(5, 1024, 96), (16, 2560, 6912), (17, 512, 300), (32, 2048, 8192), (9, 9216, 64),
+              (16, 768, 4000)]
+    items, singles, refs = [], [], []
+    for i, (M, K, N) in enumerate(shapes):
+        x, w, t, g = mm_case(M, K, N, 1700 + i)
+        packed_r, s = orc.pack_i2s(w)
+        X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+        out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        ws = bl.new_workspace(M, K)
+        items.append((X, P, s, G, 1e-6, out, ws))
+        singles.append(host(bl.forward(X, P, s, G, 1e-6, N)).copy())
+        rows = np.arange(0, N, max(1, N // 97))
+        refs.append((rows, orc.forward(x, orc.packed_rows(packed_r, K, rows), s, g, 1e-6,
+                                       rows.size)))
+    announce("forward_batch few-token tiles", len(items))
+    bl.forward_batch(items)
+    torch.cuda.synchronize()
+    for it, single, (rows, y64), sh in zip(items, singles, refs, shapes):
+        got = host(it[5])
+        assert np.array_equal(got, single), sh
+        check_y(got[:, rows], y64)
