@@ -481,8 +481,9 @@ def main():
                          "copy (the calibration kernel for HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(the multi-GPU N-split is described in DESIGN.md, not built)", file=sys.stderr)
+        print("bench.py: one GPU only; --gpus must be 1 "
+              "(the library runs one GPU per process; a multi-GPU split of N is not built)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -198,7 +198,7 @@ typedef struct {
 } bl_forward_desc;
 
 /* Several independent BitLinear forwards, e.g. the BitLinears of one decoder
- * layer at decode (the survey's decode-layer launch).  Results are
+ * layer at decode (one launch for the whole layer).  Results are
  * bit-identical to calling bitlinear_forward_ex(descs[i], launch) for each i.
  * The decode-sized ones (M <= 4 with the fused quantisation) share one
  * kernel launch per 8; with the automatic launch shape, the prefill-sized
