@@ -825,7 +825,7 @@ hipError_t launch_shape_fused(const FusedDecode *d, int count, hipStream_t s) {
 // shape; kNumShapes + 1: the one-shot form (gemv_shot.hip) where it applies,
 // launch shape picked from the problems; kNumShapes + 1 + j: the one-shot
 // form with its launch shape j (taken when every problem fits it).
-constexpr int kShotVariants = 7;
+constexpr int kShotVariants = 9;
 int gemv_num_variants() { return kNumShapes + kShotVariants; }
 
 static int shot_shape_of(int variant) { return variant - kNumShapes - 1; }

@@ -39,7 +39,7 @@
 namespace bl {
 namespace {
 
-constexpr int kW = 4;          // waves per workgroup
+constexpr int kMaxKs = 4;      // waves splitting one tile group's K range, at most
 constexpr int kTileRows = 8;   // weight rows per tile
 constexpr int kStep = 128;     // packed bytes of a row per step (512 k)
 constexpr int kU = 2;          // steps per batch
@@ -114,23 +114,29 @@ __device__ __forceinline__ v4i field_sum(const v4i (&a)[4]) {
 // IO: storage type of x and y with the fused quantisation (float, bf16_t,
 // _Float16): x is widened to fp32 as it is loaded, y rounded as it is
 // stored.
+// W: waves per workgroup, 4, 8 or 16.  The quantisation is the 256-thread
+// block form; in a larger workgroup waves 4..W-1 issue their weights and
+// meet its barriers, so a CU that holds one such workgroup normalises x once
+// where several 4-wave workgroups would each do it.
 template <int NB, int R, bool OUT_Y, int FM, int CH, bool LONG, bool GLU = false,
-          typename IO = float>
-__global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, int b3, int b4,
+          typename IO = float, int W = 4>
+__global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b2, int b3, int b4,
                                                         int b5, int b6, int b7, ShotBatch B) {
     static_assert(NB >= 1 && NB <= 8, "batches per wave");
     static_assert(R == 1 || R == 2 || R == 4, "tiles per wave");
     static_assert(kMaxShotBatch == 8, "one leading argument per problem");
-    static_assert(kU == 2 && kW == 4, "shift forms below assume kU == 2, kW == 4");
+    static_assert(W == 4 || W == 8 || W == 16, "waves per workgroup");
+    static_assert(kU == 2, "shift forms below assume kU == 2");
+    constexpr int LW = W == 16 ? 4 : W == 8 ? 3 : 2;  // log2(W)
     static_assert(FM >= 0 && FM <= kMaxShotM, "fused token rows");
     extern __shared__ __align__(16) int8_t q_lds[];
     // One LDS object per batch (rows: waves), so that the compiler's own
     // LDS-DMA tracking tells the batches apart and waits for each alone.
     constexpr int SZ = R * kU * 1024;  // one batch of one wave
-    __shared__ __align__(16) int8_t w0[kW][SZ], w1[NB > 1 ? kW : 1][NB > 1 ? SZ : 16],
-        w2[NB > 2 ? kW : 1][NB > 2 ? SZ : 16], w3[NB > 3 ? kW : 1][NB > 3 ? SZ : 16],
-        w4[NB > 4 ? kW : 1][NB > 4 ? SZ : 16], w5[NB > 5 ? kW : 1][NB > 5 ? SZ : 16],
-        w6[NB > 6 ? kW : 1][NB > 6 ? SZ : 16], w7[NB > 7 ? kW : 1][NB > 7 ? SZ : 16];
+    __shared__ __align__(16) int8_t w0[W][SZ], w1[NB > 1 ? W : 1][NB > 1 ? SZ : 16],
+        w2[NB > 2 ? W : 1][NB > 2 ? SZ : 16], w3[NB > 3 ? W : 1][NB > 3 ? SZ : 16],
+        w4[NB > 4 ? W : 1][NB > 4 ? SZ : 16], w5[NB > 5 ? W : 1][NB > 5 ? SZ : 16],
+        w6[NB > 6 ? W : 1][NB > 6 ? SZ : 16], w7[NB > 7 ? W : 1][NB > 7 ? SZ : 16];
     __shared__ float red[kRedWords];
     __shared__ float inv_sh[FM > 0 ? FM : 1];
     __shared__ int qsum_sh[FM > 0 ? FM : 1];
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
     const int sg = wid >> kl, kp = wid & (ks - 1);
     const int nb = (nsteps + ks * kU - 1) >> (kl + 1);   // <= NB (kU == 2)
     const int st = bx - P.wg_begin;                     // this workgroup's set
-    const int tg = (st << (2 - kl)) + sg;               // this wave's tile group (kW == 4)
+    const int tg = (st << (LW - kl)) + sg;              // this wave's tile group
     const int n0 = tg * kTileRows * R;
     auto batch = [&](auto I) -> int8_t * {
         constexpr int b = decltype(I)::value;
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
         //    wave load, loads spread over the waves; 2. the weights.
         const uint32_t qbytes = (uint32_t)(M * K);
         const auto rq = make_rsrc(P.q, qbytes);
-        for (uint32_t c = (uint32_t)wid * 1024u; c < qbytes; c += kW * 1024u)
+        for (uint32_t c = (uint32_t)wid * 1024u; c < qbytes; c += W * 1024u)
             buf_load16_lds(rq, q_lds + c, c + 16u * lane, 0);
         issue_weights();
         // 3. Own activation loads done (only weight loads may still be in
@@ -229,22 +235,37 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
         // 1. x and gamma of the first row go out first, the weights right
         //    behind them; 2. RMSNorm + quantisation of every row into LDS
         //    while the weights stream in.
-        {
-            ShotRowSink sink{q_lds, inv_sh, qsum_sh, st == 0 ? P.q_out : nullptr, P.inv_out,
-                             P.qsum_out};
-            block_act_quant_row<CH, LONG, false, GLU, IO>(reinterpret_cast<const IO *>(P.x),
-                                                          P.gamma, P.eps, K, red, sink,
-                                                          issue_weights, P.u);
-        }
+        if (W == 4 || wid < 4) {
+            {
+                ShotRowSink sink{q_lds, inv_sh, qsum_sh, st == 0 ? P.q_out : nullptr, P.inv_out,
+                                 P.qsum_out};
+                block_act_quant_row<CH, LONG, false, GLU, IO>(reinterpret_cast<const IO *>(P.x),
+                                                              P.gamma, P.eps, K, red, sink,
+                                                              issue_weights, P.u);
+            }
 #pragma unroll
-        for (int m = 1; m < FM; ++m) {
-            if (m < M) {
-                ShotRowSink sink{q_lds + m * K, inv_sh + m, qsum_sh + m,
-                                 st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m,
-                                 P.qsum_out + m};
-                block_act_quant_row<CH, LONG, false, GLU, IO>(
-                    reinterpret_cast<const IO *>(P.x) + (size_t)m * K, P.gamma, P.eps, K, red,
-                    sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr);
+            for (int m = 1; m < FM; ++m) {
+                if (m < M) {
+                    ShotRowSink sink{q_lds + m * K, inv_sh + m, qsum_sh + m,
+                                     st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m,
+                                     P.qsum_out + m};
+                    block_act_quant_row<CH, LONG, false, GLU, IO>(
+                        reinterpret_cast<const IO *>(P.x) + (size_t)m * K, P.gamma, P.eps, K,
+                        red, sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr);
+                }
+            }
+        } else {
+            // Waves 4..W-1: their weights, then one barrier per block
+            // reduction of each row (sum of squares with RMSNorm, max, sum).
+            issue_weights();
+            const bool norm = P.gamma != nullptr;
+#pragma unroll
+            for (int m = 0; m < FM; ++m) {
+                if (m < M) {
+                    if (norm) lds_barrier();
+                    lds_barrier();
+                    lds_barrier();
+                }
             }
         }
         lds_barrier();
@@ -336,7 +357,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
     }
     // ks > 1: the partial tiles go to each wave's first weight buffer, no
     // longer needed, and the first wave of each group sums them.
-    v4i *part = reinterpret_cast<v4i *>(&w0[0][0]);  // [kW][SZ / 16] v4i, R * 64 used
+    v4i *part = reinterpret_cast<v4i *>(&w0[0][0]);  // [W][SZ / 16] v4i, R * 64 used
     constexpr int PS = SZ / 16;
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -357,7 +378,7 @@ __global__ __launch_bounds__(256) void gemv_shot_kernel(int b0, int b1, int b2, 
 // row into NB batches, or 0.
 int shot_ks(int64_t K, int nbmax) {
     const int64_t nsteps = (K / 4 + kStep - 1) / kStep;
-    for (int ks = 1; ks <= kW; ks *= 2)
+    for (int ks = 1; ks <= kMaxKs; ks *= 2)
         if ((nsteps + ks * kU - 1) / (ks * kU) <= nbmax) return ks;
     return 0;
 }
@@ -365,14 +386,14 @@ int shot_ks(int64_t K, int nbmax) {
 // Fills the batch: each problem's K split and first workgroup (begin[i];
 // INT_MAX past the last problem).  Returns the grid size; *qmax receives the
 // largest activation block (bytes).
-int64_t fill_batch(ShotBatch &B, int *begin, int count, int nb, int R, const int64_t *M,
+int64_t fill_batch(ShotBatch &B, int *begin, int count, int nb, int R, int W, const int64_t *M,
                    const int64_t *K, const int64_t *N, int64_t *qmax) {
     int64_t gx = 0;
     *qmax = 0;
     for (int i = 0; i < count; ++i) {
         const int ks = shot_ks(K[i], nb);
         const int64_t ntg = (N[i] + kTileRows * R - 1) / (kTileRows * R);
-        const int64_t nset = (ntg + kW / ks - 1) / (kW / ks);
+        const int64_t nset = (ntg + W / ks - 1) / (W / ks);
         ShotProblem &P = B.p[i];
         P.M = (int)M[i];
         P.K = (int)K[i];
@@ -388,22 +409,24 @@ int64_t fill_batch(ShotBatch &B, int *begin, int count, int nb, int R, const int
 }
 
 template <class Kernel>
-hipError_t launch_batch(Kernel kern, const ShotBatch &B, const int *b, int64_t gx, int64_t qmax,
-                        hipStream_t s) {
+hipError_t launch_batch(Kernel kern, int W, const ShotBatch &B, const int *b, int64_t gx,
+                        int64_t qmax, hipStream_t s) {
     const size_t lds = (size_t)((qmax + 1023) / 1024 * 1024);
     if (gx < 1 || gx > INT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(256), lds, s, b[0], b[1], b[2], b[3], b[4],
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(64 * W), lds, s, b[0], b[1], b[2], b[3], b[4],
                        b[5], b[6], b[7], B);
     return hipGetLastError();
 }
 
-// Launch shapes: weight batches per wave (NB) x tiles per wave (R).  A
-// workgroup holds NB * R * 8 KB of weights in LDS.
+// Launch shapes: weight batches per wave (NB) x tiles per wave (R) x waves
+// per workgroup (W).  A workgroup holds NB * R * W * 2 KB of weights in LDS.
 struct ShotShape {
     int nb, R;
     int occupancy;  // workgroups per CU that the registers allow
+    int w;
 };
-constexpr ShotShape kShotShapes[] = {{3, 1, 4}, {4, 1, 4}, {8, 1, 4}, {3, 2, 3}, {4, 2, 3}, {3, 4, 3}};
+constexpr ShotShape kShotShapes[] = {{3, 1, 4, 4}, {4, 1, 4, 4}, {8, 1, 4, 4}, {3, 2, 3, 4},
+                                     {4, 2, 3, 4}, {3, 4, 3, 4}, {3, 2, 1, 8}, {3, 1, 1, 16}};
 constexpr int kNumShotShapes = sizeof(kShotShapes) / sizeof(kShotShapes[0]);
 
 int device_cus() {
@@ -428,9 +451,45 @@ int device_cus() {
 // underfilled; over q from global memory one tile per wave is the faster
 // (measured on MI355X, M = 1..4, K = 2560..8192: up to 1.4x).  One
 // workgroup per CU costs extra, four tiles per wave more.
+// One token with the quantisation fused in (the decode case) takes, after
+// rounds, an estimate of the launch time instead of that score, and is the
+// only case that considers the 8- and 16-wave shapes (one_token_cost; not
+// taken with the gated FFN input, `wide` false).
 // *rounds_out receives the chosen shape's rounds.
+// Estimated time (us) of a one-round fused launch for one token, a linear
+// model fitted to the measured times of every shape on twelve decode problem
+// sets (M = 1, K = 2048..8192, one to seven BitLinears; MI355X, two runs,
+// rms error 0.4 us).  A CU that holds c workgroups streams c times the
+// largest workgroup's weight bytes and runs c quantisation chains of up to
+// max K elements; splitting a row's K over 2 or 4 waves costs the
+// partial-sum reduction and shorter streams; four tiles per wave, eight
+// batches per wave and weight batches past a row's end cost their own.
+// Over the sets it picks the fastest shape in eleven, and in the twelfth
+// one as fast as the score's pick.
+double one_token_cost(const ShotShape &h, const int64_t *K, const int64_t *N, int count,
+                      int cus) {
+    int64_t wgs = 0, kmax = 0, unused = 0;
+    double wg_bytes = 0.0;
+    int ksmax = 1;
+    for (int i = 0; i < count; ++i) {
+        const int ks = shot_ks(K[i], h.nb);
+        const int slots = h.w / ks;
+        const int64_t ntg = (N[i] + kTileRows * h.R - 1) / (kTileRows * h.R);
+        wgs += (ntg + slots - 1) / slots;
+        wg_bytes = std::max(wg_bytes, (double)slots * kTileRows * h.R * (double)(K[i] / 4));
+        kmax = std::max<int64_t>(kmax, K[i]);
+        ksmax = std::max(ksmax, ks);
+        const int64_t nsteps = (K[i] / 4 + kStep - 1) / kStep;
+        unused = std::max<int64_t>(unused, h.nb - (nsteps + ks * kU - 1) / (ks * kU));
+    }
+    const double c = (double)((wgs + cus - 1) / cus);
+    return 0.043 * c * wg_bytes / 1024.0 + 0.063 * c * (double)kmax / 1024.0 +
+           (ksmax == 4 ? 0.93 : ksmax == 2 ? 0.60 : 0.0) + (h.R == 4 ? 0.71 : 0.0) +
+           (h.nb == 8 ? 0.67 : 0.0) + 0.037 * (double)(unused * h.R);
+}
+
 int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, int pref,
-               int64_t *rounds_out, bool fused) {
+               int64_t *rounds_out, bool fused, bool wide = true) {
     auto fits = [&](int nb) {
         for (int i = 0; i < count; ++i)
             if (shot_ks(K[i], nb) == 0) return false;
@@ -445,13 +504,13 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
         for (int i = 0; i < count; ++i) {
             const int ks = shot_ks(K[i], h.nb);
             const int64_t ntg = (N[i] + kTileRows * h.R - 1) / (kTileRows * h.R);
-            wgs += (ntg + kW / ks - 1) / (kW / ks);
+            wgs += (ntg + h.w / ks - 1) / (h.w / ks);
         }
         return wgs;
     };
     auto rounds_of = [&](const ShotShape &h) -> int64_t {
         const int64_t wgs = wgs_of(h);
-        const int64_t lds = (int64_t)h.nb * h.R * 8192 + q + 256;
+        const int64_t lds = (int64_t)h.nb * h.R * h.w * 2048 + q + 256;
         const int64_t per_cu = std::min<int64_t>(h.occupancy, (160 * 1024) / lds);
         return per_cu < 1 ? INT64_MAX : (wgs + per_cu * cus - 1) / (per_cu * cus);
     };
@@ -459,14 +518,25 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
         *rounds_out = rounds_of(kShotShapes[pref - 1]);
         return pref - 1;
     }
+    bool one_token = fused && wide;
+    for (int i = 0; i < count; ++i) one_token = one_token && M[i] == 1;
     int best = -1;
     int64_t best_rounds = 0;
     double best_score = 0.0;
     for (int v = 0; v < kNumShotShapes; ++v) {
         const ShotShape &h = kShotShapes[v];
-        if (!fits(h.nb)) continue;
+        if (!fits(h.nb) || (h.w != 4 && !one_token)) continue;
         const int64_t rounds = rounds_of(h);
         if (rounds == INT64_MAX) continue;
+        if (one_token) {
+            const double est = one_token_cost(h, K, N, count, cus);
+            if (best < 0 || rounds < best_rounds || (rounds == best_rounds && est < best_score)) {
+                best = v;
+                best_rounds = rounds;
+                best_score = est;
+            }
+            continue;
+        }
         double used = 0.0, total = 0.0;
         for (int i = 0; i < count; ++i) {
             const int64_t nsteps = (K[i] / 4 + kStep - 1) / kStep;
@@ -475,7 +545,7 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
             used += bytes * ((double)nsteps / ks) / (h.nb * kU);
             total += bytes;
         }
-        const int64_t lds = (int64_t)h.nb * h.R * 8192 + q + 256;
+        const int64_t lds = (int64_t)h.nb * h.R * h.w * 2048 + q + 256;
         const int64_t per_cu = std::min<int64_t>(h.occupancy, (160 * 1024) / lds);
         double score = 100.0 * (1.0 - used / total);
         if (fused)
@@ -509,7 +579,7 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
     return best;
 }
 
-template <int NB, int R, bool OUT_Y>
+template <int NB, int R, int W, bool OUT_Y>
 hipError_t launch_shot_nb(const ShotDecode *d, int count, hipStream_t s) {
     ShotBatch B{};
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
@@ -527,11 +597,12 @@ hipError_t launch_shot_nb(const ShotDecode *d, int count, hipStream_t s) {
         P.w_scale = d[i].w_scale;
     }
     int begin[kMaxShotBatch];
-    const int64_t gx = fill_batch(B, begin, count, NB, R, M, K, N, &qmax);
-    return launch_batch(gemv_shot_kernel<NB, R, OUT_Y, 0, 1, false>, B, begin, gx, qmax, s);
+    const int64_t gx = fill_batch(B, begin, count, NB, R, W, M, K, N, &qmax);
+    return launch_batch(gemv_shot_kernel<NB, R, OUT_Y, 0, 1, false, false, float, W>, W, B, begin,
+                        gx, qmax, s);
 }
 
-template <int NB, int R, int FM, int CH, bool LONG, bool GLU, typename IO>
+template <int NB, int R, int W, int FM, int CH, bool LONG, bool GLU, typename IO>
 hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) {
     ShotBatch B{};
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
@@ -552,32 +623,34 @@ hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) 
         P.u = d[i].u;
     }
     int begin[kMaxShotBatch];
-    const int64_t gx = fill_batch(B, begin, count, NB, R, M, K, N, &qmax);
-    return launch_batch(gemv_shot_kernel<NB, R, true, FM, CH, LONG, GLU, IO>, B, begin, gx, qmax,
-                        s);
+    const int64_t gx = fill_batch(B, begin, count, NB, R, W, M, K, N, &qmax);
+    return launch_batch(gemv_shot_kernel<NB, R, true, FM, CH, LONG, GLU, IO, W>, W, B, begin, gx,
+                        qmax, s);
 }
 
 #define BL_SHOT_SHAPES(CALL)                                                   \
     switch (v) {                                                               \
-        case 0: return CALL(3, 1);                                             \
-        case 1: return CALL(4, 1);                                             \
-        case 2: return CALL(8, 1);                                             \
-        case 3: return CALL(3, 2);                                             \
-        case 4: return CALL(4, 2);                                             \
-        case 5: return CALL(3, 4);                                             \
+        case 0: return CALL(3, 1, 4);                                          \
+        case 1: return CALL(4, 1, 4);                                          \
+        case 2: return CALL(8, 1, 4);                                          \
+        case 3: return CALL(3, 2, 4);                                          \
+        case 4: return CALL(4, 2, 4);                                          \
+        case 5: return CALL(3, 4, 4);                                          \
+        case 6: return CALL(3, 2, 8);                                          \
+        case 7: return CALL(3, 1, 16);                                         \
         default: return hipErrorInvalidValue;                                  \
     }
 
 template <int FM, int CH, bool LONG, bool GLU = false, typename IO = float>
 hipError_t launch_fused_ch(const FusedDecode *d, int count, int v, hipStream_t s) {
-#define BL_F(NB_, R_) launch_shot_fused_nb<NB_, R_, FM, CH, LONG, GLU, IO>(d, count, s)
+#define BL_F(NB_, R_, W_) launch_shot_fused_nb<NB_, R_, W_, FM, CH, LONG, GLU, IO>(d, count, s)
     BL_SHOT_SHAPES(BL_F)
 #undef BL_F
 }
 
 template <bool OUT_Y>
 hipError_t launch_sep(const ShotDecode *d, int count, int v, hipStream_t s) {
-#define BL_S(NB_, R_) launch_shot_nb<NB_, R_, OUT_Y>(d, count, s)
+#define BL_S(NB_, R_, W_) launch_shot_nb<NB_, R_, W_, OUT_Y>(d, count, s)
     BL_SHOT_SHAPES(BL_S)
 #undef BL_S
 }
@@ -634,7 +707,7 @@ hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hi
         mmax = std::max<int64_t>(mmax, d[i].M);
     }
     int64_t rounds;
-    const int v = pick_shape(M, K, N, count, shape, &rounds, true);
+    const int v = pick_shape(M, K, N, count, shape, &rounds, true, !glu);
     // One token everywhere (the decode case): the kernel that normalises a
     // single row, whose code is a quarter of the general one's.
     if (io == kIoBf16) {

@@ -405,6 +405,69 @@ def test_forward_batch_matches_single_calls(torch, bl, orc):
             assert np.array_equal(host(it[5]), single), v
 
 
+@pytest.mark.parametrize("norm", [True, False])
+def test_decode_every_shape_wide_workgroups(torch, bl, orc, norm):
+    """One-token decode batches whose rows take K splits of 1, 2 and 4 waves
+    and ragged N, forced through every launch shape -- the 4-wave shapes and
+    the 8- and 16-wave workgroups, where only the first four waves normalise
+    and quantise and the others meet their barriers -- and the persistent
+    form: y bit for bit the same in every shape and within 1e-5 of the
+    oracle; the first workgroup's q / inv / qsum are the oracle's."""
+    shapes = [(2560, 640), (6912, 2560), (8192, 1000), (1024, 200), (384, 40), (2560, 6912)]
+    items, refs, xs = [], [], []
+    for i, (K, N) in enumerate(shapes):
+        x, w, t, g = mm_case(1, K, N, 1700 + 7 * i + (0 if norm else 3))
+        gg = g if norm else None
+        packed_r, s = orc.pack_i2s(w)
+        refs.append(orc.forward(x, packed_r, s, gg, 1e-6, N))
+        X, P = dev(torch, x), dev(torch, packed_r)
+        G = dev(torch, g) if norm else None
+        out = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda")
+        items.append((X, P, s, G, 1e-6, out, bl.new_workspace(1, K)))
+        xs.append((x, gg, K))
+    announce("decode every shape", norm)
+    bl.forward_batch(items)
+    torch.cuda.synchronize()
+    ref_bits = [host(it[5]).copy() for it in items]
+    for y, y64 in zip(ref_bits, refs):
+        check_y(y, y64)
+    for v in range(1, bl.num_variants(1) + 1):
+        for it in items:
+            it[5].fill_(float("nan"))
+            it[6].fill_(0)
+        bl.forward_batch(items, path=1, variant=v)
+        torch.cuda.synchronize()
+        for it, y, (x, gg, K) in zip(items, ref_bits, xs):
+            assert np.array_equal(host(it[5]), y), v
+            q, inv, qs = bl.workspace_views(it[6], 1, K)
+            q_r, inv_r, qs_r = orc.act_quant(x, gg, 1e-6)
+            assert np.array_equal(host(q), q_r) and np.array_equal(host(inv), inv_r), v
+            assert np.array_equal(host(qs), qs_r), v
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_forward_io_decode_layer(torch, bl, orc, dt):
+    """The decoder layer's seven BitLinears at full size, one token, x and y
+    in bf16 / fp16, as one typed batch (one fused launch): y bit for bit the
+    oracle's."""
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    work = wl.DECODE_LAYER
+    items, refs = [], []
+    for i, L in enumerate(work.linears):
+        x32, w, t, g = work.inputs(i)
+        x = orc.from_f32(x32, dt)
+        packed_r, s = orc.pack_i2s(w)
+        refs.append(orc.forward_io(x, dt, packed_r, s, g, work.eps, L.N, dt))
+        out = torch.empty((L.M, L.N), dtype=tdt, device="cuda")
+        items.append((torch_io(torch, x, dt), dev(torch, packed_r), s, dev(torch, g), work.eps,
+                      out, bl.io_workspace(L.M, L.K, L.N)))
+    announce("forward_io decode layer", dt)
+    bl.forward_io_batch(items)
+    torch.cuda.synchronize()
+    for it, ref, L in zip(items, refs, work.linears):
+        assert np.array_equal(bits16(torch, it[5]), np.asarray(ref).view(np.uint16)), L
+
+
 def test_forward_batch_grouped_prefill(torch, bl, orc):
     """Prefill-sized problems of a batch (K a whole number of 256-k steps,
     K <= 8192) go out as one batched quantisation launch and one grouped
