@@ -201,9 +201,12 @@ typedef struct {
  * layer at decode (one launch for the whole layer).  Results are
  * bit-identical to calling bitlinear_forward_ex(descs[i], launch) for each i.
  * The decode-sized ones (M <= 4 with the fused quantisation) share one
- * kernel launch per 8; with the automatic launch shape, the prefill-sized
- * ones with K % 256 == 0 and K <= 8192 share one quantisation launch and one
- * tile-kernel launch per 8; the others run one by one.
+ * kernel launch per 8.  With the automatic launch shape, the other
+ * decode-sized ones with M * K <= 32768 and K <= 8192 (a few tokens) share
+ * one quantisation launch and one one-shot contraction launch per 8, and
+ * the prefill-sized ones with K % 256 == 0 and K <= 8192 share one
+ * quantisation launch and one tile-kernel launch per 8; the others run one
+ * by one.
  *   descs:  HOST array of `count` descriptors (1 <= count <= 64, else
  *           BL_ERR_INVALID_ARG); each is validated as bitlinear_forward
  *           validates its arguments, all before anything is enqueued.
@@ -262,9 +265,12 @@ size_t bitlinear_io_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * fp16: IEEE binary16, overflow to inf).  With both types BL_F32 the bits
  * equal bitlinear_forward's.  One token with K <= 8192 and x_dtype ==
  * y_dtype: one launch (the one-shot decode kernel with the quantisation and
- * the rescale inside) when its workgroups fit on the device at once;
- * otherwise three launches: quantisation, contraction to the int32
- * accumulator in the workspace, rescale.
+ * the rescale inside) when its workgroups fit on the device at once.
+ * Otherwise two launches, the quantisation and a contraction that rounds y
+ * in its epilogue, when K <= 8192 and either M <= 4 with M * K <= 32768
+ * (the one-shot kernel) or M > 4 with K % 256 == 0 (the tile kernel); else
+ * three: quantisation, contraction to the int32 accumulator in the
+ * workspace, rescale.
  *   x: device [M][K] of x_dtype; y: device [M][N] of y_dtype; both 16-byte
  *   aligned.  Other arguments and errors as bitlinear_forward; an unknown
  *   dtype is BL_ERR_INVALID_ARG.  workspace: >=
@@ -296,10 +302,13 @@ typedef struct {
  * with bf16 activations); per descriptor bit-identical to
  * bitlinear_forward_io.  Those with M = 1, K <= 8192 and x_dtype ==
  * y_dtype share one one-shot launch per 8 and per type (quantisation and
- * rescale inside it) when their workgroups fit on the device at once; the
- * prefill-sized ones (M > 4, K % 256 == 0, K <= 8192) share one typed
- * quantisation launch and one tile-kernel launch (rounding y in its
- * epilogue) per 8 of one (x_dtype, y_dtype) pair; the others run as
+ * rescale inside it) when their workgroups fit on the device at once.  The
+ * other ones with M <= 4, M * K <= 32768 and K <= 8192 (a few tokens, or
+ * one token with x_dtype != y_dtype) share one typed quantisation launch
+ * and one one-shot contraction launch (rounding y in its epilogue) per 8
+ * of one (x_dtype, y_dtype) pair; the prefill-sized ones (M > 4,
+ * K % 256 == 0, K <= 8192) share one typed quantisation launch and one
+ * tile-kernel launch per 8 of one pair; the others run as
  * bitlinear_forward_io does.
  *   descs: HOST array, 1 <= count <= 64, each validated as
  *   bitlinear_forward_io validates its arguments, all before anything is

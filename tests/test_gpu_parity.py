@@ -1030,6 +1030,51 @@ def test_forward_io_batch_mixed(torch, bl, orc):
             assert np.array_equal(bits16(torch, out), bits16(torch, single)), c
 
 
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_few_token_batches(torch, bl, orc, M):
+    """The decoder layer's seven BitLinears at M = 2..4 tokens: fp32 through
+    forward_batch (one batched quantisation and one one-shot contraction
+    launch), bf16 and fp16 through forward_io_batch, with a problem whose
+    x and y types differ: every output the oracle's (fp32 within 1e-5,
+    half types bit for bit) and each fp32 one equal to its single call."""
+    work = wl.DECODE_LAYER
+    items, refs, singles = [], [], []
+    for i, L in enumerate(work.linears):
+        x, w, t, g = mm_case(M, L.K, L.N, 1800 + 10 * M + i)
+        packed_r, s = orc.pack_i2s(w)
+        X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+        out = torch.full((M, L.N), float("nan"), dtype=torch.float32, device="cuda")
+        items.append((X, P, s, G, 1e-6, out, bl.new_workspace(M, L.K)))
+        refs.append(orc.forward(x, packed_r, s, g, 1e-6, L.N))
+        singles.append(host(bl.forward(X, P, s, G, 1e-6, L.N)).copy())
+    announce("few-token batch", M)
+    bl.forward_batch(items)
+    torch.cuda.synchronize()
+    for it, ref, single in zip(items, refs, singles):
+        check_y(host(it[5]), ref)
+        assert np.array_equal(host(it[5]), single)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    types = [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "bf16")]
+    titems, trefs = [], []
+    for i, L in enumerate(work.linears):
+        xd, yd = types[i % len(types)]
+        x32, w, t, g = mm_case(M, L.K, L.N, 1900 + 10 * M + i)
+        x = orc.from_f32(x32, xd)
+        packed_r, s = orc.pack_i2s(w)
+        trefs.append((orc.forward_io(x, xd, packed_r, s, g, 1e-6, L.N, yd), yd))
+        out = torch.empty((M, L.N), dtype=tdt[yd], device="cuda")
+        titems.append((torch_io(torch, x, xd), dev(torch, packed_r), s, dev(torch, g), 1e-6, out,
+                       bl.io_workspace(M, L.K, L.N)))
+    announce("few-token typed batch", M)
+    bl.forward_io_batch(titems)
+    torch.cuda.synchronize()
+    for it, (ref, yd) in zip(titems, trefs):
+        if yd == "f32":
+            assert np.array_equal(host(it[5]).view(np.uint32), ref.view(np.uint32))
+        else:
+            assert np.array_equal(bits16(torch, it[5]), np.asarray(ref).view(np.uint16))
+
+
 # ---------------------------------------------------------------- dequantisation
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
