@@ -70,8 +70,10 @@ typedef enum {
 } bl_status;
 
 /* Matmul route.  Both routes return bit-identical results; the choice only
- * affects speed.  AUTO takes the decode kernel for M <= 4 and the MFMA
- * tile kernel above. */
+ * affects speed.  AUTO takes the decode kernels for M <= 4 and the MFMA
+ * tile kernel above, except that a forward of M <= 8 tokens whose block
+ * fits the one-shot decode kernel (M * K <= 65536, K <= 8192) takes that
+ * kernel (see bitlinear_forward_batch). */
 typedef enum {
     BL_PATH_AUTO = 0,
     BL_PATH_GEMV = 1, /* decode kernel, any M (tokens in groups of 16) */
@@ -201,9 +203,10 @@ typedef struct {
  * layer at decode (one launch for the whole layer).  Results are
  * bit-identical to calling bitlinear_forward_ex(descs[i], launch) for each i.
  * The decode-sized ones (M <= 4 with the fused quantisation) share one
- * kernel launch per 8.  With the automatic launch shape, the other
- * decode-sized ones with M * K <= 32768 and K <= 8192 (a few tokens) share
- * one quantisation launch and one one-shot contraction launch per 8, and
+ * kernel launch per 8.  With the automatic launch shape (and not forced
+ * onto the tile route), the others with M <= 8, M * K <= 65536 and
+ * K <= 8192 (a few tokens) share one quantisation launch and one one-shot
+ * contraction launch per 8, and
  * the prefill-sized ones with K % 256 == 0 and K <= 8192 share one
  * quantisation launch and one tile-kernel launch per 8; the others run one
  * by one.
@@ -267,7 +270,7 @@ size_t bitlinear_io_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * y_dtype: one launch (the one-shot decode kernel with the quantisation and
  * the rescale inside) when its workgroups fit on the device at once.
  * Otherwise two launches, the quantisation and a contraction that rounds y
- * in its epilogue, when K <= 8192 and either M <= 4 with M * K <= 32768
+ * in its epilogue, when K <= 8192 and either M <= 8 with M * K <= 65536
  * (the one-shot kernel) or M > 4 with K % 256 == 0 (the tile kernel); else
  * three: quantisation, contraction to the int32 accumulator in the
  * workspace, rescale.
@@ -303,7 +306,7 @@ typedef struct {
  * bitlinear_forward_io.  Those with M = 1, K <= 8192 and x_dtype ==
  * y_dtype share one one-shot launch per 8 and per type (quantisation and
  * rescale inside it) when their workgroups fit on the device at once.  The
- * other ones with M <= 4, M * K <= 32768 and K <= 8192 (a few tokens, or
+ * other ones with M <= 8, M * K <= 65536 and K <= 8192 (a few tokens, or
  * one token with x_dtype != y_dtype) share one typed quantisation launch
  * and one one-shot contraction launch (rounding y in its epilogue) per 8
  * of one (x_dtype, y_dtype) pair; the prefill-sized ones (M > 4,

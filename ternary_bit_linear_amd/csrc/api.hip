@@ -166,17 +166,17 @@ bool takes_group(const bl_forward_desc &d, const bl_launch *launch) {
            d.K <= bl::kActQuantBatchMaxK;
 }
 
-// Whether a validated forward that takes neither the fused kernel nor a
-// grouped prefill launch can join a batched decode launch pair (one batched
-// quantisation launch, one one-shot contraction launch over up to 8
-// problems): the decode route with its automatic launch shape, and q of the
-// problem fitting the one-shot kernel's LDS block.  For a few tokens
-// (M = 2..4) this replaces two launches per BitLinear by two per eight:
-// the decoder layer at M = 4 went from 47 to 12 us (measured on MI355X).
+// Whether a validated forward that does not take the fused kernel joins a
+// batched decode launch pair (one batched quantisation launch, one one-shot
+// contraction launch over up to 8 problems): automatic launch shape, not
+// forced onto the tile route, and a token block the one-shot kernel holds
+// (M <= 8, M * K <= 64 KB, K <= 8192).  Measured on MI355X against two
+// launches per BitLinear at M = 2..4 (decoder layer at M = 4: 47 -> 12 us)
+// and against the grouped tile pair at M = 5..8 (decoder layer at M = 8:
+// 14.7 -> 13.8 us; K = N = 8192: 13.6 -> 11.6 us).
 bool takes_shot_batch(const bl_forward_desc &d, const bl_launch *launch) {
-    if (launch && launch->variant != 0) return false;
-    return route_of(d.M, launch) == BL_PATH_GEMV && bl::shot_supported(d.M, d.K) &&
-           d.K <= bl::kActQuantBatchMaxK;
+    if (launch && (launch->variant != 0 || launch->path == BL_PATH_GEMM)) return false;
+    return bl::shot_supported(d.M, d.K) && d.K <= bl::kActQuantBatchMaxK;
 }
 
 // Enqueue one validated forward that does not take the fused kernel.
@@ -428,7 +428,8 @@ bl_status bitlinear_forward_ex(const float *x, const uint8_t *packed_w, float w_
         const bl::FusedDecode f = fused_of(d);
         return hip_status(bl::launch_gemv_fused(&f, 1, launch ? launch->variant : 0, s));
     }
-    if (takes_group(d, launch)) return bitlinear_forward_batch(&d, 1, launch, stream);
+    if (takes_shot_batch(d, launch) || takes_group(d, launch))
+        return bitlinear_forward_batch(&d, 1, launch, stream);
     return enqueue_unfused(d, launch, s);
 }
 
@@ -466,9 +467,9 @@ bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count,
         G.n = 0;
         return BL_OK;
     };
-    // A few tokens (M <= 4), and one token with x and y of different types:
-    // one batched typed quantisation and one one-shot contraction launch
-    // (typed epilogue) per 8 of one type pair.
+    // A few tokens (M <= 8, M * K <= 64 KB), and one token with x and y of
+    // different types: one batched typed quantisation and one one-shot
+    // contraction launch (typed epilogue) per 8 of one type pair.
     struct ShotGroup {
         bl::ActQuantDesc aq[kShotPerLaunch];
         bl::ShotDecode sd[kShotPerLaunch];
@@ -485,8 +486,7 @@ bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count,
     for (int i = 0; i < count; ++i) {
         const bl_forward_io_desc &d = descs[i];
         if (!io_fusable(d)) {
-            if (route_of(d.M, nullptr) == BL_PATH_GEMV && bl::shot_supported(d.M, d.K) &&
-                d.K <= bl::kActQuantBatchMaxK) {
+            if (bl::shot_supported(d.M, d.K) && d.K <= bl::kActQuantBatchMaxK) {
                 ShotGroup &G = sgp[d.x_dtype][d.y_dtype];
                 const Workspace ws = carve(d.workspace, d.M, d.K);
                 bl::ActQuantDesc &a = G.aq[G.n];
@@ -580,7 +580,18 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
     const bl_forward_desc gu[2] = {
         {d.x, d.packed_gate, d.s_gate, d.gamma_in, d.eps, M, H, F, w.g, w.ws_gate, w.b_gate},
         {d.x, d.packed_up, d.s_up, d.gamma_in, d.eps, M, H, F, w.u, w.ws_up, w.b_gate}};
-    if (!takes_fused(gu[0], nullptr) && takes_group(gu[0], nullptr)) {
+    if (!takes_fused(gu[0], nullptr) && takes_shot_batch(gu[0], nullptr)) {
+        // A few tokens: x is quantised once (into the gate's workspace) and
+        // both contractions read that q in one one-shot launch.
+        const Workspace wq = carve(w.ws_gate, M, H);
+        const bl::ActQuantDesc aq{d.x, d.gamma_in, d.eps, M, H, wq.q, wq.inv, wq.qsum};
+        const bl::ShotDecode sd[2] = {
+            {wq.q, wq.inv, wq.qsum, d.packed_gate, w.g, nullptr, d.s_gate, M, H, F},
+            {wq.q, wq.inv, wq.qsum, d.packed_up, w.u, nullptr, d.s_up, M, H, F}};
+        if (bl::launch_act_quant_batch(&aq, 1, s) != hipSuccess ||
+            bl::launch_gemv_shot(sd, 2, 0, s) != hipSuccess)
+            return BL_ERR_HIP;
+    } else if (!takes_fused(gu[0], nullptr) && takes_group(gu[0], nullptr)) {
         // Prefill: x is quantised once (into the gate's workspace) and both
         // contractions read that q in one grouped tile launch.
         const Workspace wq = carve(w.ws_gate, M, H);
@@ -629,6 +640,12 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
                 hipSuccess)
             return BL_ERR_HIP;
     }
+    if (F <= bl::kActQuantBatchMaxK && bl::shot_supported(M, F)) {
+        // the one-shot kernel, as a batch of a few tokens takes it
+        const bl::ShotDecode sd{wd.q, wd.inv, wd.qsum, d.packed_down, d.y, nullptr, d.s_down,
+                                M,    F,      H};
+        return hip_status(bl::launch_gemv_shot(&sd, 1, 0, s));
+    }
     return run_contraction(wd.q, wd.inv, wd.qsum, d.packed_down, d.s_down, M, F, H, d.y, nullptr,
                            nullptr, s);
 }
@@ -670,13 +687,6 @@ bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
                 if (bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
                 n = 0;
             }
-        } else if (takes_group(d, launch)) {
-            const Workspace ws = carve(d.workspace, d.M, d.K);
-            aq[g] = bl::ActQuantDesc{d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum};
-            gd[g] = bl::GemmDesc{ws.q, ws.inv, ws.qsum, d.packed_w, d.w_scale,
-                                 d.M, d.K, d.N, d.y, nullptr};
-            if (++g == kGroupPerLaunch)
-                if (bl_status st = flush_group()) return st;
         } else if (takes_shot_batch(d, launch)) {
             const Workspace ws = carve(d.workspace, d.M, d.K);
             sq[ns] = bl::ActQuantDesc{d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum};
@@ -684,6 +694,13 @@ bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
                                     nullptr, d.w_scale, d.M, d.K, d.N};
             if (++ns == kShotPerLaunch)
                 if (bl_status st = flush_shot()) return st;
+        } else if (takes_group(d, launch)) {
+            const Workspace ws = carve(d.workspace, d.M, d.K);
+            aq[g] = bl::ActQuantDesc{d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum};
+            gd[g] = bl::GemmDesc{ws.q, ws.inv, ws.qsum, d.packed_w, d.w_scale,
+                                 d.M, d.K, d.N, d.y, nullptr};
+            if (++g == kGroupPerLaunch)
+                if (bl_status st = flush_group()) return st;
         } else if (bl_status st = enqueue_unfused(d, launch, s)) {
             return st;
         }

@@ -735,7 +735,11 @@ hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipSt
 // One-shot decode contraction of up to 8 problems in one launch, int8
 // activations in global memory (M <= 8, M*K <= kShotMaxQ, K <= 32768).
 // y (rescaled) when every y is non-null, else acc (int32).
-constexpr int64_t kShotMaxQ = 32 * 1024;
+constexpr int64_t kShotMaxQ = 64 * 1024;
+constexpr int64_t kShotFusedMaxQ = 32 * 1024;  // fused form: x rows in registers
+// Automatic one-shot choice for a single contraction (the range it was
+// measured on); batches take blocks up to kShotMaxQ through the batched pair.
+constexpr int64_t kShotSingleMaxQ = 32 * 1024;
 struct ShotDecode {
     const int8_t *q;
     const float *inv;

@@ -864,6 +864,7 @@ hipError_t launch_gemv(const int8_t *q, const float *inv, const int32_t *qsum,
     // form for longer rows (faster at K = 28672).
     const bool shot = is_shot(variant) ? shot_supported(M, K)
                                        : variant == 0 && shot_supported(M, K) && K <= 16384 &&
+                                             M * K <= kShotSingleMaxQ &&
                                              shot_rounds(&M, &K, &N, 1, false) != INT64_MAX;
     if (shot) {
         const ShotDecode d{q, inv, qsum, packed, y, acc, w_scale, M, K, N};

@@ -514,7 +514,10 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
         const int64_t per_cu = std::min<int64_t>(h.occupancy, (160 * 1024) / lds);
         return per_cu < 1 ? INT64_MAX : (wgs + per_cu * cus - 1) / (per_cu * cus);
     };
-    if (pref >= 1 && pref <= kNumShotShapes && fits(kShotShapes[pref - 1].nb)) {
+    // A requested shape is taken when every problem fits it and its LDS
+    // (weights and activation block) fits a CU.
+    if (pref >= 1 && pref <= kNumShotShapes && fits(kShotShapes[pref - 1].nb) &&
+        rounds_of(kShotShapes[pref - 1]) != INT64_MAX) {
         *rounds_out = rounds_of(kShotShapes[pref - 1]);
         return pref - 1;
     }
@@ -671,7 +674,7 @@ bool shot_supported(int64_t M, int64_t K) {
 }
 
 bool shot_fused_supported(int64_t M, int64_t K) {
-    return M >= 1 && M <= kFuseMaxM && M * K <= kShotMaxQ && shot_ks(K, 8) != 0;
+    return M >= 1 && M <= kFuseMaxM && M * K <= kShotFusedMaxQ && shot_ks(K, 8) != 0;
 }
 
 hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream_t s) {

@@ -741,10 +741,12 @@ def ffn_case(seed, M, H, F, norm=True):
 
 # (M, H, F, norm): M = 1 with F <= 8192 takes the two-launch form (the down
 # projection's quantisation inside the one-shot kernel); F > 8192 and M > 1
-# take the separate gated quantisation; M = 64 the tile kernel.
+# take the separate gated quantisation; M <= 8 with M * H and M * F up to
+# 64 KB the one-shot kernel for all three projections; M = 64 the tile
+# kernel.
 FFN_SHAPES = [(1, 2560, 6912, True), (1, 256, 384, False), (1, 1024, 9216, True),
-              (3, 512, 1280, True), (17, 256, 384, True), (64, 1024, 2816, True),
-              (64, 256, 640, False)]
+              (3, 512, 1280, True), (8, 2560, 6912, True), (6, 1024, 2816, False),
+              (17, 256, 384, True), (64, 1024, 2816, True), (64, 256, 640, False)]
 
 
 @pytest.mark.parametrize("M,H,F,norm", FFN_SHAPES)
@@ -1030,9 +1032,9 @@ def test_forward_io_batch_mixed(torch, bl, orc):
             assert np.array_equal(bits16(torch, out), bits16(torch, single)), c
 
 
-@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8])
 def test_few_token_batches(torch, bl, orc, M):
-    """The decoder layer's seven BitLinears at M = 2..4 tokens: fp32 through
+    """The decoder layer's seven BitLinears at M = 2..8 tokens: fp32 through
     forward_batch (one batched quantisation and one one-shot contraction
     launch), bf16 and fp16 through forward_io_batch, with a problem whose
     x and y types differ: every output the oracle's (fp32 within 1e-5,
