@@ -243,14 +243,16 @@ __device__ __forceinline__ void store_out(YT *y, size_t i, float v) {
 // Halving-tree reduction of the 64 lanes of a wave into lane 0:
 // level s = 32, 16, 8, 4, 2, 1 adds lane j + s into lane j (j < s).  Lane
 // 0's result is exactly the tree the pinned sum-of-squares order defines.
-// Level 32 crosses the wave halves (ds_bpermute), level 16 swaps 16-lane
-// groups (ds_swizzle, bitmask mode xor 16), levels 8..1 stay inside a
-// 16-lane row (DPP row_shl).  Other lanes end with partial values; the
-// result is read with readfirstlane (a wave-uniform scalar).
+// Levels 32 and 16 take gfx950's VALU lane swaps, with no LDS round trip:
+// v_permlane32_swap(v, v) returns in its second result lanes 32..63 of v in
+// lanes 0..31, and v_permlane16_swap(v, v) the odd 16-lane rows in the even
+// ones (lanes 16..31 in 0..15).  Levels 8..1 stay inside a 16-lane row (DPP
+// row_shl).  Other lanes end with partial values; the result is read with
+// readfirstlane (a wave-uniform scalar).
 template <class Op>
 __device__ __forceinline__ int wave_tree_i(int v, Op op) {
-    v = op(v, __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) << 2), v));
-    v = op(v, __builtin_amdgcn_ds_swizzle(v, 0x401F));
+    v = op(v, (int)__builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false)[1]);
+    v = op(v, (int)__builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false)[1]);
     v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x108, 0xF, 0xF, false));  // row_shl:8
     v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false));  // row_shl:4
     v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x102, 0xF, 0xF, false));  // row_shl:2
