@@ -10,7 +10,7 @@
 // activation sum; every output must be written.  HF-38087: RMSNorm on the
 // activations before their quantisation.]
 //
-// Design.  Each workgroup owns one set of weight rows (4 / ks waves' worth,
+// Design.  Each workgroup owns one set of weight rows (W / ks waves' worth,
 // a wave holding R tiles of 8 consecutive rows, ks waves splitting each
 // tile group's K range) for the whole of K, and runs once: it issues every
 // load it will need at the start -- the activation block (or x and gamma)
@@ -20,11 +20,11 @@
 // each lands, reduces the ks partial tiles through LDS, writes its outputs
 // and exits.  With no loop around the loads, a workgroup keeps its whole
 // share in flight from its first instruction.  The host picks the launch
-// shape (batches per wave, tiles per wave) so that every workgroup of the
-// launch is resident at once where it can be: a problem set that fits in
-// one round streams near the rate of a plain read of the same bytes, where
-// a persistent loop with a deep ring stays ~15% below it.  Larger sets take
-// the persistent form (gemv.hip).
+// shape (batches per wave, tiles per wave, waves per workgroup) so that
+// every workgroup of the launch is resident at once where it can be: a
+// problem set that fits in one round streams near the rate of a plain read
+// of the same bytes, where a persistent loop with a deep ring stays ~15%
+// below it.  Larger fused sets take the persistent form (gemv.hip).
 //
 // The arithmetic is the decode route's: the 16 bytes a lane copies hold,
 // per 2-bit field g, the codes of 16 consecutive k of one weight row (row
