@@ -549,6 +549,19 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
     }
 }
 
+// Barriers block_act_quant_row<..., SYNC = false> takes per row: one per
+// block reduction (sum of squares with RMSNorm, max, sum of q).  Waves of a
+// larger workgroup that do not run the 256-thread block form call
+// block_act_quant_row_barriers instead, so every wave meets the same
+// barriers; a change to the block reductions must change both.
+__device__ __forceinline__ int block_act_quant_row_barrier_count(bool norm) {
+    return norm ? 3 : 2;
+}
+__device__ __forceinline__ void block_act_quant_row_barriers(bool norm) {
+    const int n = block_act_quant_row_barrier_count(norm);
+    for (int i = 0; i < n; ++i) lds_barrier();
+}
+
 // Wave form (64 threads, no LDS, no barrier): lane j owns the four O256
 // chains j, 64 + j, 128 + j, 192 + j, i.e. the float4 groups at
 // k = 1024 i + 256 w + 4 j (w = 0..3).  Each chain group w is reduced by the

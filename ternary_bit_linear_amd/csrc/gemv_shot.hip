@@ -255,18 +255,12 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
                 }
             }
         } else {
-            // Waves 4..W-1: their weights, then one barrier per block
-            // reduction of each row (sum of squares with RMSNorm, max, sum).
+            // Waves 4..W-1: their weights, then the barriers of each row's
+            // block form.
             issue_weights();
-            const bool norm = P.gamma != nullptr;
 #pragma unroll
-            for (int m = 0; m < FM; ++m) {
-                if (m < M) {
-                    if (norm) lds_barrier();
-                    lds_barrier();
-                    lds_barrier();
-                }
-            }
+            for (int m = 0; m < FM; ++m)
+                if (m < M) block_act_quant_row_barriers(P.gamma != nullptr);
         }
         lds_barrier();
     }
