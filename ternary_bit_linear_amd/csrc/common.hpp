@@ -162,7 +162,7 @@ __device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t
 
 // Activation storage types.  bf16 is carried as its bit pattern; widening
 // to fp32 is exact for every type (bf16: the 16 bits become the high half
-// of the fp32 word; fp16: f16_bits_to_f32 below).
+// of the fp32 word; fp16: f16_low_to_f32 below).
 struct bf16_t {
     uint16_t bits;
 };
@@ -183,23 +183,17 @@ __device__ __forceinline__ float4 load_x4<bf16_t>(__amdgpu_buffer_rsrc_t r, uint
     return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
                        __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
 }
-// IEEE binary16 bits -> fp32 by integer operations: exact for every input,
-// subnormals included, whatever the hardware's fp16 denormal mode.
-__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
-    const uint32_t sign = (h & 0x8000u) << 16;
-    const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
-    if (e == 0) {  // zero or subnormal: m * 2^-24, exact in fp32
-        const float v = (float)m * 5.9604644775390625e-8f;
-        return __uint_as_float(__float_as_uint(v) | sign);
-    }
-    if (e == 31) return __uint_as_float(sign | 0x7F800000u | (m << 13));
-    return __uint_as_float(sign | ((e + 112u) << 23) | (m << 13));
+// Hardware widening of one binary16 value held in the low 16 bits of a
+// word (v_cvt_f32_f16): exact for every input, subnormals included, as the
+// kernels keep fp16 denormals (the default mode).
+__device__ __forceinline__ float f16_low_to_f32(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
 }
 template <>
 __device__ __forceinline__ float4 load_x4<_Float16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    return make_float4(f16_bits_to_f32(v.x & 0xFFFFu), f16_bits_to_f32(v.x >> 16),
-                       f16_bits_to_f32(v.y & 0xFFFFu), f16_bits_to_f32(v.y >> 16));
+    return make_float4(f16_low_to_f32(v.x), f16_low_to_f32(v.x >> 16), f16_low_to_f32(v.y),
+                       f16_low_to_f32(v.y >> 16));
 }
 
 // fp32 -> bf16 bits, nearest even (NaN stays a quiet NaN).
