@@ -15,7 +15,7 @@ not from the 256 MB last-level cache.
 
 Prints one JSON line (see the "metric" of the workload).  Options:
   --gpus N (only 1 is supported), --steps K, --warmup W,
-  --workload decode|prefill|ffn70b-1|ffn70b-16|sweep-M,
+  --workload decode|prefill|decode-mM|ffn70b-1|ffn70b-16|sweep-M,
   --no-cpu-baseline, --no-secondary, --pack-only, --ffn-only, --io-only,
   --dense-only.
 """
@@ -45,6 +45,8 @@ def workload_by_name(name: str):
         return wl.DECODE_LAYER
     if name == "prefill":
         return wl.PREFILL_LAYER
+    if name.startswith("decode-m"):
+        return wl.decode_layer(int(name.split("-m")[1]))
     if name.startswith("ffn70b-"):
         return wl.ffn70b(int(name.split("-")[1]))
     if name.startswith("sweep-"):

@@ -119,6 +119,14 @@ PREFILL_LAYER = Workload(3, "decoder-layer BitLinears, prefill M=512 (2560/640/6
                          _layer(512, 0.4, 0.015, "u0.8-1.2", outlier=0.01))
 
 
+def decode_layer(M: int) -> Workload:
+    """The decoder layer's seven BitLinears at M tokens (few-token decode:
+    batched serving or draft tokens), with the decode layer's weights and
+    activations recipe."""
+    return Workload(6, f"decoder-layer BitLinears, decode M={M} (2560/640/6912)",
+                    _layer(M, 0.4, 0.015, "u0.8-1.2"))
+
+
 def ffn70b(M: int) -> Workload:
     return Workload(4, f"70B-shaped FFN BitLinears M={M}",
                     (Linear("gate", M, 8192, 28672, 0.35, 0.01, "ones"),
