@@ -227,6 +227,29 @@ bl_status bitlinear_act_quant(const float *x, const float *gamma, float eps,
                               int64_t M, int64_t K, int8_t *q, float *inv,
                               int32_t *qsum, void *stream);
 
+/* Stage: the fp32 arithmetic of the normalisation and quantisation scales,
+ * elementwise, computed by the same device functions and build as every
+ * kernel of the library [HF-38087: r = 1 / sqrt(mean(x^2) + eps) before the
+ * absmax int8 quantisation, whose codes depend on r and on the quantisation
+ * scale bit for bit].  Exported so that tests can compare the device's
+ * square root and division with correctly rounded host arithmetic.
+ *   op 0 (BL_FP_SQRT):        out[i] = sqrtf(a[i])               (b unused)
+ *   op 1 (BL_FP_DIV):         out[i] = a[i] / b[i]
+ *   op 2 (BL_FP_RMS_SCALE):   out[i] = 1 / sqrtf(a[i] / b[i] + eps), with
+ *                             b[i] = (float)K, an integer in [1, 2^22]
+ *   op 3 (BL_FP_QUANT_SCALE): out[i] = 127 / max(a[i], 1e-5)     (b unused)
+ * a, b, out: device fp32 [n] (b may be NULL for ops 0 and 3); n >= 1
+ * (BL_ERR_SHAPE otherwise); eps finite (op 2 only).  Unknown op or NULL
+ * pointers -> BL_ERR_INVALID_ARG.  Asynchronous on `stream`. */
+typedef enum {
+    BL_FP_SQRT = 0,
+    BL_FP_DIV = 1,
+    BL_FP_RMS_SCALE = 2,
+    BL_FP_QUANT_SCALE = 3
+} bl_fp_op;
+bl_status bitlinear_fp32_ops(int op, const float *a, const float *b, float eps, int64_t n,
+                             float *out, void *stream);
+
 /* Stage: acc[m][n] = sum_k code(n,k) * q[m][k] - qsum[m] (int32, exact).
  * qsum is taken as given (it is sum_k q[m][k] when it comes from
  * bitlinear_act_quant).  acc: device int32 [M][N].  Asynchronous. */

@@ -81,6 +81,7 @@ SIGNATURES = {
     "bitlinear_forward_io": (_i, [_p, _i, _p, _f, _p, _f, _i64, _i64, _i64, _p, _i, _p, _sz, _p]),
     "bitlinear_forward_io_batch": (_i, [ctypes.POINTER(IoDesc), _i, _p]),
     "bitlinear_ffn_forward": (_i, [ctypes.POINTER(FfnDesc), _p]),
+    "bitlinear_fp32_ops": (_i, [_i, _p, _p, _f, _i64, _p, _p]),
     "bitlinear_matmul_i2s": (_i, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "bitlinear_matmul_i2s_ex": (_i, [_p, _p, _p, _i64, _i64, _i64, _p,
                                      ctypes.POINTER(Launch), _p]),
@@ -205,6 +206,21 @@ def act_quant(x, gamma, eps: float = 1e-6):
                                      ctypes.c_void_p(inv.data_ptr()),
                                      ctypes.c_void_p(qsum.data_ptr()), _stream()), "act_quant")
     return q, inv, qsum
+
+
+FP_SQRT, FP_DIV, FP_RMS_SCALE, FP_QUANT_SCALE = range(4)
+
+
+def fp32_ops(op: int, a, b=None, eps: float = 0.0):
+    """Elementwise device fp32 arithmetic of the normalisation and
+    quantisation scales (bl_fp_op): sqrtf(a), a / b, 1 / sqrtf(a / b + eps)
+    with b = K, or 127 / max(a, 1e-5).  -> fp32 tensor like a."""
+    torch = _torch()
+    out = torch.empty_like(a)
+    bp = ctypes.c_void_p(None) if b is None else _dev(b, torch.float32, "b")
+    _check(lib().bitlinear_fp32_ops(op, _dev(a, torch.float32, "a"), bp, eps, a.numel(),
+                                    ctypes.c_void_p(out.data_ptr()), _stream()), "fp32_ops")
+    return out
 
 
 def matmul_i2s(q, qsum, packed, N: int, path: int = PATH_AUTO, variant: int = 0):

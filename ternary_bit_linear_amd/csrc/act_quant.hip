@@ -199,6 +199,26 @@ hipError_t launch_rescale_t(const int32_t *acc, const float *inv, float w_scale,
     return hipGetLastError();
 }
 
+// The fp32 arithmetic the normalisation and quantisation rest on, exposed
+// elementwise so that it can be checked against correctly rounded host
+// arithmetic: op 0 sqrtf(a), op 1 a / b, op 2 rms_scale(a, K = b, eps),
+// op 3 quant_scale(a).  The same device functions and build flags as every
+// kernel of the library.
+__global__ __launch_bounds__(256) void fp32_ops_kernel(int op, const float *__restrict__ a,
+                                                       const float *__restrict__ b, float eps,
+                                                       int64_t n, float *__restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float va = a[i];
+        float r;
+        if (op == 0) r = sqrtf(va);
+        else if (op == 1) r = va / b[i];
+        else if (op == 2) r = rms_scale(va, (int)b[i], eps);
+        else r = quant_scale(va);
+        out[i] = r;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_act_quant_batch(const ActQuantDesc *d, int count, hipStream_t s) {
@@ -299,6 +319,14 @@ hipError_t launch_rescale_io(const int32_t *acc, const float *inv, float w_scale
             return launch_rescale_t(acc, inv, w_scale, M, N, static_cast<_Float16 *>(y), s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_fp32_ops(int op, const float *a, const float *b, float eps, int64_t n,
+                           float *out, hipStream_t s) {
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 8192));
+    hipLaunchKernelGGL(fp32_ops_kernel, dim3((unsigned)blocks), dim3(256), 0, s, op, a, b, eps, n,
+                       out);
+    return hipGetLastError();
 }
 
 }  // namespace bl

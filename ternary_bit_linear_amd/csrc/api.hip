@@ -398,6 +398,15 @@ bl_status bitlinear_act_quant(const float *x, const float *gamma, float eps, int
     return hip_status(bl::launch_act_quant(x, gamma, eps, M, K, q, inv, qsum, as_stream(stream)));
 }
 
+bl_status bitlinear_fp32_ops(int op, const float *a, const float *b, float eps, int64_t n,
+                             float *out, void *stream) {
+    if (n < 1 || n >= kMaxElems) return BL_ERR_SHAPE;
+    if (op < BL_FP_SQRT || op > BL_FP_QUANT_SCALE || !a || !out) return BL_ERR_INVALID_ARG;
+    if ((op == BL_FP_DIV || op == BL_FP_RMS_SCALE) && !b) return BL_ERR_INVALID_ARG;
+    if (op == BL_FP_RMS_SCALE && !std::isfinite(eps)) return BL_ERR_INVALID_ARG;
+    return hip_status(bl::launch_fp32_ops(op, a, b, eps, n, out, as_stream(stream)));
+}
+
 bl_status bitlinear_matmul_i2s_ex(const int8_t *q, const int32_t *qsum, const uint8_t *packed_w,
                                   int64_t M, int64_t K, int64_t N, int32_t *acc,
                                   const bl_launch *launch, void *stream) {

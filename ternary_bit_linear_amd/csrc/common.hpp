@@ -270,6 +270,22 @@ __device__ __forceinline__ int wave_sum_int(int v) {
     return wave_tree_i(v, [](int a, int b) { return a + b; });
 }
 
+// RMSNorm scale of a row from its sum of squares (HF-38087: RMSNorm before
+// the quantisation, eps inside the root): r = 1 / sqrt(ss / K + eps), with
+// IEEE division and square root (the library is built with correctly
+// rounded fp32 division and square root, and without fp contraction), so
+// the int8 codes that depend on r are the same on any conforming fp32
+// implementation.
+__device__ __forceinline__ float rms_scale(float ss, int K, float eps) {
+    return 1.0f / sqrtf(ss / (float)K + eps);
+}
+
+// Quantisation scale of a row from its absolute maximum: 127 / max(amax,
+// 1e-5) (IEEE division; the floor only acts on an all-zero row).
+__device__ __forceinline__ float quant_scale(float amax) {
+    return 127.0f / fmaxf(amax, 1e-5f);
+}
+
 // q = clamp(rint(xn * inv), -128, 127).  The clamp never acts, so it is not
 // evaluated: |xn| <= amax' = max(amax, 1e-5) and inv = fl(127 / amax') <=
 // (127 / amax') (1 + 2^-24), so |fl(xn * inv)| <= 127 (1 + 2^-24)^2 < 127.5
@@ -443,7 +459,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                 }
             }
             const float ss = block_sumsq_finish(p, red);
-            r = 1.0f / sqrtf(ss / (float)K + eps);
+            r = rms_scale(ss, K, eps);
         }
         float amax = 0.0f;
 #pragma unroll
@@ -454,7 +470,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
             }
         }
         amax = block_max(amax, red + 4);
-        const float inv = 127.0f / fmaxf(amax, 1e-5f);
+        const float inv = quant_scale(amax);
         int qs = 0;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
@@ -502,7 +518,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
             }
         }
         const float ss = block_sumsq_finish(p, red);
-        r = 1.0f / sqrtf(ss / (float)K + eps);
+        r = rms_scale(ss, K, eps);
     }
     float amax = 0.0f;
     for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
@@ -516,7 +532,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
         for (int i = 0; i < CH; ++i) amax = amax4(amax, xn4(xv[i], gv[i], r));
     }
     amax = block_max(amax, red + 4);
-    const float inv = 127.0f / fmaxf(amax, 1e-5f);
+    const float inv = quant_scale(amax);
     int qs = 0;
     for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {
         float4 xv[CH], gv[CH];
@@ -602,7 +618,7 @@ __device__ __forceinline__ void wave_act_quant_row(const XT *__restrict__ x,
 #pragma unroll
         for (int w = 0; w < 4; ++w) p[w] = wave_tree_sum_f(p[w]);
         const float ss = (p[0] + p[1]) + (p[2] + p[3]);
-        r = 1.0f / sqrtf(ss / (float)K + eps);
+        r = rms_scale(ss, K, eps);
     }
     float amax = 0.0f;
     for (int c0 = 0; c0 < K; c0 += 1024 * CI) {
@@ -623,7 +639,7 @@ __device__ __forceinline__ void wave_act_quant_row(const XT *__restrict__ x,
             for (int w = 0; w < 4; ++w) amax = amax4(amax, xn4(xv[i][w], gv[i][w], r));
     }
     amax = wave_max(amax);
-    const float inv = 127.0f / fmaxf(amax, 1e-5f);
+    const float inv = quant_scale(amax);
     int qs = 0;
     for (int c0 = 0; c0 < K; c0 += 1024 * CI) {
         if (!in_regs) {
@@ -687,6 +703,12 @@ hipError_t launch_act_quant_io(const void *x, int xtype, const float *gamma, flo
 // even).
 hipError_t launch_rescale_io(const int32_t *acc, const float *inv, float w_scale, int64_t M,
                              int64_t N, void *y, int ytype, hipStream_t s);
+
+// Elementwise fp32 arithmetic of the normalisation and quantisation (op 0
+// sqrtf(a), 1 a / b, 2 rms_scale(a, (int)b, eps), 3 quant_scale(a)), for
+// checking it against host arithmetic.
+hipError_t launch_fp32_ops(int op, const float *a, const float *b, float eps, int64_t n,
+                           float *out, hipStream_t s);
 
 // a = relu2_mul(g, u) elementwise over n floats (n % 4 == 0, 16-byte
 // aligned arrays).

@@ -32,6 +32,7 @@
 // B operand of v_mfma_i32_16x16x64_i8 whose 16 columns are 8 rows x 2 chunk
 // parities, and the A operand holds the tokens in both halves of its 16 rows
 // with the matching chunk; one lane + 40 add joins the two parities.
+#include <atomic>
 #include <climits>
 
 #include "common.hpp"
@@ -423,15 +424,23 @@ constexpr ShotShape kShotShapes[] = {{3, 1, 4, 4}, {4, 1, 4, 4}, {8, 1, 4, 4}, {
                                      {4, 2, 3, 4}, {3, 4, 3, 4}, {3, 2, 1, 8}, {3, 1, 1, 16}};
 constexpr int kNumShotShapes = sizeof(kShotShapes) / sizeof(kShotShapes[0]);
 
+// Compute units of the current device, looked up once per device (the
+// launch-shape choice runs on every call).  Devices beyond the table are
+// queried each time.
 int device_cus() {
-    static int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-            n = 256;
-        return n;
-    }();
-    return cus;
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];  // 0: not looked up yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        return 256;
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 // Launch-shape choice.  A shape costs (in this order): the rounds of

@@ -268,3 +268,15 @@ def test_dequant_validation(L):
     assert dq(F(A), 4, 128, F(0), 1, None) == api.ERR_INVALID_ARG
     assert dq(F(A), 4, 128, F(A), 5, None) == api.ERR_INVALID_ARG
     assert dq(F(A), 4, 128, F(MIS), 2, None) == api.ERR_ALIGN
+
+
+def test_fp32_ops_validation(L):
+    fo = L.bitlinear_fp32_ops
+    assert fo(0, F(A), F(0), 0.0, 0, F(A), None) == api.ERR_SHAPE
+    assert fo(4, F(A), F(A), 0.0, 8, F(A), None) == api.ERR_INVALID_ARG
+    assert fo(-1, F(A), F(A), 0.0, 8, F(A), None) == api.ERR_INVALID_ARG
+    assert fo(0, F(0), F(0), 0.0, 8, F(A), None) == api.ERR_INVALID_ARG
+    assert fo(3, F(A), F(0), 0.0, 8, F(0), None) == api.ERR_INVALID_ARG
+    assert fo(1, F(A), F(0), 0.0, 8, F(A), None) == api.ERR_INVALID_ARG  # division needs b
+    assert fo(2, F(A), F(0), 1e-6, 8, F(A), None) == api.ERR_INVALID_ARG
+    assert fo(2, F(A), F(A), float("inf"), 8, F(A), None) == api.ERR_INVALID_ARG

@@ -184,7 +184,8 @@ def test_matmul_parity(torch, bl, orc, path, M, K, N):
 
 
 FWD_SHAPES = [(1, 256, 256), (1, 2560, 640), (2, 384, 100), (3, 1024, 77), (4, 6912, 160),
-              (7, 512, 513), (16, 2560, 256), (17, 256, 64), (64, 1024, 200), (100, 384, 90)]
+              (7, 512, 513), (10, 2560, 300), (12, 1024, 129), (15, 6912, 200), (16, 2560, 256),
+              (17, 256, 64), (63, 640, 333), (64, 1024, 200), (100, 384, 90)]
 
 
 @pytest.mark.parametrize("M,K,N", FWD_SHAPES)
@@ -252,16 +253,25 @@ def run_linear(torch, bl, orc, work, i, sample_rows=None, sample_cols=None):
     X, G = dev(torch, x), dev(torch, g)
     P, s = bl.pack_i2s(dev(torch, w))
     ws = bl.new_workspace(L.M, L.K)
-    y = host(bl.forward(X, P, s, G, work.eps, L.N, workspace=ws))
-    assert np.all(np.isfinite(y))
+    # y starts as NaN, so an output the kernels leave unwritten cannot pass
+    # as a finite leftover of the allocator.
+    out = torch.full((L.M, L.N), float("nan"), dtype=torch.float32, device="cuda")
+    y = host(bl.forward(X, P, s, G, work.eps, L.N, out=out, workspace=ws))
+    assert np.all(np.isfinite(y)), f"{np.sum(~np.isfinite(y))} outputs unwritten or non-finite"
     q_r, inv_r, qs_r = orc.act_quant(x, g, work.eps)
     q, inv, qs = (host(a) for a in bl.workspace_views(ws, L.M, L.K))
     assert np.array_equal(q, q_r) and np.array_equal(inv, inv_r) and np.array_equal(qs, qs_r)
-    rows = np.arange(L.M) if sample_rows is None else sample_rows
+    # every row of the sampled columns (and the sampled rows of every
+    # column when rows are sampled): |acc| < 2^24, so the fp64 products and
+    # sums below are exact
     cols = np.arange(L.N) if sample_cols is None else sample_cols
-    acc = q_r[rows].astype(np.int64) @ t[cols].astype(np.int64).T
-    y64 = acc * (np.float64(s) / inv_r[rows].astype(np.float64))[:, None]
-    check_y(y[np.ix_(rows, cols)], y64)
+    acc = q_r.astype(np.float64) @ t[cols].astype(np.float64).T
+    y64 = acc * (np.float64(s) / inv_r.astype(np.float64))[:, None]
+    check_y(y[:, cols], y64)
+    if sample_rows is not None:
+        acc = q_r[sample_rows].astype(np.float64) @ t.astype(np.float64).T
+        y64 = acc * (np.float64(s) / inv_r[sample_rows].astype(np.float64))[:, None]
+        check_y(y[sample_rows], y64)
     return y
 
 
@@ -993,6 +1003,136 @@ def test_forward_io_f16_subnormals_exact(torch, bl, orc):
         assert np.array_equal(bits16(torch, y), y_r.view(np.uint16))
         q, inv, qs = orc.act_quant(orc.to_f32(x, "f16"), None, 1e-6)
         assert np.array_equal(q.astype(np.float32), m)
+
+
+def one_token_io(torch, bl, x, dt, packed, s, g, N):
+    """forward_io of one token with x and y of type dt: the one-shot kernel
+    with the quantisation inside.  -> (y bits, q, inv, qsum)."""
+    K = x.shape[-1]
+    ws = torch.empty(bl.lib().bitlinear_io_workspace_bytes(1, K, N), dtype=torch.uint8,
+                     device="cuda")
+    ydt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    out = torch.full((1, N), float("nan"), dtype=ydt, device="cuda")
+    y = bl.forward_io(torch_io(torch, x.reshape(1, K), dt), dev(torch, packed), s,
+                      None if g is None else dev(torch, g), 1e-6, N, y_dtype=ydt, out=out,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    q, inv, qs = bl.workspace_views(ws, 1, K)
+    return bits16(torch, y), host(q), host(inv), host(qs)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_forward_io_one_token_fused_edges(torch, bl, orc, dt):
+    """One token with the same half type in and out takes the one-shot
+    kernel with the RMSNorm + quantisation inside.  Edge cases through it,
+    bit for bit against the oracle: exact ties in the output rounding
+    (integer accumulators rescaled by exactly 1), ties in the quantisation
+    (x * inv = m + 1/2), fp16 subnormal inputs and subnormal outputs
+    (including ties between subnormals), fp16 overflow to inf, with and
+    without RMSNorm."""
+    K = 1024
+    rng = np.random.default_rng(1500)
+    # x = m / 64 with m integer in [-127, 127] and amax = 127 / 64: with no
+    # RMSNorm inv = 64 exactly and q = m; w_scale = 64 makes the output
+    # scale w_scale / inv exactly 1, so y = acc as an fp32 integer.
+    m = rng.integers(-127, 128, K).astype(np.float32)
+    m[5] = -127.0
+    x_int = orc.from_f32(m / np.float32(64.0), dt)
+    w, t = wl.ternary(1501, 512, K, 1 / 3, 64.0)
+    packed, s = orc.pack_i2s(w)
+    assert s == 64.0
+    acc = m.astype(np.int64) @ t.astype(np.int64).T
+    half = (np.abs(acc) >= 2048) & (acc % 2 == 1) if dt == "f16" else (np.abs(acc) >= 256) & (acc % 2 == 1)
+    assert half.sum() > 50, "the case must hold many exact ties of the output rounding"
+    cases = [("integer acc", x_int, packed, s, None, 512)]
+    cases.append(("integer acc, RMSNorm", x_int, packed, s, wl.gamma(1502, K, "u0.8-1.2"), 512))
+    # quantisation ties: x = (2j + 1) / 128, so x * 64 = j + 1/2
+    j = rng.integers(-64, 63, K).astype(np.float32)
+    xt = (2 * j + 1) / np.float32(128.0)
+    xt[0] = np.float32(-127.0 / 64.0)
+    x_tie = orc.from_f32(xt, dt)
+    eye, s_eye = orc.pack_i2s(np.eye(K, dtype=np.float32) * np.float32(0.5))
+    cases.append(("quantisation ties", x_tie, eye, s_eye, None, K))
+    if dt == "f16":
+        # fp16 subnormal inputs x = m 2^-20: inv = 2^20 and q = m, so W = s I
+        # gives y = m s 2^-20 exactly before rounding: subnormal (s = 2^-4),
+        # ties between subnormals (s = 2^-5: odd m gives m 2^-25) and normal
+        # (s = 2^10); over x = m / 64, s = 2^16 gives y = 1024 m, which
+        # overflows to inf from |m| >= 64
+        xs = m * np.float32(2.0 ** -20)
+        x_sub = orc.from_f32(xs, "f16")
+        assert np.array_equal(orc.to_f32(x_sub, "f16"), xs)
+        for e in (-4, -5, 10, 16):
+            pk, sk = orc.pack_i2s(np.eye(K, dtype=np.float32) * np.float32(2.0 ** e))
+            cases.append((f"subnormal x, s = 2^{e}", x_sub if e < 16 else x_int, pk, sk, None, K))
+    for name, x, pk, sk, g, N in cases:
+        announce("forward_io one token", dt, name)
+        y_r = orc.forward_io(x.reshape(1, K), dt, pk, sk, g, 1e-6, N, dt)
+        yb, q, inv, qs = one_token_io(torch, bl, x, dt, pk, sk, g, N)
+        assert np.array_equal(yb, np.asarray(y_r).view(np.uint16)), name
+        q_r, inv_r, qs_r = orc.act_quant(orc.to_f32(x.reshape(1, K), dt), g, 1e-6)
+        assert np.array_equal(q, q_r) and np.array_equal(inv, inv_r) and np.array_equal(qs, qs_r)
+        if name == "quantisation ties":
+            # round half to even by hand: j + 1/2 -> the even one of j, j + 1
+            expect = np.where(j % 2 == 0, j, j + 1)
+            assert np.array_equal(q[0, 1:].astype(np.float32), expect[1:])
+        if name.endswith("2^16"):
+            yh = yb.view(np.float16).astype(np.float32)
+            assert np.all(np.isinf(yh[0, np.abs(m) >= 64])) and np.all(np.isfinite(yh[0, np.abs(m) < 64]))
+
+
+def test_fp32_ops_correctly_rounded(torch, bl):
+    """The device's fp32 square root and division, as the normalisation and
+    quantisation use them, are correctly rounded: bit for bit against the
+    host's IEEE arithmetic on every exponent (subnormals included) with
+    65536 mantissas each, on wide random divisions, and on the RMSNorm and
+    quantisation scales at every row length K % 128 == 0 up to 32768."""
+    rng = np.random.default_rng(1600)
+    e = np.repeat(np.arange(255, dtype=np.uint32), 65536)
+    mant = (np.tile(np.arange(65536, dtype=np.uint32), 255) * 128 +
+            rng.integers(0, 128, 255 * 65536, dtype=np.uint32))
+    a = ((e << 23) | mant).view(np.float32)
+    announce("fp32 ops sqrt", a.size)
+    A = dev(torch, a)
+    got = host(bl.fp32_ops(bl.FP_SQRT, A))
+    torch.cuda.synchronize()
+    ref = np.sqrt(a)
+    bad = got.view(np.uint32) != ref.view(np.uint32)
+    assert not bad.any(), f"sqrtf differs on {bad.sum()} inputs, e.g. {a[bad][:4]}"
+    del A
+    # division over wide random operands (normal range)
+    n = 1 << 24
+    num = ((rng.integers(64, 190, n, dtype=np.uint32) << 23) |
+           rng.integers(0, 1 << 23, n, dtype=np.uint32)).view(np.float32)
+    den = ((rng.integers(64, 190, n, dtype=np.uint32) << 23) |
+           rng.integers(0, 1 << 23, n, dtype=np.uint32)).view(np.float32)
+    announce("fp32 ops div", n)
+    got = host(bl.fp32_ops(bl.FP_DIV, dev(torch, num), dev(torch, den)))
+    torch.cuda.synchronize()
+    ref = num / den
+    bad = got.view(np.uint32) != ref.view(np.uint32)
+    assert not bad.any(), f"division differs on {bad.sum()} pairs"
+    # the RMSNorm scale 1 / sqrt(ss / K + eps) at every K, ss over the range
+    # of sums of squares (and the quantisation scale 127 / max(amax, 1e-5))
+    Ks = np.arange(128, 32768 + 1, 128, dtype=np.float32)
+    per = 1 << 16
+    ss = np.exp(rng.uniform(np.log(1e-12), np.log(1e9), Ks.size * per)).astype(np.float32)
+    kk = np.repeat(Ks, per)
+    for eps in (1e-6, 1e-5):
+        announce("fp32 ops rms scale", eps)
+        got = host(bl.fp32_ops(bl.FP_RMS_SCALE, dev(torch, ss), dev(torch, kk), eps))
+        torch.cuda.synchronize()
+        ref = np.float32(1.0) / np.sqrt(ss / kk + np.float32(eps))
+        bad = got.view(np.uint32) != ref.view(np.uint32)
+        assert not bad.any(), f"rms scale differs on {bad.sum()} rows"
+    amax = np.exp(rng.uniform(np.log(1e-7), np.log(1e6), 1 << 22)).astype(np.float32)
+    amax[:3] = (0.0, 1e-5, np.float32(127.0 / 64.0))
+    announce("fp32 ops quant scale")
+    got = host(bl.fp32_ops(bl.FP_QUANT_SCALE, dev(torch, amax)))
+    torch.cuda.synchronize()
+    ref = np.float32(127.0) / np.maximum(amax, np.float32(1e-5))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert got[2] == np.float32(64.0)
 
 
 def test_forward_io_batch_mixed(torch, bl, orc):
