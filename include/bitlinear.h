@@ -24,8 +24,9 @@
  *     fp32 [M][N] row-major, gamma is fp32 [K]; y = RMSNorm/quant(x) W^T.
  *   - Every array pointer is a DEVICE pointer owned by the caller, except
  *     where a parameter says "host".  The library allocates no device memory
- *     and keeps no mutable global state; calls on different streams may run
- *     concurrently.
+ *     and keeps no mutable global state, except the per-device scratch array
+ *     of bitlinear_forward_noalloc; calls on different streams may run
+ *     concurrently (bitlinear_forward_noalloc excepted).
  *   - `stream` is a hipStream_t passed as void*; NULL means the default
  *     stream.
  *   - Arguments are validated on the host before anything is enqueued; a
@@ -176,6 +177,31 @@ bl_status bitlinear_forward(const float *x, const uint8_t *packed_w,
                             int64_t M, int64_t K, int64_t N, float *y,
                             void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): bitlinear_forward with the same arguments and results but no
+ * workspace argument.  The stage results q / inv / qsum go to a scratch
+ * array the library holds on each device (BITLINEAR_NOALLOC_SCRATCH_BYTES,
+ * allocated with the library's code on that device and held until the
+ * process ends) instead of a caller-owned workspace.
+ *   bitlinear_workspace_bytes(M, K) > BITLINEAR_NOALLOC_SCRATCH_BYTES ->
+ *   BL_ERR_WORKSPACE (e.g. M * K > 16 MiB); the other checks are
+ *   bitlinear_forward's.  The scratch array of the current device is used
+ *   (the device `stream` belongs to must be current); its address is looked
+ *   up on the first call on each device (BL_ERR_HIP if that fails).
+ *   Nothing in the scratch array needs to start at zero: each call writes
+ *   every q / inv / qsum value it reads.  Every call on a device shares that
+ *   device's array, which keeps the last call's contents: calls that may
+ *   overlap in time on one device (different streams, or several host
+ *   threads without ordering) race and give undefined results; calls on
+ *   one stream are ordered and safe.  No hipMalloc / hipFree or other
+ *   allocating call is made.  Asynchronous on `stream`. */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES ((size_t)(16u << 20) + (size_t)(64u << 10))
+bl_status bitlinear_forward_noalloc(const float *x, const uint8_t *packed_w,
+                                    float w_scale, const float *gamma, float eps,
+                                    int64_t M, int64_t K, int64_t N, float *y,
+                                    void *stream);
 
 /* bitlinear_forward with explicit launch options (NULL = automatic).  For
  * route/launch-shape independence tests and tuning. */

@@ -73,6 +73,7 @@ SIGNATURES = {
     "bitlinear_forward": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p, _sz, _p]),
     "bitlinear_forward_ex": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p, _sz,
                                   ctypes.POINTER(Launch), _p]),
+    "bitlinear_forward_noalloc": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p]),
     "bitlinear_forward_batch": (_i, [ctypes.POINTER(ForwardDesc), _i, ctypes.POINTER(Launch), _p]),
     "bitlinear_act_quant": (_i, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
     "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64]),
@@ -257,6 +258,23 @@ def forward(x, packed, w_scale: float, gamma, eps: float = 1e-6, N: int | None =
         _gamma(gamma), eps, M, K, N, _dev(out, torch.float32, "out"),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
         _launch(path, fuse, variant), _stream()), "forward")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = (16 << 20) + (64 << 10)  # BITLINEAR_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(x, packed, w_scale: float, gamma, eps: float, out):
+    """forward() through the allocation-free entry point: q / inv / qsum go
+    to the library's per-device scratch array; `out` (fp32 [M][N]) must be
+    preallocated.  Calls that overlap on one device race."""
+    torch = _torch()
+    M, K = x.shape
+    N = out.shape[1]
+    _check(lib().bitlinear_forward_noalloc(
+        _dev(x, torch.float32, "x"), _dev(packed, torch.uint8, "packed"), w_scale,
+        _gamma(gamma), eps, M, K, N, _dev(out, torch.float32, "out"), _stream()),
+        "forward_noalloc")
     return out
 
 

@@ -1,8 +1,10 @@
 // api.hip -- the exported C ABI (declared in include/bitlinear.h): host-side
 // argument validation, workspace carving and route dispatch.  Every check
 // runs before anything is enqueued; no exception leaves this file.
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/bitlinear.h"
 #include "common.hpp"
@@ -295,6 +297,42 @@ bl_status flush_io_group(const bl_forward_io_desc *const *g, int n, hipStream_t 
     return BL_OK;
 }
 
+// Scratch array of the allocation-free forward: one per device (each GPU
+// that loads the library's code holds its own copy), held until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host the
+// name is only a stand-in); it uses the device address looked up once per
+// device with hipGetSymbolAddress.
+constexpr size_t kScratchBytes = BITLINEAR_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device, with that device current).
+bl_status scratch_of_current_device(void **out);
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+bl_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BL_ERR_HIP;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BL_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,6 +485,20 @@ bl_status bitlinear_forward(const float *x, const uint8_t *packed_w, float w_sca
                             float *y, void *workspace, size_t workspace_bytes, void *stream) {
     return bitlinear_forward_ex(x, packed_w, w_scale, gamma, eps, M, K, N, y, workspace,
                                 workspace_bytes, nullptr, stream);
+}
+
+bl_status bitlinear_forward_noalloc(const float *x, const uint8_t *packed_w, float w_scale,
+                                    const float *gamma, float eps, int64_t M, int64_t K, int64_t N,
+                                    float *y, void *stream) {
+    // Every host-side check first (the aligned stand-in address is never
+    // dereferenced), then the size limit, then the scratch address.
+    const bl_forward_desc probe{x, packed_w, w_scale, gamma, eps, M, K, N, y,
+                                reinterpret_cast<void *>(uintptr_t(256)), kScratchBytes};
+    if (bl_status st = validate_forward(probe, nullptr)) return st;
+    void *ws = nullptr;
+    if (bl_status st = scratch_of_current_device(&ws)) return st;
+    return bitlinear_forward_ex(x, packed_w, w_scale, gamma, eps, M, K, N, y, ws, kScratchBytes,
+                                nullptr, stream);
 }
 
 size_t bitlinear_io_workspace_bytes(int64_t M, int64_t K, int64_t N) {

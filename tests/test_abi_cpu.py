@@ -280,3 +280,23 @@ def test_fp32_ops_validation(L):
     assert fo(1, F(A), F(0), 0.0, 8, F(A), None) == api.ERR_INVALID_ARG  # division needs b
     assert fo(2, F(A), F(0), 1e-6, 8, F(A), None) == api.ERR_INVALID_ARG
     assert fo(2, F(A), F(A), float("inf"), 8, F(A), None) == api.ERR_INVALID_ARG
+
+
+def test_forward_noalloc_validation(L):
+    """Host-side checks of the allocation-free forward run before the scratch
+    array is looked up (no device is touched here)."""
+    fn = L.bitlinear_forward_noalloc
+    assert api.NOALLOC_SCRATCH_BYTES == (16 << 20) + (64 << 10)
+
+    def call(x=A, p=A, s=0.02, g=A, eps=1e-6, M=1, K=256, N=256, y=A):
+        return fn(F(x), F(p), s, F(g), eps, M, K, N, F(y), None)
+    assert call(M=0) == api.ERR_SHAPE
+    assert call(K=100) == api.ERR_SHAPE
+    assert call(x=0) == api.ERR_INVALID_ARG
+    assert call(y=0) == api.ERR_INVALID_ARG
+    assert call(eps=0.0) == api.ERR_INVALID_ARG
+    assert call(s=float("inf")) == api.ERR_INVALID_ARG
+    assert call(y=MIS) == api.ERR_ALIGN
+    # beyond the scratch array: 16 MiB of q plus inv / qsum
+    assert call(M=2048, K=8192 + 128) == api.ERR_WORKSPACE
+    assert call(M=(16 << 20) // 128 + 1, K=128) == api.ERR_WORKSPACE
