@@ -13,11 +13,18 @@ resident in HBM.  Algorithmic bytes per BitLinear = N*K/4 (packed W) +
 enough copies (>= 768 MB in total) that every step streams them from HBM,
 not from the 256 MB last-level cache.
 
-Prints one JSON line (see the "metric" of the workload).  Options:
+Prints one JSON line (see the "metric" of the workload).  Beside the main
+value: the prefill layer (M = 512) and the square K = N = 8192 sweep
+(M = 1 .. 2048) in int8 TOPS / GB/s, the 70B FFN BitLinears at M = 1 and 16,
+the single 256 x 256 BitLinear, the packer, the FFN block, half-precision
+I/O, a dequantised-weights library comparison and the layer without
+RMSNorm, each with its roofline fraction; measured ceilings (one-launch HBM
+read at the decode sizes, back-to-back int8 MFMA); and the oracle on the
+host cores (all threads and one thread).  Options:
   --gpus N (only 1 is supported), --steps K, --warmup W,
-  --workload decode|prefill|decode-mM|ffn70b-1|ffn70b-16|sweep-M,
+  --workload decode|prefill|decode-mM|ffn70b-1|ffn70b-16|sweep-M|tiny,
   --no-cpu-baseline, --no-secondary, --pack-only, --ffn-only, --io-only,
-  --dense-only.
+  --dense-only, --pmc-app.
 """
 from __future__ import annotations
 
@@ -170,13 +177,38 @@ def traffic_from_profiles(name: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(work, budget_s=12.0):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def set_oracle_threads(n):
+    """OpenMP threads of the oracle (its library is built with -fopenmp;
+    results do not depend on the count)."""
+    import ctypes
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+        return True
+    except OSError:
+        return False
+
+
+def cpu_baseline(work, budget_s=12.0, threads=None):
     """The oracle, untuned, on the host cores: whole steps of the workload
     (inputs prepared outside the timed region), repeated until the budget is
     spent; scaled to GB/s of algorithmic bytes.  For workloads whose step is
-    too large, a subset of the weight rows is used and scaled."""
+    too large, a subset of the weight rows is used and scaled.  threads:
+    OpenMP threads (None: all of them)."""
     from oracle import oracle as orc
     orc.lib()
+    all_cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    used = all_cores if threads is None else threads
+    set_oracle_threads(used)
     items = []
     total_bytes = 0
     row_frac = 1.0
@@ -199,15 +231,99 @@ def cpu_baseline(work, budget_s=12.0):
         if el > budget_s or n >= 100000:
             break
     per_step = el / n / row_frac
-    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    set_oracle_threads(all_cores)
     sample = (f"{n} oracle forward step(s) of the whole workload" if row_frac == 1.0 else
               f"{n} oracle step(s) over {row_frac:.4f} of the weight rows, scaled")
-    return {"value": round(total_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "sample": sample, "seconds": round(el, 2)}
+    return {"value": round(total_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle", "sample": sample, "seconds": round(el, 2),
+            "ms_per_step": round(per_step * 1e3, 3), "cpu_model": cpu_model()}
+
+
+def time_fn(torch, fn, steps, warmup):
+    """Seconds per call of fn(r) (which enqueues on the current stream):
+    HIP events around a graph replay of `steps` calls, after `warmup`
+    untimed ones."""
+    gw = capture(torch, lambda: [fn(r) for r in range(max(1, warmup))])
+    gt = capture(torch, lambda: [fn(warmup + r) for r in range(steps)])
+    gw.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gt.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del gw, gt
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def roofline_of(L_list, sec, kernel):
+    """Roofline block of a step of BitLinears taking `sec` seconds: the bound
+    is min(int8 peak, intensity x HBM peak) over the step's algorithmic bytes
+    and int ops; `achieved` is in that bound's unit."""
+    nbytes = sum(linear_bytes(L) for L in L_list)
+    ops = sum(2 * L.M * L.N * L.K for L in L_list)
+    if ops / nbytes * HBM_PEAK_GBS * 1e9 < INT8_PEAK_TOPS * 1e12:
+        ach = nbytes / sec / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "avg_step_us": round(sec * 1e6, 2),
+                "kernel": kernel}
+    ach = ops / sec / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+            "frac": round(ach / INT8_PEAK_TOPS, 4), "avg_step_us": round(sec * 1e6, 2),
+            "kernel": kernel}
+
+
+class DeviceLinears:
+    """BitLinears whose ternary weights are drawn on the device (seeded,
+    with the workload's P(0) and scale; x and gamma from the workload's host
+    recipe), packed once and rotated over >= 768 MB of copies.  For timing
+    legs of large shapes, where drawing the weights on the host would
+    dominate the run."""
+
+    def __init__(self, torch, api, linears, seed, eps=1e-6, packs=None):
+        from ternary_bit_linear_amd import workloads as wl
+        self.eps = eps
+        self.lin = []
+        total = 0
+        gen = torch.Generator(device="cuda")
+        for i, L in enumerate(linears):
+            if packs is not None:
+                P, sc = packs[i]
+            else:
+                gen.manual_seed(seed + 3 * i + 1)
+                u = torch.rand((L.N, L.K), generator=gen, device="cuda")
+                w = torch.where(u < L.p0, 0.0, torch.where(u < L.p0 + (1 - L.p0) / 2, 1.0, -1.0))
+                del u
+                w.mul_(L.scale)
+                P, sc = api.pack_i2s(w)
+                del w
+            x = torch.from_numpy(wl.activations(seed + 3 * i, L.M, L.K, L.outlier_frac)).cuda()
+            g = torch.from_numpy(wl.gamma(seed + 3 * i + 2, L.K, L.gamma)).cuda()
+            y = torch.empty((L.M, L.N), dtype=torch.float32, device="cuda")
+            self.lin.append({"L": L, "x": x, "g": g, "P": [P], "s": sc, "y": y,
+                             "ws": api.new_workspace(L.M, L.K)})
+            total += P.numel()
+        self.copies = max(2, -(-ROTATE_BYTES // total))
+        for d in self.lin:
+            d["P"] += [d["P"][0].clone() for _ in range(self.copies - 1)]
+        torch.cuda.synchronize()
+
+    def packs(self):
+        return [(d["P"][0], d["s"]) for d in self.lin]
+
+    def step(self, api, r):
+        api.forward_batch([(d["x"], d["P"][r % self.copies], d["s"], d["g"], self.eps, d["y"],
+                            d["ws"]) for d in self.lin])
+
+    def single(self, api, d, r):
+        api.forward(d["x"], d["P"][r % self.copies], d["s"], d["g"], self.eps, d["L"].N,
+                    out=d["y"], workspace=d["ws"])
 
 
 def secondary_prefill(torch, api, steps, warmup):
-    """int8 TOPS of the prefill layer (M = 512): 2*M*N*K over the forward time."""
+    """int8 TOPS of the prefill layer (M = 512): 2*M*N*K over the forward
+    time (one batched quantisation launch and one grouped contraction
+    launch per step), and each BitLinear alone."""
     from ternary_bit_linear_amd import workloads as wl
     prep = Prepared(torch, api, wl.PREFILL_LAYER)
     ms = time_steps(torch, api, prep, steps, warmup)
@@ -217,22 +333,115 @@ def secondary_prefill(torch, api, steps, warmup):
     per = {}
     for name, (L, t) in by.items():
         per[name] = {"M": L.M, "K": L.K, "N": L.N, "us": round(t * 1e6, 2),
-                     "TOPS": round(2 * L.M * L.N * L.K / t / 1e12, 1)}
+                     "TOPS": round(2 * L.M * L.N * L.K / t / 1e12, 1),
+                     "roofline": roofline_of([L], t, "act_quant + contraction")}
     del prep
     torch.cuda.empty_cache()
-    # The square M = 512 point (K = N = 8192) of the sweep, same measurement.
-    sq = wl.sweep(512)
-    prep = Prepared(torch, api, sq)
-    ms_sq = time_steps(torch, api, prep, steps, warmup)
-    tops_sq = sq.int_ops() / (ms_sq * 1e-3) / 1e12
-    del prep
-    torch.cuda.empty_cache()
+    roof = roofline_of(list(wl.PREFILL_LAYER.linears), ms * 1e-3,
+                       "act_quant_batch_kernel + grouped contraction (7 BitLinears per launch "
+                       "pair)")
+    roof_mfma = {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
+                 "unit": "TOPS", "frac": round(tops / INT8_PEAK_TOPS, 4)}
     return {"workload": wl.PREFILL_LAYER.name, "metric": "int8 TOPS (M=512 GEMM)",
             "value": round(tops, 2), "unit": "TOPS", "ms_per_step": round(ms, 4),
-            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "per_linear": per,
-            "square_m512": {"workload": sq.name, "value": round(tops_sq, 2), "unit": "TOPS",
-                            "ms_per_step": round(ms_sq, 4),
-                            "frac_of_int8_peak": round(tops_sq / INT8_PEAK_TOPS, 4)}}
+            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+            "roofline": roof, "roofline_vs_int8_peak": roof_mfma, "per_linear": per}
+
+
+def secondary_sweep(torch, api, steps, warmup):
+    """The square BitLinear K = N = 8192 at M = 1 .. 2048 tokens, one
+    forward per step (quantisation and contraction launches included), with
+    the roofline of each point (HBM-bound up to M = 64, MFMA-bound from
+    M = 256)."""
+    from ternary_bit_linear_amd import workloads as wl
+    res = {}
+    packs = None
+    for M in (1, 4, 16, 64, 256, 512, 2048):
+        work = wl.sweep(M)
+        dl = DeviceLinears(torch, api, work.linears, 5000 + M, work.eps, packs)
+        packs = dl.packs()
+        sec = time_fn(torch, lambda r: dl.step(api, r), steps, warmup)
+        L = work.linears[0]
+        res[f"M{M}"] = {"M": M, "us": round(sec * 1e6, 2),
+                        "GBs": round(linear_bytes(L) / sec / 1e9, 1),
+                        "TOPS": round(2 * M * L.N * L.K / sec / 1e12, 1),
+                        "roofline": roofline_of([L], sec, "act_quant + contraction, one "
+                                                "forward")}
+        del dl
+        torch.cuda.empty_cache()
+    return {"workload": "square BitLinear K=N=8192, M = 1..2048 (weights drawn on the device)",
+            **res}
+
+
+def secondary_ffn70b(torch, api, steps, warmup):
+    """The 70B-shaped FFN BitLinears (gate / up 8192 -> 28672, down
+    28672 -> 8192) one forward at a time, at M = 1 and M = 16: GB/s of
+    algorithmic bytes and the HBM roofline fraction of each."""
+    from ternary_bit_linear_amd import workloads as wl
+    res = {}
+    packs = None
+    for M in (1, 16):
+        work = wl.ffn70b(M)
+        dl = DeviceLinears(torch, api, work.linears, 4000, work.eps, packs)
+        packs = dl.packs()
+        per = {}
+        for d in dl.lin:
+            L = d["L"]
+            sec = time_fn(torch, lambda r, d=d: dl.single(api, d, r), max(4, steps // 2), 2)
+            per[L.name] = {"M": M, "K": L.K, "N": L.N, "us": round(sec * 1e6, 2),
+                           "GBs": round(linear_bytes(L) / sec / 1e9, 1),
+                           "roofline": roofline_of([L], sec, "one forward (all its launches)")}
+        sec = time_fn(torch, lambda r: dl.step(api, r), max(4, steps // 2), 2)
+        per["all_three_batched"] = {"us": round(sec * 1e6, 2),
+                                    "roofline": roofline_of(list(work.linears), sec,
+                                                            "forward_batch of the three")}
+        res[f"M{M}"] = per
+        del dl
+        torch.cuda.empty_cache()
+    del packs
+    torch.cuda.empty_cache()
+    return {"workload": "70B-shaped FFN BitLinears (weights drawn on the device)", **res}
+
+
+def secondary_tiny(torch, api, steps, warmup):
+    """The single 256 x 256 BitLinear at M = 1 (correctness-sized: its time
+    is the launch floor, so no roofline claim)."""
+    from ternary_bit_linear_amd import workloads as wl
+    prep = Prepared(torch, api, wl.TINY)
+    ms = time_steps(torch, api, prep, steps, warmup)
+    del prep
+    return {"workload": wl.TINY.name, "us": round(ms * 1e3, 2)}
+
+
+def measured_ceilings(torch, api):
+    """Measured ceilings: one launch reading the decode layer's weight bytes
+    (17.6 MB) and a 70B FFN matrix (58.7 MB) from HBM (buffers rotated over
+    >= 768 MB so the reads miss the last-level cache), a device copy of the
+    same sizes, and back-to-back int8 MFMAs over the whole device."""
+    res = {}
+    for name, nbytes in (("decode_layer_17.6MB", 17636352), ("ffn70b_matrix_58.7MB", 58720256)):
+        nbytes = nbytes // 16 * 16
+        copies = max(2, -(-ROTATE_BYTES // nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i & 255)
+                for i in range(copies)]
+        sink = api.probe_read(bufs[0])
+        sec = time_fn(torch, lambda r: api.probe_read(bufs[r % copies], sink), 50, 5)
+        dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        sec_c = time_fn(torch, lambda r: dst.copy_(bufs[r % copies]), 50, 5)
+        res[name] = {"read_GBs": round(nbytes / sec / 1e9, 1), "read_us": round(sec * 1e6, 2),
+                     "copy_GBs_read_plus_write": round(2 * nbytes / sec_c / 1e9, 1),
+                     "copy_us": round(sec_c * 1e6, 2)}
+        del bufs, dst, sink
+        torch.cuda.empty_cache()
+    iters, wgs = 4096, 512
+    sink = api.probe_mfma(iters, wgs)
+    sec = time_fn(torch, lambda r: api.probe_mfma(iters, wgs, sink), 10, 2)
+    ops = 4 * 65536 * iters * 4 * wgs
+    res["int8_mfma_back_to_back"] = {"TOPS": round(ops / sec / 1e12, 1),
+                                     "frac_of_published": round(ops / sec / 1e12 / INT8_PEAK_TOPS,
+                                                                4),
+                                     "workgroups": wgs, "rounds_per_wave": iters}
+    return res
 
 
 def secondary_ffn(torch, api, steps, warmup):
@@ -478,6 +687,12 @@ def main():
                     help="time only the bf16-I/O legs (--steps steps each) and print their line")
     ap.add_argument("--ffn-only", action="store_true",
                     help="time only the FFN block legs (--steps steps each) and print their line")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="time only the K = N = 8192 sweep and print its line")
+    ap.add_argument("--ffn70b-only", action="store_true",
+                    help="time only the 70B FFN BitLinears at M = 1 and 16 and print their line")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="measure only the read / copy / MFMA ceilings and print their line")
     ap.add_argument("--pmc-app", action="store_true",
                     help="no timing: run --steps steps of the workload and a 256 MiB device "
                          "copy (the calibration kernel for HBM byte counters), then exit")
@@ -506,6 +721,16 @@ def main():
         return
     if args.ffn_only:
         print(json.dumps(secondary_ffn(torch, api, max(1, args.steps), args.warmup)), flush=True)
+        return
+    if args.sweep_only:
+        print(json.dumps(secondary_sweep(torch, api, max(1, args.steps), args.warmup)), flush=True)
+        return
+    if args.ffn70b_only:
+        print(json.dumps(secondary_ffn70b(torch, api, max(1, args.steps), args.warmup)),
+              flush=True)
+        return
+    if args.ceilings_only:
+        print(json.dumps(measured_ceilings(torch, api)), flush=True)
         return
     work = workload_by_name(args.workload)
     prep = Prepared(torch, api, work)
@@ -538,7 +763,9 @@ def main():
                 "kernel": "gemv_shot_kernel (one-shot decode: RMSNorm + int8 quant + "
                           f"I2_S x int8 MFMA, {len(work.linears)} BitLinears per launch)",
                 "launches_per_step": launches,
-                "avg_launch_us": round(avg_s * 1e6, 3),
+                # HIP-event time per launch over the graph-replayed timed
+                # region (back-to-back steps, launch gaps included)
+                "avg_step_us": round(avg_s * 1e6, 3),
                 "bytes_per_launch": step_bytes // launches}
     else:
         dom_name, (dom_L, dom_s) = max(by.items(), key=lambda kv: linear_bytes(kv[1][0]))
@@ -549,7 +776,7 @@ def main():
                     "traffic": traffic_from_profiles(args.workload),
                     "kernel": "act_quant + gemv (decode route)",
                     "launch": f"{dom_name} M={dom_L.M} K={dom_L.K} N={dom_L.N}",
-                    "avg_launch_us": round(dom_s * 1e6, 3),
+                    "avg_step_us": round(dom_s * 1e6, 3),
                     "bytes_per_launch": linear_bytes(dom_L)}
         else:
             # A step of prefill-sized BitLinears is one batched quantisation
@@ -560,7 +787,7 @@ def main():
             roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS,
                     "unit": "TOPS", "frac": round(ach / INT8_PEAK_TOPS, 4),
                     "traffic": None,
-                    "kernel": "act_quant_batch_kernel + gemm_group_kernel (I2_S x int8 MFMA), "
+                    "kernel": "act_quant_batch_kernel + grouped I2_S x int8 MFMA contraction, "
                               f"{len(work.linears)} BitLinears per launch pair",
                     "launches_per_step": 2 * groups,
                     "avg_step_us": round(ms * 1e3, 3),
@@ -587,7 +814,17 @@ def main():
     del prep
     torch.cuda.empty_cache()
     if not args.no_secondary and args.workload == "decode":
-        out["secondary"] = secondary_prefill(torch, api, max(20, args.steps // 4), 5)
+        sec_steps = max(20, args.steps // 4)
+        out["secondary"] = secondary_prefill(torch, api, sec_steps, 5)
+        torch.cuda.empty_cache()
+        out["secondary"]["sweep"] = secondary_sweep(torch, api, sec_steps, 5)
+        out["secondary"]["square_m512"] = {
+            "workload": "square BitLinear K=N=8192 M=512",
+            **{k: out["secondary"]["sweep"]["M512"][k] for k in ("us", "TOPS", "roofline")}}
+        torch.cuda.empty_cache()
+        out["secondary"]["ffn70b_linears"] = secondary_ffn70b(torch, api, sec_steps, 5)
+        torch.cuda.empty_cache()
+        out["secondary"]["tiny"] = secondary_tiny(torch, api, sec_steps, 5)
         torch.cuda.empty_cache()
         out["secondary"]["pack"] = secondary_pack(torch, api)
         torch.cuda.empty_cache()
@@ -598,8 +835,14 @@ def main():
         out["secondary"]["dense_comparison"] = secondary_dense(torch, api, max(20, args.steps // 4), 5)
         torch.cuda.empty_cache()
         out["secondary"]["no_rmsnorm"] = secondary_nonorm(torch, api, max(20, args.steps // 4), 5)
+        torch.cuda.empty_cache()
+        out["measured_ceilings"] = measured_ceilings(torch, api)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work)
+        one = cpu_baseline(work, budget_s=8.0, threads=1)
+        out["cpu_baseline"]["single_thread"] = {k: one[k] for k in
+                                                ("value", "unit", "cores", "sample", "seconds",
+                                                 "ms_per_step")}
     print(json.dumps(out), flush=True)
 
 

@@ -419,6 +419,26 @@ size_t bitlinear_ffn_workspace_bytes(int64_t M, int64_t H, int64_t F);
 
 bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream);
 
+/* Calibration probes, used by the benchmark to measure the ceilings the
+ * BitLinear kernels are read against; not part of the BitLinear path.
+ *   bitlinear_probe_read: one launch that reads `bytes` bytes of `src`
+ *     (device, 16-byte aligned, bytes a multiple of 16 and < 2^40) with
+ *     coalesced 16-byte loads, all of a thread's loads in flight at once;
+ *     sink: device uint32, at least bitlinear_probe_read_sink_words(bytes)
+ *     words (one per workgroup, the XOR of what it read).
+ *   bitlinear_probe_mfma: `workgroups` workgroups of 256 threads, each wave
+ *     issuing `iters` rounds of four independent v_mfma_i32_32x32x32_i8
+ *     (2 * 32 * 32 * 32 int ops each); sink: device int32, at least
+ *     workgroups * 256 words.  iters >= 1, 1 <= workgroups < 2^31.
+ * Errors: BL_ERR_SHAPE for sizes out of range, BL_ERR_INVALID_ARG for NULL
+ * pointers or a short sink, BL_ERR_ALIGN for a misaligned src.
+ * Asynchronous on `stream`. */
+size_t bitlinear_probe_read_sink_words(size_t bytes);
+bl_status bitlinear_probe_read(const void *src, size_t bytes, uint32_t *sink, size_t sink_words,
+                               void *stream);
+bl_status bitlinear_probe_mfma(int64_t iters, int64_t workgroups, int32_t *sink,
+                               size_t sink_words, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,6 +74,9 @@ SIGNATURES = {
     "bitlinear_forward_ex": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p, _sz,
                                   ctypes.POINTER(Launch), _p]),
     "bitlinear_forward_noalloc": (_i, [_p, _p, _f, _p, _f, _i64, _i64, _i64, _p, _p]),
+    "bitlinear_probe_read_sink_words": (_sz, [_sz]),
+    "bitlinear_probe_read": (_i, [_p, _sz, _p, _sz, _p]),
+    "bitlinear_probe_mfma": (_i, [_i64, _i64, _p, _sz, _p]),
     "bitlinear_forward_batch": (_i, [ctypes.POINTER(ForwardDesc), _i, ctypes.POINTER(Launch), _p]),
     "bitlinear_act_quant": (_i, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
     "bitlinear_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64]),
@@ -276,6 +279,31 @@ def forward_noalloc(x, packed, w_scale: float, gamma, eps: float, out):
         _gamma(gamma), eps, M, K, N, _dev(out, torch.float32, "out"), _stream()),
         "forward_noalloc")
     return out
+
+
+def probe_read(src, sink=None):
+    """Calibration probe: one launch reading every byte of `src` (a device
+    tensor).  Returns the sink tensor (so a caller can reuse it)."""
+    torch = _torch()
+    nb = src.numel() * src.element_size()
+    words = int(lib().bitlinear_probe_read_sink_words(nb))
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=src.device)
+    _check(lib().bitlinear_probe_read(ctypes.c_void_p(src.data_ptr()), nb,
+                                      ctypes.c_void_p(sink.data_ptr()), sink.numel(), _stream()),
+           "probe_read")
+    return sink
+
+
+def probe_mfma(iters: int, workgroups: int, sink=None):
+    """Calibration probe: back-to-back int8 32x32x32 MFMAs (4 per round per
+    wave, 65536 int ops each) in `workgroups` workgroups of 256 threads."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(workgroups * 256, dtype=torch.int32, device="cuda")
+    _check(lib().bitlinear_probe_mfma(iters, workgroups, ctypes.c_void_p(sink.data_ptr()),
+                                      sink.numel(), _stream()), "probe_mfma")
+    return sink
 
 
 def forward_batch(items, path: int = PATH_AUTO, fuse: int = -1, variant: int = 0):

@@ -45,6 +45,7 @@ def sources() -> list[str]:
 EXTRA = {
     "gemv_shot.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
     "gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+    "gemm32.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
     "act_quant.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
 }
 

@@ -487,6 +487,28 @@ bl_status bitlinear_forward(const float *x, const uint8_t *packed_w, float w_sca
                                 workspace_bytes, nullptr, stream);
 }
 
+size_t bitlinear_probe_read_sink_words(size_t bytes) {
+    if (bytes < 16 || bytes % 16 != 0 || bytes >= ((size_t)1 << 40)) return 0;
+    return (size_t)bl::probe_read_blocks(bytes);
+}
+
+bl_status bitlinear_probe_read(const void *src, size_t bytes, uint32_t *sink, size_t sink_words,
+                               void *stream) {
+    const size_t need = bitlinear_probe_read_sink_words(bytes);
+    if (need == 0 || need > (size_t)kMaxDim) return BL_ERR_SHAPE;
+    if (!src || !sink || sink_words < need) return BL_ERR_INVALID_ARG;
+    if (!aligned16(src)) return BL_ERR_ALIGN;
+    return hip_status(bl::launch_probe_read(static_cast<const uint8_t *>(src), bytes, sink,
+                                            as_stream(stream)));
+}
+
+bl_status bitlinear_probe_mfma(int64_t iters, int64_t workgroups, int32_t *sink,
+                               size_t sink_words, void *stream) {
+    if (iters < 1 || workgroups < 1 || workgroups > kMaxDim) return BL_ERR_SHAPE;
+    if (!sink || sink_words < (size_t)workgroups * 256) return BL_ERR_INVALID_ARG;
+    return hip_status(bl::launch_probe_mfma(iters, workgroups, sink, as_stream(stream)));
+}
+
 bl_status bitlinear_forward_noalloc(const float *x, const uint8_t *packed_w, float w_scale,
                                     const float *gamma, float eps, int64_t M, int64_t K, int64_t N,
                                     float *y, void *stream) {

@@ -823,6 +823,22 @@ struct GemmDesc {
 bool gemm_group_supported(int64_t K);
 hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s);
 
+// Prefill route on the 32 x 32 x 32 int8 MFMA (activations and packed
+// weights staged through LDS rings, one I2_S block per step): up to 8
+// problems (any K % 128 == 0) in one launch, bit-identical to launch_gemm.
+// shape: 1..gemm32_num_shapes() (0 picks the first).
+int gemm32_num_shapes();
+hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStream_t s);
+// Whether the automatic choice takes the 32 x 32 x 32 kernel for a group.
+bool gemm32_preferred(const GemmDesc *d, int count);
+
+// Calibration probes: one pass reading `bytes` (a multiple of 16; one
+// sink word per workgroup, probe_read_blocks(bytes) of them), and `blocks`
+// workgroups of back-to-back int8 MFMAs (256 sink words each).
+int64_t probe_read_blocks(uint64_t bytes);
+hipError_t launch_probe_read(const uint8_t *src, uint64_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_probe_mfma(int64_t iters, int64_t blocks, int32_t *sink, hipStream_t s);
+
 // I2_S packing: scan (codes + magnitude statistics into the trailer words),
 // then finalize (trailer = scale + 28 zero bytes).
 hipError_t launch_pack_scan(const float *w, int64_t N, int64_t K,

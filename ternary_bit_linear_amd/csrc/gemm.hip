@@ -356,7 +356,7 @@ hipError_t launch_tile(const int8_t *q, const float *inv, const int32_t *qsum,
 
 }  // namespace
 
-int gemm_num_variants() { return kNumTiles; }
+int gemm_num_variants() { return kNumTiles + gemm32_num_shapes(); }
 
 bool gemm_group_supported(int64_t K) { return K % kStepK == 0; }
 
@@ -412,6 +412,7 @@ hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
 
 hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
     if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    if (gemm32_preferred(d, count)) return launch_gemm32_group(d, count, 0, s);
     const bool y = d[0].y != nullptr;
     int64_t t64x512 = 0, t64x256 = 0, t64x128 = 0, t32x128 = 0, t16x128 = 0, t16x64 = 0, kmax = 0,
             mmax = 0;
@@ -486,7 +487,10 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         // (8 waves; long K only: short rows do not amortise its fill), 64x128
         // down to one per CU, then 32-row tiles (the wider one for long K).
         auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-        if (M <= 32)
+        const GemmDesc one{q, inv, qsum, packed, w_scale, M, K, N, y, acc};
+        if (gemm32_preferred(&one, 1)) {
+            return launch_gemm32_group(&one, 1, 0, s);
+        } else if (M <= 32)
             // Few tokens: 16-row tiles, the widest that still gives about one
             // tile per CU (M = 16, K = 8192: N = 8192 16x32 8.8 us against
             // 32x64 10.3 us; N = 28672 16x128; measured).
@@ -501,6 +505,12 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
             v = 5;
         else
             v = 4;
+    }
+    if (v > kNumTiles) {
+        // Variants past the 16 x 16 x 64 table: the 32 x 32 x 32 kernel's
+        // launch shapes (K % 128 == 0 always holds here).
+        GemmDesc d{q, inv, qsum, packed, w_scale, M, K, N, y, acc};
+        return launch_gemm32_group(&d, 1, v - kNumTiles, s);
     }
 #define BL_GEMM_CASE(idx)                                                                  \
     case idx:                                                                              \

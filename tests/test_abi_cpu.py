@@ -300,3 +300,20 @@ def test_forward_noalloc_validation(L):
     # beyond the scratch array: 16 MiB of q plus inv / qsum
     assert call(M=2048, K=8192 + 128) == api.ERR_WORKSPACE
     assert call(M=(16 << 20) // 128 + 1, K=128) == api.ERR_WORKSPACE
+
+
+def test_probe_validation(L):
+    assert L.bitlinear_probe_read_sink_words(0) == 0
+    assert L.bitlinear_probe_read_sink_words(100) == 0
+    assert L.bitlinear_probe_read_sink_words(32768) == 1
+    assert L.bitlinear_probe_read_sink_words(32768 + 16) == 2
+    pr = L.bitlinear_probe_read
+    assert pr(F(A), 100, F(A), 10, None) == api.ERR_SHAPE
+    assert pr(F(0), 1 << 20, F(A), 1 << 10, None) == api.ERR_INVALID_ARG
+    assert pr(F(A), 1 << 20, F(A), 31, None) == api.ERR_INVALID_ARG  # needs 32 words
+    assert pr(F(MIS), 1 << 20, F(A), 32, None) == api.ERR_ALIGN
+    pm = L.bitlinear_probe_mfma
+    assert pm(0, 4, F(A), 1024, None) == api.ERR_SHAPE
+    assert pm(10, 0, F(A), 1024, None) == api.ERR_SHAPE
+    assert pm(10, 4, F(A), 1023, None) == api.ERR_INVALID_ARG
+    assert pm(10, 4, F(0), 1024, None) == api.ERR_INVALID_ARG

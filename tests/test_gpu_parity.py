@@ -1262,3 +1262,29 @@ def test_forward_batch_few_token_tiles(torch, bl, orc):
         got = host(it[5])
         assert np.array_equal(got, single), sh
         check_y(got[:, rows], y64)
+
+
+# ---------------------------------------------------------------- calibration probes
+
+def test_probe_read_reads_every_byte(torch, bl):
+    """The read-ceiling probe reads every byte once: each workgroup's sink
+    word is the XOR of the 32-bit words of its 32 KB share (a ragged last
+    share included)."""
+    announce("probe read")
+    nb = 3 * 32768 + 48
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    buf = torch.randint(0, 256, (nb,), generator=g, dtype=torch.uint8, device="cuda")
+    sink = bl.probe_read(buf)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    expect = [np.bitwise_xor.reduce(h[i:i + 32768].view(np.uint32)) for i in range(0, nb, 32768)]
+    assert host(sink).view(np.uint32).tolist() == [int(e) for e in expect]
+
+
+def test_probe_mfma_deterministic(torch, bl):
+    announce("probe mfma")
+    a = host(bl.probe_mfma(64, 8)).copy()
+    b = host(bl.probe_mfma(64, 8))
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b) and np.any(a != 0)
