@@ -98,6 +98,10 @@ def lib() -> ctypes.CDLL:
     """Load the HIP library (raises if it was not built)."""
     global _lib
     if _lib is None:
+        # PyTorch ships its own HIP runtime; importing it first makes the
+        # library bind to that same runtime (its device pointers and streams),
+        # instead of loading a second one from the system ROCm.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with `python -m ternary_bit_linear_amd.build`")

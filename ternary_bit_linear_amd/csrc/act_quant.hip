@@ -21,6 +21,7 @@ namespace bl {
 namespace {
 
 struct GlobalRowSink {
+    static constexpr bool kDeferSum = false;
     int8_t *q;  // row base
     float *inv;
     int32_t *qsum;

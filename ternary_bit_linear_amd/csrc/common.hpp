@@ -391,7 +391,27 @@ __device__ __forceinline__ float amax4(float a, const float4 &v) {
 // With gamma == nullptr there is no RMSNorm: xn = x (no sum of squares).
 // GLU: the row is not read from x but formed as relu2_mul(x, u) from the
 // gate row x and the up row u (the FFN's down projection input).
-// Sink receives store_q(k, 4 packed int8) and store_row(inv, qsum).
+// Sink receives store_q(k, 4 packed int8) and store_row(inv, qsum); or, when
+// Sink::kDeferSum is true, store_inv(inv) and store_qsum_part(wave, partial)
+// (one int per wave of the 256-thread block, written to LDS before the
+// caller's next barrier): the activation sum is only needed by the
+// contraction's epilogue, so its block reduction (and barrier) is left off
+// the path to the first MFMA, and the caller adds the four partials after
+// the barrier that publishes q.
+
+// The last step of the block form: inv and the activation sum of the row
+// (see kDeferSum above).
+template <class Sink>
+__device__ __forceinline__ void finish_row(Sink &sink, float inv, int qs, float *red) {
+    if constexpr (Sink::kDeferSum) {
+        qs = wave_sum_int(qs);
+        if ((threadIdx.x & 63) == 0) sink.store_qsum_part((int)(threadIdx.x >> 6), qs);
+        if (threadIdx.x == 0) sink.store_inv(inv);
+    } else {
+        qs = block_sum_int(qs, red + 8);
+        if (threadIdx.x == 0) sink.store_row(inv, qs);
+    }
+}
 
 // Block form (256 threads): thread t owns O256 chain t, i.e. the float4
 // groups at k = 4t + 1024 i.  Rows of up to 1024 * CH elements keep x and
@@ -484,8 +504,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                 sink.store_q(k, w);
             }
         }
-        qs = block_sum_int(qs, red + 8);
-        if (threadIdx.x == 0) sink.store_row(inv, qs);
+        finish_row(sink, inv, qs, red);
         return;
     } else {
     issued();
@@ -554,21 +573,21 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
             }
         }
     }
-    qs = block_sum_int(qs, red + 8);
-    if (threadIdx.x == 0) sink.store_row(inv, qs);
+    finish_row(sink, inv, qs, red);
     }
 }
 
 // Barriers block_act_quant_row<..., SYNC = false> takes per row: one per
-// block reduction (sum of squares with RMSNorm, max, sum of q).  Waves of a
+// block reduction (sum of squares with RMSNorm, max, and the sum of q unless
+// the sink defers it).  Waves of a
 // larger workgroup that do not run the 256-thread block form call
 // block_act_quant_row_barriers instead, so every wave meets the same
 // barriers; a change to the block reductions must change both.
-__device__ __forceinline__ int block_act_quant_row_barrier_count(bool norm) {
-    return norm ? 3 : 2;
+__device__ __forceinline__ int block_act_quant_row_barrier_count(bool norm, bool defer_sum) {
+    return (norm ? 3 : 2) - (defer_sum ? 1 : 0);
 }
-__device__ __forceinline__ void block_act_quant_row_barriers(bool norm) {
-    const int n = block_act_quant_row_barrier_count(norm);
+__device__ __forceinline__ void block_act_quant_row_barriers(bool norm, bool defer_sum) {
+    const int n = block_act_quant_row_barrier_count(norm, defer_sum);
     for (int i = 0; i < n; ++i) lds_barrier();
 }
 

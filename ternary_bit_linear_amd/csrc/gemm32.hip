@@ -495,6 +495,10 @@ int gemm32_num_shapes() { return kNumShapes32; }
 // (N = 2560 at M = 512, or M = 256 at N = 8192) the smaller tiles of the
 // 16 x 16 x 64 kernel fill the device better and stay faster.
 constexpr int kAutoShape32 = 3;
+// With >= 512 tiles of 128 x 256 (two per CU), the wider tile halves the
+// activation traffic and wins (K = N = 8192 at M = 2048: 113-118 against
+// 126-130 us).
+constexpr int kWideShape32 = 6;
 
 bool gemm32_preferred(const GemmDesc *d, int count) {
     int64_t tiles = 0;
@@ -512,7 +516,11 @@ hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStrea
         if (d[i].K % kBlk != 0 || (d[i].y != nullptr) != y || d[i].io != d[0].io)
             return hipErrorInvalidValue;
     int v = shape;
-    if (v <= 0 || v > kNumShapes32) v = kAutoShape32;
+    if (v <= 0 || v > kNumShapes32) {
+        int64_t wide = 0;
+        for (int i = 0; i < count; ++i) wide += ((d[i].M + 127) / 128) * ((d[i].N + 255) / 256);
+        v = wide >= 512 ? kWideShape32 : kAutoShape32;
+    }
     // Two blocks per step need an even block count in every row.
     if (kShapes32[v - 1].KB == 2)
         for (int i = 0; i < count; ++i)

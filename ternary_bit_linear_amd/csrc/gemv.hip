@@ -49,6 +49,7 @@ constexpr int kTileRows = 8;    // weight rows per tile
 constexpr int kStep = 128;      // packed bytes of a row per step (512 k)
 
 struct LdsRowSink {
+    static constexpr bool kDeferSum = false;
     int8_t *q;
     float *inv;
     int *qsum;

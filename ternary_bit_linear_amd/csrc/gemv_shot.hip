@@ -71,29 +71,28 @@ struct ShotBatch {
 };
 static_assert(alignof(ShotBatch) == 8, "the batch follows eight ints in the argument segment");
 
-// q / inv / qsum of one token row into LDS and, for the problem's first
+// q and inv of one token row into LDS and, for the problem's first
 // workgroup (gq non-null), also into global memory -- straight from
 // registers, so that no LDS read of them has to wait for the weight loads
-// in flight.
+// in flight.  The activation sum is left as four per-wave partials in LDS
+// (qpart): the epilogue adds them after the barrier that publishes q, so its
+// block reduction is not on the path to the first MFMA.
 struct ShotRowSink {
+    static constexpr bool kDeferSum = true;
     int8_t *q;
     float *inv;
-    int *qsum;
+    int *qpart;  // [4]
     int8_t *gq;
     float *ginv;
-    int32_t *gqsum;
     __device__ void store_q(int k, uint32_t v) {
         *reinterpret_cast<uint32_t *>(q + k) = v;
         if (gq) *reinterpret_cast<uint32_t *>(gq + k) = v;
     }
-    __device__ void store_row(float iv, int qs) {
+    __device__ void store_inv(float iv) {
         *inv = iv;
-        *qsum = qs;
-        if (gq) {
-            *ginv = iv;
-            *gqsum = qs;
-        }
+        if (gq) *ginv = iv;
     }
+    __device__ void store_qsum_part(int w, int qs) { qpart[w] = qs; }
 };
 
 // Sum over the four fields of per-field accumulators of scaled codes
@@ -140,7 +139,7 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
         w6[NB > 6 ? W : 1][NB > 6 ? SZ : 16], w7[NB > 7 ? W : 1][NB > 7 ? SZ : 16];
     __shared__ float red[kRedWords];
     __shared__ float inv_sh[FM > 0 ? FM : 1];
-    __shared__ int qsum_sh[FM > 0 ? FM : 1];
+    __shared__ int qpart_sh[FM > 0 ? FM : 1][4];  // per-wave partial sums of q
 
     // The batch is read in place from the kernel-argument segment (constant
     // memory, wave-uniform addresses, so scalar loads): every field of this
@@ -238,8 +237,8 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
         //    while the weights stream in.
         if (W == 4 || wid < 4) {
             {
-                ShotRowSink sink{q_lds, inv_sh, qsum_sh, st == 0 ? P.q_out : nullptr, P.inv_out,
-                                 P.qsum_out};
+                ShotRowSink sink{q_lds, inv_sh, qpart_sh[0], st == 0 ? P.q_out : nullptr,
+                                 P.inv_out};
                 block_act_quant_row<CH, LONG, false, GLU, IO>(reinterpret_cast<const IO *>(P.x),
                                                               P.gamma, P.eps, K, red, sink,
                                                               issue_weights, P.u);
@@ -247,9 +246,8 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
 #pragma unroll
             for (int m = 1; m < FM; ++m) {
                 if (m < M) {
-                    ShotRowSink sink{q_lds + m * K, inv_sh + m, qsum_sh + m,
-                                     st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m,
-                                     P.qsum_out + m};
+                    ShotRowSink sink{q_lds + m * K, inv_sh + m, qpart_sh[m],
+                                     st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m};
                     block_act_quant_row<CH, LONG, false, GLU, IO>(
                         reinterpret_cast<const IO *>(P.x) + (size_t)m * K, P.gamma, P.eps, K,
                         red, sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr);
@@ -261,9 +259,14 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
             issue_weights();
 #pragma unroll
             for (int m = 0; m < FM; ++m)
-                if (m < M) block_act_quant_row_barriers(P.gamma != nullptr);
+                if (m < M) block_act_quant_row_barriers(P.gamma != nullptr, true);
         }
         lds_barrier();
+        // The problem's first workgroup also stores the rows' activation
+        // sums (the partials are visible after the barrier).
+        if (st == 0 && tid < M && tid < FM)
+            P.qsum_out[tid] = (qpart_sh[tid][0] + qpart_sh[tid][1]) +
+                              (qpart_sh[tid][2] + qpart_sh[tid][3]);
     }
 
     // 4. Contract each batch as it lands.  The activation fragments of the
@@ -324,7 +327,10 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
         for (int c = 0; c < 4; ++c) {
             const int m = 4 * (l >> 4) + c;
             if (m < M) {
-                const int qs = FM > 0 ? qsum_sh[m < FM ? m : 0] : qs_pre[c];
+                const int mm = m < FM ? m : 0;
+                const int qs = FM > 0 ? (qpart_sh[mm][0] + qpart_sh[mm][1]) +
+                                            (qpart_sh[mm][2] + qpart_sh[mm][3])
+                                      : qs_pre[c];
                 const int v = t[c] - qs;
                 if (OUT_Y) {
                     const float iv = FM > 0 ? inv_sh[m < FM ? m : 0] : iv_pre[c];
