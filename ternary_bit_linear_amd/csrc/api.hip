@@ -127,17 +127,7 @@ bl_status validate_forward(const bl_forward_desc &d, const bl_launch *launch) {
     return check_grid(d.M, launch);
 }
 
-// Whether a validated forward takes the fused decode kernel.  Automatic
-// choice: fused for one token with K <= 8192 (the whole row of x and gamma
-// fits in registers, one round trip); otherwise the separate quantisation
-// kernel is faster (measured on MI355X).
-bool takes_fused(const bl_forward_desc &d, const bl_launch *launch) {
-    const bool gemv = route_of(d.M, launch) == BL_PATH_GEMV;
-    const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
-    if (launch && launch->fuse == 0) return false;
-    if (launch && launch->fuse == 1) return gemv && fits;
-    return gemv && fits && d.M == 1 && d.K <= 8 * 1024;
-}
+constexpr int kFusedPerLaunch = 8;
 
 bl::FusedDecode fused_of(const bl_forward_desc &d) {
     const Workspace ws = carve(d.workspace, d.M, d.K);
@@ -156,6 +146,20 @@ bl::FusedDecode fused_of(const bl_forward_desc &d) {
     f.N = d.N;
     return f;
 }
+
+// Whether a validated forward takes the fused decode kernel.  Automatic
+// choice: fused for one token (rows up to 32768: the one-shot kernel holds
+// rows up to 8192 in the registers of its 256-thread quantisation, the
+// rolling kernel rows up to 32768 in those of its 1024 threads); for more
+// tokens the separate quantisation kernel is faster (measured on MI355X).
+bool takes_fused(const bl_forward_desc &d, const bl_launch *launch) {
+    const bool gemv = route_of(d.M, launch) == BL_PATH_GEMV;
+    const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
+    if (launch && launch->fuse == 0) return false;
+    if (launch && launch->fuse == 1) return gemv && fits;
+    return gemv && fits && d.M == 1 && (d.K <= 8 * 1024 || bl::roll_fused_supported(d.M, d.K));
+}
+
 
 // Whether a validated forward that does not take the fused kernel can join
 // a grouped prefill launch (one batched quantisation launch, one grouped
@@ -217,7 +221,6 @@ FfnWorkspace carve_ffn(void *ws, int64_t M, int64_t H, int64_t F) {
 }
 
 constexpr int kMaxBatchDescs = 64;
-constexpr int kFusedPerLaunch = 8;
 constexpr int kGroupPerLaunch = 8;
 constexpr int kShotPerLaunch = 8;
 
@@ -672,7 +675,7 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
             {wq.q, wq.inv, wq.qsum, d.packed_gate, w.g, nullptr, d.s_gate, M, H, F},
             {wq.q, wq.inv, wq.qsum, d.packed_up, w.u, nullptr, d.s_up, M, H, F}};
         if (bl::launch_act_quant_batch(&aq, 1, s) != hipSuccess ||
-            bl::launch_gemv_shot(sd, 2, 0, s) != hipSuccess)
+            bl::launch_gemv_shot_auto(sd, 2, s) != hipSuccess)
             return BL_ERR_HIP;
     } else if (!takes_fused(gu[0], nullptr) && takes_group(gu[0], nullptr)) {
         // Prefill: x is quantised once (into the gate's workspace) and both
@@ -692,7 +695,7 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
     const Workspace wd = carve(w.ws_down, M, F);
     const int64_t Ms[1] = {M}, Ks[1] = {F}, Ns[1] = {H};
     if (M == 1 && F <= 8 * 1024 && bl::shot_fused_supported(M, F) &&
-        bl::shot_rounds(Ms, Ks, Ns, 1, true) == 1) {
+        bl::shot_rounds(Ms, Ks, Ns, 1, true, true) == 1) {
         bl::FusedDecode f;
         f.x = w.g;
         f.gamma = d.gamma_sub;
@@ -727,7 +730,7 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
         // the one-shot kernel, as a batch of a few tokens takes it
         const bl::ShotDecode sd{wd.q, wd.inv, wd.qsum, d.packed_down, d.y, nullptr, d.s_down,
                                 M,    F,      H};
-        return hip_status(bl::launch_gemv_shot(&sd, 1, 0, s));
+        return hip_status(bl::launch_gemv_shot_auto(&sd, 1, s));
     }
     return run_contraction(wd.q, wd.inv, wd.qsum, d.packed_down, d.s_down, M, F, H, d.y, nullptr,
                            nullptr, s);
@@ -758,18 +761,21 @@ bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
     auto flush_shot = [&]() -> bl_status {
         if (ns == 0) return BL_OK;
         if (bl::launch_act_quant_batch(sq, ns, s) != hipSuccess) return BL_ERR_HIP;
-        if (bl::launch_gemv_shot(sd, ns, 0, s) != hipSuccess) return BL_ERR_HIP;
+        if (bl::launch_gemv_shot_auto(sd, ns, s) != hipSuccess) return BL_ERR_HIP;
         ns = 0;
+        return BL_OK;
+    };
+    auto flush_fused = [&]() -> bl_status {
+        if (n > 0 && bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
+        n = 0;
         return BL_OK;
     };
     for (int i = 0; i < count; ++i) {
         const bl_forward_desc &d = descs[i];
         if (takes_fused(d, launch)) {
             group[n++] = fused_of(d);
-            if (n == kFusedPerLaunch) {
-                if (bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
-                n = 0;
-            }
+            if (n == kFusedPerLaunch)
+                if (bl_status st = flush_fused()) return st;
         } else if (takes_shot_batch(d, launch)) {
             const Workspace ws = carve(d.workspace, d.M, d.K);
             sq[ns] = bl::ActQuantDesc{d.x, d.gamma, d.eps, d.M, d.K, ws.q, ws.inv, ws.qsum};
@@ -788,7 +794,7 @@ bl_status bitlinear_forward_batch(const bl_forward_desc *descs, int count,
             return st;
         }
     }
-    if (n > 0 && bl::launch_gemv_fused(group, n, variant, s) != hipSuccess) return BL_ERR_HIP;
+    if (bl_status st = flush_fused()) return st;
     if (bl_status st = flush_shot()) return st;
     return flush_group();
 }

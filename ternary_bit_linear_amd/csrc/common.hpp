@@ -804,10 +804,13 @@ struct ShotDecode {
 // shape: 1..shot_num_shapes() asks for that launch shape (taken when every
 // problem fits it), 0 picks one.
 int shot_num_shapes();
+constexpr int kShotShapeCount = 8;  // shot_num_shapes()
 // Rounds of workgroups the device needs for these problems in the one-shot
 // form with its own choice of launch shape (INT64_MAX: not supported).  One
-// round means every workgroup is resident at once.
-int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count, bool fused);
+// round means every workgroup is resident at once.  glu: fused, over the
+// gated FFN input (u set).
+int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count, bool fused,
+                    bool glu = false);
 bool shot_supported(int64_t M, int64_t K);
 hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream_t s);
 // The same with the RMSNorm + quantisation fused in (M <= kFuseMaxM): every
@@ -815,6 +818,18 @@ hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream
 // flight; the first workgroup of each problem also writes q / inv / qsum.
 bool shot_fused_supported(int64_t M, int64_t K);
 hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hipStream_t s);
+// Rolling form of the one-shot contraction (each wave streams its weights
+// through a small register ring), for problem sets the device does not hold
+// in one round: q from global memory (M <= 8, M * K <= kShotMaxQ), or fused
+// for one token per problem (fp32 x / y, no gated input).
+bool roll_supported(int64_t M, int64_t K);
+hipError_t launch_gemv_roll(const ShotDecode *d, int count, hipStream_t s);
+bool roll_fused_supported(int64_t M, int64_t K);
+hipError_t launch_gemv_roll_fused(const FusedDecode *d, int count, hipStream_t s);
+// One-shot launch of up to 8 problems with q from global memory where all
+// of its workgroups are resident at once, else the rolling form where it
+// applies (measured faster), else the one-shot form over several rounds.
+hipError_t launch_gemv_shot_auto(const ShotDecode *d, int count, hipStream_t s);
 int gemv_num_variants();
 
 // Prefill route (activation tiles staged in LDS, int8 MFMA).  Same

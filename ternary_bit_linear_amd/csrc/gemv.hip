@@ -826,8 +826,10 @@ hipError_t launch_shape_fused(const FusedDecode *d, int count, hipStream_t s) {
 // shape; kNumShapes + 1: the one-shot form (gemv_shot.hip) where it applies,
 // launch shape picked from the problems; kNumShapes + 1 + j: the one-shot
 // form with its launch shape j (taken when every problem fits it).
-constexpr int kShotVariants = 9;
-int gemv_num_variants() { return kNumShapes + kShotVariants; }
+constexpr int kShotVariants = kShotShapeCount + 1;
+// Last variant: the rolling form of the one-shot kernel (where it applies).
+constexpr int kRollVariant = kNumShapes + kShotVariants + 1;
+int gemv_num_variants() { return kRollVariant; }
 
 static int shot_shape_of(int variant) { return variant - kNumShapes - 1; }
 static bool is_shot(int variant) {
@@ -859,18 +861,22 @@ hipError_t launch_gemv(const int8_t *q, const float *inv, const int32_t *qsum,
                        float *y, int32_t *acc, int variant, hipStream_t s) {
     const int64_t mg = M < 16 ? M : 16;
     const int mode = mg * K <= kGemvStageMaxLds ? 1 : 2;
-    // Automatic: the one-shot form for rows up to 16384, also when its
-    // workgroups take several rounds of the device (measured faster than the
-    // persistent form there, by up to 1.4x at N = 28672); the persistent
-    // form for longer rows (faster at K = 28672).
-    const bool shot = is_shot(variant) ? shot_supported(M, K)
-                                       : variant == 0 && shot_supported(M, K) && K <= 16384 &&
-                                             M * K <= kShotSingleMaxQ &&
-                                             shot_rounds(&M, &K, &N, 1, false) != INT64_MAX;
-    if (shot) {
-        const ShotDecode d{q, inv, qsum, packed, y, acc, w_scale, M, K, N};
-        return launch_gemv_shot(&d, 1, is_shot(variant) ? shot_shape_of(variant) : 0, s);
+    const ShotDecode d{q, inv, qsum, packed, y, acc, w_scale, M, K, N};
+    if (variant == kRollVariant && roll_supported(M, K)) return launch_gemv_roll(&d, 1, s);
+    if (variant == kRollVariant) variant = 0;
+    // Automatic: the one-shot form where all of its workgroups are resident
+    // at once, else the rolling form (measured faster than the one-shot form
+    // over several rounds and than the persistent form: M = 1..8 at the 70B
+    // FFN shapes, 1.1-1.5x), else the one-shot form for rows up to 16384
+    // and the persistent form beyond.
+    if (variant == 0) {
+        const bool shot = M * K <= kShotSingleMaxQ && K <= 16384 && shot_supported(M, K);
+        if (shot && shot_rounds(&M, &K, &N, 1, false) == 1) variant = kNumShapes + 1;
+        else if (roll_supported(M, K)) return launch_gemv_roll(&d, 1, s);
+        else if (shot) variant = kNumShapes + 1;
     }
+    if (is_shot(variant) && shot_supported(M, K))
+        return launch_gemv_shot(&d, 1, shot_shape_of(variant), s);
     const int v = variant > 0 && variant <= kNumShapes ? variant : auto_variant(M);
 #define BL_SEP(R_, U_, D_) \
     launch_shape_sep<R_, U_, D_>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, mode, s)
@@ -881,6 +887,14 @@ hipError_t launch_gemv(const int8_t *q, const float *inv, const int32_t *qsum,
 hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipStream_t s) {
     bool fits = true;
     int64_t M[8], K[8], N[8];
+    const bool glu = count > 0 && d[0].u != nullptr;
+    if (variant == kRollVariant) {
+        bool roll = count <= 8;
+        for (int i = 0; i < count; ++i)
+            roll = roll && roll_fused_supported(d[i].M, d[i].K) && !d[i].u && d[i].io == kIoF32;
+        if (roll) return launch_gemv_roll_fused(d, count, s);
+        variant = 0;
+    }
     for (int i = 0; i < count; ++i) {
         fits = fits && shot_fused_supported(d[i].M, d[i].K);
         if (i < 8) {
@@ -890,9 +904,21 @@ hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipSt
         }
     }
     // Automatic: the one-shot form when all of its workgroups fit on the
-    // device at once, else the persistent form.
-    const bool shot = fits && count <= 8 &&
-                      (is_shot(variant) || (variant == 0 && shot_rounds(M, K, N, count, true) == 1));
+    // device at once and every row is held in registers by the block form
+    // (K <= 8192); else, one token per problem, the rolling form (its
+    // 1024-thread quantisation holds rows up to 32768: faster than the
+    // one-shot form for longer rows and than the persistent form, measured
+    // on the 70B FFN shapes); else the one-shot form when it fits, else the
+    // persistent form.
+    bool roll = variant == 0 && count <= 8 && !glu;
+    int64_t kmax = 0;
+    for (int i = 0; i < count && i < 8; ++i) {
+        roll = roll && roll_fused_supported(d[i].M, d[i].K) && d[i].io == kIoF32;
+        kmax = std::max<int64_t>(kmax, d[i].K);
+    }
+    const bool fits_one = fits && count <= 8 && shot_rounds(M, K, N, count, true, glu) == 1;
+    if (variant == 0 && roll && !(fits_one && kmax <= 8192)) return launch_gemv_roll_fused(d, count, s);
+    const bool shot = fits && count <= 8 && (is_shot(variant) || (variant == 0 && fits_one));
     if (shot)
         return launch_gemv_shot_fused(d, count, is_shot(variant) ? shot_shape_of(variant) : 0, s);
     // The persistent form reads and writes fp32 activations only.
@@ -906,5 +932,18 @@ hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipSt
 }
 
 #undef BL_GEMV_SWITCH
+
+hipError_t launch_gemv_shot_auto(const ShotDecode *d, int count, hipStream_t s) {
+    int64_t M[8], K[8], N[8];
+    bool roll = count >= 1 && count <= 8;
+    for (int i = 0; i < count && i < 8; ++i) {
+        M[i] = d[i].M;
+        K[i] = d[i].K;
+        N[i] = d[i].N;
+        roll = roll && roll_supported(d[i].M, d[i].K) && d[i].io == kIoF32;
+    }
+    if (roll && shot_rounds(M, K, N, count, false) != 1) return launch_gemv_roll(d, count, s);
+    return launch_gemv_shot(d, count, 0, s);
+}
 
 }  // namespace bl

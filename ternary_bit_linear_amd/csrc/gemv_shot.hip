@@ -62,7 +62,7 @@ struct ShotProblem {
     float w_scale;
     int M, K, N;
     int wg_begin;          // first workgroup of this problem
-    int ks_log;            // log2 of the K split: 0, 1 or 2
+    int ks_log;            // log2 of the K split: 0..2 (one-shot), 0..4 (rolling)
     const float *u;        // GLU: up rows (the input row is relu2_mul(x, u))
 };
 constexpr int kMaxShotBatch = 8;
@@ -117,7 +117,12 @@ __device__ __forceinline__ v4i field_sum(const v4i (&a)[4]) {
 // W: waves per workgroup, 4, 8 or 16.  The quantisation is the 256-thread
 // block form; in a larger workgroup waves 4..W-1 issue their weights and
 // meet its barriers, so a CU that holds one such workgroup normalises x once
-// where several 4-wave workgroups would each do it.
+// where several 4-wave workgroups would each do it.  In such a workgroup
+// waves 0..3 issue their weights after the quantisation: a wave that issues
+// many loads stalls at the issue until the memory pipeline takes them, and
+// the quantisation's barriers would make every wave wait for it (measured:
+// the decoder layer's codes are ready 0.6 us earlier, the launch 0.35 us
+// shorter).
 template <int NB, int R, bool OUT_Y, int FM, int CH, bool LONG, bool GLU = false,
           typename IO = float, int W = 4>
 __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b2, int b3, int b4,
@@ -222,10 +227,16 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
     if constexpr (FM == 0) {
         // 1. The activation block (M rows of K int8, contiguous), 1 KB per
         //    wave load, loads spread over the waves; 2. the weights.
+        //    The barrier between them puts every activation load of the
+        //    workgroup ahead of its weight loads in the compute unit's
+        //    memory pipeline (requests leave it in order): issued
+        //    interleaved, the activations would arrive only after the
+        //    weights queued before them.
         const uint32_t qbytes = (uint32_t)(M * K);
         const auto rq = make_rsrc(P.q, qbytes);
         for (uint32_t c = (uint32_t)wid * 1024u; c < qbytes; c += W * 1024u)
             buf_load16_lds(rq, q_lds + c, c + 16u * lane, 0);
+        __builtin_amdgcn_s_barrier();
         issue_weights();
         // 3. Own activation loads done (only weight loads may still be in
         //    flight), then every wave's: the block is complete in LDS.
@@ -233,15 +244,24 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
         lds_barrier();
     } else {
         // 1. x and gamma of the first row go out first, the weights right
-        //    behind them; 2. RMSNorm + quantisation of every row into LDS
-        //    while the weights stream in.
+        //    behind them: a barrier after the x / gamma loads (rows held in
+        //    registers) puts them ahead of every weight load of the
+        //    workgroup in the memory pipeline, so they return at their own
+        //    latency instead of after the weights queued before them;
+        // 2. RMSNorm + quantisation of every row into LDS while the weights
+        //    stream in.
+        constexpr bool kLate = W > 4;  // waves 0..3: weights after the quantisation
+        constexpr bool kSync = !LONG;
         if (W == 4 || wid < 4) {
             {
                 ShotRowSink sink{q_lds, inv_sh, qpart_sh[0], st == 0 ? P.q_out : nullptr,
                                  P.inv_out};
-                block_act_quant_row<CH, LONG, false, GLU, IO>(reinterpret_cast<const IO *>(P.x),
-                                                              P.gamma, P.eps, K, red, sink,
-                                                              issue_weights, P.u);
+                auto hook = [&] {
+                    if constexpr (!kLate) issue_weights();
+                };
+                block_act_quant_row<CH, LONG, kSync, GLU, IO>(reinterpret_cast<const IO *>(P.x),
+                                                              P.gamma, P.eps, K, red, sink, hook,
+                                                              P.u);
             }
 #pragma unroll
             for (int m = 1; m < FM; ++m) {
@@ -253,9 +273,12 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
                         red, sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr);
                 }
             }
+            if constexpr (kLate) issue_weights();
         } else {
-            // Waves 4..W-1: their weights, then the barriers of each row's
-            // block form.
+            // Waves 4..W-1: the barrier behind the first row's x / gamma
+            // loads, their weights, then the barriers of each row's block
+            // form.
+            if constexpr (kSync) __builtin_amdgcn_s_barrier();
             issue_weights();
 #pragma unroll
             for (int m = 0; m < FM; ++m)
@@ -375,6 +398,317 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
     }
 }
 
+// RMSNorm + int8 quantisation of one token row by a 1024-thread workgroup
+// with the whole row in registers (rows of up to 4096 * SQ elements), the
+// same arithmetic in the same order as the 256-thread block form: O256
+// chain t (float4 groups k = 4t + 1024 i) is held by four threads, thread
+// 256 h + t holding the groups i in [h SQ, (h + 1) SQ); the chain's sum of
+// squares is carried from segment to segment through LDS (one barrier
+// each), so every chain is the same sequence of fused multiply-adds, and
+// the chain totals are added by the block form's tree.  The maximum and the
+// code sum are order-free.  Every wave loads its part of x and gamma at the
+// start -- one round trip for the whole row -- then runs `issued()` after a
+// barrier, so the loads the caller issues there queue behind all of them.
+// q goes to q (LDS) and, when gq is set, to global memory; inv to *inv (and
+// *ginv); the per-wave code sums to qpart[16].
+template <int SQ, class Hook>
+__device__ __forceinline__ void wide_act_quant_row(const float *__restrict__ x,
+                                                   const float *__restrict__ gamma, float eps,
+                                                   int K, float *red, float *chain, int8_t *q,
+                                                   int8_t *gq, float *inv, float *ginv, int *qpart,
+                                                   Hook &&issued) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int h = __builtin_amdgcn_readfirstlane(wid >> 2);  // segment of the chain
+    const int t = tid & 255;                                  // chain
+    const int ni = (K + 1023) / 1024;                         // float4 groups per chain
+    const bool norm = gamma != nullptr;
+    const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+    const auto rg = gamma_rsrc(gamma, K);
+    float4 xv[SQ], gv[SQ];
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        const int gi = h * SQ + i;
+        if (gi < ni) {  // wave-uniform; lanes past K read zeros
+            const uint32_t off = 4u * (uint32_t)(4 * t + 1024 * gi);
+            xv[i] = load_x4<float>(rx, off);
+            gv[i] = gamma_f4(rg, off, norm);
+        } else {
+            xv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            gv[i] = xv[i];
+        }
+    }
+    __builtin_amdgcn_s_barrier();
+    issued();
+    float r = 1.0f;
+    if (norm) {
+        float p = 0.0f;
+        for (int s = 0; s < 4; ++s) {
+            if (h == s) {
+                if (s > 0) p = chain[t];
+#pragma unroll
+                for (int i = 0; i < SQ; ++i) {
+                    if (h * SQ + i < ni) {
+                        p = __builtin_fmaf(xv[i].x, xv[i].x, p);
+                        p = __builtin_fmaf(xv[i].y, xv[i].y, p);
+                        p = __builtin_fmaf(xv[i].z, xv[i].z, p);
+                        p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+                    }
+                }
+                if (s < 3) chain[t] = p;
+            }
+            if (s < 3) lds_barrier();
+        }
+        // Segment 3 holds the chain totals: waves 12..15 are the block
+        // form's four waves.
+        if (h == 3) {
+            p = wave_tree_sum_f(p);
+            if (lane == 0) red[wid - 12] = p;
+        }
+        lds_barrier();
+        r = rms_scale((red[0] + red[1]) + (red[2] + red[3]), K, eps);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        xv[i] = xn4(xv[i], gv[i], r);
+        amax = amax4(amax, xv[i]);
+    }
+    amax = wave_max(amax);
+    if (lane == 0) red[4 + wid] = amax;
+    lds_barrier();
+    float m = red[4];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) m = fmaxf(m, red[4 + w]);
+    const float iv = quant_scale(m);
+    int qs = 0;
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        const int k = 4 * t + 1024 * (h * SQ + i);
+        if (k < K) {
+            const float4 v = xv[i];
+            const uint32_t w = pack_char4(quant_one(v.x, iv), quant_one(v.y, iv),
+                                          quant_one(v.z, iv), quant_one(v.w, iv));
+            qs = sum_char4(w, qs);
+            *reinterpret_cast<uint32_t *>(q + k) = w;
+            if (gq) *reinterpret_cast<uint32_t *>(gq + k) = w;
+        }
+    }
+    qs = wave_sum_int(qs);
+    if (lane == 0) qpart[wid] = qs;
+    if (tid == 0) {
+        *inv = iv;
+        if (gq) *ginv = iv;
+    }
+}
+
+// Rolling form of the same contraction, for problem sets larger than the
+// device holds at once (the 70B FFN matrices at one token).  The one-shot
+// kernel issues all of a wave's loads up front; once the compute unit's
+// memory pipeline is full, a wave stalls at the issue of its remaining loads
+// and cannot contract what has arrived, and the quantisation's barriers make
+// every wave of the workgroup wait for the slowest issuer -- so the
+// contraction only starts near the end of the stream.  Here each wave keeps
+// a ring of ND batches in registers: it issues ND batches before the
+// quantisation, then contracts batch b and issues batch b + ND into its
+// slot, so no issue waits long and the contraction keeps pace with the
+// stream.  A wave covers its tile group's K share (ks waves per tile group)
+// in any number of batches; the batch count is padded to a multiple of ND
+// with range-checked loads that read nothing, so the loop body is the same
+// every time and the compiler's load counts stay exact.  Launch: one
+// workgroup per tile-group set, W = 16 waves (one per CU by registers).
+template <int ND, int R, bool OUT_Y, int FM, int SQ, typename IO = float, int W = 16>
+__global__ __launch_bounds__(64 * W) void gemv_roll_kernel(int b0, int b1, int b2, int b3, int b4,
+                                                        int b5, int b6, int b7, ShotBatch B) {
+    static_assert(ND >= 1 && ND <= 4, "ring depth");
+    static_assert(R == 1 || R == 2, "tiles per wave");
+    static_assert(W == 4 || W == 8 || W == 16, "waves per workgroup");
+    static_assert(kU == 2, "shift forms below assume kU == 2");
+    static_assert(FM == 0 || (FM == 1 && W == 16), "fused: one token, 16 waves");
+    static_assert(SQ == 1 || SQ == 2 || SQ == 4 || SQ == 8, "row segment");
+    constexpr int LW = W == 16 ? 4 : W == 8 ? 3 : 2;
+    extern __shared__ __align__(16) int8_t q_lds[];
+    __shared__ float red[20];
+    __shared__ float chain_sh[FM > 0 ? 256 : 1];
+    __shared__ float inv_sh[1];
+    __shared__ int qpart_sh[16];
+    __shared__ __align__(16) v4i part[W][R * 64];  // partial tiles when ks > 1
+
+    (void)b0;
+    const int bx = (int)blockIdx.x;
+    const int pi = (bx >= b1) + (bx >= b2) + (bx >= b3) + (bx >= b4) + (bx >= b5) + (bx >= b6) +
+                   (bx >= b7);
+    const ShotBatch *Bk = reinterpret_cast<const ShotBatch *>(
+        (const char *)__builtin_amdgcn_kernarg_segment_ptr() + 8 * sizeof(int));
+    const ShotProblem P = Bk->p[pi];
+    asm volatile("" ::"s"(P.q), "s"(P.inv), "s"(P.qsum), "s"(P.x), "s"(P.gamma), "s"(P.q_out),
+                 "s"(P.inv_out), "s"(P.qsum_out), "s"(P.packed), "s"(P.y), "s"(P.acc), "s"(P.eps),
+                 "s"(P.w_scale), "s"(P.M), "s"(P.K), "s"(P.N), "s"(P.wg_begin), "s"(P.ks_log));
+    const int M = P.M, K = P.K, N = P.N;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r8 = lane & 7;
+    const int ch = lane >> 3;
+    const uint32_t rowbytes = (uint32_t)K / 4;
+    const int nsteps = (int)((rowbytes + kStep - 1) / kStep);
+    const int kl = P.ks_log;
+    const int ks = 1 << kl;
+    const int sg = wid >> kl, kp = wid & (ks - 1);
+    const int nb = (nsteps + ks * kU - 1) >> (kl + 1);
+    const int nbp = (nb + ND - 1) / ND * ND;  // padded to whole rounds of the ring
+    const int st = bx - P.wg_begin;
+    const int tg = (st << (LW - kl)) + sg;
+    const int n0 = tg * kTileRows * R;
+    const int rows = max(0, min(kTileRows * R, N - n0));
+    const auto rw = make_rsrc(P.packed + (size_t)min(n0, N) * rowbytes, (uint32_t)rows * rowbytes);
+
+    // Batch b of this wave into a ring slot (past the wave's batches:
+    // range-checked to read nothing).
+    v4i ring[ND][R][kU];
+    auto issue = [&](v4i(&slot)[R][kU], int b) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int s = b * ks * kU + kp * kU + u;
+                const uint32_t cb = (uint32_t)s * kStep + 16u * ch;
+                const bool kv = b < nb && s < nsteps && cb < rowbytes;
+                slot[r][u] = buf_load16(rw, kv ? (uint32_t)(r * kTileRows + r8) * rowbytes + cb : kOOB);
+            }
+        }
+    };
+    auto prologue = [&] {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < ND; ++j) issue(ring[j], j);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    int qs_pre[4];
+    float iv_pre[4];
+    if constexpr (FM == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = min(4 * (lane >> 4) + c, M - 1);
+            qs_pre[c] = P.qsum[m];
+            iv_pre[c] = OUT_Y ? P.inv[m] : 1.0f;
+        }
+        // The activation block goes ahead of every weight load of the
+        // workgroup (barrier), the ring's first batches behind it.
+        const uint32_t qbytes = (uint32_t)(M * K);
+        const auto rq = make_rsrc(P.q, qbytes);
+        for (uint32_t c = (uint32_t)wid * 1024u; c < qbytes; c += W * 1024u)
+            buf_load16_lds(rq, q_lds + c, c + 16u * lane, 0);
+        __builtin_amdgcn_s_barrier();
+        prologue();
+        wait_vmcnt<ND * R * kU>();
+        lds_barrier();
+    } else {
+        // The whole row of x and gamma over all 16 waves (one round trip,
+        // ahead of every weight load of the workgroup), then the ring's
+        // first batches; the quantisation runs while they stream in.
+        wide_act_quant_row<SQ>(P.x, P.gamma, P.eps, K, red, chain_sh, q_lds,
+                               st == 0 ? P.q_out : nullptr, inv_sh, P.inv_out, qpart_sh,
+                               prologue);
+        lds_barrier();
+        if (st == 0 && tid == 0) {
+            int t = 0;
+            for (int w = 0; w < 16; ++w) t += qpart_sh[w];
+            P.qsum_out[0] = t;
+        }
+    }
+
+    // Contraction: batch b from ring slot b % ND, then batch b + ND into it.
+    const int qrow = min(r8, M - 1) * K;
+    v4i acc[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[r][g] = v4i{0, 0, 0, 0};
+    for (int bb = 0; bb < nbp; bb += ND) {
+#pragma unroll
+        for (int j = 0; j < ND; ++j) {
+            const int b = bb + j;
+            if (b < nb) {  // the padding batches hold zeros: no contraction
+                v4i aq[kU][4];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int s = b * ks * kU + kp * kU + u;
+                    const uint32_t cb = (uint32_t)s * kStep + 16u * ch;
+                    const bool kv = s < nsteps && cb < rowbytes;
+                    const int kb =
+                        kv ? (int)(cb / 32) * kBlockWeights + 16 * (int)((cb / 16) & 1) : 0;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        aq[u][g] = *reinterpret_cast<const v4i *>(q_lds + qrow + kb + 32 * g);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int u = 0; u < kU; ++u)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            acc[r][g] =
+                                mfma16(aq[u][g], unpack_scaled(ring[j][r][u], g), acc[r][g]);
+            }
+            issue(ring[j], b + ND);
+        }
+    }
+
+    // Fields, then the ks waves of each tile group (as in the one-shot form).
+    const int l = lane;
+    auto store = [&](int r, const v4i &t) {
+        const int n = n0 + r * kTileRows + (l & 7);
+        if (n >= N) return;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = 4 * (l >> 4) + c;
+            if (m < M) {
+                int qs = qs_pre[c];
+                if constexpr (FM > 0) {
+                    qs = 0;
+                    for (int w = 0; w < 16; ++w) qs += qpart_sh[w];
+                }
+                const int v = t[c] - qs;
+                if (OUT_Y) {
+                    const float iv = FM > 0 ? inv_sh[0] : iv_pre[c];
+                    store_out(reinterpret_cast<IO *>(P.y), (size_t)m * N + n,
+                              (float)v * (P.w_scale / iv));
+                } else {
+                    P.acc[(size_t)m * N + n] = v;
+                }
+            }
+        }
+    };
+    if (ks == 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const v4i s4 = field_sum(acc[r]);
+            v4i t;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                t[c] = s4[c] + __builtin_amdgcn_ds_bpermute(((l + 40) & 63) << 2, s4[c]);
+            if ((l & 8) == 0 && l < 24) store(r, t);
+        }
+        return;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[wid][r * 64 + lane] = field_sum(acc[r]);
+    lds_barrier();
+    if (kp == 0 && (l & 8) == 0 && l < 24) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int o = r * 64 + l;
+            v4i t = part[wid][o] + part[wid][o + 40];
+            for (int w = 1; w < ks; ++w) t += part[wid + w][o] + part[wid + w][o + 40];
+            store(r, t);
+        }
+    }
+}
+
 // Smallest K split (waves per tile group) that fits a wave's share of a
 // row into NB batches, or 0.
 int shot_ks(int64_t K, int nbmax) {
@@ -429,6 +763,7 @@ struct ShotShape {
 constexpr ShotShape kShotShapes[] = {{3, 1, 4, 4}, {4, 1, 4, 4}, {8, 1, 4, 4}, {3, 2, 3, 4},
                                      {4, 2, 3, 4}, {3, 4, 3, 4}, {3, 2, 1, 8}, {3, 1, 1, 16}};
 constexpr int kNumShotShapes = sizeof(kShotShapes) / sizeof(kShotShapes[0]);
+static_assert(kNumShotShapes == kShotShapeCount, "shape count the variant numbering uses");
 
 // Compute units of the current device, looked up once per device (the
 // launch-shape choice runs on every call).  Devices beyond the table are
@@ -671,11 +1006,12 @@ hipError_t launch_sep(const ShotDecode *d, int count, int v, hipStream_t s) {
 
 int shot_num_shapes() { return kNumShotShapes; }
 
-int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count, bool fused) {
+int64_t shot_rounds(const int64_t *M, const int64_t *K, const int64_t *N, int count, bool fused,
+                    bool glu) {
     for (int i = 0; i < count; ++i)
         if (!shot_supported(M[i], K[i])) return INT64_MAX;
     int64_t rounds;
-    return pick_shape(M, K, N, count, 0, &rounds, fused) < 0 ? INT64_MAX : rounds;
+    return pick_shape(M, K, N, count, 0, &rounds, fused, !glu) < 0 ? INT64_MAX : rounds;
 }
 
 bool shot_supported(int64_t M, int64_t K) {
@@ -752,5 +1088,148 @@ hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hi
 }
 
 #undef BL_SHOT_SHAPES
+
+namespace {
+
+constexpr int kRollW = 16;  // waves per workgroup of the rolling form
+constexpr int kRollND = 3;  // ring depth (batches per wave in flight)
+
+// K split of each problem for the rolling form.  Workgroups should carry
+// about the same bytes (a workgroup's rows are 16 / ks tile groups of K / 4
+// bytes each): each problem first splits until its workgroups carry at most
+// 1.5 times those of the shortest rows' (rows of 28672 beside rows of 8192
+// take 4 waves per tile group).  Then, while the launch has fewer
+// workgroups than about the compute units, the problem whose workgroups
+// carry the most bytes splits further -- up to all 16 waves on one tile
+// group, each keeping at least two 128-byte steps of the row.  Fills ks_log,
+// wg_begin and M/K/N; returns the grid.
+int64_t fill_roll(ShotBatch &B, int *begin, int count, const int64_t *M, const int64_t *K,
+                  const int64_t *N, int64_t *qmax) {
+    const int cus = device_cus();
+    int ks[kMaxShotBatch];
+    int64_t ntg[kMaxShotBatch];
+    auto wgs_of = [&](int i) { return (ntg[i] + kRollW / ks[i] - 1) / (kRollW / ks[i]); };
+    auto per_wg = [&](int i) { return (double)(kRollW / ks[i]) * kTileRows * (double)(K[i] / 4); };
+    auto can_split = [&](int i) {
+        return ks[i] < kRollW && (K[i] / 4 + kStep - 1) / kStep >= 4 * ks[i];
+    };
+    int64_t kmin = INT64_MAX;
+    *qmax = 0;
+    for (int i = 0; i < count; ++i) {
+        ks[i] = 1;
+        ntg[i] = (N[i] + kTileRows - 1) / kTileRows;
+        kmin = std::min(kmin, K[i]);
+        *qmax = std::max<int64_t>(*qmax, M[i] * K[i]);
+    }
+    const double floor_bytes = (double)kRollW * kTileRows * (double)(kmin / 4);
+    int64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        while (can_split(i) && per_wg(i) > 1.5 * floor_bytes) ks[i] *= 2;
+        total += wgs_of(i);
+    }
+    while (total * 8 < (int64_t)cus * 7) {
+        int best = -1;
+        for (int i = 0; i < count; ++i)
+            if (can_split(i) && (best < 0 || per_wg(i) > per_wg(best))) best = i;
+        if (best < 0) break;
+        total -= wgs_of(best);
+        ks[best] *= 2;
+        total += wgs_of(best);
+    }
+    int64_t gx = 0;
+    for (int i = 0; i < count; ++i) {
+        ShotProblem &P = B.p[i];
+        P.M = (int)M[i];
+        P.K = (int)K[i];
+        P.N = (int)N[i];
+        P.ks_log = ks[i] == 1 ? 0 : ks[i] == 2 ? 1 : ks[i] == 4 ? 2 : ks[i] == 8 ? 3 : 4;
+        P.wg_begin = (int)gx;
+        begin[i] = (int)gx;
+        gx += wgs_of(i);
+    }
+    for (int i = count; i < kMaxShotBatch; ++i) begin[i] = INT_MAX;
+    return gx;
+}
+
+template <bool OUT_Y>
+hipError_t launch_roll_sep(const ShotDecode *d, int count, hipStream_t s) {
+    ShotBatch B{};
+    int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
+    for (int i = 0; i < count; ++i) {
+        M[i] = d[i].M;
+        K[i] = d[i].K;
+        N[i] = d[i].N;
+        ShotProblem &P = B.p[i];
+        P.q = d[i].q;
+        P.inv = d[i].inv;
+        P.qsum = d[i].qsum;
+        P.packed = d[i].packed;
+        P.y = d[i].y;
+        P.acc = d[i].acc;
+        P.w_scale = d[i].w_scale;
+    }
+    int begin[kMaxShotBatch];
+    const int64_t gx = fill_roll(B, begin, count, M, K, N, &qmax);
+    return launch_batch(gemv_roll_kernel<kRollND, 1, OUT_Y, 0, 1, float, kRollW>, kRollW, B,
+                        begin, gx, qmax, s);
+}
+
+template <int SQ>
+hipError_t launch_roll_fused(const FusedDecode *d, int count, hipStream_t s) {
+    ShotBatch B{};
+    int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
+    for (int i = 0; i < count; ++i) {
+        M[i] = d[i].M;
+        K[i] = d[i].K;
+        N[i] = d[i].N;
+        ShotProblem &P = B.p[i];
+        P.x = d[i].x;
+        P.gamma = d[i].gamma;
+        P.q_out = d[i].q;
+        P.inv_out = d[i].inv;
+        P.qsum_out = d[i].qsum;
+        P.packed = d[i].packed;
+        P.y = d[i].y;
+        P.eps = d[i].eps;
+        P.w_scale = d[i].w_scale;
+    }
+    int begin[kMaxShotBatch];
+    const int64_t gx = fill_roll(B, begin, count, M, K, N, &qmax);
+    return launch_batch(gemv_roll_kernel<kRollND, 1, true, 1, SQ, float, kRollW>, kRollW, B, begin,
+                        gx, qmax, s);
+}
+
+}  // namespace
+
+bool roll_supported(int64_t M, int64_t K) {
+    return M >= 1 && M <= kMaxShotM && M * K <= kShotMaxQ && K % kBlockWeights == 0;
+}
+
+hipError_t launch_gemv_roll(const ShotDecode *d, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
+    const bool y = d[0].y != nullptr;
+    for (int i = 0; i < count; ++i)
+        if (!roll_supported(d[i].M, d[i].K) || (d[i].y != nullptr) != y || d[i].io != kIoF32)
+            return hipErrorInvalidValue;
+    return y ? launch_roll_sep<true>(d, count, s) : launch_roll_sep<false>(d, count, s);
+}
+
+bool roll_fused_supported(int64_t M, int64_t K) {
+    return M == 1 && K <= kShotFusedMaxQ && K % kBlockWeights == 0;
+}
+
+hipError_t launch_gemv_roll_fused(const FusedDecode *d, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
+    int64_t kmax = 0;
+    for (int i = 0; i < count; ++i) {
+        if (!roll_fused_supported(d[i].M, d[i].K) || !d[i].y || d[i].u || d[i].io != kIoF32)
+            return hipErrorInvalidValue;
+        kmax = std::max<int64_t>(kmax, d[i].K);
+    }
+    if (kmax <= 4096) return launch_roll_fused<1>(d, count, s);
+    if (kmax <= 8192) return launch_roll_fused<2>(d, count, s);
+    if (kmax <= 16384) return launch_roll_fused<4>(d, count, s);
+    return launch_roll_fused<8>(d, count, s);
+}
 
 }  // namespace bl

@@ -455,6 +455,70 @@ def test_decode_every_shape_wide_workgroups(torch, bl, orc, norm):
             assert np.array_equal(host(qs), qs_r), v
 
 
+# Rolling form: one token with the 1024-thread quantisation (rows up to
+# 32768, K a multiple of 1024 or not), q from the workspace for up to 8
+# tokens; K splits of 1..16 waves per tile group, ragged N.
+ROLL_CASES = [(1, 28672, 100, True), (1, 28672, 1500, True), (1, 6912, 1000, True),
+              (1, 2560, 77, False), (1, 16384, 333, True), (1, 4096, 2048, True),
+              (1, 640, 9000, True), (3, 4096, 500, True), (8, 8192, 64, True),
+              (2, 28672, 40, False)]
+
+
+@pytest.mark.parametrize("M,K,N,norm", ROLL_CASES)
+def test_roll_parity(torch, bl, orc, M, K, N, norm):
+    """The rolling form, forced, fused (one token) and over q from the
+    workspace: within 1e-5 of the oracle and the same bits as the automatic
+    route; the fused launch's first workgroup leaves the oracle's q / inv /
+    qsum in the workspace."""
+    announce("roll", M, K, N, norm)
+    x, w, t, g = mm_case(M, K, N, 3100 + M + K + N)
+    gg = g if norm else None
+    packed_r, s = orc.pack_i2s(w)
+    y64 = orc.forward(x, packed_r, s, gg, 1e-6, N)
+    q_r, inv_r, qs_r = orc.act_quant(x, gg, 1e-6)
+    X, P = dev(torch, x), dev(torch, packed_r)
+    G = dev(torch, g) if norm else None
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = bl.new_workspace(M, K)
+    ref = host(bl.forward(X, P, s, G, 1e-6, N, out=out, workspace=ws)).copy()
+    check_y(ref, y64)
+    vroll = bl.num_variants(1)
+    for fuse in ((1, 0) if M == 1 else (0,)):
+        out.fill_(float("nan"))
+        ws.fill_(0)
+        y = host(bl.forward(X, P, s, G, 1e-6, N, out=out, workspace=ws, path=1, fuse=fuse,
+                            variant=vroll))
+        assert np.array_equal(y, ref), fuse
+        q, inv, qs = bl.workspace_views(ws, M, K)
+        assert np.array_equal(host(q), q_r) and np.array_equal(host(inv), inv_r), fuse
+        assert np.array_equal(host(qs), qs_r), fuse
+
+
+def test_roll_batch_mixed_rows(torch, bl, orc):
+    """One rolling launch over problems of different row lengths (different
+    K splits and quantisation segments per problem): each output the same
+    bits as its single call and within 1e-5 of the oracle."""
+    shapes = [(8192, 3000), (28672, 700), (2560, 5000), (6912, 1200)]
+    items, singles, refs = [], [], []
+    for i, (K, N) in enumerate(shapes):
+        x, w, t, g = mm_case(1, K, N, 3300 + i)
+        packed_r, s = orc.pack_i2s(w)
+        refs.append(orc.forward(x, packed_r, s, g, 1e-6, N))
+        X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+        out = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda")
+        ws = bl.new_workspace(1, K)
+        singles.append(host(bl.forward(X, P, s, G, 1e-6, N, out=out, workspace=ws)).copy())
+        items.append((X, P, s, G, 1e-6, out, ws))
+    announce("roll batch")
+    for it in items:
+        it[5].fill_(float("nan"))
+    bl.forward_batch(items, path=1, variant=bl.num_variants(1))
+    torch.cuda.synchronize()
+    for it, single, y64 in zip(items, singles, refs):
+        assert np.array_equal(host(it[5]), single)
+        check_y(host(it[5]), y64)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_forward_io_decode_layer(torch, bl, orc, dt):
     """The decoder layer's seven BitLinears at full size, one token, x and y
