@@ -84,7 +84,7 @@ typedef enum {
 /* Launch options for bitlinear_forward_ex / bitlinear_matmul_i2s_ex.
  *   path:    a bl_path value.
  *   fuse:    forward only.  -1 = automatic (fused for M == 1 and
- *            K <= 8192); 0 = separate quantisation kernel; 1 = RMSNorm +
+ *            K <= 32768); 0 = separate quantisation kernel; 1 = RMSNorm +
  *            quantisation recomputed inside every workgroup of the decode
  *            kernel (GEMV route only, M <= 4 and M*K <= 32768).
  *   variant: 0 = automatic; otherwise an index into the route's table of
@@ -228,8 +228,9 @@ typedef struct {
 /* Several independent BitLinear forwards, e.g. the BitLinears of one decoder
  * layer at decode (one launch for the whole layer).  Results are
  * bit-identical to calling bitlinear_forward_ex(descs[i], launch) for each i.
- * The decode-sized ones (M <= 4 with the fused quantisation) share one
- * kernel launch per 8.  With the automatic launch shape (and not forced
+ * The decode-sized ones (M <= 4 with the fused quantisation; automatically,
+ * M == 1 with K <= 32768) share one kernel launch per 8.  With the
+ * automatic launch shape (and not forced
  * onto the tile route), the others with M <= 8, M * K <= 65536 and
  * K <= 8192 (a few tokens) share one quantisation launch and one one-shot
  * contraction launch per 8, and
