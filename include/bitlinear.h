@@ -377,10 +377,10 @@ bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count,
  *   g = BitLinear(x; gate, gamma_in), u = BitLinear(x; up, gamma_in)   fp32 [M][F]
  *   a = (max(g, 0) * max(g, 0)) * u                                    fp32 [M][F]
  *   y = BitLinear(a; down, gamma_sub)                                  fp32 [M][H]
- * For F <= 8192, a is never stored: the down projection's quantisation
- * forms it from g and u as it reads them.  At M = 1 with F <= 8192 the
- * block is two launches (gate and up in one, the down projection with its
- * quantisation in the other); otherwise gate and up take
+ * For F <= 8192, or at M = 1 (F <= 32768), a is never stored: the down
+ * projection's quantisation forms it from g and u as it reads them.  At
+ * M = 1 the block is two launches (gate and up in one, the down projection
+ * with its quantisation in the other); otherwise gate and up take
  * bitlinear_forward_batch's launches and the down projection one
  * quantisation and one contraction launch (for F > 8192, after one
  * elementwise launch that stores a in the workspace).
@@ -393,7 +393,8 @@ bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count,
  *   workspace: device, >= bitlinear_ffn_workspace_bytes(M, H, F) bytes,
  *             16-byte aligned; after the call it holds g at offset 0 and u
  *             at offset align256(4*M*F) (fp32 [M][F] each), then the three
- *             projections' q / inv / qsum (and a, when F > 8192); on the
+ *             projections' q / inv / qsum (and a, when F > 8192 and
+ *             M > 1); on the
  *             grouped prefill route x is quantised once, into the gate's
  *             part, which both contractions read.
  *   No output may overlap an input.  Errors as bitlinear_forward; all

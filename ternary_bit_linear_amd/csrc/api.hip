@@ -694,8 +694,12 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
     // 2. down over relu2_mul(g, u), formed while its quantisation reads g, u.
     const Workspace wd = carve(w.ws_down, M, F);
     const int64_t Ms[1] = {M}, Ks[1] = {F}, Ns[1] = {H};
-    if (M == 1 && F <= 8 * 1024 && bl::shot_fused_supported(M, F) &&
-        bl::shot_rounds(Ms, Ks, Ns, 1, true, true) == 1) {
+    const bool shot_glu = M == 1 && F <= 8 * 1024 && bl::shot_fused_supported(M, F) &&
+                          bl::shot_rounds(Ms, Ks, Ns, 1, true, true) == 1;
+    if (shot_glu || (M == 1 && bl::roll_fused_supported(M, F))) {
+        // One launch: the down projection's quantisation forms relu2(g) * u
+        // as it reads g and u (the one-shot kernel when its workgroups fit
+        // the device at once, else the rolling kernel).
         bl::FusedDecode f;
         f.x = w.g;
         f.gamma = d.gamma_sub;
@@ -710,7 +714,8 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
         f.K = F;
         f.N = H;
         f.u = w.u;
-        return hip_status(bl::launch_gemv_shot_fused(&f, 1, 0, s));
+        return hip_status(shot_glu ? bl::launch_gemv_shot_fused(&f, 1, 0, s)
+                                   : bl::launch_gemv_roll_fused(&f, 1, s));
     }
     if (F <= bl::kActQuantBatchMaxK) {
         // rows in registers: the product is formed inside the quantisation

@@ -821,7 +821,8 @@ hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hi
 // Rolling form of the one-shot contraction (each wave streams its weights
 // through a small register ring), for problem sets the device does not hold
 // in one round: q from global memory (M <= 8, M * K <= kShotMaxQ), or fused
-// for one token per problem (fp32 x / y, no gated input).
+// for one token per problem (fp32 x / y; all problems of a launch with the
+// gated FFN input u, or none).
 bool roll_supported(int64_t M, int64_t K);
 hipError_t launch_gemv_roll(const ShotDecode *d, int count, hipStream_t s);
 bool roll_fused_supported(int64_t M, int64_t K);

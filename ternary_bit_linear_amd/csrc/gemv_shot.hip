@@ -411,12 +411,17 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
 // barrier, so the loads the caller issues there queue behind all of them.
 // q goes to q (LDS) and, when gq is set, to global memory; inv to *inv (and
 // *ginv); the per-wave code sums to qpart[16].
-template <int SQ, class Hook>
+// GLU: the row is relu2_mul(x, u) of the gate row x and the up row u (the
+// FFN's down projection input), formed as they arrive; gamma is then loaded
+// after the product (it is first needed after the sum of squares), so that
+// x, u and gamma are never all held at once.
+template <int SQ, bool GLU = false, class Hook>
 __device__ __forceinline__ void wide_act_quant_row(const float *__restrict__ x,
                                                    const float *__restrict__ gamma, float eps,
                                                    int K, float *red, float *chain, int8_t *q,
                                                    int8_t *gq, float *inv, float *ginv, int *qpart,
-                                                   Hook &&issued) {
+                                                   Hook &&issued,
+                                                   const float *__restrict__ u = nullptr) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = tid >> 6;
@@ -425,15 +430,15 @@ __device__ __forceinline__ void wide_act_quant_row(const float *__restrict__ x,
     const int ni = (K + 1023) / 1024;                         // float4 groups per chain
     const bool norm = gamma != nullptr;
     const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+    const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
     const auto rg = gamma_rsrc(gamma, K);
     float4 xv[SQ], gv[SQ];
+    auto off_of = [&](int i) { return 4u * (uint32_t)(4 * t + 1024 * (h * SQ + i)); };
 #pragma unroll
     for (int i = 0; i < SQ; ++i) {
-        const int gi = h * SQ + i;
-        if (gi < ni) {  // wave-uniform; lanes past K read zeros
-            const uint32_t off = 4u * (uint32_t)(4 * t + 1024 * gi);
-            xv[i] = load_x4<float>(rx, off);
-            gv[i] = gamma_f4(rg, off, norm);
+        if (h * SQ + i < ni) {  // wave-uniform; lanes past K read zeros
+            xv[i] = load_x4<float>(rx, off_of(i));
+            gv[i] = GLU ? buf_load_f4(ru, off_of(i)) : gamma_f4(rg, off_of(i), norm);
         } else {
             xv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             gv[i] = xv[i];
@@ -441,6 +446,15 @@ __device__ __forceinline__ void wide_act_quant_row(const float *__restrict__ x,
     }
     __builtin_amdgcn_s_barrier();
     issued();
+    if constexpr (GLU) {
+        // x <- relu2_mul(x, u), then gamma into the registers u held
+#pragma unroll
+        for (int i = 0; i < SQ; ++i) {
+            xv[i] = relu2_mul4(xv[i], gv[i]);
+            gv[i] = h * SQ + i < ni ? gamma_f4(rg, off_of(i), norm)
+                                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
     float r = 1.0f;
     if (norm) {
         float p = 0.0f;
@@ -518,7 +532,8 @@ __device__ __forceinline__ void wide_act_quant_row(const float *__restrict__ x,
 // with range-checked loads that read nothing, so the loop body is the same
 // every time and the compiler's load counts stay exact.  Launch: one
 // workgroup per tile-group set, W = 16 waves (one per CU by registers).
-template <int ND, int R, bool OUT_Y, int FM, int SQ, typename IO = float, int W = 16>
+template <int ND, int R, bool OUT_Y, int FM, int SQ, typename IO = float, int W = 16,
+          bool GLU = false>
 __global__ __launch_bounds__(64 * W) void gemv_roll_kernel(int b0, int b1, int b2, int b3, int b4,
                                                         int b5, int b6, int b7, ShotBatch B) {
     static_assert(ND >= 1 && ND <= 4, "ring depth");
@@ -526,6 +541,7 @@ __global__ __launch_bounds__(64 * W) void gemv_roll_kernel(int b0, int b1, int b
     static_assert(W == 4 || W == 8 || W == 16, "waves per workgroup");
     static_assert(kU == 2, "shift forms below assume kU == 2");
     static_assert(FM == 0 || (FM == 1 && W == 16), "fused: one token, 16 waves");
+    static_assert(!GLU || FM == 1, "the gated input is fused");
     static_assert(SQ == 1 || SQ == 2 || SQ == 4 || SQ == 8, "row segment");
     constexpr int LW = W == 16 ? 4 : W == 8 ? 3 : 2;
     extern __shared__ __align__(16) int8_t q_lds[];
@@ -545,6 +561,7 @@ __global__ __launch_bounds__(64 * W) void gemv_roll_kernel(int b0, int b1, int b
     asm volatile("" ::"s"(P.q), "s"(P.inv), "s"(P.qsum), "s"(P.x), "s"(P.gamma), "s"(P.q_out),
                  "s"(P.inv_out), "s"(P.qsum_out), "s"(P.packed), "s"(P.y), "s"(P.acc), "s"(P.eps),
                  "s"(P.w_scale), "s"(P.M), "s"(P.K), "s"(P.N), "s"(P.wg_begin), "s"(P.ks_log));
+    if constexpr (GLU) asm volatile("" ::"s"(P.u));
     const int M = P.M, K = P.K, N = P.N;
 
     const int tid = threadIdx.x;
@@ -610,9 +627,9 @@ __global__ __launch_bounds__(64 * W) void gemv_roll_kernel(int b0, int b1, int b
         // The whole row of x and gamma over all 16 waves (one round trip,
         // ahead of every weight load of the workgroup), then the ring's
         // first batches; the quantisation runs while they stream in.
-        wide_act_quant_row<SQ>(P.x, P.gamma, P.eps, K, red, chain_sh, q_lds,
-                               st == 0 ? P.q_out : nullptr, inv_sh, P.inv_out, qpart_sh,
-                               prologue);
+        wide_act_quant_row<SQ, GLU>(P.x, P.gamma, P.eps, K, red, chain_sh, q_lds,
+                                    st == 0 ? P.q_out : nullptr, inv_sh, P.inv_out, qpart_sh,
+                                    prologue, P.u);
         lds_barrier();
         if (st == 0 && tid == 0) {
             int t = 0;
@@ -1174,7 +1191,7 @@ hipError_t launch_roll_sep(const ShotDecode *d, int count, hipStream_t s) {
                         begin, gx, qmax, s);
 }
 
-template <int SQ>
+template <int SQ, bool GLU>
 hipError_t launch_roll_fused(const FusedDecode *d, int count, hipStream_t s) {
     ShotBatch B{};
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], qmax;
@@ -1192,11 +1209,12 @@ hipError_t launch_roll_fused(const FusedDecode *d, int count, hipStream_t s) {
         P.y = d[i].y;
         P.eps = d[i].eps;
         P.w_scale = d[i].w_scale;
+        P.u = d[i].u;
     }
     int begin[kMaxShotBatch];
     const int64_t gx = fill_roll(B, begin, count, M, K, N, &qmax);
-    return launch_batch(gemv_roll_kernel<kRollND, 1, true, 1, SQ, float, kRollW>, kRollW, B, begin,
-                        gx, qmax, s);
+    return launch_batch(gemv_roll_kernel<kRollND, 1, true, 1, SQ, float, kRollW, GLU>, kRollW, B,
+                        begin, gx, qmax, s);
 }
 
 }  // namespace
@@ -1221,15 +1239,22 @@ bool roll_fused_supported(int64_t M, int64_t K) {
 hipError_t launch_gemv_roll_fused(const FusedDecode *d, int count, hipStream_t s) {
     if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
     int64_t kmax = 0;
+    const bool glu = d[0].u != nullptr;
     for (int i = 0; i < count; ++i) {
-        if (!roll_fused_supported(d[i].M, d[i].K) || !d[i].y || d[i].u || d[i].io != kIoF32)
+        if (!roll_fused_supported(d[i].M, d[i].K) || !d[i].y || (d[i].u != nullptr) != glu ||
+            d[i].io != kIoF32)
             return hipErrorInvalidValue;
         kmax = std::max<int64_t>(kmax, d[i].K);
     }
-    if (kmax <= 4096) return launch_roll_fused<1>(d, count, s);
-    if (kmax <= 8192) return launch_roll_fused<2>(d, count, s);
-    if (kmax <= 16384) return launch_roll_fused<4>(d, count, s);
-    return launch_roll_fused<8>(d, count, s);
+    if (glu) {
+        // the FFN's down projection: rows of F (up to 32768)
+        if (kmax <= 8192) return launch_roll_fused<2, true>(d, count, s);
+        return launch_roll_fused<8, true>(d, count, s);
+    }
+    if (kmax <= 4096) return launch_roll_fused<1, false>(d, count, s);
+    if (kmax <= 8192) return launch_roll_fused<2, false>(d, count, s);
+    if (kmax <= 16384) return launch_roll_fused<4, false>(d, count, s);
+    return launch_roll_fused<8, false>(d, count, s);
 }
 
 }  // namespace bl

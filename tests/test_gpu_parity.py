@@ -929,6 +929,13 @@ def test_ffn_70b_shapes_sampled(torch, bl, orc):
         sub = orc.packed_rows(host(packs[2][0]), F, outs)
         y64 = orc.rescale(orc.matmul_i2s(qa, qsa, sub, outs.size), inva, packs[2][1])
         check_y(y[:, outs], y64)
+        # the down projection's own q / inv / qsum in its part of the
+        # workspace (at M = 1 written by the fused launch's first workgroup)
+        al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+        off = 2 * al(4 * M * F) + 2 * al(bl.workspace_bytes(M, H))
+        wq, winv, wqs = bl.workspace_views(ws[off:], M, F)
+        assert np.array_equal(host(wq), qa) and np.array_equal(host(winv), inva)
+        assert np.array_equal(host(wqs), qsa)
         del packs, ws
         torch.cuda.empty_cache()
 
