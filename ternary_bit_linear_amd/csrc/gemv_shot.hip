@@ -1246,11 +1246,9 @@ hipError_t launch_gemv_roll_fused(const FusedDecode *d, int count, hipStream_t s
             return hipErrorInvalidValue;
         kmax = std::max<int64_t>(kmax, d[i].K);
     }
-    if (glu) {
-        // the FFN's down projection: rows of F (up to 32768)
-        if (kmax <= 8192) return launch_roll_fused<2, true>(d, count, s);
-        return launch_roll_fused<8, true>(d, count, s);
-    }
+    // The FFN's down projection (rows of F up to 32768; shorter rows skip
+    // the segments past their end): one instantiation.
+    if (glu) return launch_roll_fused<8, true>(d, count, s);
     if (kmax <= 4096) return launch_roll_fused<1, false>(d, count, s);
     if (kmax <= 8192) return launch_roll_fused<2, false>(d, count, s);
     if (kmax <= 16384) return launch_roll_fused<4, false>(d, count, s);
