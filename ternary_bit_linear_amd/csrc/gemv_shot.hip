@@ -818,15 +818,16 @@ int device_cus() {
 // taken with the gated FFN input, `wide` false).
 // *rounds_out receives the chosen shape's rounds.
 // Estimated time (us) of a one-round fused launch for one token, a linear
-// model fitted to the measured times of every shape on twelve decode problem
-// sets (M = 1, K = 2048..8192, one to seven BitLinears; MI355X, two runs,
-// rms error 0.4 us).  A CU that holds c workgroups streams c times the
-// largest workgroup's weight bytes and runs c quantisation chains of up to
-// max K elements; splitting a row's K over 2 or 4 waves costs the
-// partial-sum reduction and shorter streams; four tiles per wave, eight
-// batches per wave and weight batches past a row's end cost their own.
-// Over the sets it picks the fastest shape in eleven, and in the twelfth
-// one as fast as the score's pick.
+// model fitted to the measured times of every shape on ten decode problem
+// sets (M = 1, K = 2048..8192, one to seven BitLinears, 1.7 to 37 MB;
+// MI355X, rms error 0.4 us).  A CU that holds c workgroups streams c times
+// the largest workgroup's weight bytes and runs c quantisation chains of up
+// to max K elements; splitting a row's K over 2 or 4 waves costs the
+// partial-sum reduction and shorter streams; two and four tiles per wave,
+// eight batches per wave and weight batches past a row's end cost their
+// own, and 8- and 16-wave workgroups (one quantisation per CU, its waves
+// issuing their weights after it) save some.  Over the sets it picks the
+// fastest shape in nine, and in the tenth one within 5 % of it.
 double one_token_cost(const ShotShape &h, const int64_t *K, const int64_t *N, int count,
                       int cus) {
     int64_t wgs = 0, kmax = 0, unused = 0;
@@ -844,9 +845,10 @@ double one_token_cost(const ShotShape &h, const int64_t *K, const int64_t *N, in
         unused = std::max<int64_t>(unused, h.nb - (nsteps + ks * kU - 1) / (ks * kU));
     }
     const double c = (double)((wgs + cus - 1) / cus);
-    return 0.043 * c * wg_bytes / 1024.0 + 0.063 * c * (double)kmax / 1024.0 +
-           (ksmax == 4 ? 0.93 : ksmax == 2 ? 0.60 : 0.0) + (h.R == 4 ? 0.71 : 0.0) +
-           (h.nb == 8 ? 0.67 : 0.0) + 0.037 * (double)(unused * h.R);
+    return 0.0425 * c * wg_bytes / 1024.0 + 0.0749 * c * (double)kmax / 1024.0 +
+           (ksmax == 4 ? 0.76 : ksmax == 2 ? 0.60 : 0.0) +
+           (h.R == 4 ? 1.08 : h.R == 2 ? 0.42 : 0.0) + (h.nb == 8 ? 0.82 : 0.0) +
+           0.031 * (double)(unused * h.R) + (h.w == 8 ? -0.70 : h.w == 16 ? -0.14 : 0.0);
 }
 
 int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, int pref,
