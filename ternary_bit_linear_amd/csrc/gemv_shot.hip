@@ -778,7 +778,7 @@ struct ShotShape {
     int w;
 };
 constexpr ShotShape kShotShapes[] = {{3, 1, 4, 4}, {4, 1, 4, 4}, {8, 1, 4, 4}, {3, 2, 3, 4},
-                                     {4, 2, 3, 4}, {3, 4, 3, 4}, {3, 2, 1, 8}, {3, 1, 1, 16}};
+                                     {4, 2, 3, 4}, {2, 2, 1, 8}, {3, 2, 1, 8}, {3, 1, 1, 16}};
 constexpr int kNumShotShapes = sizeof(kShotShapes) / sizeof(kShotShapes[0]);
 static_assert(kNumShotShapes == kShotShapeCount, "shape count the variant numbering uses");
 
@@ -811,7 +811,7 @@ int device_cus() {
 // workgroups repeat the quantisation) unless the device would be left
 // underfilled; over q from global memory one tile per wave is the faster
 // (measured on MI355X, M = 1..4, K = 2560..8192: up to 1.4x).  One
-// workgroup per CU costs extra, four tiles per wave more.
+// workgroup per CU costs extra.
 // One token with the quantisation fused in (the decode case) takes, after
 // rounds, an estimate of the launch time instead of that score, and is the
 // only case that considers the 8- and 16-wave shapes (one_token_cost; not
@@ -823,11 +823,11 @@ int device_cus() {
 // MI355X, rms error 0.4 us).  A CU that holds c workgroups streams c times
 // the largest workgroup's weight bytes and runs c quantisation chains of up
 // to max K elements; splitting a row's K over 2 or 4 waves costs the
-// partial-sum reduction and shorter streams; two and four tiles per wave,
-// eight batches per wave and weight batches past a row's end cost their
-// own, and 8- and 16-wave workgroups (one quantisation per CU, its waves
-// issuing their weights after it) save some.  Over the sets it picks the
-// fastest shape in nine, and in the tenth one within 5 % of it.
+// partial-sum reduction and shorter streams; two tiles per wave, eight
+// batches per wave and weight batches past a row's end cost their own, and
+// 8-wave workgroups (one quantisation per CU, its waves issuing their
+// weights after it) save some.  Over the sets it picks the fastest shape in
+// every one.
 double one_token_cost(const ShotShape &h, const int64_t *K, const int64_t *N, int count,
                       int cus) {
     int64_t wgs = 0, kmax = 0, unused = 0;
@@ -845,10 +845,10 @@ double one_token_cost(const ShotShape &h, const int64_t *K, const int64_t *N, in
         unused = std::max<int64_t>(unused, h.nb - (nsteps + ks * kU - 1) / (ks * kU));
     }
     const double c = (double)((wgs + cus - 1) / cus);
-    return 0.0425 * c * wg_bytes / 1024.0 + 0.0749 * c * (double)kmax / 1024.0 +
-           (ksmax == 4 ? 0.76 : ksmax == 2 ? 0.60 : 0.0) +
-           (h.R == 4 ? 1.08 : h.R == 2 ? 0.42 : 0.0) + (h.nb == 8 ? 0.82 : 0.0) +
-           0.031 * (double)(unused * h.R) + (h.w == 8 ? -0.70 : h.w == 16 ? -0.14 : 0.0);
+    return 0.0415 * c * wg_bytes / 1024.0 + 0.0808 * c * (double)kmax / 1024.0 +
+           (ksmax == 4 ? 0.58 : ksmax == 2 ? 0.53 : 0.0) + (h.R == 2 ? 0.47 : 0.0) +
+           (h.nb == 8 ? 0.81 : 0.0) + 0.024 * (double)(unused * h.R) +
+           (h.w == 8 ? -0.74 : h.w == 16 ? -0.03 : 0.0);
 }
 
 int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, int pref,
@@ -915,9 +915,9 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
         const int64_t per_cu = std::min<int64_t>(h.occupancy, (160 * 1024) / lds);
         double score = 100.0 * (1.0 - used / total);
         if (fused)
-            score += h.R == 1 ? 10.0 : h.R == 4 ? 50.0 : 0.0;
+            score += h.R == 1 ? 10.0 : 0.0;
         else
-            score += h.R == 2 ? 10.0 : h.R == 4 ? 50.0 : 0.0;
+            score += h.R == 2 ? 10.0 : 0.0;
         // Fewer workgroups than CUs leave CUs without weights to stream:
         // with the quantisation fused in this outweighs the tile
         // preference (one BitLinear of N = 2560 at K = 6912: one tile per
@@ -1001,7 +1001,7 @@ hipError_t launch_shot_fused_nb(const FusedDecode *d, int count, hipStream_t s) 
         case 2: return CALL(8, 1, 4);                                          \
         case 3: return CALL(3, 2, 4);                                          \
         case 4: return CALL(4, 2, 4);                                          \
-        case 5: return CALL(3, 4, 4);                                          \
+        case 5: return CALL(2, 2, 8);                                          \
         case 6: return CALL(3, 2, 8);                                          \
         case 7: return CALL(3, 1, 16);                                         \
         default: return hipErrorInvalidValue;                                  \
