@@ -118,11 +118,10 @@ __device__ __forceinline__ v4i field_sum(const v4i (&a)[4]) {
 // block form; in a larger workgroup waves 4..W-1 issue their weights and
 // meet its barriers, so a CU that holds one such workgroup normalises x once
 // where several 4-wave workgroups would each do it.  In such a workgroup
-// waves 0..3 issue their weights after the quantisation: a wave that issues
-// many loads stalls at the issue until the memory pipeline takes them, and
-// the quantisation's barriers would make every wave wait for it (measured:
-// the decoder layer's codes are ready 0.6 us earlier, the launch 0.35 us
-// shorter).
+// waves 0..3 issue their weights after the quantisation, past the barrier
+// that publishes q: a wave that issues many loads stalls at the issue until
+// the memory pipeline takes them, and the quantisation's barriers would make
+// every wave wait for it.
 template <int NB, int R, bool OUT_Y, int FM, int CH, bool LONG, bool GLU = false,
           typename IO = float, int W = 4>
 __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b2, int b3, int b4,
@@ -273,7 +272,6 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
                         red, sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr);
                 }
             }
-            if constexpr (kLate) issue_weights();
         } else {
             // Waves 4..W-1: the barrier behind the first row's x / gamma
             // loads, their weights, then the barriers of each row's block
@@ -285,6 +283,11 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
                 if (m < M) block_act_quant_row_barriers(P.gamma != nullptr, true);
         }
         lds_barrier();
+        // The quantising waves of a larger workgroup issue their weights
+        // only now, past the barrier that publishes q: an issue that stalls
+        // then delays only their own contraction.
+        if constexpr (kLate)
+            if (wid < 4) issue_weights();
         // The problem's first workgroup also stores the rows' activation
         // sums (the partials are visible after the barrier).
         if (st == 0 && tid < M && tid < FM)
