@@ -306,11 +306,66 @@ __device__ __forceinline__ int sum_char4(uint32_t v, int acc) {
     return __builtin_amdgcn_sdot4((int)v, 0x01010101, acc, false);
 }
 
+// Arrival counters in LDS.  A wave's LDS operations complete in order, and
+// once a wave has waited for its own (lgkmcnt(0)) they are visible to every
+// wave of the workgroup; so a wave arrives by waiting for its LDS writes and
+// then adding one (lane 0), and a waiting wave polls the counter and issues
+// its later LDS reads only after the poll that ends the wait has returned.
+// The memory clobbers keep the compiler's LDS writes ahead of the add and
+// its later reads behind the poll.  The add and the poll are written as
+// instructions because the compiler, unable to tell the counter from the
+// LDS targets of weight loads still in flight, would otherwise wait for
+// every outstanding global load of the wave first; the poll waits for its
+// own result within its statement.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void lds_arrive(int *ctr) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if ((threadIdx.x & 63) == 0)
+        asm volatile("ds_add_u32 %0, %1" ::"v"(lds_offset(ctr)), "v"(1) : "memory");
+}
+__device__ __forceinline__ void lds_wait_count(const int *ctr, int target) {
+    const uint32_t a = lds_offset(ctr);
+    for (;;) {
+        int v;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+        if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Meeting point of the block form's four waves: a workgroup barrier, or,
+// with `spin` set (the four quantising waves of a larger workgroup, whose
+// other waves do not take part), an LDS arrival counter: each wave adds one
+// per meeting once its own LDS writes are done, then waits until all four
+// have (`phase`, kept per wave, is four times the meetings so far).  The
+// counter is zero, and visible to the four waves, before their first
+// meeting.  The waits end: the four waves are resident in one workgroup and
+// each arrives after a bounded amount of work.  Reuse of red[] between
+// meetings is safe: a wave writes an entry only after a meeting that every
+// wave reaches after its reads of the entry's previous value.
+struct QuadSpin {
+    int *ctr;
+    int phase;
+};
+__device__ __forceinline__ void quad_meet(QuadSpin *spin) {
+    if (!spin) {
+        lds_barrier();
+        return;
+    }
+    spin->phase += 4;
+    lds_arrive(spin->ctr);
+    lds_wait_count(spin->ctr, spin->phase);
+}
+
 // Block-wide reductions over exactly 256 threads (4 waves).  `red` is 4
 // words of shared memory; the caller's block must reach these uniformly.
-// Each takes one barrier: a caller that runs several reductions gives each
-// its own 4 words (or separates reuses of the same words by another
-// barrier), so no trailing barrier is needed.
+// Each takes one barrier (or one quad_meet): a caller that runs several
+// reductions gives each its own 4 words (or separates reuses of the same
+// words by another barrier), so no trailing barrier is needed.
 //
 // Sum of squares of one row in the library's fixed order "O256": thread t
 // owns the elements k with (k / 4) % 256 == t and accumulates their squares
@@ -319,19 +374,20 @@ __device__ __forceinline__ int sum_char4(uint32_t v, int acc) {
 // combined by a halving tree (lane j + 32 into j, then j + 16, ... j + 1;
 // wave_tree_sum_f); the four wave totals are then added as
 // (g0 + g1) + (g2 + g3).
-__device__ __forceinline__ float block_sumsq_finish(float p, float *red) {
+__device__ __forceinline__ float block_sumsq_finish(float p, float *red,
+                                                   QuadSpin *spin = nullptr) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     p = wave_tree_sum_f(p);
     if (lane == 0) red[wid] = p;
-    lds_barrier();
+    quad_meet(spin);
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-__device__ __forceinline__ float block_max(float v, float *red) {
+__device__ __forceinline__ float block_max(float v, float *red, QuadSpin *spin = nullptr) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     v = wave_max(v);
     if (lane == 0) red[wid] = v;
-    lds_barrier();
+    quad_meet(spin);
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
@@ -421,13 +477,17 @@ __device__ __forceinline__ void finish_row(Sink &sink, float inv, int qs, float 
 // not delay the normalisation.  A wave skips the loads of a chunk that lies
 // wholly past K.  LONG rows (K > 1024 * CH) are streamed in chunks of CH
 // float4 per thread, three times.
+// spin: null (the reductions meet at workgroup barriers) or the LDS counter
+// on which only the four waves of the block meet (quad_meet; the sink must
+// defer the activation sum, whose block form takes a barrier).
 template <int CH, bool LONG, bool SYNC = true, bool GLU = false, typename XT = float, class Sink,
           class Hook>
 __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                                                     const float *__restrict__ gamma,
                                                     float eps, int K, float *red,
                                                     Sink &sink, Hook &&issued,
-                                                    const float *__restrict__ u = nullptr) {
+                                                    const float *__restrict__ u = nullptr,
+                                                    QuadSpin *spin = nullptr) {
     static_assert(!GLU || std::is_same<XT, float>::value, "the gated input is fp32");
     constexpr uint32_t XB = kXBytes<XT>;
     const int t4 = 4 * threadIdx.x;
@@ -478,7 +538,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                     p = __builtin_fmaf(xv[i].w, xv[i].w, p);
                 }
             }
-            const float ss = block_sumsq_finish(p, red);
+            const float ss = block_sumsq_finish(p, red, spin);
             r = rms_scale(ss, K, eps);
         }
         float amax = 0.0f;
@@ -489,7 +549,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                 amax = amax4(amax, xv[i]);
             }
         }
-        amax = block_max(amax, red + 4);
+        amax = block_max(amax, red + 4, spin);
         const float inv = quant_scale(amax);
         int qs = 0;
 #pragma unroll
@@ -536,7 +596,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                 p = __builtin_fmaf(xv[i].w, xv[i].w, p);
             }
         }
-        const float ss = block_sumsq_finish(p, red);
+        const float ss = block_sumsq_finish(p, red, spin);
         r = rms_scale(ss, K, eps);
     }
     float amax = 0.0f;
@@ -550,7 +610,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
 #pragma unroll
         for (int i = 0; i < CH; ++i) amax = amax4(amax, xn4(xv[i], gv[i], r));
     }
-    amax = block_max(amax, red + 4);
+    amax = block_max(amax, red + 4, spin);
     const float inv = quant_scale(amax);
     int qs = 0;
     for (int c0 = 0; c0 < K; c0 += STRIDE * CH) {

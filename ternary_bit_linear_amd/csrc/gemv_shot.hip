@@ -251,6 +251,20 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
         //    stream in.
         constexpr bool kLate = W > 4;  // waves 0..3: weights after the quantisation
         constexpr bool kSync = !LONG;
+        // In a larger workgroup (rows held in registers) the four quantising
+        // waves meet on an LDS counter instead of workgroup barriers, so the
+        // other waves -- which may stall at the issue of their weights --
+        // never hold the quantisation up.
+        constexpr bool kSpin = kSync && W > 4;
+        __shared__ int spin_sh;
+        if constexpr (kSpin) {
+            // Zero, and visible to every wave past the first barrier below.
+            if (tid == 0) spin_sh = 0;
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        }
+        QuadSpin meet{&spin_sh, 0};
+        QuadSpin *const spin = kSpin ? &meet : nullptr;
         if (W == 4 || wid < 4) {
             {
                 ShotRowSink sink{q_lds, inv_sh, qpart_sh[0], st == 0 ? P.q_out : nullptr,
@@ -260,7 +274,7 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
                 };
                 block_act_quant_row<CH, LONG, kSync, GLU, IO>(reinterpret_cast<const IO *>(P.x),
                                                               P.gamma, P.eps, K, red, sink, hook,
-                                                              P.u);
+                                                              P.u, spin);
             }
 #pragma unroll
             for (int m = 1; m < FM; ++m) {
@@ -269,19 +283,23 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
                                      st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m};
                     block_act_quant_row<CH, LONG, false, GLU, IO>(
                         reinterpret_cast<const IO *>(P.x) + (size_t)m * K, P.gamma, P.eps, K,
-                        red, sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr);
+                        red, sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr, spin);
                 }
             }
         } else {
             // Waves 4..W-1: the barrier behind the first row's x / gamma
-            // loads, their weights, then the barriers of each row's block
-            // form.
+            // loads and their weights; with streamed rows also the barriers
+            // of each row's block form.
             if constexpr (kSync) __builtin_amdgcn_s_barrier();
             issue_weights();
+            if constexpr (!kSpin) {
 #pragma unroll
-            for (int m = 0; m < FM; ++m)
-                if (m < M) block_act_quant_row_barriers(P.gamma != nullptr, true);
+                for (int m = 0; m < FM; ++m)
+                    if (m < M) block_act_quant_row_barriers(P.gamma != nullptr, true);
+            }
         }
+        // (Published by a barrier: a count of the quantising waves polled
+        // by the others measured slower.)
         lds_barrier();
         // The quantising waves of a larger workgroup issue their weights
         // only now, past the barrier that publishes q: an issue that stalls
@@ -823,17 +841,21 @@ int device_cus() {
 // Estimated time (us) of a one-round fused launch for one token, a linear
 // model fitted to the measured times of every shape on ten decode problem
 // sets (M = 1, K = 2048..8192, one to seven BitLinears, 1.7 to 37 MB;
-// MI355X, rms error 0.4 us).  A CU that holds c workgroups streams c times
-// the largest workgroup's weight bytes and runs c quantisation chains of up
-// to max K elements; splitting a row's K over 2 or 4 waves costs the
-// partial-sum reduction and shorter streams; two tiles per wave, eight
-// batches per wave and weight batches past a row's end cost their own, and
-// 8-wave workgroups (one quantisation per CU, its waves issuing their
-// weights after it) save some.  Over the sets it picks the fastest shape in
-// every one.
-double one_token_cost(const ShotShape &h, const int64_t *K, const int64_t *N, int count,
-                      int cus) {
-    int64_t wgs = 0, kmax = 0, unused = 0;
+// MI355X, two runs averaged; rms error 0.3 us).  A CU that holds c
+// workgroups streams c times the largest workgroup's weight bytes and runs
+// c quantisation chains of up to max K elements; splitting a row's K over 2
+// or 4 waves costs the partial-sum reduction and shorter streams; a launch
+// of fewer workgroups than CUs runs faster than those terms say; the rest
+// is a fixed cost per shape (lower for the 8- and 16-wave workgroups: one
+// quantisation per CU, its four waves meeting among themselves while the
+// others issue their weights).  It picks the fastest shape in every set;
+// fitted with each set left out in turn, its picks sum to within 0.7 % of
+// the fastest shapes'.
+constexpr double kOneTokenBase[kShotShapeCount] = {3.52, 3.74, 4.69, 4.19,
+                                                   4.52, 3.76, 3.49, 3.20};
+double one_token_cost(int v, const int64_t *K, const int64_t *N, int count, int cus) {
+    const ShotShape &h = kShotShapes[v];
+    int64_t wgs = 0, kmax = 0;
     double wg_bytes = 0.0;
     int ksmax = 1;
     for (int i = 0; i < count; ++i) {
@@ -844,14 +866,11 @@ double one_token_cost(const ShotShape &h, const int64_t *K, const int64_t *N, in
         wg_bytes = std::max(wg_bytes, (double)slots * kTileRows * h.R * (double)(K[i] / 4));
         kmax = std::max<int64_t>(kmax, K[i]);
         ksmax = std::max(ksmax, ks);
-        const int64_t nsteps = (K[i] / 4 + kStep - 1) / kStep;
-        unused = std::max<int64_t>(unused, h.nb - (nsteps + ks * kU - 1) / (ks * kU));
     }
     const double c = (double)((wgs + cus - 1) / cus);
-    return 0.0415 * c * wg_bytes / 1024.0 + 0.0808 * c * (double)kmax / 1024.0 +
-           (ksmax == 4 ? 0.58 : ksmax == 2 ? 0.53 : 0.0) + (h.R == 2 ? 0.47 : 0.0) +
-           (h.nb == 8 ? 0.81 : 0.0) + 0.024 * (double)(unused * h.R) +
-           (h.w == 8 ? -0.74 : h.w == 16 ? -0.03 : 0.0);
+    const double under = std::max(0.0, 1.0 - (double)wgs / cus);
+    return 0.035 * c * wg_bytes / 1024.0 + 0.098 * c * (double)kmax / 1024.0 +
+           (ksmax == 4 ? 0.50 : ksmax == 2 ? 0.37 : 0.0) - 0.89 * under + kOneTokenBase[v];
 }
 
 int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, int pref,
@@ -898,7 +917,7 @@ int pick_shape(const int64_t *M, const int64_t *K, const int64_t *N, int count, 
         const int64_t rounds = rounds_of(h);
         if (rounds == INT64_MAX) continue;
         if (one_token) {
-            const double est = one_token_cost(h, K, N, count, cus);
+            const double est = one_token_cost(v, K, N, count, cus);
             if (best < 0 || rounds < best_rounds || (rounds == best_rounds && est < best_score)) {
                 best = v;
                 best_rounds = rounds;
