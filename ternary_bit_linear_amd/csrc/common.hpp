@@ -927,6 +927,9 @@ hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStrea
 // Whether the automatic choice takes the 32 x 32 x 32 kernel for a group.
 bool gemm32_preferred(const GemmDesc *d, int count);
 
+// Compute units of the current device (looked up once per device).
+int device_cus();
+
 // Calibration probes: one pass reading `bytes` (a multiple of 16; one
 // sink word per workgroup, probe_read_blocks(bytes) of them), and `blocks`
 // workgroups of back-to-back int8 MFMAs (256 sink words each).

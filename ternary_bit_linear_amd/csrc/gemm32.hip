@@ -36,6 +36,13 @@
 // checked buffer loads (rows past M or N read zeros); K is a whole number of
 // blocks on every path, so there is no K tail.
 //
+// k groups (KG = 2, with two blocks per step): the workgroup's waves form
+// two groups of WM x WN, group g contracting block g of every step into its
+// own accumulators, which group 1 hands to group 0 through LDS at the end.
+// With the same tile and wave count, each wave then owns twice the output
+// (64 x 64 instead of 64 x 32), so the fragments read from LDS per k fall
+// by 44 %.
+//
 // LDS layouts (bank-conflict-free 16-byte reads of 16 lanes): activation
 // row r (128 bytes, chunk c = 2 g + h) keeps chunk c at c ^ ((r >> 1) & 7);
 // weight row r (32 bytes, half h) keeps half h at h ^ ((r >> 3) & 1).
@@ -94,20 +101,23 @@ __device__ __forceinline__ int chunk_pos(int r, int c) {
 // One BM x BN output tile at (m0, n0) of one problem, by the whole
 // workgroup, KB I2_S blocks per step.  YT: storage type of y (float,
 // bf16_t, _Float16).
-template <int BM, int BN, int WM, int WN, int KB, int RA, int RB, bool OUT_Y, typename YT>
+template <int BM, int BN, int WM, int WN, int KB, int RA, int RB, int KG, bool OUT_Y,
+          typename YT>
 __device__ __forceinline__ void gemm32_tile(const int8_t *__restrict__ q,
                                             const float *__restrict__ inv,
                                             const int32_t *__restrict__ qsum,
                                             const uint8_t *__restrict__ packed, float w_scale,
                                             int M, int K, int N, YT *__restrict__ y,
                                             int32_t *__restrict__ acc_out, int m0, int n0) {
-    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int NW = KG * WM * WN, NT = NW * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 32, NI = TN / 32;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile of whole 32 x 32 MFMA tiles");
     static_assert(KB == 1 || KB == 2, "blocks per step");
+    static_assert(KG == 1 || KG == KB, "k groups: one block of each step per group");
+    constexpr int BW = KB / KG;                // blocks of a step this wave contracts
     constexpr int NCA = 8 * KB, NCB = 2 * KB;  // 16-byte chunks per row of a step
-    constexpr int NF = 4 * KB;                 // (block, field) pairs per step
+    constexpr int NF = 4 * BW;                 // (block, field) pairs per step and wave
     // Bytes of one step (activations, packed weights), each rounded up to
     // whole loads of every lane: chunks past the step's data are loaded out
     // of range (zeros), so every wave issues the same number of loads.
@@ -142,7 +152,10 @@ __device__ __forceinline__ void gemm32_tile(const int8_t *__restrict__ q,
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wid / WN, wn = wid % WN;
+    // With KG > 1 the waves form KG groups of WM x WN, group kg contracting
+    // block kg of every step into its own accumulators (summed at the end).
+    const int kg = wid / (WM * WN), wt = wid % (WM * WN);
+    const int wm = wt / WN, wn = wt % WN;
     const int l32 = lane & 31, hh = lane >> 5;
     const int nsteps = K / (kBlk * KB);
     const uint32_t rowbytes = (uint32_t)K / 4;
@@ -181,23 +194,24 @@ __device__ __forceinline__ void gemm32_tile(const int8_t *__restrict__ q,
     // LDS offsets of this lane's fragment reads: activations of (block b,
     // field g) -- chunk 8 b + 2 g + half; packed weights of block b -- chunk
     // 2 b + half.
-    int aoff[KB][4][MI];
+    int aoff[BW][4][MI];
 #pragma unroll
-    for (int b = 0; b < KB; ++b)
+    for (int b = 0; b < BW; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const int r = wm * TM + 32 * mi + l32;
-                aoff[b][g][mi] = r * 16 * NCA + 16 * chunk_pos<NCA>(r, 8 * b + 2 * g + hh);
+                aoff[b][g][mi] =
+                    r * 16 * NCA + 16 * chunk_pos<NCA>(r, 8 * (kg * BW + b) + 2 * g + hh);
             }
-    int boff[KB][NI];
+    int boff[BW][NI];
 #pragma unroll
-    for (int b = 0; b < KB; ++b)
+    for (int b = 0; b < BW; ++b)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
             const int r = wn * TN + 32 * ni + l32;
-            boff[b][ni] = r * 16 * NCB + 16 * chunk_pos<NCB>(r, 2 * b + hh);
+            boff[b][ni] = r * 16 * NCB + 16 * chunk_pos<NCB>(r, 2 * (kg * BW + b) + hh);
         }
 
     // Loads of step s: activations (A ring) and, RB - RA steps further on,
@@ -226,20 +240,20 @@ __device__ __forceinline__ void gemm32_tile(const int8_t *__restrict__ q,
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0;
 
-    v4i af[2][KB][4][MI];  // activation fragments, ping-pong by step parity
-    v4i bp[2][KB][NI];     // packed weights, ping-pong by step parity
+    v4i af[2][BW][4][MI];  // activation fragments, ping-pong by step parity
+    v4i bp[2][BW][NI];     // packed weights, ping-pong by step parity
     v4i bx0[2][NI];        // expanded codes of block 0, field 0, by parity
     auto read_frags = [&](auto P, auto I) {
         constexpr int pp = decltype(P)::value;
         const uint8_t *bb = ringB(I);
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
+        for (int b = 0; b < BW; ++b)
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
                 bp[pp][b][ni] = *reinterpret_cast<const v4i *>(bb + boff[b][ni]);
         const int8_t *ab = ringA(I);
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
+        for (int b = 0; b < BW; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -314,8 +328,8 @@ __device__ __forceinline__ void gemm32_tile(const int8_t *__restrict__ q,
     // followed by one fragment read while any are left and a few expansion
     // instructions.
     constexpr int NMF = (NF - 1) * MI * NI;     // MFMAs after the barrier
-    constexpr int NRA = KB * 4 * MI;            // activation fragment reads
-    constexpr int NVX = NI * (28 * KB);         // expansion instructions
+    constexpr int NRA = BW * 4 * MI;            // activation fragment reads
+    constexpr int NVX = NI * (28 * BW);         // expansion instructions
     constexpr int VPER = (NVX + NMF - 1) / NMF;
     auto step = [&](auto I, int t) {
         constexpr int i = decltype(I)::value;
@@ -327,7 +341,7 @@ __device__ __forceinline__ void gemm32_tile(const int8_t *__restrict__ q,
         read_frags(ic<pp ^ 1>{}, ic<i + 1>{});
         compute_rest(ic<pp>{});
         __builtin_amdgcn_sched_group_barrier(0x020, NG, 0);       // VMEM loads
-        __builtin_amdgcn_sched_group_barrier(0x100, KB * NI, 0);  // packed-weight reads
+        __builtin_amdgcn_sched_group_barrier(0x100, BW * NI, 0);  // packed-weight reads
         unroll_ic([&](auto Kk) {
             constexpr int k = decltype(Kk)::value;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -346,6 +360,44 @@ __device__ __forceinline__ void gemm32_tile(const int8_t *__restrict__ q,
     }, std::make_integer_sequence<int, UNROLL - 1>{});
     // Drain the trailing loads before the workgroup's LDS is released.
     wait_vm_barrier32<0>();
+
+    if constexpr (KG == 2) {
+        // Group 1 hands its accumulators to the group-0 wave of the same
+        // (wm, wn) through the activation ring (free now): per wave MI x NI
+        // x 16 ints a lane, 16-byte lane-contiguous chunks.
+        static_assert(RA >= 2 && MI * NI * 4 * 1024 <= SAP, "hand-off space");
+        int8_t *xa = wt < (WM * WN) / 2 ? a0 : a1;
+        int8_t *xw = xa + (wt % ((WM * WN) / 2)) * (MI * NI * 4 * 1024);
+        static_assert(((WM * WN) / 2) * MI * NI * 4 * 1024 <= SAP && (WM * WN) % 2 == 0,
+                      "hand-off space per buffer");
+        if (kg == 1) {
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const v4i v = {acc[mi][ni][4 * c], acc[mi][ni][4 * c + 1],
+                                       acc[mi][ni][4 * c + 2], acc[mi][ni][4 * c + 3]};
+                        *reinterpret_cast<v4i *>(xw + (((mi * NI + ni) * 4 + c) * 64 + lane) * 16) = v;
+                    }
+        }
+        lds_barrier();
+        if (kg == 1) return;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const v4i v = *reinterpret_cast<const v4i *>(
+                        xw + (((mi * NI + ni) * 4 + c) * 64 + lane) * 16);
+                    acc[mi][ni][4 * c] += v.x;
+                    acc[mi][ni][4 * c + 1] += v.y;
+                    acc[mi][ni][4 * c + 2] += v.z;
+                    acc[mi][ni][4 * c + 3] += v.w;
+                }
+    }
 
     // Epilogue: D(i, j) of tile (mi, ni) in lane j + 32 ((i / 4) % 2),
     // register 4 (i / 8) + i % 4.
@@ -399,9 +451,9 @@ struct G32Batch {
 // (b % 8) * ceil-share + b / 8, so each chiplet works through one
 // contiguous run of tiles (the N tiles of a few row blocks) and its L2
 // holds those rows' activations.
-template <int BM, int BN, int WM, int WN, int KB, int RA, int RB, bool XCD, bool OUT_Y,
+template <int BM, int BN, int WM, int WN, int KB, int RA, int RB, int KG, bool XCD, bool OUT_Y,
           typename YT>
-__global__ __launch_bounds__(WM * WN * 64) void gemm32_group_kernel(int b0, int b1, int b2, int b3,
+__global__ __launch_bounds__(KG * WM * WN * 64) void gemm32_group_kernel(int b0, int b1, int b2, int b3,
                                                                     int b4, int b5, int b6, int b7,
                                                                     G32Batch B) {
     static_assert(kMaxG32 == 8, "one leading argument per problem");
@@ -418,26 +470,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm32_group_kernel(int b0, int 
     const G32Problem P = Bk->p[pi];
     const int t = bx - P.tile_begin;
     const int tm = t / P.ntn, tn = t - tm * P.ntn;
-    gemm32_tile<BM, BN, WM, WN, KB, RA, RB, OUT_Y, YT>(P.q, P.inv, P.qsum, P.packed, P.w_scale, P.M,
+    gemm32_tile<BM, BN, WM, WN, KB, RA, RB, KG, OUT_Y, YT>(P.q, P.inv, P.qsum, P.packed, P.w_scale, P.M,
                                                     P.K, P.N, static_cast<YT *>(P.y), P.acc,
                                                     tm * BM, tn * BN);
 }
 
 struct Shape32 {
-    int BM, BN, WM, WN, KB, RA, RB;
+    int BM, BN, WM, WN, KB, RA, RB, KG;
     bool xcd;
 };
 // Launch-shape table; every entry computes bit-identical results.
 constexpr Shape32 kShapes32[] = {
-    {128, 128, 2, 2, 1, 3, 6, false}, {128, 128, 2, 2, 2, 3, 6, false},
-    {128, 128, 2, 4, 1, 3, 3, false}, {128, 128, 2, 4, 2, 3, 3, false},
-    {128, 128, 2, 2, 1, 3, 3, false}, {128, 256, 2, 4, 1, 3, 6, false},
-    {128, 128, 2, 2, 2, 2, 4, false}, {64, 128, 2, 2, 1, 3, 6, false},
-    {128, 128, 2, 2, 2, 3, 6, true},  {128, 128, 2, 2, 1, 4, 4, false},
-    {128, 256, 2, 4, 1, 3, 6, true},  {64, 128, 2, 2, 2, 3, 6, false}};
+    {128, 128, 2, 2, 1, 3, 6, 1, false}, {128, 128, 2, 2, 2, 3, 6, 1, false},
+    {128, 128, 2, 4, 1, 3, 3, 1, false}, {128, 128, 2, 4, 2, 3, 3, 1, false},
+    {128, 128, 2, 2, 1, 3, 3, 1, false}, {128, 256, 2, 4, 1, 3, 6, 1, false},
+    {128, 128, 2, 2, 2, 2, 4, 1, false}, {64, 128, 2, 2, 1, 3, 6, 1, false},
+    {128, 128, 2, 2, 2, 3, 6, 1, true},  {128, 128, 2, 2, 1, 4, 4, 1, false},
+    {128, 256, 2, 4, 1, 3, 6, 1, true},  {64, 128, 2, 2, 2, 3, 6, 1, false},
+    {128, 128, 2, 2, 2, 3, 3, 2, false}};
 constexpr int kNumShapes32 = sizeof(kShapes32) / sizeof(kShapes32[0]);
 
-template <int BM, int BN, int WM, int WN, int KB, int RA, int RB, bool XCD>
+template <int BM, int BN, int WM, int WN, int KB, int RA, int RB, int KG, bool XCD>
 hipError_t launch_g32(const GemmDesc *d, int count, hipStream_t s) {
     G32Batch B{};
     int begin[kMaxG32];
@@ -463,10 +516,11 @@ hipError_t launch_g32(const GemmDesc *d, int count, hipStream_t s) {
         if (total > INT32_MAX) return hipErrorInvalidConfiguration;
     }
     for (int i = count; i < kMaxG32; ++i) begin[i] = INT32_MAX;
-    const dim3 grid((unsigned)total), block(WM * WN * 64);
+    const dim3 grid((unsigned)total), block(KG * WM * WN * 64);
     const int io = d[0].io;
 #define BL_G32(OY, YT)                                                                            \
-    hipLaunchKernelGGL((gemm32_group_kernel<BM, BN, WM, WN, KB, RA, RB, XCD, OY, YT>), grid, block, \
+    hipLaunchKernelGGL((gemm32_group_kernel<BM, BN, WM, WN, KB, RA, RB, KG, XCD, OY, YT>), grid,    \
+                       block,                                                                     \
                        0,                                                                         \
                        s,                                                                        \
                        begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],     \
@@ -499,6 +553,14 @@ constexpr int kAutoShape32 = 3;
 // activation traffic and wins (K = N = 8192 at M = 2048: 113-118 against
 // 126-130 us).
 constexpr int kWideShape32 = 6;
+// With at most one 128 x 128 tile per CU (every K a whole number of 256-k
+// steps), the two k groups of 4 waves, each wave a 64 x 64 tile over its
+// own block of every step: 44 % fewer LDS fragment reads per k than the
+// 64 x 32 waves (K = N = 8192 at M = 512: 43-44.6 against 45-46.7 us per
+// forward).  With more tiles its 121 KB of LDS (one workgroup per CU)
+// loses to the 72 KB shape's two (prefill layer, 712 tiles: 74 against
+// 68 us).
+constexpr int kSplitShape32 = 13;
 
 bool gemm32_preferred(const GemmDesc *d, int count) {
     int64_t tiles = 0;
@@ -517,9 +579,16 @@ hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStrea
             return hipErrorInvalidValue;
     int v = shape;
     if (v <= 0 || v > kNumShapes32) {
-        int64_t wide = 0;
-        for (int i = 0; i < count; ++i) wide += ((d[i].M + 127) / 128) * ((d[i].N + 255) / 256);
-        v = wide >= 512 ? kWideShape32 : kAutoShape32;
+        int64_t wide = 0, tiles = 0;
+        bool even = true;
+        for (int i = 0; i < count; ++i) {
+            wide += ((d[i].M + 127) / 128) * ((d[i].N + 255) / 256);
+            tiles += ((d[i].M + 127) / 128) * ((d[i].N + 127) / 128);
+            even = even && d[i].K % (2 * kBlk) == 0;
+        }
+        v = wide >= 512 ? kWideShape32
+            : (even && tiles <= device_cus()) ? kSplitShape32
+                                              : kAutoShape32;
     }
     // Two blocks per step need an even block count in every row.
     if (kShapes32[v - 1].KB == 2)
@@ -529,7 +598,8 @@ hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStrea
     case idx:                                                                                 \
         return launch_g32<kShapes32[idx - 1].BM, kShapes32[idx - 1].BN, kShapes32[idx - 1].WM, \
                           kShapes32[idx - 1].WN, kShapes32[idx - 1].KB, kShapes32[idx - 1].RA, \
-                          kShapes32[idx - 1].RB, kShapes32[idx - 1].xcd>(d, count, s);
+                          kShapes32[idx - 1].RB, kShapes32[idx - 1].KG,                       \
+                          kShapes32[idx - 1].xcd>(d, count, s);
     switch (v) {
         BL_SHAPE32(1)
         BL_SHAPE32(2)
@@ -543,6 +613,7 @@ hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStrea
         BL_SHAPE32(10)
         BL_SHAPE32(11)
         BL_SHAPE32(12)
+        BL_SHAPE32(13)
         default:
             return hipErrorInvalidValue;
     }

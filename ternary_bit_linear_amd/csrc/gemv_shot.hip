@@ -803,6 +803,8 @@ constexpr ShotShape kShotShapes[] = {{3, 1, 4, 4}, {4, 1, 4, 4}, {8, 1, 4, 4}, {
 constexpr int kNumShotShapes = sizeof(kShotShapes) / sizeof(kShotShapes[0]);
 static_assert(kNumShotShapes == kShotShapeCount, "shape count the variant numbering uses");
 
+}  // namespace
+
 // Compute units of the current device, looked up once per device (the
 // launch-shape choice runs on every call).  Devices beyond the table are
 // queried each time.
@@ -821,6 +823,8 @@ int device_cus() {
     if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
+
+namespace {
 
 // Launch-shape choice.  A shape costs (in this order): the rounds of
 // workgroups the device needs to hold them all (resident workgroups per CU
