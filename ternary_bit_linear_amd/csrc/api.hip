@@ -150,14 +150,18 @@ bl::FusedDecode fused_of(const bl_forward_desc &d) {
 // Whether a validated forward takes the fused decode kernel.  Automatic
 // choice: fused for one token (rows up to 32768: the one-shot kernel holds
 // rows up to 8192 in the registers of its 256-thread quantisation, the
-// rolling kernel rows up to 32768 in those of its 1024 threads); for more
-// tokens the separate quantisation kernel is faster (measured on MI355X).
+// rolling kernel rows up to 32768 in those of its 1024 threads), and for 2
+// or 3 tokens with rows up to 8192 (their sets go out fused when the
+// one-shot kernel's 16-wave shape holds them in one round, else as the
+// separate quantisation + contraction pair; measured on MI355X).
 bool takes_fused(const bl_forward_desc &d, const bl_launch *launch) {
     const bool gemv = route_of(d.M, launch) == BL_PATH_GEMV;
     const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
     if (launch && launch->fuse == 0) return false;
     if (launch && launch->fuse == 1) return gemv && fits;
-    return gemv && fits && d.M == 1 && (d.K <= 8 * 1024 || bl::roll_fused_supported(d.M, d.K));
+    if (d.M == 1) return gemv && fits && (d.K <= 8 * 1024 || bl::roll_fused_supported(d.M, d.K));
+    return gemv && fits && d.M <= bl::kFewFusedMaxM && d.K <= 8 * 1024 &&
+           bl::shot_fused_supported(d.M, d.K);
 }
 
 
@@ -666,7 +670,12 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
     const bl_forward_desc gu[2] = {
         {d.x, d.packed_gate, d.s_gate, d.gamma_in, d.eps, M, H, F, w.g, w.ws_gate, w.b_gate},
         {d.x, d.packed_up, d.s_up, d.gamma_in, d.eps, M, H, F, w.u, w.ws_up, w.b_gate}};
-    if (!takes_fused(gu[0], nullptr) && takes_shot_batch(gu[0], nullptr)) {
+    // (A few tokens take the fused kernel only where its 16-wave shape
+    // holds gate and up in one round; else x is quantised once below.)
+    const int64_t gM[2] = {M, M}, gK[2] = {H, H}, gN[2] = {F, F};
+    const bool fuse_gu = takes_fused(gu[0], nullptr) &&
+                         (M == 1 || bl::few_fused_one_round(gM, gK, gN, 2));
+    if (!fuse_gu && takes_shot_batch(gu[0], nullptr)) {
         // A few tokens: x is quantised once (into the gate's workspace) and
         // both contractions read that q in one one-shot launch.
         const Workspace wq = carve(w.ws_gate, M, H);
@@ -677,7 +686,7 @@ bl_status bitlinear_ffn_forward(const bl_ffn_desc *desc, void *stream) {
         if (bl::launch_act_quant_batch(&aq, 1, s) != hipSuccess ||
             bl::launch_gemv_shot_auto(sd, 2, s) != hipSuccess)
             return BL_ERR_HIP;
-    } else if (!takes_fused(gu[0], nullptr) && takes_group(gu[0], nullptr)) {
+    } else if (!fuse_gu && takes_group(gu[0], nullptr)) {
         // Prefill: x is quantised once (into the gate's workspace) and both
         // contractions read that q in one grouped tile launch.
         const Workspace wq = carve(w.ws_gate, M, H);

@@ -376,7 +376,7 @@ __device__ __forceinline__ void quad_meet(QuadSpin *spin) {
 // (g0 + g1) + (g2 + g3).
 __device__ __forceinline__ float block_sumsq_finish(float p, float *red,
                                                    QuadSpin *spin = nullptr) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wid = (threadIdx.x >> 6) & 3;
     p = wave_tree_sum_f(p);
     if (lane == 0) red[wid] = p;
     quad_meet(spin);
@@ -384,7 +384,7 @@ __device__ __forceinline__ float block_sumsq_finish(float p, float *red,
 }
 
 __device__ __forceinline__ float block_max(float v, float *red, QuadSpin *spin = nullptr) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wid = (threadIdx.x >> 6) & 3;
     v = wave_max(v);
     if (lane == 0) red[wid] = v;
     quad_meet(spin);
@@ -461,8 +461,8 @@ template <class Sink>
 __device__ __forceinline__ void finish_row(Sink &sink, float inv, int qs, float *red) {
     if constexpr (Sink::kDeferSum) {
         qs = wave_sum_int(qs);
-        if ((threadIdx.x & 63) == 0) sink.store_qsum_part((int)(threadIdx.x >> 6), qs);
-        if (threadIdx.x == 0) sink.store_inv(inv);
+        if ((threadIdx.x & 63) == 0) sink.store_qsum_part((int)(threadIdx.x >> 6) & 3, qs);
+        if ((threadIdx.x & 255) == 0) sink.store_inv(inv);
     } else {
         qs = block_sum_int(qs, red + 8);
         if (threadIdx.x == 0) sink.store_row(inv, qs);
@@ -490,7 +490,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
                                                     QuadSpin *spin = nullptr) {
     static_assert(!GLU || std::is_same<XT, float>::value, "the gated input is fp32");
     constexpr uint32_t XB = kXBytes<XT>;
-    const int t4 = 4 * threadIdx.x;
+    const int t4 = 4 * (threadIdx.x & 255);
     constexpr int STRIDE = 1024;
     if constexpr (!LONG) {  // K <= 1024 * CH
         const bool norm = gamma != nullptr;
@@ -498,7 +498,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
         const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
         const auto rg = gamma_rsrc(gamma, K);
         float4 xv[CH], gv[CH], uv[GLU ? CH : 1];
-        const int wk = 256 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        const int wk = 256 * __builtin_amdgcn_readfirstlane(((int)threadIdx.x >> 6) & 3);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int k = t4 + STRIDE * i;
@@ -878,6 +878,13 @@ hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream
 // flight; the first workgroup of each problem also writes q / inv / qsum.
 bool shot_fused_supported(int64_t M, int64_t K);
 hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hipStream_t s);
+// A few tokens (up to kFewFusedMaxM) with the quantisation fused in: the
+// one-shot launch shape whose workgroups quantise their rows in parallel
+// groups of four waves.  Whether every problem has M <= kFewFusedMaxM rows
+// of K <= 8192 (in registers) and that shape holds the set in one round.
+constexpr int64_t kFewFusedMaxM = 3;
+constexpr int kFewFusedShapeVariant = 8;  // the `shape` launch_gemv_shot_fused takes for it
+bool few_fused_one_round(const int64_t *M, const int64_t *K, const int64_t *N, int count);
 // Rolling form of the one-shot contraction (each wave streams its weights
 // through a small register ring), for problem sets the device does not hold
 // in one round: q from global memory (M <= 8, M * K <= kShotMaxQ), or fused

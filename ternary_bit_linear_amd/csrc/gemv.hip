@@ -903,6 +903,43 @@ hipError_t launch_gemv_fused(const FusedDecode *d, int count, int variant, hipSt
             N[i] = d[i].N;
         }
     }
+    // A few tokens (some problem with 2..kFewFusedMaxM rows): the one-shot
+    // form whose quads quantise rows side by side, when it holds the set in
+    // one round; else the one-token problems go out fused on their own and
+    // the others as the batched quantisation + one-shot / rolling pair.
+    int64_t mmax = 0;
+    for (int i = 0; i < count && i < 8; ++i) mmax = std::max<int64_t>(mmax, d[i].M);
+    if (variant == 0 && mmax >= 2 && count <= 8 && !glu) {
+        bool all_f32 = true;
+        for (int i = 0; i < count; ++i) all_f32 = all_f32 && d[i].io == kIoF32;
+        if (all_f32 && few_fused_one_round(M, K, N, count))
+            return launch_gemv_shot_fused(d, count, kFewFusedShapeVariant, s);
+        bool pairable = all_f32 && mmax <= kFewFusedMaxM;
+        for (int i = 0; i < count; ++i)
+            pairable = pairable && (d[i].M == 1 || (d[i].K <= kActQuantBatchMaxK &&
+                                                    shot_supported(d[i].M, d[i].K)));
+        if (pairable) {
+            FusedDecode one[8];
+            ActQuantDesc aq[8];
+            ShotDecode sd[8];
+            int n1 = 0, n2 = 0;
+            for (int i = 0; i < count; ++i) {
+                const FusedDecode &f = d[i];
+                if (f.M == 1) {
+                    one[n1++] = f;
+                } else {
+                    aq[n2] = ActQuantDesc{f.x, f.gamma, f.eps, f.M, f.K, f.q, f.inv, f.qsum};
+                    sd[n2] = ShotDecode{f.q, f.inv, f.qsum, f.packed, f.y, nullptr, f.w_scale,
+                                        f.M, f.K, f.N};
+                    ++n2;
+                }
+            }
+            if (n1 > 0)
+                if (hipError_t e = launch_gemv_fused(one, n1, 0, s)) return e;
+            if (hipError_t e = launch_act_quant_batch(aq, n2, s)) return e;
+            return launch_gemv_shot_auto(sd, n2, s);
+        }
+    }
     // Automatic: the one-shot form when all of its workgroups fit on the
     // device at once and every row is held in registers by the block form
     // (K <= 8192); else, one token per problem, the rolling form (its

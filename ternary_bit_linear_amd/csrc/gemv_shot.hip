@@ -141,7 +141,7 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
         w2[NB > 2 ? W : 1][NB > 2 ? SZ : 16], w3[NB > 3 ? W : 1][NB > 3 ? SZ : 16],
         w4[NB > 4 ? W : 1][NB > 4 ? SZ : 16], w5[NB > 5 ? W : 1][NB > 5 ? SZ : 16],
         w6[NB > 6 ? W : 1][NB > 6 ? SZ : 16], w7[NB > 7 ? W : 1][NB > 7 ? SZ : 16];
-    __shared__ float red[kRedWords];
+    __shared__ float red[kRedWords * (W > 4 ? W / 4 : 1)];  // one block per quad
     __shared__ float inv_sh[FM > 0 ? FM : 1];
     __shared__ int qpart_sh[FM > 0 ? FM : 1][4];  // per-wave partial sums of q
 
@@ -249,45 +249,55 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
         //    latency instead of after the weights queued before them;
         // 2. RMSNorm + quantisation of every row into LDS while the weights
         //    stream in.
-        constexpr bool kLate = W > 4;  // waves 0..3: weights after the quantisation
+        constexpr bool kLate = W > 4;  // quantising waves: weights after the quantisation
         constexpr bool kSync = !LONG;
-        // In a larger workgroup (rows held in registers) the four quantising
-        // waves meet on an LDS counter instead of workgroup barriers, so the
-        // other waves -- which may stall at the issue of their weights --
-        // never hold the quantisation up.
+        // In a larger workgroup (rows held in registers) each group of four
+        // waves (a quad) quantises its own rows -- quad j rows j, j + W / 4,
+        // ... -- its waves meeting on an LDS counter of their own instead of
+        // workgroup barriers: the other waves, which may stall at the issue
+        // of their weights, never hold a quantisation up, and the rows of a
+        // few-token block are normalised side by side.  Otherwise waves 0..3
+        // quantise every row in turn.
         constexpr bool kSpin = kSync && W > 4;
-        __shared__ int spin_sh;
+        constexpr int Q = kSpin ? W / 4 : 1;  // quads quantising rows
+        const int quad = kSpin ? (wid >> 2) : 0;
+        const int rows = min(M, FM);
+        const bool quantises = kSpin ? quad < rows : (W == 4 || wid < 4);
+        __shared__ int spin_sh[Q];
         if constexpr (kSpin) {
             // Zero, and visible to every wave past the first barrier below.
-            if (tid == 0) spin_sh = 0;
+            if (tid < Q) spin_sh[tid] = 0;
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         }
-        QuadSpin meet{&spin_sh, 0};
+        QuadSpin meet{&spin_sh[quad], 0};
         QuadSpin *const spin = kSpin ? &meet : nullptr;
-        if (W == 4 || wid < 4) {
+        float *const qred = red + quad * kRedWords;
+        if (quantises) {
             {
-                ShotRowSink sink{q_lds, inv_sh, qpart_sh[0], st == 0 ? P.q_out : nullptr,
-                                 P.inv_out};
+                const int m = quad;
+                ShotRowSink sink{q_lds + m * K, inv_sh + m, qpart_sh[m],
+                                 st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m};
                 auto hook = [&] {
                     if constexpr (!kLate) issue_weights();
                 };
-                block_act_quant_row<CH, LONG, kSync, GLU, IO>(reinterpret_cast<const IO *>(P.x),
-                                                              P.gamma, P.eps, K, red, sink, hook,
-                                                              P.u, spin);
+                block_act_quant_row<CH, LONG, kSync, GLU, IO>(
+                    reinterpret_cast<const IO *>(P.x) + (size_t)m * K, P.gamma, P.eps, K, qred,
+                    sink, hook, GLU ? P.u + (size_t)m * K : nullptr, spin);
             }
 #pragma unroll
-            for (int m = 1; m < FM; ++m) {
-                if (m < M) {
+            for (int i = 1; i < (FM + Q - 1) / Q; ++i) {
+                const int m = quad + Q * i;
+                if (m < rows) {
                     ShotRowSink sink{q_lds + m * K, inv_sh + m, qpart_sh[m],
                                      st == 0 ? P.q_out + (size_t)m * K : nullptr, P.inv_out + m};
                     block_act_quant_row<CH, LONG, false, GLU, IO>(
                         reinterpret_cast<const IO *>(P.x) + (size_t)m * K, P.gamma, P.eps, K,
-                        red, sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr, spin);
+                        qred, sink, [] {}, GLU ? P.u + (size_t)m * K : nullptr, spin);
                 }
             }
         } else {
-            // Waves 4..W-1: the barrier behind the first row's x / gamma
+            // The other waves: the barrier behind the first rows' x / gamma
             // loads and their weights; with streamed rows also the barriers
             // of each row's block form.
             if constexpr (kSync) __builtin_amdgcn_s_barrier();
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(64 * W) void gemv_shot_kernel(int b0, int b1, int b
         // only now, past the barrier that publishes q: an issue that stalls
         // then delays only their own contraction.
         if constexpr (kLate)
-            if (wid < 4) issue_weights();
+            if (quantises) issue_weights();
         // The problem's first workgroup also stores the rows' activation
         // sums (the partials are visible after the barrier).
         if (st == 0 && tid < M && tid < FM)
@@ -1065,6 +1075,28 @@ bool shot_supported(int64_t M, int64_t K) {
 
 bool shot_fused_supported(int64_t M, int64_t K) {
     return M >= 1 && M <= kFuseMaxM && M * K <= kShotFusedMaxQ && shot_ks(K, 8) != 0;
+}
+
+// The 16-wave shape: four quads quantise up to four rows side by side.
+// Measured on MI355X with the quantisation fused in, against the separate
+// quantisation + contraction pair (us, M = 2 / 3): decoder layer 8.1 / 9.6
+// against 10.5 / 11.8; K = N = 8192 8.4 / 10.2 against 9.7 / 10.0; three
+// 4096 x 4096 BitLinears 7.0 / 8.4 against 8.7 / 9.0.  At M = 4 every wave
+// quantises and all weights go out after it: slower on two of the three
+// (12.1 against 10.5 us at K = N = 8192), so the pair keeps M = 4.  The
+// 8-wave shapes measured slower than this one on all three.
+constexpr int kFewTokenShape = 7;
+static_assert(kShotShapes[kFewTokenShape].w == 16, "four quads");
+static_assert(kFewFusedShapeVariant == kFewTokenShape + 1, "shape numbering of launch_gemv_shot_fused");
+
+bool few_fused_one_round(const int64_t *M, const int64_t *K, const int64_t *N, int count) {
+    if (count < 1 || count > kMaxShotBatch) return false;
+    for (int i = 0; i < count; ++i)
+        if (M[i] < 1 || M[i] > kFewFusedMaxM || K[i] > 8192 || !shot_fused_supported(M[i], K[i]))
+            return false;
+    int64_t rounds = 0;
+    return pick_shape(M, K, N, count, kFewTokenShape + 1, &rounds, true) == kFewTokenShape &&
+           rounds == 1;
 }
 
 hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream_t s) {

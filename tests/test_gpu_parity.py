@@ -816,10 +816,12 @@ def ffn_case(seed, M, H, F, norm=True):
 # (M, H, F, norm): M = 1 with F <= 8192 takes the two-launch form (the down
 # projection's quantisation inside the one-shot kernel); F > 8192 and M > 1
 # take the separate gated quantisation; M <= 8 with M * H and M * F up to
-# 64 KB the one-shot kernel for all three projections; M = 64 the tile
-# kernel.
+# 64 KB the one-shot kernel for all three projections (M = 2, 3: gate and up
+# with the quantisation fused in, groups of four waves per row); M = 64 the
+# tile kernel.
 FFN_SHAPES = [(1, 2560, 6912, True), (1, 256, 384, False), (1, 1024, 9216, True),
-              (3, 512, 1280, True), (8, 2560, 6912, True), (6, 1024, 2816, False),
+              (3, 512, 1280, True), (2, 2560, 6912, True), (8, 2560, 6912, True),
+              (6, 1024, 2816, False),
               (17, 256, 384, True), (64, 1024, 2816, True), (64, 256, 640, False)]
 
 
@@ -1286,6 +1288,47 @@ def test_few_token_batches(torch, bl, orc, M):
             assert np.array_equal(host(it[5]).view(np.uint32), ref.view(np.uint32))
         else:
             assert np.array_equal(bits16(torch, it[5]), np.asarray(ref).view(np.uint16))
+
+
+# Few-token sets with the quantisation fused in: (M, K, N) per problem.  The
+# first set fits the 16-wave one-shot shape in one round (groups of four
+# waves quantise the rows of 2- and 3-token problems side by side, beside a
+# one-token problem); the second needs two rounds, so its one-token problem
+# goes out fused alone and the others as the batched quantisation +
+# contraction pair.
+FEW_FUSED_SETS = [
+    [(1, 2560, 2560), (2, 2560, 640), (3, 6912, 2560), (2, 1024, 1000)],
+    [(1, 2560, 2560), (2, 2560, 20480), (2, 4096, 16384), (3, 512, 72)],
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(len(FEW_FUSED_SETS)))
+def test_few_token_fused_sets(torch, bl, orc, case):
+    """Automatic forward_batch over a few-token set: every y the oracle's
+    (fp32 within 1e-5, NaN-prefilled so an unwritten output fails), each
+    workspace holding the oracle's q / inv / qsum, and each output equal to
+    its single forward."""
+    items, refs, aqs, singles = [], [], [], []
+    for i, (M, K, N) in enumerate(FEW_FUSED_SETS[case]):
+        x, w, t, g = mm_case(M, K, N, 2100 + 10 * case + i)
+        packed_r, s = orc.pack_i2s(w)
+        X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
+        out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        items.append((X, P, s, G, 1e-6, out, bl.new_workspace(M, K)))
+        refs.append(orc.forward(x, packed_r, s, g, 1e-6, N))
+        aqs.append(orc.act_quant(x, g, 1e-6))
+        singles.append(host(bl.forward(X, P, s, G, 1e-6, N)).copy())
+    announce("few-token fused set", case)
+    bl.forward_batch(items)
+    torch.cuda.synchronize()
+    for it, ref, (q_r, inv_r, qs_r), single, (M, K, N) in zip(items, refs, aqs, singles,
+                                                               FEW_FUSED_SETS[case]):
+        check_y(host(it[5]), ref)
+        assert np.array_equal(host(it[5]), single)
+        q, inv, qs = bl.workspace_views(it[6], M, K)
+        assert np.array_equal(host(q), q_r) and np.array_equal(host(inv), inv_r)
+        assert np.array_equal(host(qs), qs_r)
 
 
 # ---------------------------------------------------------------- dequantisation
