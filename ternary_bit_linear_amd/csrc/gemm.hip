@@ -368,8 +368,14 @@ hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
     int begin[kMaxGroup];
     int64_t total = 0;
     const bool y = d[0].y != nullptr;
-    for (int i = 0; i < count; ++i) {
-        GroupProblem &P = B.p[i];
+    // Problems in order of decreasing K (stable): the longest tiles are
+    // dispatched first, the short ones fill in behind them.
+    int order[kMaxGroup];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order, order + count, [&](int a, int b) { return d[a].K > d[b].K; });
+    for (int j = 0; j < count; ++j) {
+        const int i = order[j];
+        GroupProblem &P = B.p[j];
         P.q = d[i].q;
         P.inv = d[i].inv;
         P.qsum = d[i].qsum;
@@ -383,7 +389,7 @@ hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
         const int64_t ntn = (d[i].N + BN - 1) / BN, ntm = (d[i].M + BM - 1) / BM;
         P.ntn = (int)ntn;
         P.tile_begin = (int)total;
-        begin[i] = (int)total;
+        begin[j] = (int)total;
         total += ntn * ntm;
         if (total > INT32_MAX) return hipErrorInvalidConfiguration;
     }

@@ -46,6 +46,7 @@
 // LDS layouts (bank-conflict-free 16-byte reads of 16 lanes): activation
 // row r (128 bytes, chunk c = 2 g + h) keeps chunk c at c ^ ((r >> 1) & 7);
 // weight row r (32 bytes, half h) keeps half h at h ^ ((r >> 3) & 1).
+#include <algorithm>
 #include <climits>
 
 #include "common.hpp"
@@ -496,8 +497,16 @@ hipError_t launch_g32(const GemmDesc *d, int count, hipStream_t s) {
     int begin[kMaxG32];
     int64_t total = 0;
     const bool y = d[0].y != nullptr;
-    for (int i = 0; i < count; ++i) {
-        G32Problem &P = B.p[i];
+    // Problems in order of decreasing K (stable): workgroups are dispatched
+    // in index order, so the longest tiles start first and the short ones
+    // fill in behind them, instead of the longest starting last (the
+    // prefill layer's K = 6912 down projection behind six K = 2560 ones).
+    int order[kMaxG32];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order, order + count, [&](int a, int b) { return d[a].K > d[b].K; });
+    for (int j = 0; j < count; ++j) {
+        const int i = order[j];
+        G32Problem &P = B.p[j];
         P.q = d[i].q;
         P.inv = d[i].inv;
         P.qsum = d[i].qsum;
@@ -511,7 +520,7 @@ hipError_t launch_g32(const GemmDesc *d, int count, hipStream_t s) {
         const int64_t ntn = (d[i].N + BN - 1) / BN, ntm = (d[i].M + BM - 1) / BM;
         P.ntn = (int)ntn;
         P.tile_begin = (int)total;
-        begin[i] = (int)total;
+        begin[j] = (int)total;
         total += ntn * ntm;
         if (total > INT32_MAX) return hipErrorInvalidConfiguration;
     }
