@@ -196,6 +196,37 @@ __device__ __forceinline__ float4 load_x4<_Float16>(__amdgpu_buffer_rsrc_t r, ui
                        f16_low_to_f32(v.y >> 16));
 }
 
+// The same in two parts: the raw words of the four values (out of range:
+// zeros), and their widening.  A caller that issues several loads before
+// using any widens them only afterwards: a widening placed right behind its
+// load makes the compiler wait for that load before the next one goes out.
+template <typename XT>
+struct XRaw {
+    typedef v2u type;  // two words of two half-precision values each
+};
+template <>
+struct XRaw<float> {
+    typedef float4 type;
+};
+template <typename XT>
+__device__ __forceinline__ typename XRaw<XT>::type load_x_raw(__amdgpu_buffer_rsrc_t r,
+                                                              uint32_t off) {
+    if constexpr (std::is_same<XT, float>::value) return buf_load_f4(r, off);
+    else return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+template <typename XT>
+__device__ __forceinline__ float4 widen_x(const typename XRaw<XT>::type &v) {
+    if constexpr (std::is_same<XT, float>::value) {
+        return v;
+    } else if constexpr (std::is_same<XT, bf16_t>::value) {
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+    } else {
+        return make_float4(f16_low_to_f32(v.x), f16_low_to_f32(v.x >> 16), f16_low_to_f32(v.y),
+                           f16_low_to_f32(v.y >> 16));
+    }
+}
+
 // fp32 -> bf16 bits, nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -498,6 +529,7 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
         const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
         const auto rg = gamma_rsrc(gamma, K);
         float4 xv[CH], gv[CH], uv[GLU ? CH : 1];
+        typename XRaw<XT>::type xr[CH];
         const int wk = 256 * __builtin_amdgcn_readfirstlane(((int)threadIdx.x >> 6) & 3);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
@@ -508,8 +540,16 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
             const uint32_t off = 4u * (uint32_t)k;
             // Chunks wholly past K (wave-uniform) are never read below: no
             // load and no initialisation.
-            if (STRIDE * i + wk < K) {
-                xv[i] = load_x4<XT>(rx, XB * (uint32_t)k);
+            const bool live = STRIDE * i + wk < K;
+            // Half-precision words are loaded for every chunk (a chunk past
+            // K at an offset outside the resource: zeros), so no branch
+            // leaves them to be merged -- the merge would copy them, and
+            // wait for each load before the next goes out.
+            if constexpr (!std::is_same<XT, float>::value)
+                xr[i] = load_x_raw<XT>(rx, live ? XB * (uint32_t)k : kOOB);
+            if (live) {
+                if constexpr (std::is_same<XT, float>::value)
+                    xr[i] = load_x_raw<XT>(rx, XB * (uint32_t)k);
                 if constexpr (GLU) uv[i] = buf_load_f4(ru, off);
                 gv[i] = gamma_f4(rg, off, norm);
             }
@@ -518,6 +558,11 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
         // issues, so they do not queue behind another wave's weight misses.
         if constexpr (SYNC) __builtin_amdgcn_s_barrier();
         issued();
+        // Half-precision x is widened only now, behind every load.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            if (STRIDE * i + wk < K) xv[i] = widen_x<XT>(xr[i]);
         if constexpr (GLU) {
 #pragma unroll
             for (int i = 0; i < CH; ++i)
