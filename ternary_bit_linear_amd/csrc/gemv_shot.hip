@@ -654,6 +654,34 @@ __global__ __launch_bounds__(64 * W) void gemv_roll_kernel(int b0, int b1, int b
         prologue();
         wait_vmcnt<ND * R * kU>();
         lds_barrier();
+    } else if constexpr (SQ <= 2) {
+        // Rows of up to 8192: waves 0..3 quantise the row in the 256-thread
+        // block form (its reductions meeting on an LDS counter among the
+        // four), the other waves issue their rings at once, behind the
+        // barrier that puts the x / gamma loads first, and the quantising
+        // waves issue theirs once q is published, so that their issue
+        // stalls never hold the quantisation up.
+        __shared__ int spin_sh;
+        if (tid < 16) qpart_sh[tid] = 0;  // waves 4..15 add no partial sum
+        if (tid == 0) spin_sh = 0;
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): visible past the barrier below
+        QuadSpin meet{&spin_sh, 0};
+        if (wid < 4) {
+            ShotRowSink sink{q_lds, inv_sh, qpart_sh, st == 0 ? P.q_out : nullptr, P.inv_out};
+            block_act_quant_row<8, false, true, GLU, float>(P.x, P.gamma, P.eps, K, red, sink,
+                                                            [] {}, P.u, &meet);
+        } else {
+            __builtin_amdgcn_s_barrier();  // behind the x / gamma loads
+            prologue();
+        }
+        lds_barrier();
+        if (wid < 4) prologue();
+        if (st == 0 && tid == 0) {
+            int t = 0;
+            for (int w = 0; w < 16; ++w) t += qpart_sh[w];
+            P.qsum_out[0] = t;
+        }
     } else {
         // The whole row of x and gamma over all 16 waves (one round trip,
         // ahead of every weight load of the workgroup), then the ring's
