@@ -10,8 +10,10 @@
 // barrier).  Longer rows: one 256-thread block per row (block_act_quant_row)
 // holding the whole row of x and gamma in registers -- CH float4 of each per
 // thread, CH picked from K -- so every row is read with a single round trip
-// of fully issued loads.  HBM traffic per row: 4K (x) + 4K (gamma, L2-
-// resident after the first rows) + K (q) + 8 bytes.
+// of fully issued loads.  Rows of 8193..32768 in launches of no more rows
+// than CUs: one 1024-thread block per row (wide_act_quant_row, the same
+// codes).  HBM traffic per row: 4K (x) + 4K (gamma, L2-resident after the
+// first rows) + K (q) + 8 bytes.
 #include <algorithm>
 #include <climits>
 
@@ -63,6 +65,30 @@ __global__ __launch_bounds__(256) void act_quant_long_kernel(
     GlobalRowSink sink{q + (size_t)m * K, inv + m, qsum + m};
     block_act_quant_row<8, true, true, false, XT>(x + (size_t)m * K, gamma, eps, K, red, sink,
                                                   [] {});
+}
+
+// One 1024-thread block per token row (fp32 x), through wide_act_quant_row:
+// the same codes as the 256-thread form with a quarter of its serial work
+// per thread, for long rows in launches with no more rows than CUs (every
+// row has a CU to itself, and the row's chain of dependent VALU work is the
+// launch's critical path).  qsum: the sixteen per-wave code sums, order-free.
+template <int SQ>
+__global__ __launch_bounds__(1024) void act_quant_wide_kernel(
+    const float *__restrict__ x, const float *__restrict__ gamma, float eps, int K,
+    int8_t *__restrict__ q, float *__restrict__ inv, int32_t *__restrict__ qsum) {
+    __shared__ float red[20];
+    __shared__ float chain[256];
+    __shared__ int qpart[16];
+    __shared__ float inv_sh;
+    const int m = blockIdx.x;
+    wide_act_quant_row<SQ, false, false>(x + (size_t)m * K, gamma, eps, K, red, chain, nullptr,
+                                         q + (size_t)m * K, &inv_sh, inv + m, qpart, [] {});
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        int t = 0;
+        for (int w = 0; w < 16; ++w) t += qpart[w];
+        qsum[m] = t;
+    }
 }
 
 // y[m][n] = (float)acc[m][n] * (w_scale / inv[m]) rounded to the output
@@ -164,6 +190,23 @@ __global__ __launch_bounds__(256) void act_quant_batch_kernel(int b0, int b1, in
                                                     P.gamma, P.eps, K, red, sink, [] {});
 }
 
+template <int SQ>
+hipError_t launch_wide(const float *x, const float *gamma, float eps, int64_t M, int64_t K,
+                       int8_t *q, float *inv, int32_t *qsum, hipStream_t s) {
+    hipLaunchKernelGGL((act_quant_wide_kernel<SQ>), dim3((unsigned)M), dim3(1024), 0, s, x, gamma,
+                       eps, (int)K, q, inv, qsum);
+    return hipGetLastError();
+}
+
+// Whether M rows of K take the 1024-thread form: fp32 rows of 8193..32768,
+// no more rows than CUs.  There the 256-thread form's per-thread chain is
+// 9-32 float4 groups long (70B FFN down projection, K = 28672, M = 16:
+// 32.6 -> 31.9 us per forward).  Up to K = 8192 the two forms measured the
+// same (K = N = 8192 at M = 4 / 16 / 64), the launch itself dominating.
+bool wide_rows(int64_t rows, int64_t K) {
+    return K > 8 * 1024 && K <= 32 * 1024 && rows <= device_cus();
+}
+
 template <int CH, typename XT>
 hipError_t launch_block(const XT *x, const float *gamma, float eps, int64_t M, int64_t K,
                         int8_t *q, float *inv, int32_t *qsum, hipStream_t s) {
@@ -179,6 +222,12 @@ hipError_t launch_act_quant_t(const XT *x, const float *gamma, float eps, int64_
         hipLaunchKernelGGL((act_quant_wave_kernel<XT>), dim3((unsigned)M), dim3(64), 0, s, x,
                            gamma, eps, (int)K, q, inv, qsum);
         return hipGetLastError();
+    }
+    if constexpr (std::is_same<XT, float>::value) {
+        if (wide_rows(M, K)) {
+            if (K <= 16 * 1024) return launch_wide<4>(x, gamma, eps, M, K, q, inv, qsum, s);
+            return launch_wide<8>(x, gamma, eps, M, K, q, inv, qsum, s);
+        }
     }
     if (K <= 4 * 1024) return launch_block<4>(x, gamma, eps, M, K, q, inv, qsum, s);
     if (K <= 8 * 1024) return launch_block<8>(x, gamma, eps, M, K, q, inv, qsum, s);

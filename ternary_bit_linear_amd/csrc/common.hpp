@@ -691,6 +691,125 @@ __device__ __forceinline__ void block_act_quant_row(const XT *__restrict__ x,
 __device__ __forceinline__ int block_act_quant_row_barrier_count(bool norm, bool defer_sum) {
     return (norm ? 3 : 2) - (defer_sum ? 1 : 0);
 }
+
+// RMSNorm + int8 quantisation of one token row by a 1024-thread workgroup
+// with the whole row in registers (rows of up to 4096 * SQ elements), the
+// same arithmetic in the same order as the 256-thread block form: O256
+// chain t (float4 groups k = 4t + 1024 i) is held by four threads, thread
+// 256 h + t holding the groups i in [h SQ, (h + 1) SQ); the chain's sum of
+// squares is carried from segment to segment through LDS (one barrier
+// each), so every chain is the same sequence of fused multiply-adds, and
+// the chain totals are added by the block form's tree.  The maximum and the
+// code sum are order-free.  Every wave loads its part of x and gamma at the
+// start -- one round trip for the whole row -- then runs `issued()` after a
+// barrier, so the loads the caller issues there queue behind all of them.
+// q goes to q (LDS; not with TO_LDS false) and, when gq is set, to global
+// memory; inv to *inv (and *ginv); the per-wave code sums to qpart[16].
+// GLU: the row is relu2_mul(x, u) of the gate row x and the up row u (the
+// FFN's down projection input), formed as they arrive; gamma is then loaded
+// after the product (it is first needed after the sum of squares), so that
+// x, u and gamma are never all held at once.
+template <int SQ, bool GLU = false, bool TO_LDS = true, class Hook>
+__device__ __forceinline__ void wide_act_quant_row(const float *__restrict__ x,
+                                                   const float *__restrict__ gamma, float eps,
+                                                   int K, float *red, float *chain, int8_t *q,
+                                                   int8_t *gq, float *inv, float *ginv, int *qpart,
+                                                   Hook &&issued,
+                                                   const float *__restrict__ u = nullptr) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int h = __builtin_amdgcn_readfirstlane(wid >> 2);  // segment of the chain
+    const int t = tid & 255;                                  // chain
+    const int ni = (K + 1023) / 1024;                         // float4 groups per chain
+    const bool norm = gamma != nullptr;
+    const auto rx = make_rsrc(x, 4u * (uint32_t)K);
+    const auto ru = make_rsrc(u, GLU ? 4u * (uint32_t)K : 0u);
+    const auto rg = gamma_rsrc(gamma, K);
+    float4 xv[SQ], gv[SQ];
+    auto off_of = [&](int i) { return 4u * (uint32_t)(4 * t + 1024 * (h * SQ + i)); };
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        if (h * SQ + i < ni) {  // wave-uniform; lanes past K read zeros
+            xv[i] = load_x4<float>(rx, off_of(i));
+            gv[i] = GLU ? buf_load_f4(ru, off_of(i)) : gamma_f4(rg, off_of(i), norm);
+        } else {
+            xv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            gv[i] = xv[i];
+        }
+    }
+    __builtin_amdgcn_s_barrier();
+    issued();
+    if constexpr (GLU) {
+        // x <- relu2_mul(x, u), then gamma into the registers u held
+#pragma unroll
+        for (int i = 0; i < SQ; ++i) {
+            xv[i] = relu2_mul4(xv[i], gv[i]);
+            gv[i] = h * SQ + i < ni ? gamma_f4(rg, off_of(i), norm)
+                                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+    float r = 1.0f;
+    if (norm) {
+        float p = 0.0f;
+        for (int s = 0; s < 4; ++s) {
+            if (h == s) {
+                if (s > 0) p = chain[t];
+#pragma unroll
+                for (int i = 0; i < SQ; ++i) {
+                    if (h * SQ + i < ni) {
+                        p = __builtin_fmaf(xv[i].x, xv[i].x, p);
+                        p = __builtin_fmaf(xv[i].y, xv[i].y, p);
+                        p = __builtin_fmaf(xv[i].z, xv[i].z, p);
+                        p = __builtin_fmaf(xv[i].w, xv[i].w, p);
+                    }
+                }
+                if (s < 3) chain[t] = p;
+            }
+            if (s < 3) lds_barrier();
+        }
+        // Segment 3 holds the chain totals: waves 12..15 are the block
+        // form's four waves.
+        if (h == 3) {
+            p = wave_tree_sum_f(p);
+            if (lane == 0) red[wid - 12] = p;
+        }
+        lds_barrier();
+        r = rms_scale((red[0] + red[1]) + (red[2] + red[3]), K, eps);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        xv[i] = xn4(xv[i], gv[i], r);
+        amax = amax4(amax, xv[i]);
+    }
+    amax = wave_max(amax);
+    if (lane == 0) red[4 + wid] = amax;
+    lds_barrier();
+    float m = red[4];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) m = fmaxf(m, red[4 + w]);
+    const float iv = quant_scale(m);
+    int qs = 0;
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        const int k = 4 * t + 1024 * (h * SQ + i);
+        if (k < K) {
+            const float4 v = xv[i];
+            const uint32_t w = pack_char4(quant_one(v.x, iv), quant_one(v.y, iv),
+                                          quant_one(v.z, iv), quant_one(v.w, iv));
+            qs = sum_char4(w, qs);
+            if constexpr (TO_LDS) *reinterpret_cast<uint32_t *>(q + k) = w;
+            if (gq) *reinterpret_cast<uint32_t *>(gq + k) = w;
+        }
+    }
+    qs = wave_sum_int(qs);
+    if (lane == 0) qpart[wid] = qs;
+    if (tid == 0) {
+        *inv = iv;
+        if (gq) *ginv = iv;
+    }
+}
 __device__ __forceinline__ void block_act_quant_row_barriers(bool norm, bool defer_sum) {
     const int n = block_act_quant_row_barrier_count(norm, defer_sum);
     for (int i = 0; i < n; ++i) lds_barrier();
@@ -837,6 +956,8 @@ hipError_t launch_fp32_ops(int op, const float *a, const float *b, float eps, in
 // a = relu2_mul(g, u) elementwise over n floats (n % 4 == 0, 16-byte
 // aligned arrays).
 hipError_t launch_relu2_mul(const float *g, const float *u, float *a, int64_t n, hipStream_t s);
+
+
 
 // Batched quantisation: up to 8 independent (x, gamma, eps, M, K) with
 // K <= 8192 each, one launch, bit-identical to launch_act_quant per problem.

@@ -560,7 +560,9 @@ int gemm32_num_shapes() { return kNumShapes32; }
 constexpr int kAutoShape32 = 3;
 // With >= 512 tiles of 128 x 256 (two per CU), the wider tile halves the
 // activation traffic and wins (K = N = 8192 at M = 2048: 113-118 against
-// 126-130 us).
+// 126-130 us); with >= 256 of them (one per CU) too when every row is long
+// (K = N = 8192 at M = 1024: 53.1 against 59.6 us for the 128 x 128 tiles;
+// the prefill layer's K = 2560 rows keep the narrower tile).
 constexpr int kWideShape32 = 6;
 // With at most one 128 x 128 tile per CU (every K a whole number of 256-k
 // steps), the two k groups of 4 waves, each wave a 64 x 64 tile over its
@@ -568,8 +570,11 @@ constexpr int kWideShape32 = 6;
 // 64 x 32 waves (K = N = 8192 at M = 512: 43-44.6 against 45-46.7 us per
 // forward).  With more tiles its 121 KB of LDS (one workgroup per CU)
 // loses to the 72 KB shape's two (prefill layer, 712 tiles: 74 against
-// 68 us).
+// 68 us), and so it does on short rows, whose ten 256-k steps per tile do
+// not amortise the two groups' hand-off (K = 2560, N = 6912 at M = 512:
+// 15.4 against 14.4 us).
 constexpr int kSplitShape32 = 13;
+constexpr int64_t kLongRowK = 4096;
 
 bool gemm32_preferred(const GemmDesc *d, int count) {
     int64_t tiles = 0;
@@ -589,15 +594,17 @@ hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStrea
     int v = shape;
     if (v <= 0 || v > kNumShapes32) {
         int64_t wide = 0, tiles = 0;
-        bool even = true;
+        bool even = true, long_rows = true;
         for (int i = 0; i < count; ++i) {
             wide += ((d[i].M + 127) / 128) * ((d[i].N + 255) / 256);
             tiles += ((d[i].M + 127) / 128) * ((d[i].N + 127) / 128);
             even = even && d[i].K % (2 * kBlk) == 0;
+            long_rows = long_rows && d[i].K >= kLongRowK;
         }
-        v = wide >= 512 ? kWideShape32
-            : (even && tiles <= device_cus()) ? kSplitShape32
-                                              : kAutoShape32;
+        const int cus = device_cus();
+        v = (wide >= 2 * cus || (long_rows && wide >= cus)) ? kWideShape32
+            : (even && long_rows && tiles <= cus)            ? kSplitShape32
+                                                             : kAutoShape32;
     }
     // Two blocks per step need an even block count in every row.
     if (kShapes32[v - 1].KB == 2)

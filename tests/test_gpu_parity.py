@@ -119,8 +119,12 @@ def test_pack_all_zero(torch, bl):
 
 # ---------------------------------------------------------------- RMSNorm + int8
 
+# Rows past 8192 in launches of at most one row per CU take the 1024-thread
+# form (8320: a ragged last chain segment; 12288 / 16384: four float4 groups
+# per thread; 28672: eight); 300 rows of 9216 keep the 256-thread form.
 AQ_CASES = [(1, 128, 0.0), (1, 256, 0.0), (3, 384, 0.0), (4, 2560, 0.01), (5, 6912, 0.0),
-            (16, 8192, 0.01), (64, 2560, 0.01), (7, 28672, 0.0), (33, 640, 0.0)]
+            (16, 8192, 0.01), (64, 2560, 0.01), (7, 28672, 0.0), (33, 640, 0.0),
+            (3, 8320, 0.01), (2, 12288, 0.0), (16, 16384, 0.01), (300, 9216, 0.0)]
 
 
 @pytest.mark.parametrize("M,K,outl", AQ_CASES)
