@@ -106,19 +106,60 @@ def capture(torch, fn):
     return g
 
 
-def time_steps(torch, api, prep, steps, warmup):
-    """ms per step over exactly `steps` steps, replayed from one HIP graph
-    (the host does not pace the GPU), after `warmup` untimed steps."""
-    gw = capture(torch, lambda: [prep.step(api, r) for r in range(max(1, warmup))])
-    gt = capture(torch, lambda: [prep.step(api, warmup + r) for r in range(steps)])
-    gw.replay()
+# Untimed GPU work before every timed region.  The MI355X runs short
+# launches faster once it has been under load for some milliseconds: the
+# decode layer's 200 timed steps took 6.65-6.67 us each right after 20
+# warm-up steps (0.13 ms of work), 6.39-6.43 us after 13-100 ms of warm-up
+# steps (one long graph, or short ones with a synchronisation every ~7 ms),
+# and were back at 6.66 us after a 50 ms pause; K = N = 8192 at M = 512
+# 44.5 against 42.1 us, the prefill layer 62.2 against 57.8 us.  Hundreds of
+# short graph replays issued without a synchronisation made the timed steps
+# slower and erratic instead (6.6-7.4 us), so the warm-up goes in chunks of
+# at least CLOCK_CHUNK_S of work, each followed by a synchronisation.
+CLOCK_WARM_S = 0.025
+CLOCK_CHUNK_S = 0.005
+
+
+def warm_clock(torch, g):
+    """Replays graph g (untimed) in chunks of at least CLOCK_CHUNK_S seconds
+    of GPU work, synchronising after each, until about CLOCK_WARM_S seconds
+    have run; returns the seconds of GPU work run."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
     torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
+    per_chunk = max(1, int(CLOCK_CHUNK_S / one + 0.999))
+    chunks = max(0, int(CLOCK_WARM_S / (per_chunk * one) + 0.5))
+    for _ in range(chunks):
+        for _ in range(per_chunk):
+            g.replay()
+        torch.cuda.synchronize()
+    return one * (1 + chunks * per_chunk)
+
+
+def replay_timed(torch, gw, gt, steps):
+    """Seconds per step of graph gt (`steps` steps), timed with HIP events on
+    the current stream, after the warm-up graph gw (the `warmup` untimed
+    steps) and the clock warm-up over replays of gw."""
+    gw.replay()
+    warm_clock(torch, gw)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     gt.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps  # ms per step
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def time_steps(torch, api, prep, steps, warmup):
+    """ms per step over exactly `steps` steps, replayed from one HIP graph
+    (the host does not pace the GPU), after `warmup` untimed steps and the
+    clock warm-up."""
+    gw = capture(torch, lambda: [prep.step(api, r) for r in range(max(1, warmup))])
+    gt = capture(torch, lambda: [prep.step(api, warmup + r) for r in range(steps)])
+    return replay_timed(torch, gw, gt, steps) * 1e3  # ms per step
 
 
 def time_launches(torch, api, prep, reps=None):
@@ -135,14 +176,7 @@ def time_launches(torch, api, prep, reps=None):
                 api.forward(d["x"], d["P"][r % prep.copies], d["s"], d["g"], prep.work.eps, L.N,
                             out=d["y"], workspace=d["ws"])
         g = capture(torch, run)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        out[L.name] = (L, e0.elapsed_time(e1) * 1e-3 / reps)  # s per launch
+        out[L.name] = (L, replay_timed(torch, g, g, reps))  # s per launch
         del g
     return out
 
@@ -245,15 +279,9 @@ def time_fn(torch, fn, steps, warmup):
     untimed ones."""
     gw = capture(torch, lambda: [fn(r) for r in range(max(1, warmup))])
     gt = capture(torch, lambda: [fn(warmup + r) for r in range(steps)])
-    gw.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    gt.replay()
-    e1.record()
-    torch.cuda.synchronize()
+    t = replay_timed(torch, gw, gt, steps)
     del gw, gt
-    return e0.elapsed_time(e1) * 1e-3 / steps
+    return t
 
 
 def roofline_of(L_list, sec, kernel):
@@ -493,15 +521,9 @@ def secondary_ffn(torch, api, steps, warmup):
         def timed(fn):
             gw = capture(torch, lambda: [fn(r) for r in range(max(1, warmup))])
             gt = capture(torch, lambda: [fn(warmup + r) for r in range(steps)])
-            gw.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            gt.replay()
-            e1.record()
-            torch.cuda.synchronize()
+            t = replay_timed(torch, gw, gt, steps)
             del gw, gt
-            return e0.elapsed_time(e1) * 1e-3 / steps  # s per step
+            return t  # s per step
 
         t_f = timed(fused)
         t_p = timed(plain)
@@ -545,14 +567,7 @@ def secondary_io(torch, api, steps, warmup):
                                    b["y"], b["ws"]) for d, b in zip(prep.lin, io)])
         gw = capture(torch, lambda: [step(r) for r in range(max(1, warmup))])
         gt = capture(torch, lambda: [step(warmup + r) for r in range(steps)])
-        gw.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        gt.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / steps
+        t = replay_timed(torch, gw, gt, steps)
         del gw, gt
         t32 = time_steps(torch, api, prep, steps, warmup) * 1e-3
         nbytes = sum(L.N * L.K // 4 + 2 * L.M * L.K + 4 * L.K + 2 * L.M * L.N for L in work.linears)
@@ -580,14 +595,7 @@ def secondary_nonorm(torch, api, steps, warmup):
                             d["ws"]) for d in prep.lin])
     gw = capture(torch, lambda: [step(r) for r in range(max(1, warmup))])
     gt = capture(torch, lambda: [step(warmup + r) for r in range(steps)])
-    gw.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    gt.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / steps
+    t = replay_timed(torch, gw, gt, steps)
     del gw, gt
     t_norm = time_steps(torch, api, prep, steps, warmup) * 1e-3
     nbytes = sum(L.N * L.K // 4 + 4 * L.M * L.K + 4 * L.M * L.N for L in work.linears)
@@ -625,14 +633,7 @@ def secondary_dense(torch, api, steps, warmup):
                 torch.mm(m["x"], m["wt"][r % copies], out=m["y"])
         gw = capture(torch, lambda: [step(r) for r in range(max(1, warmup))])
         gt = capture(torch, lambda: [step(warmup + r) for r in range(steps)])
-        gw.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        gt.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / steps
+        t = replay_timed(torch, gw, gt, steps)
         del gw, gt
         t_i2s = time_steps(torch, api, prep, steps, warmup) * 1e-3
         res[key] = {"dense_bf16_library_us": round(t * 1e6, 2), "i2s_us": round(t_i2s * 1e6, 2),
@@ -801,6 +802,7 @@ def main():
         "value": round(gbs, 2) if decode else round(work.int_ops() / (ms * 1e-3) / 1e12, 2),
         "unit": "GB/s" if decode else "TOPS",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "clock_warmup_s": CLOCK_WARM_S, "clock_warmup_chunk_s": CLOCK_CHUNK_S,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8", "data": "synthetic",
