@@ -303,7 +303,9 @@ def test_workload_ffn70b(torch, bl, orc, M, i):
     run_linear(torch, bl, orc, work, i, None, cols)
 
 
-@pytest.mark.parametrize("M", wl.SWEEP_M)
+# M = 1024: the 128 x 256 tiles at one per CU (rows of 8192); the rest as
+# the bench's sweep.
+@pytest.mark.parametrize("M", list(wl.SWEEP_M) + [1024])
 def test_workload_sweep(torch, bl, orc, M):
     work = wl.sweep(M)
     rng = np.random.default_rng(M)
