@@ -201,7 +201,7 @@ hipError_t launch_wide(const float *x, const float *gamma, float eps, int64_t M,
 // Whether M rows of K take the 1024-thread form: fp32 rows of 8193..32768,
 // no more rows than CUs.  There the 256-thread form's per-thread chain is
 // 9-32 float4 groups long (70B FFN down projection, K = 28672, M = 16:
-// 32.6 -> 31.9 us per forward).  Up to K = 8192 the two forms measured the
+// 32.6 -> 31.7-31.9 us per forward).  Up to K = 8192 the two forms measured the
 // same (K = N = 8192 at M = 4 / 16 / 64), the launch itself dominating.
 bool wide_rows(int64_t rows, int64_t K) {
     return K > 8 * 1024 && K <= 32 * 1024 && rows <= device_cus();
