@@ -1029,8 +1029,15 @@ hipError_t launch_gemv_shot(const ShotDecode *d, int count, int shape, hipStream
     return launch_sep<true>(d, count, v, s);
 }
 
-hipError_t launch_gemv_shot_fused(const FusedDecode *d, int count, int shape, hipStream_t s) {
+hipError_t launch_gemv_shot_fused(const FusedDecode *d_in, int count, int shape, hipStream_t s) {
     if (count < 1 || count > kMaxShotBatch) return hipErrorInvalidValue;
+    // Problems in order of decreasing K (stable): workgroups are dispatched
+    // in index order, so the longest quantisation chains start first.
+    FusedDecode ord[kMaxShotBatch];
+    for (int i = 0; i < count; ++i) ord[i] = d_in[i];
+    std::stable_sort(ord, ord + count,
+                     [](const FusedDecode &a, const FusedDecode &b) { return a.K > b.K; });
+    const FusedDecode *d = ord;
     int64_t M[kMaxShotBatch], K[kMaxShotBatch], N[kMaxShotBatch], kmax = 0, mmax = 0;
     const bool glu = d[0].u != nullptr;
     const int io = d[0].io;
