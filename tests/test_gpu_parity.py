@@ -124,7 +124,10 @@ def test_pack_all_zero(torch, bl):
 # per thread; 28672: eight); 300 rows of 9216 keep the 256-thread form.
 AQ_CASES = [(1, 128, 0.0), (1, 256, 0.0), (3, 384, 0.0), (4, 2560, 0.01), (5, 6912, 0.0),
             (16, 8192, 0.01), (64, 2560, 0.01), (7, 28672, 0.0), (33, 640, 0.0),
-            (3, 8320, 0.01), (2, 12288, 0.0), (16, 16384, 0.01), (300, 9216, 0.0)]
+            (3, 8320, 0.01), (2, 12288, 0.0), (16, 16384, 0.01), (300, 9216, 0.0),
+            # rows past 32768 are streamed (three passes); the longest row the
+            # library takes, K = 2^22
+            (3, 40960, 0.01), (2, 1 << 22, 0.0)]
 
 
 @pytest.mark.parametrize("M,K,outl", AQ_CASES)
@@ -167,7 +170,8 @@ def mm_case(M, K, N, seed):
 
 MM_SHAPES = [(1, 128, 16), (1, 256, 100), (2, 384, 33), (5, 2560, 640), (16, 1024, 48),
              (17, 384, 70), (31, 256, 64), (32, 640, 129), (33, 1280, 31), (64, 2560, 256),
-             (65, 384, 300), (130, 1152, 200), (16, 4096, 40), (9, 8192, 33)]
+             (65, 384, 300), (130, 1152, 200), (16, 4096, 40), (9, 8192, 33),
+             (2, 1 << 22, 16)]  # the longest row the library takes
 
 
 @pytest.mark.parametrize("path", [1, 2])
@@ -189,7 +193,8 @@ def test_matmul_parity(torch, bl, orc, path, M, K, N):
 
 FWD_SHAPES = [(1, 256, 256), (1, 2560, 640), (2, 384, 100), (3, 1024, 77), (4, 6912, 160),
               (7, 512, 513), (10, 2560, 300), (12, 1024, 129), (15, 6912, 200), (16, 2560, 256),
-              (17, 256, 64), (63, 640, 333), (64, 1024, 200), (100, 384, 90)]
+              (17, 256, 64), (63, 640, 333), (64, 1024, 200), (100, 384, 90),
+              (1, 1 << 22, 3), (3, 65536, 40)]  # rows past 32768, up to the longest
 
 
 @pytest.mark.parametrize("M,K,N", FWD_SHAPES)
