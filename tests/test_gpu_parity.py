@@ -194,7 +194,8 @@ def test_matmul_parity(torch, bl, orc, path, M, K, N):
 FWD_SHAPES = [(1, 256, 256), (1, 2560, 640), (2, 384, 100), (3, 1024, 77), (4, 6912, 160),
               (7, 512, 513), (10, 2560, 300), (12, 1024, 129), (15, 6912, 200), (16, 2560, 256),
               (17, 256, 64), (63, 640, 333), (64, 1024, 200), (100, 384, 90),
-              (1, 1 << 22, 3), (3, 65536, 40)]  # rows past 32768, up to the longest
+              (1, 1 << 22, 3), (3, 65536, 40),  # rows past 32768, up to the longest
+              (1, 128, 1 << 18), (20000, 256, 16)]  # a wide single token, a tall batch
 
 
 @pytest.mark.parametrize("M,K,N", FWD_SHAPES)
