@@ -74,7 +74,9 @@ typedef enum {
  * affects speed.  AUTO takes the decode kernels for M <= 4 and the MFMA
  * tile kernel above, except that a forward of M <= 8 tokens whose block
  * fits the one-shot decode kernel (M * K <= 65536, K <= 8192) takes that
- * kernel (see bitlinear_forward_batch). */
+ * kernel (see bitlinear_forward_batch), and that 2..4 tokens with
+ * M * K > 65536 (a block the one-shot and rolling decode forms do not
+ * hold) take the tile kernel. */
 typedef enum {
     BL_PATH_AUTO = 0,
     BL_PATH_GEMV = 1, /* decode kernel, any M (tokens in groups of 16) */

@@ -18,6 +18,10 @@ constexpr int64_t kMaxK = int64_t(1) << 22;
 // AUTO: decode route up to 4 tokens; from 5 on the MFMA tile kernel, which
 // reads the weights once per 32- or 64-token tile, is faster on MI355X
 // (measured at K = N = 8192 and on the 70B FFN shapes, M = 4, 8, 16).
+// 2..4 tokens whose block the one-shot and rolling decode forms do not hold
+// (M * K past 64 KB) take the tile kernel too: the decode route would take
+// its persistent form there (70B down projection, K = 28672, at M = 4:
+// 28.2 against 23.1 us per forward).
 constexpr int kGemvMaxM = 4;
 using bl::kFuseMaxLds;
 using bl::kFuseMaxM;
@@ -81,17 +85,21 @@ Workspace carve(void *ws, int64_t M, int64_t K) {
     return w;
 }
 
-// The contraction route a launch takes for M tokens.
-int route_of(int64_t M, const bl_launch *l) {
+// The contraction route a launch takes for M tokens of rows of K.
+int route_of(int64_t M, int64_t K, const bl_launch *l) {
     const int path = l ? l->path : BL_PATH_AUTO;
     if (path != BL_PATH_AUTO) return path;
-    return (M <= kGemvMaxM) ? BL_PATH_GEMV : BL_PATH_GEMM;
+    if (M == 1) return BL_PATH_GEMV;
+    return M <= kGemvMaxM && bl::roll_supported(M, K) ? BL_PATH_GEMV : BL_PATH_GEMM;
 }
 
 // Launch-grid row limit of a route: 16 tokens per decode workgroup row,
-// 32 per row of the smallest prefill tile, at most 65535 rows.
+// 32 per row of the smallest prefill tile, at most 65535 rows (either route
+// fits the few tokens whose automatic route depends on K).
 bl_status check_grid(int64_t M, const bl_launch *l) {
-    const int64_t rows = route_of(M, l) == BL_PATH_GEMV ? (M + 15) / 16 : (M + 31) / 32;
+    const int path = l ? l->path : BL_PATH_AUTO;
+    const bool gemv = path == BL_PATH_GEMV || (path == BL_PATH_AUTO && M <= kGemvMaxM);
+    const int64_t rows = gemv ? (M + 15) / 16 : (M + 31) / 32;
     return rows > 65535 ? BL_ERR_SHAPE : BL_OK;
 }
 
@@ -102,7 +110,7 @@ bl_status run_contraction(const int8_t *q, const float *inv, const int32_t *qsum
                           int64_t N, float *y, int32_t *acc, const bl_launch *l, hipStream_t s) {
     if (bl_status st = check_grid(M, l)) return st;
     const int variant = l ? l->variant : 0;
-    if (route_of(M, l) == BL_PATH_GEMV)
+    if (route_of(M, K, l) == BL_PATH_GEMV)
         return hip_status(bl::launch_gemv(q, inv, qsum, packed, w_scale, M, K, N, y, acc,
                                           variant, s));
     return hip_status(bl::launch_gemm(q, inv, qsum, packed, w_scale, M, K, N, y, acc, variant, s));
@@ -121,7 +129,7 @@ bl_status validate_forward(const bl_forward_desc &d, const bl_launch *launch) {
         !aligned16(d.workspace))
         return BL_ERR_ALIGN;
     if (d.workspace_bytes < bitlinear_workspace_bytes(d.M, d.K)) return BL_ERR_WORKSPACE;
-    const bool gemv = route_of(d.M, launch) == BL_PATH_GEMV;
+    const bool gemv = route_of(d.M, d.K, launch) == BL_PATH_GEMV;
     const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
     if (launch && launch->fuse == 1 && !(gemv && fits)) return BL_ERR_INVALID_ARG;
     return check_grid(d.M, launch);
@@ -155,7 +163,7 @@ bl::FusedDecode fused_of(const bl_forward_desc &d) {
 // one-shot kernel's 16-wave shape holds them in one round, else as the
 // separate quantisation + contraction pair; measured on MI355X).
 bool takes_fused(const bl_forward_desc &d, const bl_launch *launch) {
-    const bool gemv = route_of(d.M, launch) == BL_PATH_GEMV;
+    const bool gemv = route_of(d.M, d.K, launch) == BL_PATH_GEMV;
     const bool fits = d.M <= kFuseMaxM && d.M * d.K <= kFuseMaxLds;
     if (launch && launch->fuse == 0) return false;
     if (launch && launch->fuse == 1) return gemv && fits;
@@ -172,7 +180,7 @@ bool takes_fused(const bl_forward_desc &d, const bl_launch *launch) {
 // registers.
 bool takes_group(const bl_forward_desc &d, const bl_launch *launch) {
     if (launch && launch->variant != 0) return false;
-    return route_of(d.M, launch) == BL_PATH_GEMM && bl::gemm_group_supported(d.K) &&
+    return route_of(d.M, d.K, launch) == BL_PATH_GEMM && bl::gemm_group_supported(d.K) &&
            d.K <= bl::kActQuantBatchMaxK;
 }
 
@@ -590,7 +598,7 @@ bl_status bitlinear_forward_io_batch(const bl_forward_io_desc *descs, int count,
                     if (bl_status st = flush_sg(G)) return st;
                 continue;
             }
-            if (route_of(d.M, nullptr) == BL_PATH_GEMM && bl::gemm_group_supported(d.K) &&
+            if (route_of(d.M, d.K, nullptr) == BL_PATH_GEMM && bl::gemm_group_supported(d.K) &&
                 d.K <= bl::kActQuantBatchMaxK) {
                 PrefillGroup &G = pg[d.x_dtype][d.y_dtype];
                 const Workspace ws = carve(d.workspace, d.M, d.K);

@@ -57,36 +57,51 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // One BM x BN output tile at (m0, n0) of one problem, by the whole
 // workgroup.
 // YT: storage type of y (float, bf16_t, _Float16; rounded to nearest even).
-template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y, typename YT = float>
+// WK: k groups.  With WK > 1 the workgroup holds WK groups of WM x WN
+// waves; group g walks its own contiguous run of ceil(steps / WK) steps
+// through a ring of its own, and the groups' int32 partial tiles are added
+// in LDS at the end (integer sums: the result does not depend on WK).  This
+// multiplies the loads in flight per tile, for grids of few tiles over long
+// rows.
+template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y, typename YT = float,
+          int WK = 1>
 __device__ __forceinline__ void gemm_tile(
     const int8_t *__restrict__ q, const float *__restrict__ inv,
     const int32_t *__restrict__ qsum, const uint8_t *__restrict__ packed,
     float w_scale, int M, int K, int N, YT *__restrict__ y,
     int32_t *__restrict__ acc_out, int m0, int n0) {
-    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int NW = WM * WN, NT = NW * 64;  // waves and threads of one k group
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 16, NI = TN / 16;
     constexpr int SB = BM * kStepK;            // activation bytes of one step
     constexpr int ND = SB / (NT * 16);         // LDS-direct loads per lane per step
+    constexpr int GB = SB * WK;                // one ring slot of every k group
     static_assert(SB % (NT * 16) == 0, "step tile splits into whole wave loads");
-    static_assert(R >= 3 && R <= 5 && R * SB <= 160 * 1024, "ring depth");
-    __shared__ __align__(16) int8_t l0[SB], l1[SB], l2[SB], l3[R > 3 ? SB : 16],
-        l4[R > 4 ? SB : 16];
-    auto ring = [&](auto I) -> int8_t * {
-        constexpr int i = decltype(I)::value % R;
-        if constexpr (i == 0) return l0;
-        else if constexpr (i == 1) return l1;
-        else if constexpr (i == 2) return l2;
-        else if constexpr (i == 3) return l3;
-        else return l4;
-    };
+    static_assert(R >= 3 && R <= 5 && R * GB <= 160 * 1024, "ring depth");
+    static_assert(WK >= 1 && NW * WK <= 16, "at most 16 waves");
+    __shared__ __align__(16) int8_t l0[GB], l1[GB], l2[GB], l3[R > 3 ? GB : 16],
+        l4[R > 4 ? GB : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps derived resources scalar
+    // Wave-uniform (keeps derived resources scalar): k group and wave in it.
+    const int wall = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kgi = WK > 1 ? wall / NW : 0;
+    const int wid = WK > 1 ? wall - kgi * NW : wall;
+    const int kgo = kgi * SB;
+    auto ring = [&](auto I) -> int8_t * {
+        constexpr int i = decltype(I)::value % R;
+        if constexpr (i == 0) return l0 + kgo;
+        else if constexpr (i == 1) return l1 + kgo;
+        else if constexpr (i == 2) return l2 + kgo;
+        else if constexpr (i == 3) return l3 + kgo;
+        else return l4 + kgo;
+    };
     const int wm = wid / WN, wn = wid % WN;
     const int j = lane & 15, kg = lane >> 4;
     const int nsteps = (K + kStepK - 1) / kStepK;
+    const int spg = WK > 1 ? (nsteps + WK - 1) / WK : nsteps;  // steps of one k group
+    const int sg0 = kgi * spg;                                  // its first step
     const int nblocks = K / kBlockWeights;
     const uint32_t rowbytes = (uint32_t)K / 4;
     const auto rq = make_rsrc(q + (size_t)m0 * K, (uint32_t)min(BM, M - m0) * (uint32_t)K);
@@ -119,28 +134,31 @@ __device__ __forceinline__ void gemm_tile(
     for (int ni = 0; ni < NI; ++ni)
         boff[ni] = (uint32_t)(wn * TN + 16 * ni + j) * rowbytes + 16u * kg;
 
-    // Loads of step s, activations then weights.  When K is a whole number
-    // of steps (KTAIL false) the step's k offset rides in the scalar offset
-    // and steps past the end are redirected out of range (they read zeros);
-    // otherwise each chunk past K is.
-    auto issue = [&](int8_t *buf, v4i(&breg)[NI], int s) {
+    // Loads of the group's step sl, activations then weights.  When K is a
+    // whole number of steps (KTAIL false) the step's k offset rides in the
+    // scalar offset and steps past the end (of K, or of the group's run) are
+    // redirected out of range (they read zeros); otherwise each chunk past K
+    // is.
+    auto issue = [&](int8_t *buf, v4i(&breg)[NI], int sl) {
+        const int s = sg0 + sl;
+        const bool run = WK == 1 || sl < spg;  // wave-uniform
         const int kb = s * kStepK;
 #pragma unroll
         for (int c = 0; c < ND; ++c) {
             uint32_t off, soff;
             if constexpr (!KTAIL) {
-                off = s < nsteps ? dsrc[c] : kOOB;
-                soff = kb;
+                off = run && s < nsteps ? dsrc[c] : kOOB;
+                soff = WK == 1 || run ? kb : 0;
             } else {
-                off = kb + dk[c] < K ? dsrc[c] + (uint32_t)kb : kOOB;
+                off = run && kb + dk[c] < K ? dsrc[c] + (uint32_t)kb : kOOB;
                 soff = 0;
             }
             buf_load16_lds(rq, buf + (c * NW + wid) * 1024, off, soff);
         }
-        const bool kv = KTAIL ? 2 * s + (kg >> 1) < nblocks : s < nsteps;
+        const bool kv = run && (KTAIL ? 2 * s + (kg >> 1) < nblocks : s < nsteps);
+        const uint32_t wso = WK == 1 || run ? (uint32_t)s * kStepBytes : 0u;
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-            breg[ni] = buf_load16_so(rw, kv ? boff[ni] : kOOB, (uint32_t)s * kStepBytes);
+        for (int ni = 0; ni < NI; ++ni) breg[ni] = buf_load16_so(rw, kv ? boff[ni] : kOOB, wso);
     };
 
     v4i acc[MI][NI];
@@ -200,7 +218,7 @@ __device__ __forceinline__ void gemm_tile(
             __builtin_amdgcn_sched_barrier(0);
         }
     }, std::make_integer_sequence<int, R>{});
-    const int turns = (nsteps + R - 1) / R;
+    const int turns = (spg + R - 1) / R;
     int s = 0;
     for (int t = 0; t < turns; ++t, s += R) {
         unroll_ic([&](auto I) {
@@ -213,6 +231,30 @@ __device__ __forceinline__ void gemm_tile(
     }
     // Drain the trailing loads before the workgroup's LDS is released.
     wait_vm_barrier<0>();
+
+    if constexpr (WK > 1) {
+        // Groups 1..WK-1 leave their partial tiles in the (now idle) first
+        // ring slot; group 0 adds them in group order and writes the tile.
+        static_assert((WK - 1) * NW * MI * NI * 64 * 16 <= GB, "partials fit one ring slot");
+        v4i *part = reinterpret_cast<v4i *>(l0);
+        auto at = [&](int g, int mi, int ni) {
+            return (((g - 1) * NW + wid) * MI * NI + mi * NI + ni) * 64 + lane;
+        };
+        if (kgi > 0) {
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) part[at(kgi, mi, ni)] = acc[mi][ni];
+        }
+        __syncthreads();
+        if (kgi > 0) return;
+#pragma unroll
+        for (int g = 1; g < WK; ++g)
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) acc[mi][ni] += part[at(g, mi, ni)];
+    }
 
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -236,14 +278,15 @@ __device__ __forceinline__ void gemm_tile(
     }
 }
 
-template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_ring_kernel(
+template <int BM, int BN, int WM, int WN, int R, bool KTAIL, bool OUT_Y, int WK>
+__global__ __launch_bounds__(WM * WN * WK * 64) void gemm_ring_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ inv,
     const int32_t *__restrict__ qsum, const uint8_t *__restrict__ packed,
     float w_scale, int M, int K, int N, float *__restrict__ y,
     int32_t *__restrict__ acc_out) {
-    gemm_tile<BM, BN, WM, WN, R, KTAIL, OUT_Y>(q, inv, qsum, packed, w_scale, M, K, N, y, acc_out,
-                                                (int)blockIdx.y * BM, (int)blockIdx.x * BN);
+    gemm_tile<BM, BN, WM, WN, R, KTAIL, OUT_Y, float, WK>(
+        q, inv, qsum, packed, w_scale, M, K, N, y, acc_out, (int)blockIdx.y * BM,
+        (int)blockIdx.x * BN);
 }
 
 // Grouped form: up to 8 independent problems (K a whole number of steps)
@@ -269,8 +312,8 @@ struct GroupBatch {
 // lead the argument list so that the build's kernel-argument preload puts
 // them in scalar registers at wave launch.  Tiles of a problem are ordered
 // N-fastest, as in the single-problem grid.
-template <int BM, int BN, int WM, int WN, int R, bool OUT_Y, typename YT = float>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_group_kernel(int b0, int b1, int b2, int b3,
+template <int BM, int BN, int WM, int WN, int R, bool OUT_Y, typename YT, int WK>
+__global__ __launch_bounds__(WM * WN * WK * 64) void gemm_group_kernel(int b0, int b1, int b2, int b3,
                                                                   int b4, int b5, int b6, int b7,
                                                                   GroupBatch B) {
     static_assert(kMaxGroup == 8, "one leading argument per problem");
@@ -283,13 +326,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_group_kernel(int b0, int b1
     const GroupProblem P = Bk->p[pi];
     const int t = bx - P.tile_begin;
     const int tm = t / P.ntn, tn = t - tm * P.ntn;
-    gemm_tile<BM, BN, WM, WN, R, false, OUT_Y, YT>(P.q, P.inv, P.qsum, P.packed, P.w_scale, P.M,
-                                                   P.K, P.N, reinterpret_cast<YT *>(P.y), P.acc,
-                                                   tm * BM, tn * BN);
+    gemm_tile<BM, BN, WM, WN, R, false, OUT_Y, YT, WK>(P.q, P.inv, P.qsum, P.packed, P.w_scale,
+                                                       P.M, P.K, P.N, reinterpret_cast<YT *>(P.y),
+                                                       P.acc, tm * BM, tn * BN);
 }
 
 struct Tile {
     int BM, BN, WM, WN, R;  // R == 0: ring depth picked from the step count
+    int WK = 1;             // k groups
 };
 // Launch-shape table; every entry computes bit-identical results.
 constexpr Tile kTiles[] = {{64, 256, 1, 4, 3}, {64, 128, 1, 4, 3}, {64, 64, 2, 2, 0},
@@ -299,29 +343,33 @@ constexpr Tile kTiles[] = {{64, 256, 1, 4, 3}, {64, 128, 1, 4, 3}, {64, 64, 2, 2
                            {128, 256, 2, 4, 3}, {64, 512, 1, 8, 3}, {64, 512, 1, 8, 4},
                            {64, 512, 1, 8, 5},  {64, 256, 1, 8, 4}, {32, 512, 1, 8, 4},
                            {16, 256, 1, 4, 0},  {16, 128, 1, 4, 0}, {32, 32, 2, 2, 0},
-                           {16, 32, 1, 2, 0},   {16, 64, 1, 4, 0}};
+                           {16, 32, 1, 2, 0},   {16, 64, 1, 4, 0},  {16, 32, 1, 2, 0, 2},
+                           {16, 32, 1, 2, 0, 4}, {16, 32, 1, 2, 0, 8}, {16, 64, 1, 4, 0, 2},
+                           {16, 64, 1, 4, 0, 4}, {16, 128, 1, 4, 0, 2}, {16, 16, 1, 1, 0, 4},
+                           {16, 16, 1, 1, 0, 8}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+static_assert(kNumTiles == 31, "one BL_GEMM_CASE per table entry");
 
 // Ring depth for a tile: the deepest of 4, 5, 3 that divides the step count
-// (no padded steps), else 4.  Depths whose ring does not fit the LDS are
-// skipped.
-int pick_depth(int bm, int64_t K) {
-    const int64_t nsteps = (K + kStepK - 1) / kStepK;
+// of one k group (no padded steps), else 4.  Depths whose ring does not fit
+// the LDS are skipped.
+int pick_depth(int bm, int64_t K, int wk = 1) {
+    const int64_t nsteps = ((K + kStepK - 1) / kStepK + wk - 1) / wk;
     for (int r : {4, 5, 3})
-        if (r * bm * kStepK <= 160 * 1024 && nsteps % r == 0) return r;
+        if ((int64_t)r * bm * kStepK * wk <= 160 * 1024 && nsteps % r == 0) return r;
     return 4;
 }
 
-template <int BM, int BN, int WM, int WN, int R>
+template <int BM, int BN, int WM, int WN, int R, int WK = 1>
 hipError_t launch_ring(const int8_t *q, const float *inv, const int32_t *qsum,
                        const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
                        float *y, int32_t *acc, hipStream_t s) {
     const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    const dim3 block(WM * WN * 64);
+    const dim3 block(WM * WN * WK * 64);
     const bool kt = K % kStepK != 0;
-#define BL_RING_LAUNCH(KT, OY)                                                                    \
-    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, R, KT, OY>), grid, block, 0, s, q, inv, \
-                       qsum, packed, w_scale, (int)M, (int)K, (int)N, y, acc)
+#define BL_RING_LAUNCH(KT, OY)                                                                  \
+    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, R, KT, OY, WK>), grid, block, 0, s, q, \
+                       inv, qsum, packed, w_scale, (int)M, (int)K, (int)N, y, acc)
     if (y) {
         if (kt)
             BL_RING_LAUNCH(true, true);
@@ -337,20 +385,24 @@ hipError_t launch_ring(const int8_t *q, const float *inv, const int32_t *qsum,
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int RFIX>
+template <int BM, int BN, int WM, int WN, int RFIX, int WK>
 hipError_t launch_tile(const int8_t *q, const float *inv, const int32_t *qsum,
                        const uint8_t *packed, float w_scale, int64_t M, int64_t K, int64_t N,
                        float *y, int32_t *acc, hipStream_t s) {
     if constexpr (RFIX != 0) {
-        return launch_ring<BM, BN, WM, WN, RFIX>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+        return launch_ring<BM, BN, WM, WN, RFIX, WK>(q, inv, qsum, packed, w_scale, M, K, N, y,
+                                                     acc, s);
     } else {
-        const int r = pick_depth(BM, K);
+        const int r = pick_depth(BM, K, WK);
         if (r == 3)
-            return launch_ring<BM, BN, WM, WN, 3>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
-        if constexpr (5 * BM * kStepK <= 160 * 1024)
+            return launch_ring<BM, BN, WM, WN, 3, WK>(q, inv, qsum, packed, w_scale, M, K, N, y,
+                                                      acc, s);
+        if constexpr (5 * BM * kStepK * WK <= 160 * 1024)
             if (r == 5)
-                return launch_ring<BM, BN, WM, WN, 5>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
-        return launch_ring<BM, BN, WM, WN, 4>(q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
+                return launch_ring<BM, BN, WM, WN, 5, WK>(q, inv, qsum, packed, w_scale, M, K, N,
+                                                          y, acc, s);
+        return launch_ring<BM, BN, WM, WN, 4, WK>(q, inv, qsum, packed, w_scale, M, K, N, y, acc,
+                                                  s);
     }
 }
 
@@ -362,7 +414,7 @@ bool gemm_group_supported(int64_t K) { return K % kStepK == 0; }
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int R>
+template <int BM, int BN, int WM, int WN, int R, int WK = 1>
 hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
     GroupBatch B{};
     int begin[kMaxGroup];
@@ -394,22 +446,23 @@ hipError_t launch_group_tile(const GemmDesc *d, int count, hipStream_t s) {
         if (total > INT32_MAX) return hipErrorInvalidConfiguration;
     }
     for (int i = count; i < kMaxGroup; ++i) begin[i] = INT32_MAX;
-    const dim3 grid((unsigned)total), block(WM * WN * 64);
+    const dim3 grid((unsigned)total), block(WM * WN * WK * 64);
     const int io = d[0].io;
     if (y && io == kIoBf16)
-        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true, bf16_t>), grid, block, 0, s,
-                           begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],
-                           begin[7], B);
-    else if (y && io == kIoF16)
-        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true, _Float16>), grid, block, 0,
+        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true, bf16_t, WK>), grid, block, 0,
                            s, begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],
                            begin[7], B);
+    else if (y && io == kIoF16)
+        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true, _Float16, WK>), grid, block,
+                           0, s, begin[0], begin[1], begin[2], begin[3], begin[4], begin[5],
+                           begin[6], begin[7], B);
     else if (y)
-        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true>), grid, block, 0, s, begin[0],
-                           begin[1], begin[2], begin[3], begin[4], begin[5], begin[6], begin[7], B);
+        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, true, float, WK>), grid, block, 0,
+                           s, begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],
+                           begin[7], B);
     else
-        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, false>), grid, block, 0, s,
-                           begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],
+        hipLaunchKernelGGL((gemm_group_kernel<BM, BN, WM, WN, R, false, float, WK>), grid, block, 0,
+                           s, begin[0], begin[1], begin[2], begin[3], begin[4], begin[5], begin[6],
                            begin[7], B);
     return hipGetLastError();
 }
@@ -456,15 +509,23 @@ hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
     }
     const bool r5 = pad5 < pad4;
     if (mmax <= 32) {
-        // Few tokens: 16-row tiles, as for a single problem.
+        // Few tokens: 16-row tiles, as for a single problem (the 16x32 tiles
+        // in 4 k groups, their ring depth from the steps of one group).
         if (t16x128 >= 200)
             return r5 ? launch_group_tile<16, 128, 1, 4, 5>(d, count, s)
                       : launch_group_tile<16, 128, 1, 4, 4>(d, count, s);
         if (t16x64 >= 200)
             return r5 ? launch_group_tile<16, 64, 1, 4, 5>(d, count, s)
                       : launch_group_tile<16, 64, 1, 4, 4>(d, count, s);
-        return r5 ? launch_group_tile<16, 32, 1, 2, 5>(d, count, s)
-                  : launch_group_tile<16, 32, 1, 2, 4>(d, count, s);
+        double g4 = 0.0, g5 = 0.0;
+        for (int i = 0; i < count; ++i) {
+            const double w = (double)d[i].M * (double)d[i].N * (double)d[i].K;
+            const int64_t ns = (d[i].K / kStepK + 3) / 4;
+            g4 += w * (double)((4 - ns % 4) % 4) / (double)ns;
+            g5 += w * (double)((5 - ns % 5) % 5) / (double)ns;
+        }
+        return g5 < g4 ? launch_group_tile<16, 32, 1, 2, 5, 4>(d, count, s)
+                       : launch_group_tile<16, 32, 1, 2, 4, 4>(d, count, s);
     }
     if (t64x512 >= 512) return launch_group_tile<64, 512, 1, 8, 4>(d, count, s);
     if (k_avg >= 6144.0 && t64x256 >= 256) return launch_group_tile<64, 256, 1, 8, 4>(d, count, s);
@@ -499,8 +560,12 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         } else if (M <= 32)
             // Few tokens: 16-row tiles, the widest that still gives about one
             // tile per CU (M = 16, K = 8192: N = 8192 16x32 8.8 us against
-            // 32x64 10.3 us; N = 28672 16x128; measured).
-            v = tiles(16, 128) >= 200 ? 20 : tiles(16, 64) >= 200 ? 23 : 22;
+            // 32x64 10.3 us; N = 28672 16x128; measured).  The 16x32 tiles
+            // run in 4 k groups: 2 waves per tile keep too few loads in
+            // flight (M = 16, N = 8192: K = 8192 8.8 -> 7.2 us, K = 28672
+            // 25.7 -> 18.4 us; K = 2560 level).  The wider tiles gained
+            // nothing from k groups.
+            v = tiles(16, 128) >= 200 ? 20 : tiles(16, 64) >= 200 ? 23 : 25;
         else if (tiles(64, 512) >= 512)
             v = 15;
         else if (K >= 6144 && tiles(64, 256) >= 256)
@@ -521,8 +586,8 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
 #define BL_GEMM_CASE(idx)                                                                  \
     case idx:                                                                              \
         return launch_tile<kTiles[idx - 1].BM, kTiles[idx - 1].BN, kTiles[idx - 1].WM,     \
-                           kTiles[idx - 1].WN, kTiles[idx - 1].R>(q, inv, qsum, packed,      \
-                                                                  w_scale, M, K, N, y, acc, s);
+                           kTiles[idx - 1].WN, kTiles[idx - 1].R, kTiles[idx - 1].WK>(       \
+            q, inv, qsum, packed, w_scale, M, K, N, y, acc, s);
     switch (v) {
         BL_GEMM_CASE(1)
         BL_GEMM_CASE(2)
@@ -547,6 +612,14 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         BL_GEMM_CASE(21)
         BL_GEMM_CASE(22)
         BL_GEMM_CASE(23)
+        BL_GEMM_CASE(24)
+        BL_GEMM_CASE(25)
+        BL_GEMM_CASE(26)
+        BL_GEMM_CASE(27)
+        BL_GEMM_CASE(28)
+        BL_GEMM_CASE(29)
+        BL_GEMM_CASE(30)
+        BL_GEMM_CASE(31)
         default:
             return hipErrorInvalidValue;
     }
