@@ -195,7 +195,10 @@ FWD_SHAPES = [(1, 256, 256), (1, 2560, 640), (2, 384, 100), (3, 1024, 77), (4, 6
               (7, 512, 513), (10, 2560, 300), (12, 1024, 129), (15, 6912, 200), (16, 2560, 256),
               (17, 256, 64), (63, 640, 333), (64, 1024, 200), (100, 384, 90),
               (1, 1 << 22, 3), (3, 65536, 40),  # rows past 32768, up to the longest
-              (1, 128, 1 << 18), (20000, 256, 16)]  # a wide single token, a tall batch
+              (1, 128, 1 << 18), (20000, 256, 16),  # a wide single token, a tall batch
+              # 2..4 tokens past 64 KB of q (tile route, 16x32 tiles in k groups;
+              # the last with a half step of K and a step count that 4 does not divide)
+              (4, 28672, 100), (2, 40960, 48), (3, 22656, 50)]
 
 
 @pytest.mark.parametrize("M,K,N", FWD_SHAPES)
