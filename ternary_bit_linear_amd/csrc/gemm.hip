@@ -346,9 +346,10 @@ constexpr Tile kTiles[] = {{64, 256, 1, 4, 3}, {64, 128, 1, 4, 3}, {64, 64, 2, 2
                            {16, 32, 1, 2, 0},   {16, 64, 1, 4, 0},  {16, 32, 1, 2, 0, 2},
                            {16, 32, 1, 2, 0, 4}, {16, 32, 1, 2, 0, 8}, {16, 64, 1, 4, 0, 2},
                            {16, 64, 1, 4, 0, 4}, {16, 128, 1, 4, 0, 2}, {16, 16, 1, 1, 0, 4},
-                           {16, 16, 1, 1, 0, 8}};
+                           {16, 16, 1, 1, 0, 8}, {32, 64, 1, 4, 0, 2}, {32, 64, 1, 4, 0, 4},
+                           {64, 128, 1, 4, 0, 2}, {32, 128, 1, 4, 0, 2}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
-static_assert(kNumTiles == 31, "one BL_GEMM_CASE per table entry");
+static_assert(kNumTiles == 35, "one BL_GEMM_CASE per table entry");
 
 // Ring depth for a tile: the deepest of 4, 5, 3 that divides the step count
 // of one k group (no padded steps), else 4.  Depths whose ring does not fit
@@ -527,9 +528,14 @@ hipError_t launch_gemm_group(const GemmDesc *d, int count, hipStream_t s) {
         return g5 < g4 ? launch_group_tile<16, 32, 1, 2, 5, 4>(d, count, s)
                        : launch_group_tile<16, 32, 1, 2, 4, 4>(d, count, s);
     }
+    // The 64-row tiles from three quarters of a tile per CU (M = 64..128 at
+    // N = 28672, K = 8192: 64x128 over 32x128 at M = 64, 28.9 -> 25.1 us;
+    // 64x256 over 64x128 at M = 96 / 128, 35.7 -> 33.5 / 37.8 -> 34.9 us;
+    // M = 192, K = N = 8192: 64x128 over 32x128, 24.2 -> 23.6 us).
+    const int64_t most = 3 * (int64_t)device_cus() / 4;
     if (t64x512 >= 512) return launch_group_tile<64, 512, 1, 8, 4>(d, count, s);
-    if (k_avg >= 6144.0 && t64x256 >= 256) return launch_group_tile<64, 256, 1, 8, 4>(d, count, s);
-    if (t64x128 >= 256)
+    if (k_avg >= 6144.0 && t64x256 >= most) return launch_group_tile<64, 256, 1, 8, 4>(d, count, s);
+    if (t64x128 >= most)
         // Short rows (a few ring turns per tile): a 3-deep ring, so that two
         // workgroups share a CU and one's fill hides behind the other's
         // MFMAs (decoder layer at M = 512, K mostly 2560: 82 -> 75 us).
@@ -568,14 +574,18 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
             v = tiles(16, 128) >= 200 ? 20 : tiles(16, 64) >= 200 ? 23 : 25;
         else if (tiles(64, 512) >= 512)
             v = 15;
-        else if (K >= 6144 && tiles(64, 256) >= 256)
+        // The 64-row tiles from three quarters of a tile per CU, as in the
+        // grouped launch.  Past 16384-long rows the 32-row tiles run in k
+        // groups (K = 28672, N = 8192: M = 64 32x64 33.4 -> 31.1 us, M = 128
+        // 32x128 48.4 -> 45.6 us; at K = 8192 level or slower).
+        else if (K >= 6144 && tiles(64, 256) >= 3 * (int64_t)device_cus() / 4)
             v = 17;
-        else if (tiles(64, 128) >= 256)
+        else if (tiles(64, 128) >= 3 * (int64_t)device_cus() / 4)
             v = 9;
         else if (K > 4096 && tiles(32, 128) >= 256)
-            v = 5;
+            v = K >= 16384 ? 35 : 5;
         else
-            v = 4;
+            v = K >= 16384 ? 32 : 4;
     }
     if (v > kNumTiles) {
         // Variants past the 16 x 16 x 64 table: the 32 x 32 x 32 kernel's
@@ -620,6 +630,10 @@ hipError_t launch_gemm(const int8_t *q, const float *inv, const int32_t *qsum,
         BL_GEMM_CASE(29)
         BL_GEMM_CASE(30)
         BL_GEMM_CASE(31)
+        BL_GEMM_CASE(32)
+        BL_GEMM_CASE(33)
+        BL_GEMM_CASE(34)
+        BL_GEMM_CASE(35)
         default:
             return hipErrorInvalidValue;
     }

@@ -556,7 +556,8 @@ int gemm32_num_shapes() { return kNumShapes32; }
 // M = 512 36.7 against 40 us, M = 2048 126 against 145-153 us; K = 2560,
 // N = 6912 at M = 512 15.3 against 21 us.  With fewer than ~200 such tiles
 // (N = 2560 at M = 512, or M = 256 at N = 8192) the smaller tiles of the
-// 16 x 16 x 64 kernel fill the device better and stay faster.
+// 16 x 16 x 64 kernel fill the device better than these (for long rows the
+// 64 x 128 shape below beats both).
 constexpr int kAutoShape32 = 3;
 // With >= 512 tiles of 128 x 256 (two per CU), the wider tile halves the
 // activation traffic and wins (K = N = 8192 at M = 2048: 113-118 against
@@ -574,16 +575,47 @@ constexpr int kWideShape32 = 6;
 // not amortise the two groups' hand-off (K = 2560, N = 6912 at M = 512:
 // 15.4 against 14.4 us).
 constexpr int kSplitShape32 = 13;
+// 64 x 128 tiles, two blocks per step: for long rows at 128..255 tokens (or
+// 256 with too few 128 x 128 tiles) whose 64 x 128 tiles number between
+// three quarters of and one per CU.
+constexpr int kHalfShape32 = 12;
 constexpr int64_t kLongRowK = 4096;
 
-bool gemm32_preferred(const GemmDesc *d, int count) {
-    int64_t tiles = 0;
+// Shape the automatic choice takes for a set, or 0 where the 16 x 16 x 64
+// kernel's tiles are taken.  Where every M >= 256 with >= 200 tiles of
+// 128 x 128, the rules above.  Below that, long rows only (K >= 4096), at
+// M >= 128: the largest tile whose count lies between three quarters of
+// and one per CU (128 x 256, the two k groups of 128 x 128, 64 x 128), each
+// measured against the 16 x 16 x 64 kernel's choice (tile kernel alone over
+// q, us): M = 192, K = 8192, N = 28672 128 x 256 47.0 against 62.3; M = 128,
+// N = 28672 split 31.7 against 34.6; N = 8192, K = 8192 at M = 192 / 256
+// 64 x 128 21.3 / 21.7 against 23.5 / 23.8, K = 28672 at M = 192 59.3
+// against 62.2.  With more tiles than that (64 x 128 at M = 192, N = 28672:
+// 60.7 us) or fewer, the 16 x 16 x 64 tiles stay.
+int gemm32_auto_shape(const GemmDesc *d, int count) {
+    int64_t wide = 0, tiles = 0, half = 0, mmin = INT64_MAX;
+    bool even = true, long_rows = true;
     for (int i = 0; i < count; ++i) {
-        if (d[i].M < 256) return false;
+        wide += ((d[i].M + 127) / 128) * ((d[i].N + 255) / 256);
         tiles += ((d[i].M + 127) / 128) * ((d[i].N + 127) / 128);
+        half += ((d[i].M + 63) / 64) * ((d[i].N + 127) / 128);
+        mmin = std::min<int64_t>(mmin, d[i].M);
+        even = even && d[i].K % (2 * kBlk) == 0;
+        long_rows = long_rows && d[i].K >= kLongRowK;
     }
-    return tiles >= 200;
+    const int64_t cus = device_cus(), most = 3 * cus / 4;
+    if (mmin >= 256 && tiles >= 200)
+        return (wide >= 2 * cus || (long_rows && wide >= cus)) ? kWideShape32
+               : (even && long_rows && tiles <= cus)            ? kSplitShape32
+                                                                : kAutoShape32;
+    if (mmin < 128 || !long_rows) return 0;
+    if (wide >= most && wide <= cus) return kWideShape32;
+    if (even && tiles >= most && tiles <= cus) return kSplitShape32;
+    if (even && half >= most && half <= cus) return kHalfShape32;
+    return 0;
 }
+
+bool gemm32_preferred(const GemmDesc *d, int count) { return gemm32_auto_shape(d, count) != 0; }
 
 hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStream_t s) {
     if (count < 1 || count > kMaxG32) return hipErrorInvalidValue;
@@ -593,18 +625,8 @@ hipError_t launch_gemm32_group(const GemmDesc *d, int count, int shape, hipStrea
             return hipErrorInvalidValue;
     int v = shape;
     if (v <= 0 || v > kNumShapes32) {
-        int64_t wide = 0, tiles = 0;
-        bool even = true, long_rows = true;
-        for (int i = 0; i < count; ++i) {
-            wide += ((d[i].M + 127) / 128) * ((d[i].N + 255) / 256);
-            tiles += ((d[i].M + 127) / 128) * ((d[i].N + 127) / 128);
-            even = even && d[i].K % (2 * kBlk) == 0;
-            long_rows = long_rows && d[i].K >= kLongRowK;
-        }
-        const int cus = device_cus();
-        v = (wide >= 2 * cus || (long_rows && wide >= cus)) ? kWideShape32
-            : (even && long_rows && tiles <= cus)            ? kSplitShape32
-                                                             : kAutoShape32;
+        v = gemm32_auto_shape(d, count);
+        if (v == 0) v = kAutoShape32;
     }
     // Two blocks per step need an even block count in every row.
     if (kShapes32[v - 1].KB == 2)

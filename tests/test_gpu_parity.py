@@ -639,11 +639,14 @@ def test_workload_prefill_layer_batched(torch, bl, orc):
 
 
 @pytest.mark.parametrize("M,K,N", [(1024, 256, 2048), (64, 4352, 16384), (2048, 256, 8192),
-                                   (512, 6144, 8192)])
+                                   (512, 6144, 8192),
+                                   # 32x32x32 kernel below 256 tokens: 64x128 tiles,
+                                   # 128x128 in two k groups, 128x256 tiles
+                                   (192, 4096, 8192), (128, 4096, 24576), (192, 4096, 24576)])
 def test_forward_batch_group_tiles(torch, bl, orc, M, K, N):
-    """The grouped tile launch with each of its larger tile shapes (64x128,
-    32x128, 64x512, 64x256 by the group's tile counts): sampled outputs
-    against the oracle, all outputs bitwise against the single call."""
+    """The grouped tile launch with each of its larger tile shapes (by the
+    group's tile counts): sampled outputs against the oracle, all outputs
+    bitwise against the single call."""
     x, w, t, g = mm_case(M, K, N, 990 + M)
     packed_r, s = orc.pack_i2s(w)
     X, P, G = dev(torch, x), dev(torch, packed_r), dev(torch, g)
