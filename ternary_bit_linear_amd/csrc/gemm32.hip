@@ -575,7 +575,7 @@ constexpr int kWideShape32 = 6;
 // not amortise the two groups' hand-off (K = 2560, N = 6912 at M = 512:
 // 15.4 against 14.4 us).
 constexpr int kSplitShape32 = 13;
-// 64 x 128 tiles, two blocks per step: for long rows at 128..255 tokens (or
+// 64 x 128 tiles, two blocks per step: for long rows at 64..255 tokens (or
 // 256 with too few 128 x 128 tiles) whose 64 x 128 tiles number between
 // three quarters of and one per CU.
 constexpr int kHalfShape32 = 12;
@@ -583,15 +583,18 @@ constexpr int64_t kLongRowK = 4096;
 
 // Shape the automatic choice takes for a set, or 0 where the 16 x 16 x 64
 // kernel's tiles are taken.  Where every M >= 256 with >= 200 tiles of
-// 128 x 128, the rules above.  Below that, long rows only (K >= 4096), at
-// M >= 128: the largest tile whose count lies between three quarters of
-// and one per CU (128 x 256, the two k groups of 128 x 128, 64 x 128), each
-// measured against the 16 x 16 x 64 kernel's choice (tile kernel alone over
-// q, us): M = 192, K = 8192, N = 28672 128 x 256 47.0 against 62.3; M = 128,
-// N = 28672 split 31.7 against 34.6; N = 8192, K = 8192 at M = 192 / 256
-// 64 x 128 21.3 / 21.7 against 23.5 / 23.8, K = 28672 at M = 192 59.3
-// against 62.2.  With more tiles than that (64 x 128 at M = 192, N = 28672:
-// 60.7 us) or fewer, the 16 x 16 x 64 tiles stay.
+// 128 x 128, the rules above.  Below that, long rows only (K >= 4096): the
+// largest tile whose count lies between three quarters of and one per CU
+// (128 x 256 and the two k groups of 128 x 128 from M = 96, 64 x 128 from
+// M = 64), each measured against the 16 x 16 x 64 kernel's choice (tile
+// kernel alone over q, K = 8192 unless given, us): M = 192, N = 28672
+// 128 x 256 47.0 against 62.3; M = 96 / 128, N = 28672 split 30.2 / 31.7
+// against 33.6 / 34.6; N = 8192 at M = 192 / 256 64 x 128 21.3 / 21.7
+// against 23.5 / 23.8, K = 28672 at M = 192 59.3 against 62.2; M = 64,
+// N = 28672 64 x 128 23.3 against 25.0 (the 128-row tiles, half empty,
+// 28.4).  With more tiles than that (64 x 128 at M = 192, N = 28672: 60.7
+// us) or fewer (M = 64, N = 16384: 21.7 against 17.5), the 16 x 16 x 64
+// tiles stay.
 int gemm32_auto_shape(const GemmDesc *d, int count) {
     int64_t wide = 0, tiles = 0, half = 0, mmin = INT64_MAX;
     bool even = true, long_rows = true;
@@ -608,9 +611,9 @@ int gemm32_auto_shape(const GemmDesc *d, int count) {
         return (wide >= 2 * cus || (long_rows && wide >= cus)) ? kWideShape32
                : (even && long_rows && tiles <= cus)            ? kSplitShape32
                                                                 : kAutoShape32;
-    if (mmin < 128 || !long_rows) return 0;
-    if (wide >= most && wide <= cus) return kWideShape32;
-    if (even && tiles >= most && tiles <= cus) return kSplitShape32;
+    if (mmin < 64 || !long_rows) return 0;
+    if (mmin >= 96 && wide >= most && wide <= cus) return kWideShape32;
+    if (mmin >= 96 && even && tiles >= most && tiles <= cus) return kSplitShape32;
     if (even && half >= most && half <= cus) return kHalfShape32;
     return 0;
 }

@@ -642,7 +642,8 @@ def test_workload_prefill_layer_batched(torch, bl, orc):
                                    (512, 6144, 8192),
                                    # 32x32x32 kernel below 256 tokens: 64x128 tiles,
                                    # 128x128 in two k groups, 128x256 tiles
-                                   (192, 4096, 8192), (128, 4096, 24576), (192, 4096, 24576)])
+                                   (192, 4096, 8192), (128, 4096, 24576), (192, 4096, 24576),
+                                   (96, 4096, 16384)])
 def test_forward_batch_group_tiles(torch, bl, orc, M, K, N):
     """The grouped tile launch with each of its larger tile shapes (by the
     group's tile counts): sampled outputs against the oracle, all outputs
